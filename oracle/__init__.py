@@ -1,0 +1,247 @@
+"""NVFP4 quantization oracle -- TEST INFRASTRUCTURE ONLY.
+
+Python access (ctypes + numpy) to the plain C definition in
+``oracle/nvfp4_oracle.c``. Only the tests, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package; the GPU
+library never does, and this package never imports the GPU library.
+
+Every array argument is a host numpy array; outputs are returned as new
+numpy arrays in the layouts the C functions document:
+
+* row-wise data ``[rows][cols/2]`` (uint8), scales ``[rows][cols/16]``;
+* column-wise data ``[cols][rows/2]``, scales ``[cols][rows/16]``;
+* scales are compact; ``swizzle_scales`` gives the GEMM-swizzled layout.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+FP32 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc: binary32 arithmetic, no contraction, no fast-math."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-Wextra",
+            "-fPIC", "-shared", _SRC, "-o", tmp, "-lm",
+        ])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    U32 = ctypes.c_uint32
+    U8 = ctypes.c_uint8
+    F = ctypes.c_float
+    sig = {
+        "oracle_load": (F, [P, I, I64]),
+        "oracle_e2m1_value": (ctypes.c_double, [U8]),
+        "oracle_e2m1_rne": (U8, [F]),
+        "oracle_e2m1_sr": (U8, [F, ctypes.c_uint16]),
+        "oracle_e4m3_value": (ctypes.c_double, [U8]),
+        "oracle_e4m3_rne_satfinite": (U8, [F]),
+        "oracle_global_encode_scale": (F, [F]),
+        "oracle_block_scale": (U8, [F, F]),
+        "oracle_block_encode_multiplier": (F, [U8, F]),
+        "oracle_fmix32": (U32, [U32]),
+        "oracle_sr_word": (U32, [U32, I, U32]),
+        "oracle_rht16": (None, [P, U32, P]),
+        "oracle_rht_colwise": (None, [P, I, I64, I64, U32, P]),
+        "oracle_compute_amax": (None, [P, I, I64, I64, I, U32, P, P]),
+        "oracle_quantize": (I, [P, I, I64, I64, I, I, I, U32, I, U32, P, P, P, P, P, P]),
+        "oracle_swizzle_offset": (I64, [I64, I64, I64]),
+        "oracle_swizzle_scales": (I, [P, I64, I64, P]),
+        "oracle_dequantize": (None, [P, P, P, I, I64, I64, P]),
+        "oracle_e2m1_rne_array": (None, [P, I64, P]),
+        "oracle_e2m1_sr_array": (None, [P, P, I64, P]),
+        "oracle_e4m3_array": (None, [P, I64, P]),
+        "oracle_fmix32_array": (None, [P, I64, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _input(x):
+    """(contiguous array, dtype code) for a BF16 (uint16 bits) or FP32 host array."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, BF16
+    if x.dtype == np.float32:
+        return x, FP32
+    raise TypeError("oracle input must be uint16 (BF16 bits) or float32")
+
+
+# ---- scalar steps -------------------------------------------------------
+
+def e2m1_rne(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e2m1_rne_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e2m1_sr(v, r16) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    r16 = np.ascontiguousarray(np.broadcast_to(r16, v.shape), dtype=np.uint16)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e2m1_sr_array(_ptr(v), _ptr(r16), v.size, _ptr(out))
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return _load().oracle_e2m1_value(code)
+
+
+def e4m3(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e4m3_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return _load().oracle_e4m3_value(code)
+
+
+def global_encode_scale(amax: float) -> float:
+    return _load().oracle_global_encode_scale(amax)
+
+
+def block_scale(block_amax: float, S: float) -> int:
+    return _load().oracle_block_scale(block_amax, S)
+
+
+def block_encode_multiplier(s: int, S: float) -> float:
+    return _load().oracle_block_encode_multiplier(s, S)
+
+
+def fmix32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint32)
+    out = np.empty(h.shape, np.uint32)
+    _load().oracle_fmix32_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def sr_word(seed: int, direction: int, byte_index: int) -> int:
+    return _load().oracle_sr_word(seed, direction, byte_index)
+
+
+def rht16(w, sign_mask: int) -> np.ndarray:
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    assert w.shape == (16,)
+    t = np.empty(16, np.float32)
+    _load().oracle_rht16(_ptr(w), sign_mask, _ptr(t))
+    return t
+
+
+def swizzle_offset(r: int, c: int, scale_cols: int) -> int:
+    return _load().oracle_swizzle_offset(r, c, scale_cols)
+
+
+# ---- whole-tensor steps -------------------------------------------------
+
+def rht_colwise(x, sign_mask: int) -> np.ndarray:
+    """Column-wise RHT image t[cols][rows] of x[rows][cols] (rows % 16 == 0)."""
+    x, dt = _input(x)
+    rows, cols = x.shape
+    t = np.empty((cols, rows), np.float32)
+    _load().oracle_rht_colwise(_ptr(x), dt, rows, cols, sign_mask, _ptr(t))
+    return t
+
+
+AMAX_PER_TENSOR = 0
+AMAX_PER_ROW = 1
+AMAX_RHT = 2
+
+
+def compute_amax(x, mode: int = AMAX_PER_TENSOR, sign_mask: int = 0):
+    """Returns (amax_row, amax_col): [1] and [1], or [rows] and None per row."""
+    x, dt = _input(x)
+    rows, cols = x.shape
+    if mode == AMAX_PER_ROW:
+        a = np.empty(rows, np.float32)
+        _load().oracle_compute_amax(_ptr(x), dt, rows, cols, mode, sign_mask, _ptr(a), None)
+        return a, None
+    a = np.empty(1, np.float32)
+    b = np.empty(1, np.float32)
+    _load().oracle_compute_amax(_ptr(x), dt, rows, cols, mode, sign_mask, _ptr(a), _ptr(b))
+    return a, b
+
+
+def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=False, rht=False,
+             sign_mask=0, stochastic=False, sr_seed=0, amax_row=None, amax_col=None):
+    """Quantize with the given amaxes (computed here when None).
+
+    Returns a dict with ``row_data``, ``row_scales``, ``col_data``,
+    ``col_scales`` (compact; absent directions are None), ``amax_row``,
+    ``amax_col``.
+    """
+    x, dt = _input(x)
+    rows, cols = x.shape
+    if amax_row is None and amax_col is None:
+        mode = AMAX_PER_ROW if row_scaled else (AMAX_RHT if rht else AMAX_PER_TENSOR)
+        amax_row, amax_col = compute_amax(x, mode, sign_mask)
+    amax_row = None if amax_row is None else np.ascontiguousarray(amax_row, np.float32)
+    amax_col = None if amax_col is None else np.ascontiguousarray(amax_col, np.float32)
+    rd = np.empty((rows, cols // 2), np.uint8) if rowwise else None
+    rs = np.empty((rows, cols // 16), np.uint8) if rowwise else None
+    cd = np.empty((cols, rows // 2), np.uint8) if columnwise else None
+    cs = np.empty((cols, rows // 16), np.uint8) if columnwise else None
+    rc = _load().oracle_quantize(
+        _ptr(x), dt, rows, cols, int(block_2d), int(row_scaled), int(rht), sign_mask,
+        int(stochastic), sr_seed, _ptr(amax_row) if rowwise else None,
+        _ptr(amax_col) if columnwise else None, _ptr(rd), _ptr(rs), _ptr(cd), _ptr(cs))
+    if rc != 0:
+        raise ValueError("unsupported oracle configuration")
+    return {"row_data": rd, "row_scales": rs, "col_data": cd, "col_scales": cs,
+            "amax_row": amax_row if rowwise else None, "amax_col": amax_col if columnwise else None}
+
+
+def swizzle_scales(compact) -> np.ndarray:
+    """Compact [rows][scale_cols] -> GEMM-swizzled flat array (rows % 128, scale_cols % 4)."""
+    compact = np.ascontiguousarray(compact, np.uint8)
+    rows, sc = compact.shape
+    out = np.empty(rows * sc, np.uint8)
+    if _load().oracle_swizzle_scales(_ptr(compact), rows, sc, _ptr(out)) != 0:
+        raise ValueError("swizzled layout needs rows % 128 == 0 and scale_cols % 4 == 0")
+    return out
+
+
+def dequantize(data, scales, amax, rows: int, cols: int, row_scaled: bool = False) -> np.ndarray:
+    """One direction, its own orientation [rows][cols], compact scales."""
+    data = np.ascontiguousarray(data, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    amax = np.ascontiguousarray(amax, np.float32)
+    y = np.empty((rows, cols), np.float32)
+    _load().oracle_dequantize(_ptr(data), _ptr(scales), _ptr(amax), int(row_scaled), rows, cols, _ptr(y))
+    return y
