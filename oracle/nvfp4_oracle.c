@@ -129,11 +129,18 @@ double oracle_e4m3_value(uint8_t code) {
 /* Round-to-nearest-even to E4M3 with saturation to the largest finite
  * value 448 (code 0x7E); the argument is a non-negative block scale, so the
  * sign bit is always 0 and NaN is never produced. */
+static double e4m3_table[0x7F];
+static int e4m3_table_ready = 0;
+
 uint8_t oracle_e4m3_rne_satfinite(float sd) {
+  if (!e4m3_table_ready) { /* the decoded values of codes 0x00..0x7E, once */
+    for (int k = 0; k < 0x7F; ++k) e4m3_table[k] = oracle_e4m3_value((uint8_t)k);
+    e4m3_table_ready = 1;
+  }
   double a = (double)sd;
   for (int k = 0; k < 0x7E; ++k) {
-    double lo = oracle_e4m3_value((uint8_t)k);
-    double hi = oracle_e4m3_value((uint8_t)(k + 1));
+    double lo = e4m3_table[k];
+    double hi = e4m3_table[k + 1];
     double mid = 0.5 * (lo + hi); /* exact in binary64 */
     if (a < mid) return (uint8_t)k;
     if (a == mid) return (uint8_t)((k % 2 == 0) ? k : k + 1);
