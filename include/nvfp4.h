@@ -1,0 +1,191 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 quantize library.
+ *
+ * NVFP4 stores a tensor as 4-bit E2M1 values, packed two per byte, with one
+ * FP8 E4M3 decode scale per 16 values and one FP32 amax per tensor (or per
+ * row) from which a global encode scale is derived. One quantize call can
+ * write both orientations of the tensor: the row-wise one (the tensor as
+ * stored) and the column-wise one (its transpose), each with its own data,
+ * scales and amax buffer.
+ *
+ * The operations follow three TransformerEngine pull-request pages:
+ *   "Write both NVFP4 amax buffers" (PR #3750): one reduction fills both
+ *     amax buffers after a zeroing pass clears both (Description, Changes);
+ *   "Fuse NVFP4 scale swizzling on SM120 and SM121" (PR #3749): scales are
+ *     written directly in the GEMM-swizzled layout when rows and columns
+ *     are multiples of 128 (Description, Changes);
+ *   "Implement row-scaled NVFP4 fprop recipe" (PR #2931): one amax per row,
+ *     row-wise output only, compact scales (Description, Changes, summary).
+ *
+ * Conventions for every call:
+ *   - Tensors are row-major. Device buffers are owned by the caller; the
+ *     library allocates nothing, keeps no state between calls, and never
+ *     synchronizes: work is queued on `stream` (a hipStream_t; NULL means
+ *     the null stream) and runs asynchronously. Pointers are never stored,
+ *     so calls can be captured in a HIP graph.
+ *   - Arguments are validated on the host before anything is queued. On a
+ *     bad argument the call returns a non-zero status, queues nothing and
+ *     writes nothing; nvfp4_last_error() then describes the problem.
+ *   - A failure reported by the HIP runtime at launch returns NVFP4_ERR_HIP.
+ *     Errors inside kernels are not detected (inputs are assumed finite).
+ *   - No call throws across the ABI.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,       /* rows/cols not supported by the requested layout */
+  NVFP4_ERR_ALIGN = 3,       /* a pointer is not aligned as required */
+  NVFP4_ERR_UNSUPPORTED = 4, /* an option or a combination of options is not supported */
+  NVFP4_ERR_HIP = 5          /* the HIP runtime reported an error */
+} nvfp4_status_t;
+
+typedef enum {
+  NVFP4_IN_BF16 = 0, /* input elements are bfloat16 */
+  NVFP4_IN_FP32 = 1  /* input elements are float */
+} nvfp4_dtype_t;
+
+typedef enum {
+  /* scales of one orientation [n][k] stored row-major as [n][k/16] bytes */
+  NVFP4_SCALES_COMPACT = 0,
+  /* the GEMM layout: the [n][k/16] scale matrix cut into tiles of 128 rows
+   * by 4 scale columns, tiles in row-major order, 512 bytes each; inside a
+   * tile, scale (r, c) sits at byte (r % 32) * 16 + (r % 128) / 32 * 4 + c % 4.
+   * Needs n % 128 == 0 and k % 128 == 0 ("Fuse NVFP4 scale swizzling ...",
+   * Description and Changes: the 128x128 alignment, and four aligned
+   * scales written as one 32-bit word). */
+  NVFP4_SCALES_GEMM_SWIZZLED = 1
+} nvfp4_scale_layout_t;
+
+typedef enum {
+  NVFP4_SCALE_E4M3 = 0, /* OCP E4M3 (bias 7, max 448), round to nearest even, saturating */
+  NVFP4_SCALE_UE5M3 = 1 /* named on "Fuse NVFP4 scale swizzling ..." (Changes) but not
+                           defined there: rejected with NVFP4_ERR_UNSUPPORTED */
+} nvfp4_scale_fmt_t;
+
+/* One orientation of an NVFP4 tensor. For the row-wise orientation of an
+ * R x C input, n = R and k = C; for the column-wise one, n = C and k = R
+ * (row j of the column-wise tensor is column j of the input).
+ *   data   [n][k/2] bytes: element 2i in the low nibble of byte i, element
+ *          2i+1 in the high nibble; E2M1 code = sign bit 3, magnitude
+ *          index 0..7 for {0, 0.5, 1, 1.5, 2, 3, 4, 6}. 16-byte aligned.
+ *   scales E4M3 bytes, compact [n][k/16] or GEMM-swizzled (n*k/16 bytes).
+ *          4-byte aligned.
+ *   amax   FP32: [1] per tensor, or [n] with row scaling. 4-byte aligned. */
+typedef struct {
+  uint8_t *data;
+  uint8_t *scales;
+  float *amax;
+} nvfp4_out_t;
+
+/* Options of a call. A NULL config means all fields zero except
+ * compute_amax = 1. */
+typedef struct {
+  /* 0: 1x16 blocks along each orientation's rows. 1: 16x16 blocks with one
+   * scale shared by both orientations ("Write both NVFP4 amax buffers",
+   * Changes: 1D and 2D quantization). Needs R % 16 == 0. */
+  uint32_t block_2d;
+  /* nvfp4_scale_layout_t, for every orientation the call writes. */
+  uint32_t scale_layout;
+  /* nvfp4_scale_fmt_t. */
+  uint32_t scale_fmt;
+  /* 0: E2M1 round to nearest even. 1: stochastic rounding: value |v| between
+   * grid neighbours lo < hi rounds up when r16 < 65536 * (|v| - lo) / (hi - lo),
+   * with r16 = 16 bits of w = fmix32(K ^ b) (low half for the byte's even
+   * element, high half for the odd one), b the byte's index in that
+   * orientation's data array, K = fmix32(fmix32(sr_seed) ^ (1 + orientation)),
+   * orientation 0 = row-wise, 1 = column-wise, and fmix32 the MurmurHash3
+   * 32-bit finalizer. Scales always use nearest even. */
+  uint32_t stochastic;
+  uint32_t sr_seed;
+  /* 1: one amax per row of the input ("Implement row-scaled NVFP4 fprop
+   * recipe", Changes): row-wise orientation only, 1x16 blocks, compact
+   * scales, no RHT; row->amax holds R floats. */
+  uint32_t row_scaled;
+  /* 1: the column-wise orientation encodes the 16-point random Hadamard
+   * transform of each group of 16 consecutive rows of a column: with
+   * w_k = sigma_k * x[16g + k][j], sigma_k = -1 where bit k of rht_sign_mask
+   * is set, t_r = 1/4 * sum_k (-1)^popcount(r & k) * w_k takes position
+   * 16g + r, and col->amax = max|t| ("Write both NVFP4 amax buffers", GPU
+   * work per quantize call and review thread). The row-wise orientation and
+   * row->amax stay plain. Needs block_2d == 0. */
+  uint32_t rht;
+  uint32_t rht_sign_mask;
+  /* nvfp4_quantize only. 1: zero the amax buffers and reduce them inside the
+   * call. 0: use the amax buffers as they are (for instance after a MAX
+   * all-reduce across devices). */
+  uint32_t compute_amax;
+  /* Device pointer or NULL. When *noop == 1.0f the call writes nothing, amax
+   * buffers included ("Write both NVFP4 amax buffers", Changes). */
+  const float *noop;
+} nvfp4_config_t;
+
+/*
+ * Amax reduction ("Write both NVFP4 amax buffers", Description and Changes).
+ * x: device, R x C elements of `dtype`, 16-byte aligned, C % 16 == 0,
+ * R * C < 2^32.
+ *   default:   both buffers are set to +0 and then to max|x| by one
+ *              reduction; either pointer may be NULL; equal pointers are
+ *              written once.
+ *   row_scaled: row_amax[i] = max_j |x[i][j]| for each of R rows;
+ *              col_amax must be NULL.
+ *   rht:       row_amax = max|x|, col_amax = max|t| over the column-wise
+ *              RHT image (needs R % 16 == 0), both from one read of x.
+ * An empty input (R == 0 or C == 0) writes +0.
+ */
+nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                  float *row_amax, float *col_amax, const nvfp4_config_t *cfg,
+                                  void *stream);
+
+/*
+ * Quantize x (R x C, device, 16-byte aligned, C % 16 == 0, R * C < 2^32)
+ * into the requested orientations; row or col may be NULL, not both. The
+ * column-wise orientation needs R % 16 == 0.
+ *
+ * Per orientation: S = 2688 / amax (1 when amax == 0, at most FLT_MAX);
+ * per block of 16 (or 16x16): m = max|v|, scale s = E4M3(fl(m / 6) * S),
+ * multiplier e = S / s (0 when s == 0, at most FLT_MAX), code =
+ * E2M1(fl(v * e)), each step one correctly rounded FP32 operation.
+ *
+ * With compute_amax == 1 this queues the zeroing pass, the amax reduction
+ * and the cast (row-scaled: one fused kernel); with compute_amax == 0 only
+ * the cast, which reads the amax buffers as given.
+ */
+nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                              const nvfp4_out_t *row, const nvfp4_out_t *col,
+                              const nvfp4_config_t *cfg, void *stream);
+
+/*
+ * Dequantize one orientation q (n = rows, k = cols in q's own orientation,
+ * k % 16 == 0) into y [rows][cols] FP32 (device, 4-byte aligned):
+ * y = (value(code) * value(s)) / S, S from q->amax[0], or q->amax[i] for
+ * row i when row_scaled ("Implement row-scaled NVFP4 fprop recipe",
+ * Changes: the dequantize kernel selects the row's amax).
+ */
+nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols,
+                                uint32_t scale_layout, uint32_t row_scaled, float *y, void *stream);
+
+/* Text for the last non-OK status returned on the calling thread ("" when
+ * none). The pointer stays valid until the next call on that thread. */
+const char *nvfp4_last_error(void);
+
+/*
+ * Test hook: the column-wise RHT image t [cols][rows] FP32 (device) of x,
+ * computed by the same device code as the quantize kernels. R % 16 == 0.
+ */
+nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t dtype, int64_t rows,
+                                       int64_t cols, uint32_t sign_mask, float *t, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

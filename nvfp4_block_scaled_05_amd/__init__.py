@@ -1,0 +1,209 @@
+"""Python binding of the MI355X NVFP4 quantize library (``libnvfp4.so``).
+
+Thin ctypes marshalling over the C ABI declared in ``include/nvfp4.h``; the
+functions keep the C names. Every step of the quantize path runs in the
+library's HIP kernels; torch only supplies device memory and the current
+stream. If the library is missing or cannot be loaded, every call raises:
+there is no fallback.
+
+Tensors passed in are torch CUDA tensors (on ROCm, HIP devices):
+  x         bfloat16 or float32, 2-D, contiguous
+  data      uint8 [n][k/2]      scales  uint8 (compact [n][k/16] or swizzled, flat)
+  amax      float32 [1] or [n]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+_LIB_PATH = _build.LIB
+
+NVFP4_OK = 0
+NVFP4_ERR_NULL = 1
+NVFP4_ERR_SHAPE = 2
+NVFP4_ERR_ALIGN = 3
+NVFP4_ERR_UNSUPPORTED = 4
+NVFP4_ERR_HIP = 5
+
+NVFP4_IN_BF16 = 0
+NVFP4_IN_FP32 = 1
+
+NVFP4_SCALES_COMPACT = 0
+NVFP4_SCALES_GEMM_SWIZZLED = 1
+
+NVFP4_SCALE_E4M3 = 0
+NVFP4_SCALE_UE5M3 = 1
+
+EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
+            "nvfp4_debug_rht_colwise")
+
+
+class nvfp4_out_t(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("amax", ctypes.c_void_p)]
+
+
+class nvfp4_config_t(ctypes.Structure):
+    _fields_ = [
+        ("block_2d", ctypes.c_uint32),
+        ("scale_layout", ctypes.c_uint32),
+        ("scale_fmt", ctypes.c_uint32),
+        ("stochastic", ctypes.c_uint32),
+        ("sr_seed", ctypes.c_uint32),
+        ("row_scaled", ctypes.c_uint32),
+        ("rht", ctypes.c_uint32),
+        ("rht_sign_mask", ctypes.c_uint32),
+        ("compute_amax", ctypes.c_uint32),
+        ("noop", ctypes.c_void_p),
+    ]
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"nvfp4 status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load(build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load libnvfp4.so (building it first only when it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError(f"{_LIB_PATH} is not built")
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    U32 = ctypes.c_uint32
+    I = ctypes.c_int
+    lib.nvfp4_compute_amax.restype = I
+    lib.nvfp4_compute_amax.argtypes = [P, I, I64, I64, P, P, ctypes.POINTER(nvfp4_config_t), P]
+    lib.nvfp4_quantize.restype = I
+    lib.nvfp4_quantize.argtypes = [P, I, I64, I64, ctypes.POINTER(nvfp4_out_t), ctypes.POINTER(nvfp4_out_t),
+                                   ctypes.POINTER(nvfp4_config_t), P]
+    lib.nvfp4_dequantize.restype = I
+    lib.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_out_t), I64, I64, U32, U32, P, P]
+    lib.nvfp4_last_error.restype = ctypes.c_char_p
+    lib.nvfp4_last_error.argtypes = []
+    lib.nvfp4_debug_rht_colwise.restype = I
+    lib.nvfp4_debug_rht_colwise.argtypes = [P, I, I64, I64, U32, P, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != NVFP4_OK:
+        raise NVFP4Error(status, nvfp4_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return NVFP4_IN_BF16
+    if x.dtype == torch.float32:
+        return NVFP4_IN_FP32
+    raise TypeError(f"input must be bfloat16 or float32, got {x.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _shape2d(x: torch.Tensor):
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    return x.shape[0], x.shape[1]
+
+
+def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, stochastic=False, sr_seed=0,
+                row_scaled=False, rht=False, rht_sign_mask=0, compute_amax=True,
+                noop: Optional[torch.Tensor] = None) -> nvfp4_config_t:
+    return nvfp4_config_t(int(block_2d), NVFP4_SCALES_GEMM_SWIZZLED if swizzled else NVFP4_SCALES_COMPACT,
+                          int(scale_fmt), int(stochastic), int(sr_seed) & 0xFFFFFFFF, int(row_scaled), int(rht),
+                          int(rht_sign_mask) & 0xFFFFFFFF, int(compute_amax),
+                          None if noop is None else noop.data_ptr())
+
+
+@dataclasses.dataclass
+class Orientation:
+    """One orientation of an NVFP4 tensor: data [n][k/2], scales, amax."""
+    data: torch.Tensor
+    scales: torch.Tensor
+    amax: torch.Tensor
+
+    def as_c(self) -> nvfp4_out_t:
+        return nvfp4_out_t(self.data.data_ptr(), self.scales.data_ptr(), self.amax.data_ptr())
+
+
+def nvfp4_last_error() -> str:
+    return load().nvfp4_last_error().decode()
+
+
+def nvfp4_compute_amax(x: torch.Tensor, row_amax: Optional[torch.Tensor], col_amax: Optional[torch.Tensor],
+                       cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
+    rows, cols = _shape2d(x)
+    _check(load().nvfp4_compute_amax(_ptr(x), _dtype_code(x), rows, cols, _ptr(row_amax), _ptr(col_amax),
+                                     None if cfg is None else ctypes.byref(cfg), _stream(stream)))
+
+
+def nvfp4_quantize(x: torch.Tensor, row: Optional[Orientation], col: Optional[Orientation],
+                   cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
+    rows, cols = _shape2d(x)
+    r = row.as_c() if row is not None else None
+    c = col.as_c() if col is not None else None
+    _check(load().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, None if r is None else ctypes.byref(r),
+                                 None if c is None else ctypes.byref(c), None if cfg is None else ctypes.byref(cfg),
+                                 _stream(stream)))
+
+
+def nvfp4_dequantize(q: Orientation, rows: int, cols: int, scale_layout: int, row_scaled: bool, y: torch.Tensor,
+                     stream=None) -> None:
+    qc = q.as_c()
+    _check(load().nvfp4_dequantize(ctypes.byref(qc), rows, cols, scale_layout, int(row_scaled), _ptr(y),
+                                   _stream(stream)))
+
+
+def nvfp4_debug_rht_colwise(x: torch.Tensor, sign_mask: int, t: torch.Tensor, stream=None) -> None:
+    rows, cols = _shape2d(x)
+    _check(load().nvfp4_debug_rht_colwise(_ptr(x), _dtype_code(x), rows, cols, sign_mask & 0xFFFFFFFF, _ptr(t),
+                                          _stream(stream)))
+
+
+# ---- allocation helpers (device memory only; no arithmetic) -----------------
+
+def empty_orientation(n: int, k: int, device, amax_len: int = 1) -> Orientation:
+    """Uninitialized buffers for one orientation with n rows of k elements."""
+    return Orientation(torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+                       torch.empty((n * (k // 16),), dtype=torch.uint8, device=device),
+                       torch.empty((amax_len,), dtype=torch.float32, device=device))
+
+
+def quantize(x: torch.Tensor, *, rowwise=True, columnwise=True, cfg: Optional[nvfp4_config_t] = None,
+             stream=None):
+    """Allocate outputs for x [R][C] and run nvfp4_quantize. Returns (row, col)."""
+    rows, cols = _shape2d(x)
+    cfg = cfg if cfg is not None else make_config()
+    row = empty_orientation(rows, cols, x.device, rows if cfg.row_scaled else 1) if rowwise else None
+    col = empty_orientation(cols, rows, x.device) if columnwise else None
+    nvfp4_quantize(x, row, col, cfg, stream)
+    return row, col

@@ -1,0 +1,207 @@
+// Amax kernels: the zeroing pass, the per-tensor max|x| reduction that fills
+// both amax buffers, and the RHT pair (max|x| and max|RHT(x)|) from one read.
+//
+// "Write both NVFP4 amax buffers" (Description, Changes): the zeroing kernel
+// clears both buffers and every block applies its atomic max to both, so no
+// copy and no second read are needed. Max is exact and order-free; on
+// non-negative binary32 values an unsigned integer max of the bit patterns
+// is the float max, so each workgroup ends with one global_atomic_umax per
+// buffer on the +0.0 that the zeroing pass wrote.
+#include "codec.h"
+#include "launch.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bool noop_set(const float *noop) { return noop != nullptr && *noop == 1.0f; }
+
+// max over the 256 threads of a workgroup (values are float bit patterns of
+// non-negative numbers, so unsigned max == float max). Result valid in all threads.
+__device__ __forceinline__ uint32_t block_umax(uint32_t v, uint32_t *lds4) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds4[wave] = v;
+  __syncthreads();
+  v = max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]));
+  return v;
+}
+
+__global__ void k_zero_amax(float *a, float *b, const float *noop) {
+  if (noop_set(noop)) return;
+  if (threadIdx.x == 0) {
+    if (a) *a = 0.0f;
+    if (b) *b = 0.0f;
+  }
+}
+
+// Per-tensor amax. nvec = number of 16-byte vectors of x.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a,
+                                                   float *b, const float *noop) {
+  __shared__ uint32_t lds4[4];
+  if (noop_set(noop)) return;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t m32 = 0;               // FP32: max of |x| bit patterns
+  ushort2_t m16 = {0, 0};         // BF16: max of 15-bit magnitudes, two lanes
+  auto take = [&](const uint4 &v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (DT == kBF16) {
+        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[k] & 0x7FFF7FFFu));
+      } else {
+        m32 = max(m32, w[k] & 0x7FFFFFFFu);
+      }
+    }
+  };
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    uint4 v0 = *(x + i);
+    uint4 v1 = *(x + i + stride);
+    uint4 v2 = *(x + i + 2 * stride);
+    uint4 v3 = *(x + i + 3 * stride);
+    take(v0);
+    take(v1);
+    take(v2);
+    take(v3);
+  }
+  for (; i < nvec; i += stride) take(x[i]);
+  uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
+  m = block_umax(m, lds4);
+  if (threadIdx.x == 0) {
+    if (a) atomicMax(reinterpret_cast<unsigned int *>(a), m);
+    if (b && b != a) atomicMax(reinterpret_cast<unsigned int *>(b), m);
+  }
+}
+
+// Load the 16 x VEC values of one thread's column strip (rows g*16 .. +15,
+// columns c .. c+VEC-1) as floats v[col][row].
+template <int DT, int VEC>
+__device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_t r0, uint32_t c,
+                                           float (&v)[VEC][16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint64_t off = static_cast<uint64_t>(r0 + r) * cols + c;
+    if (DT == kBF16) {
+      const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k][r] = bf16_lo(w[k]);
+        v[2 * k + 1][r] = bf16_hi(w[k]);
+      }
+    } else {
+      const float4 q = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
+      v[0][r] = q.x;
+      v[1][r] = q.y;
+      v[2][r] = q.z;
+      v[3][r] = q.w;
+    }
+  }
+}
+
+// RHT amax pair. Grid: (ceil(cols / (256 * VEC)), rows / 16). Each thread
+// takes VEC adjacent columns of one 16-row group: max|x| over the raw values,
+// max|t| over their 16-point transforms.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
+                                                       uint32_t mask, float *row_amax, float *col_amax,
+                                                       const float *noop) {
+  constexpr int VEC = DT == kBF16 ? 8 : 4;
+  __shared__ uint32_t lds4[4];
+  if (noop_set(noop)) return;
+  const uint32_t c = (blockIdx.x * kThreads + threadIdx.x) * VEC;
+  const uint32_t r0 = blockIdx.y * 16;
+  uint32_t mx = 0, mt = 0;
+  if (c < cols) {
+    float v[VEC][16];
+    load_strip<DT, VEC>(x, cols, r0, c, v);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = max(mx, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
+      rht16(v[j], mask);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = max(mt, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
+    }
+  }
+  mx = block_umax(mx, lds4);
+  __syncthreads();
+  mt = block_umax(mt, lds4);
+  if (threadIdx.x == 0) {
+    if (row_amax) atomicMax(reinterpret_cast<unsigned int *>(row_amax), mx);
+    if (col_amax) atomicMax(reinterpret_cast<unsigned int *>(col_amax), mt);
+  }
+}
+
+// Column-wise RHT image t[cols][rows] (test hook; same transform code).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_debug_rht(const void *__restrict__ x, uint32_t rows, uint32_t cols,
+                                                        uint32_t mask, float *__restrict__ t) {
+  constexpr int VEC = DT == kBF16 ? 8 : 4;
+  const uint32_t c = (blockIdx.x * kThreads + threadIdx.x) * VEC;
+  const uint32_t r0 = blockIdx.y * 16;
+  if (c >= cols) return;
+  float v[VEC][16];
+  load_strip<DT, VEC>(x, cols, r0, c, v);
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    rht16(v[j], mask);
+    float4 *dst = reinterpret_cast<float4 *>(t + static_cast<uint64_t>(c + j) * rows + r0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[j][4 * q], v[j][4 * q + 1], v[j][4 * q + 2], v[j][4 * q + 3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero_amax(float *a, float *b, const float *noop, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_amax, dim3(1), dim3(64), 0, s, a, b, noop);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b, const float *noop,
+                       hipStream_t s) {
+  const uint64_t nvec = n * (dtype == kBF16 ? 2 : 4) / 16;
+  if (nvec == 0) return hipSuccess;
+  uint64_t blocks = (nvec + kThreads * 4 - 1) / (kThreads * 4);
+  if (blocks > 2048) blocks = 2048;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_amax<kBF16>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s,
+                       static_cast<const uint4 *>(x), nvec, a, b, noop);
+  else
+    hipLaunchKernelGGL(k_amax<kFP32>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s,
+                       static_cast<const uint4 *>(x), nvec, a, b, noop);
+  return hipGetLastError();
+}
+
+hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t cols, uint32_t mask,
+                           float *row_amax, float *col_amax, const float *noop, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const uint32_t vec = dtype == kBF16 ? 8 : 4;
+  dim3 grid((cols + kThreads * vec - 1) / (kThreads * vec), rows / 16);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_rht_amax<kBF16>, grid, dim3(kThreads), 0, s, x, rows, cols, mask, row_amax, col_amax, noop);
+  else
+    hipLaunchKernelGGL(k_rht_amax<kFP32>, grid, dim3(kThreads), 0, s, x, rows, cols, mask, row_amax, col_amax, noop);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_rht(const void *x, int dtype, uint32_t rows, uint32_t cols, uint32_t mask, float *t,
+                            hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const uint32_t vec = dtype == kBF16 ? 8 : 4;
+  dim3 grid((cols + kThreads * vec - 1) / (kThreads * vec), rows / 16);
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_debug_rht<kBF16>, grid, dim3(kThreads), 0, s, x, rows, cols, mask, t);
+  else
+    hipLaunchKernelGGL(k_debug_rht<kFP32>, grid, dim3(kThreads), 0, s, x, rows, cols, mask, t);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,208 @@
+// C ABI of the NVFP4 quantize library: host-side validation and dispatch.
+//
+// Every argument is checked before anything is queued, so a rejected call
+// writes nothing. The gates follow the pages: swizzled scales need 128x128
+// alignment and partial tiles are rejected ("Fuse NVFP4 scale swizzling on
+// SM120 and SM121", Changes and Validation); row-scaled NVFP4 is row-wise,
+// compact and not combined with the RHT ("Implement row-scaled NVFP4 fprop
+// recipe", Changes; "Fuse NVFP4 scale swizzling ...", Changes); an RHT
+// quantize cannot share one float between its two amaxes ("Write both NVFP4
+// amax buffers", review thread).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+#include "nvfp4.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nvfp4_status_t fail(nvfp4_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+nvfp4_config_t config_or_default(const nvfp4_config_t *cfg) {
+  if (cfg) return *cfg;
+  nvfp4_config_t c{};
+  c.compute_amax = 1;
+  return c;
+}
+
+nvfp4_status_t hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared checks of an input matrix.
+nvfp4_status_t check_input(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols) {
+  if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_FP32)
+    return fail(NVFP4_ERR_UNSUPPORTED, "input dtype %d is not BF16 (0) or FP32 (1)", static_cast<int>(dtype));
+  if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape %lld x %lld", (long long)rows, (long long)cols);
+  if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 16", (long long)cols);
+  if (rows > 0 && cols > 0 && rows * cols >= (int64_t{1} << 32))
+    return fail(NVFP4_ERR_SHAPE, "rows * cols = %lld must be below 2^32", (long long)(rows * cols));
+  if (rows * cols > 0 && x == nullptr) return fail(NVFP4_ERR_NULL, "input pointer is NULL");
+  if (x != nullptr && !aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "input pointer is not 16-byte aligned");
+  return NVFP4_OK;
+}
+
+// An empty tensor may come with NULL data and scales; amax is always written.
+nvfp4_status_t check_out(const nvfp4_out_t *o, const char *name, bool empty) {
+  if (o->amax == nullptr) return fail(NVFP4_ERR_NULL, "%s output has a NULL amax pointer", name);
+  if (!empty && (o->data == nullptr || o->scales == nullptr))
+    return fail(NVFP4_ERR_NULL, "%s output has a NULL data or scales pointer", name);
+  if (!aligned(o->data, 16)) return fail(NVFP4_ERR_ALIGN, "%s data is not 16-byte aligned", name);
+  if (!aligned(o->scales, 4)) return fail(NVFP4_ERR_ALIGN, "%s scales are not 4-byte aligned", name);
+  if (!aligned(o->amax, 4)) return fail(NVFP4_ERR_ALIGN, "%s amax is not 4-byte aligned", name);
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" const char *nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                             float *row_amax, float *col_amax, const nvfp4_config_t *cfg_in,
+                                             void *stream) {
+  nvfp4_status_t st = check_input(x, dtype, rows, cols);
+  if (st != NVFP4_OK) return st;
+  const nvfp4_config_t cfg = config_or_default(cfg_in);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (row_amax == nullptr && col_amax == nullptr) return fail(NVFP4_ERR_NULL, "both amax pointers are NULL");
+  if ((row_amax && !aligned(row_amax, 4)) || (col_amax && !aligned(col_amax, 4)))
+    return fail(NVFP4_ERR_ALIGN, "amax pointers must be 4-byte aligned");
+  if (cfg.row_scaled && cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled amax cannot be combined with the RHT");
+  if (cfg.row_scaled) {
+    if (col_amax != nullptr)
+      return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled amax is row-wise only: col_amax must be NULL");
+    if (row_amax == nullptr) return fail(NVFP4_ERR_NULL, "row-scaled amax needs row_amax");
+    nvfp4::RowScaledArgs a{x, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), nullptr, nullptr,
+                           row_amax, 0u, cfg.noop};
+    return hip_status(nvfp4::launch_rowscaled(a, dtype, false, true, s), "row amax launch");
+  }
+  if (cfg.rht) {
+    if (rows % 16 != 0) return fail(NVFP4_ERR_SHAPE, "the RHT needs rows %% 16 == 0 (rows = %lld)", (long long)rows);
+    if (row_amax != nullptr && row_amax == col_amax)
+      return fail(NVFP4_ERR_UNSUPPORTED, "the RHT amax pair needs two distinct buffers");
+  }
+  float *b = (col_amax == row_amax) ? nullptr : col_amax;
+  float *a = row_amax ? row_amax : col_amax;
+  if (a == col_amax) b = nullptr;
+  st = hip_status(nvfp4::launch_zero_amax(a, b, cfg.noop, s), "zero amax launch");
+  if (st != NVFP4_OK || rows * cols == 0) return st;
+  if (cfg.rht)
+    return hip_status(nvfp4::launch_rht_amax(x, dtype, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols),
+                                             cfg.rht_sign_mask, row_amax, col_amax, cfg.noop, s),
+                      "RHT amax launch");
+  return hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, cfg.noop, s),
+                    "amax launch");
+}
+
+extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                         const nvfp4_out_t *row, const nvfp4_out_t *col,
+                                         const nvfp4_config_t *cfg_in, void *stream) {
+  nvfp4_status_t st = check_input(x, dtype, rows, cols);
+  if (st != NVFP4_OK) return st;
+  const nvfp4_config_t cfg = config_or_default(cfg_in);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (row == nullptr && col == nullptr) return fail(NVFP4_ERR_NULL, "neither a row-wise nor a column-wise output");
+  const bool empty = rows * cols == 0;
+  if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
+  if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
+  if (cfg.scale_fmt == NVFP4_SCALE_UE5M3)
+    return fail(NVFP4_ERR_UNSUPPORTED, "UE5M3 block scales are not supported (not defined on the pages)");
+  if (cfg.scale_fmt != NVFP4_SCALE_E4M3) return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale format %u", cfg.scale_fmt);
+  if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", cfg.scale_layout);
+  const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
+  if (cfg.row_scaled) {
+    if (col) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 is row-wise only");
+    if (cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 uses 1x16 blocks");
+    if (cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 cannot be combined with the RHT");
+    if (swz) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 keeps compact scales");
+  }
+  if (cfg.rht && cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "the RHT is defined for 1x16 blocks only");
+  if (cfg.rht && row && col && row->amax == col->amax)
+    return fail(NVFP4_ERR_UNSUPPORTED, "the RHT quantize needs distinct row-wise and column-wise amax buffers");
+  if ((col || cfg.block_2d) && rows % 16 != 0)
+    return fail(NVFP4_ERR_SHAPE, "rows = %lld must be a multiple of 16 for %s", (long long)rows,
+                cfg.block_2d ? "16x16 blocks" : "the column-wise output");
+  if (swz && (rows % 128 != 0 || cols % 128 != 0))
+    return fail(NVFP4_ERR_SHAPE, "GEMM-swizzled scales need rows and cols that are multiples of 128 (got %lld x %lld)",
+                (long long)rows, (long long)cols);
+
+  const uint32_t R = static_cast<uint32_t>(rows), C = static_cast<uint32_t>(cols);
+  const bool sr = cfg.stochastic != 0;
+  if (cfg.row_scaled) {
+    nvfp4::RowScaledArgs a{x, R, C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop};
+    return hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
+  }
+  float *ra = row ? row->amax : nullptr;
+  float *ca = col ? col->amax : nullptr;
+  if (cfg.compute_amax) {
+    float *a = ra ? ra : ca;
+    float *b = (ca == a) ? nullptr : ca;
+    st = hip_status(nvfp4::launch_zero_amax(a, b, cfg.noop, s), "zero amax launch");
+    if (st != NVFP4_OK) return st;
+    if (rows * cols > 0) {
+      if (cfg.rht)
+        st = hip_status(nvfp4::launch_rht_amax(x, dtype, R, C, cfg.rht_sign_mask, ra, ca, cfg.noop, s),
+                        "RHT amax launch");
+      else
+        st = hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, cfg.noop, s),
+                        "amax launch");
+      if (st != NVFP4_OK) return st;
+    }
+  }
+  nvfp4::CastArgs a{x,  R,        C,    row ? row->data : nullptr, row ? row->scales : nullptr, ra,
+                    col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
+                    cfg.rht_sign_mask, cfg.noop};
+  return hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
+}
+
+extern "C" nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols, uint32_t scale_layout,
+                                           uint32_t row_scaled, float *y, void *stream) {
+  if (q == nullptr || y == nullptr) return fail(NVFP4_ERR_NULL, "NULL quantized tensor or output");
+  if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
+  if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 16", (long long)cols);
+  if (rows * cols >= (int64_t{1} << 32)) return fail(NVFP4_ERR_SHAPE, "rows * cols must be below 2^32");
+  if (rows * cols == 0) return NVFP4_OK;
+  if (q->data == nullptr || q->scales == nullptr || q->amax == nullptr)
+    return fail(NVFP4_ERR_NULL, "quantized tensor has a NULL data, scales or amax pointer");
+  if (!aligned(q->data, 4) || !aligned(q->amax, 4)) return fail(NVFP4_ERR_ALIGN, "data and amax must be 4-byte aligned");
+  if (!aligned(y, 16)) return fail(NVFP4_ERR_ALIGN, "output must be 16-byte aligned");
+  if (scale_layout != NVFP4_SCALES_COMPACT && scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", scale_layout);
+  const bool swz = scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
+  if (swz && (rows % 128 != 0 || cols % 128 != 0))
+    return fail(NVFP4_ERR_SHAPE, "GEMM-swizzled scales need rows and cols that are multiples of 128");
+  if (row_scaled && swz) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 keeps compact scales");
+  return hip_status(nvfp4::launch_dequant(q->data, q->scales, q->amax, static_cast<uint32_t>(rows),
+                                          static_cast<uint32_t>(cols), swz, row_scaled != 0, y,
+                                          static_cast<hipStream_t>(stream)),
+                    "dequantize launch");
+}
+
+extern "C" nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                                  uint32_t sign_mask, float *t, void *stream) {
+  nvfp4_status_t st = check_input(x, dtype, rows, cols);
+  if (st != NVFP4_OK) return st;
+  if (rows % 16 != 0) return fail(NVFP4_ERR_SHAPE, "the RHT needs rows %% 16 == 0");
+  if (rows * cols > 0 && t == nullptr) return fail(NVFP4_ERR_NULL, "output pointer is NULL");
+  if (t != nullptr && !aligned(t, 16)) return fail(NVFP4_ERR_ALIGN, "output must be 16-byte aligned");
+  return hip_status(nvfp4::launch_debug_rht(x, dtype, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols),
+                                            sign_mask, t, static_cast<hipStream_t>(stream)),
+                    "RHT launch");
+}

@@ -1,0 +1,173 @@
+// Device-side NVFP4 codec helpers for gfx950 (wave64).
+//
+// Every floating-point step is one correctly rounded FP32 operation, in the
+// order the NVFP4 two-level scaling defines it (global encode scale from
+// the amax, E4M3 block scale relative to it, per-block multiplier, E2M1
+// code), so that the results are reproducible bit for bit. The library is
+// built with -ffp-contract=off, so no multiply-add is fused.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+// Largest E2M1 magnitude times largest E4M3 magnitude: 6 * 448.
+constexpr float kGlobalScaleNumerator = 2688.0f;
+
+// ---------------------------------------------------------------------------
+// Two-level scaling ("Implement row-scaled NVFP4 fprop recipe", Greptile
+// summary: FP8 block scales relative to a per-tensor or per-row FP32 amax,
+// with a zero guard).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float global_encode_scale(float amax) {
+  if (amax == 0.0f) return 1.0f;
+  float s = kGlobalScaleNumerator / amax;  // IEEE division (HIP default)
+  return fminf(s, kFltMax);                 // an overflow to +inf clamps
+}
+
+// E4M3 (bias 7, max 448) of a non-negative value, nearest even, saturating.
+__device__ __forceinline__ uint32_t e4m3_encode(float sd) {
+  if (!(sd < 448.0f)) return 0x7Eu;  // 448 and above (incl. +inf) saturate
+  if (sd < 0.015625f) {
+    // subnormal range, quantum 2^-9: the code is the nearest-even integer
+    // multiple of 2^-9 (a result of 8 is the smallest normal, code 0x08).
+    return static_cast<uint32_t>(__builtin_rintf(sd * 512.0f));
+  }
+  uint32_t u = __float_as_uint(sd);
+  uint32_t exp8 = (u >> 23) - 127u + 7u;  // 1..15
+  uint32_t man = u & 0x7FFFFFu;
+  uint32_t keep = man >> 20;               // top 3 mantissa bits
+  uint32_t rest = man & 0xFFFFFu;
+  uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & keep);
+  uint32_t code = (exp8 << 3) + keep + up;  // a mantissa carry bumps the exponent
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t code) {
+  uint32_t e = (code >> 3) & 0xFu;
+  uint32_t m = code & 7u;
+  if (e == 0) return static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+struct BlockScale {
+  uint32_t code;  // E4M3 byte
+  float mult;     // encode multiplier e
+};
+
+// sd = fl(fl(m / 6) * S); e = fl(S / value(s)), 0 when s == 0.
+__device__ __forceinline__ BlockScale block_scale(float block_amax, float S) {
+  float q = block_amax / 6.0f;
+  float sd = q * S;
+  BlockScale b;
+  b.code = e4m3_encode(sd);
+  b.mult = b.code == 0 ? 0.0f : fminf(S / e4m3_decode(b.code), kFltMax);
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 encoding of an already scaled value v' (finite).
+// Magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} are codes 0..7; bit 3 is the sign
+// bit of v'. Nearest even: a tie goes to the code with a zero low bit.
+// On non-negative binary32 values unsigned compares order like the values,
+// so the code is the number of decision points the magnitude passes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t c = (a > 0x3E800000u)     // > 0.25 (tie 0.25 -> 0)
+               + (a >= 0x3F400000u)  // >= 0.75 (tie -> 1.0)
+               + (a > 0x3FA00000u)   // > 1.25 (tie -> 1.0)
+               + (a >= 0x3FE00000u)  // >= 1.75 (tie -> 2.0)
+               + (a > 0x40200000u)   // > 2.5 (tie -> 2.0)
+               + (a >= 0x40600000u)  // >= 3.5 (tie -> 4.0)
+               + (a > 0x40A00000u);  // > 5 (tie -> 4.0); beyond 6 saturates at 7
+  return c | ((u >> 28) & 8u);
+}
+
+// Stochastic rounding with 16 random bits r16: between grid neighbours
+// lo <= |v| < hi, round up iff r16 < 65536 * (|v| - lo) / (hi - lo).
+// Grid spacing is 0.5 below 2, 1 in [2, 4), 2 in [4, 6), so y = |v| / spacing
+// is exact, and floor/fraction of y give the neighbour and the fraction.
+__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t r16) {
+  uint32_t u = __float_as_uint(v);
+  float a = __uint_as_float(u & 0x7FFFFFFFu);
+  uint32_t code;
+  if (a >= 6.0f) {
+    code = 7u;
+  } else {
+    float y;
+    uint32_t base;
+    if (a < 2.0f) {
+      y = a * 2.0f;
+      base = 0u;
+    } else if (a < 4.0f) {
+      y = a;
+      base = 2u;
+    } else {
+      y = a * 0.5f;
+      base = 4u;
+    }
+    float fl = __builtin_floorf(y);
+    float frac = y - fl;  // exact
+    code = base + static_cast<uint32_t>(fl) + (static_cast<float>(r16) < frac * 65536.0f ? 1u : 0u);
+  }
+  return code | ((u >> 28) & 8u);
+}
+
+// ---------------------------------------------------------------------------
+// Counter-based random words: fmix32, the 32-bit finalizer of MurmurHash3
+// (A. Appleby, public domain).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+__device__ __forceinline__ uint32_t sr_key(uint32_t seed, uint32_t orientation) {
+  return fmix32(fmix32(seed) ^ (orientation + 1u));
+}
+
+// ---------------------------------------------------------------------------
+// 16-point random Hadamard transform in registers: sign flips from the mask,
+// an in-place fast Walsh-Hadamard transform (natural = Sylvester order), and
+// the orthonormal factor 1/4 (exact).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t sign_mask) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(__float_as_uint(v[k]) ^ (((sign_mask >> k) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] *= 0.25f;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM-swizzled scale offset of scale (r, c) in an [n][k/16] scale matrix with
+// scale_cols = k/16 (n % 128 == 0, scale_cols % 4 == 0): 128 x 4 tiles of 512
+// bytes in row-major tile order; inside a tile (r%32)*16 + (r%128)/32*4 + c%4.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t swizzled_scale_offset(uint64_t r, uint64_t c, uint64_t scale_cols) {
+  uint64_t tile = (r >> 7) * (scale_cols >> 2) + (c >> 2);
+  return (tile << 9) + ((r & 31u) << 4) + (((r & 127u) >> 5) << 2) + (c & 3u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace nvfp4

@@ -1,0 +1,55 @@
+"""Helpers for the GPU tests: move seeded host inputs to the device, run the
+library through its C ABI, and bring results back as numpy arrays."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import nvfp4_block_scaled_05_amd as nv
+
+DEV = "cuda:0"
+
+
+def to_device(x: np.ndarray) -> torch.Tensor:
+    """uint16 BF16 bits -> bfloat16 tensor; float32 -> float32 tensor (on the GPU)."""
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def run_quantize(x: np.ndarray, *, rowwise=True, columnwise=True, **cfg_kw):
+    """Quantize on the GPU; returns a dict shaped like oracle.quantize()'s."""
+    xd = to_device(x)
+    cfg = nv.make_config(**cfg_kw)
+    row, col = nv.quantize(xd, rowwise=rowwise, columnwise=columnwise, cfg=cfg)
+    torch.cuda.synchronize()
+    rows, cols = x.shape
+    out = {"row_data": None, "row_scales": None, "col_data": None, "col_scales": None,
+           "amax_row": None, "amax_col": None}
+    if row is not None:
+        out["row_data"] = host(row.data)
+        out["row_scales"] = host(row.scales)
+        out["amax_row"] = host(row.amax)
+    if col is not None:
+        out["col_data"] = host(col.data)
+        out["col_scales"] = host(col.scales)
+        out["amax_col"] = host(col.amax)
+    return out
+
+
+def codes(data: np.ndarray) -> np.ndarray:
+    """[n][k/2] packed bytes -> [n][k] 4-bit codes."""
+    return np.stack([data & 0xF, data >> 4], -1).reshape(data.shape[0], -1)
+
+
+def e2m1_step_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in grid steps between E2M1 codes (+0 and -0 are one point)."""
+    def pos(c):
+        mag = (c & 7).astype(np.int32)
+        return np.where(c & 8, -mag, mag)
+    return np.abs(pos(a) - pos(b))

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/nvfp4.h declares, and rejects bad arguments on the host before
+queuing anything (all calls here fail validation, so no HIP call is made)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_05_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+# Fake, suitably aligned "device" addresses: validation never dereferences them.
+X = 0x100000
+D = 0x200000
+S = 0x300000
+A = 0x400000
+A2 = 0x500000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status_t|const char \*)\s*(nvfp4_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(nv.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nv.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _out(data=D, scales=S, amax=A):
+    return nv.nvfp4_out_t(data, scales, amax)
+
+
+def _q(rows, cols, row=None, col=None, cfg=None, x=X, dtype=nv.NVFP4_IN_BF16):
+    lib = nv.load()
+    r = None if row is None else ctypes.byref(row)
+    c = None if col is None else ctypes.byref(col)
+    f = None if cfg is None else ctypes.byref(cfg)
+    return lib.nvfp4_quantize(x, dtype, rows, cols, r, c, f, None)
+
+
+@pytest.mark.parametrize("case,expected", [
+    (dict(rows=64, cols=40, row=_out()), nv.NVFP4_ERR_SHAPE),                    # cols % 16
+    (dict(rows=40, cols=64, col=_out()), nv.NVFP4_ERR_SHAPE),                    # col-wise needs rows % 16
+    (dict(rows=-1, cols=64, row=_out()), nv.NVFP4_ERR_SHAPE),
+    (dict(rows=1 << 17, cols=1 << 16, row=_out()), nv.NVFP4_ERR_SHAPE),          # 2^33 elements
+    (dict(rows=64, cols=64), nv.NVFP4_ERR_NULL),                                 # no output at all
+    (dict(rows=64, cols=64, row=_out(data=0)), nv.NVFP4_ERR_NULL),
+    (dict(rows=64, cols=64, row=_out(), x=0), nv.NVFP4_ERR_NULL),
+    (dict(rows=64, cols=64, row=_out(), x=X + 2), nv.NVFP4_ERR_ALIGN),
+    (dict(rows=64, cols=64, row=_out(data=D + 4)), nv.NVFP4_ERR_ALIGN),
+    (dict(rows=64, cols=64, row=_out(scales=S + 1)), nv.NVFP4_ERR_ALIGN),
+    (dict(rows=64, cols=64, row=_out(), dtype=7), nv.NVFP4_ERR_UNSUPPORTED),
+])
+def test_quantize_rejects_bad_arguments(case, expected):
+    assert _q(**case) == expected
+    assert nv.nvfp4_last_error() != ""
+
+
+def test_swizzled_scales_reject_partial_tiles():
+    # "Fuse NVFP4 scale swizzling on SM120 and SM121": partial 128x128 scale
+    # tiles are rejected for swizzled output (e.g. the 1088x1024 tail shape).
+    cfg = nv.make_config(swizzled=True)
+    assert _q(1088, 1024, row=_out(), col=_out(A2), cfg=cfg) == nv.NVFP4_ERR_SHAPE
+    assert _q(1024, 1040, row=_out(), cfg=cfg) == nv.NVFP4_ERR_SHAPE
+    assert "128" in nv.nvfp4_last_error()
+
+
+def test_row_scaled_gates():
+    # "Implement row-scaled NVFP4 fprop recipe": row-wise only; compact scales;
+    # "Fuse NVFP4 scale swizzling ...": no row-scaled RHT.
+    rs = nv.make_config(row_scaled=True)
+    assert _q(128, 128, row=_out(), col=_out(A2), cfg=rs) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(128, 128, row=_out(), cfg=nv.make_config(row_scaled=True, swizzled=True)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(128, 128, row=_out(), cfg=nv.make_config(row_scaled=True, rht=True)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(128, 128, row=_out(), cfg=nv.make_config(row_scaled=True, block_2d=True)) == nv.NVFP4_ERR_UNSUPPORTED
+
+
+def test_rht_gates():
+    assert _q(128, 128, row=_out(), col=_out(A2), cfg=nv.make_config(rht=True, block_2d=True)) == \
+        nv.NVFP4_ERR_UNSUPPORTED
+    # "Write both NVFP4 amax buffers", review thread: one float for both RHT
+    # amaxes gives wrong data, so a shared buffer is refused.
+    assert _q(128, 128, row=_out(), col=_out(), cfg=nv.make_config(rht=True)) == nv.NVFP4_ERR_UNSUPPORTED
+
+
+def test_ue5m3_is_unsupported():
+    cfg = nv.make_config(scale_fmt=nv.NVFP4_SCALE_UE5M3)
+    assert _q(128, 128, row=_out(), cfg=cfg) == nv.NVFP4_ERR_UNSUPPORTED
+    assert "UE5M3" in nv.nvfp4_last_error()
+
+
+def test_compute_amax_rejections():
+    lib = nv.load()
+    assert lib.nvfp4_compute_amax(X, 0, 64, 64, None, None, None, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_compute_amax(X, 0, 64, 64, A + 2, None, None, None) == nv.NVFP4_ERR_ALIGN
+    rs = nv.make_config(row_scaled=True)
+    assert lib.nvfp4_compute_amax(X, 0, 64, 64, A, A2, ctypes.byref(rs), None) == nv.NVFP4_ERR_UNSUPPORTED
+    rht = nv.make_config(rht=True)
+    assert lib.nvfp4_compute_amax(X, 0, 40, 64, A, A2, ctypes.byref(rht), None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_compute_amax(X, 0, 64, 64, A, A, ctypes.byref(rht), None) == nv.NVFP4_ERR_UNSUPPORTED
+
+
+def test_dequantize_rejections():
+    lib = nv.load()
+    q = _out()
+    assert lib.nvfp4_dequantize(None, 64, 64, 0, 0, D, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 40, 0, 0, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 1, 0, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 0, 0, D + 4, None) == nv.NVFP4_ERR_ALIGN
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 128, 128, 1, 1, D, None) == nv.NVFP4_ERR_UNSUPPORTED
+
+
+def test_debug_rht_rejections():
+    lib = nv.load()
+    assert lib.nvfp4_debug_rht_colwise(X, 0, 40, 64, 0, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_debug_rht_colwise(X, 0, 64, 64, 0, None, None) == nv.NVFP4_ERR_NULL
+
+
+def test_config_struct_matches_header_layout():
+    # 9 uint32 fields then one pointer, as declared in nvfp4_config_t
+    assert ctypes.sizeof(nv.nvfp4_config_t) == 9 * 4 + 4 + 8
+    assert nv.nvfp4_config_t.noop.offset == 40
+    assert ctypes.sizeof(nv.nvfp4_out_t) == 24
