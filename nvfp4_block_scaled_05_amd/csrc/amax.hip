@@ -19,16 +19,31 @@ typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bool noop_set(const float *noop) { return noop != nullptr && *noop == 1.0f; }
 
-// max over the 256 threads of a workgroup (values are float bit patterns of
-// non-negative numbers, so unsigned max == float max). Result valid in all threads.
-__device__ __forceinline__ uint32_t block_umax(uint32_t v, uint32_t *lds4) {
+// max over the NT threads of a workgroup (values are float bit patterns of
+// non-negative numbers, so unsigned max == float max). Result valid in all
+// threads; lds holds one word per wave.
+template <int NT>
+__device__ __forceinline__ uint32_t block_umax(uint32_t v, uint32_t *lds) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) lds4[wave] = v;
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
   __syncthreads();
-  v = max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]));
+  v = lds[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) v = max(v, lds[i]);
   return v;
+}
+
+// Apply a workgroup's maximum to an amax buffer. Same-address atomics from
+// thousands of workgroups serialize at the memory side across the XCDs, so a
+// workgroup first reads the buffer (system scope: past every cache) and
+// issues the atomic max only when its value is larger. The buffer only grows
+// during the reduction (from the +0 of the zeroing pass), so a value that is
+// not larger than one already there cannot change the result.
+__device__ __forceinline__ void publish_max(float *dst, uint32_t m) {
+  if (dst == nullptr) return;
+  unsigned int *u = reinterpret_cast<unsigned int *>(dst);
+  if (m > __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) atomicMax(u, m);
 }
 
 __global__ void k_zero_amax(float *a, float *b, const float *noop) {
@@ -39,43 +54,45 @@ __global__ void k_zero_amax(float *a, float *b, const float *noop) {
   }
 }
 
-// Per-tensor amax. nvec = number of 16-byte vectors of x.
+// Per-tensor amax. nvec = number of 16-byte vectors of x. A workgroup of
+// kAmaxThreads (8 waves) owns one contiguous chunk of kAmaxThreads *
+// kVecPerThread vectors (128 KiB) and every thread issues all its loads
+// before reducing, so the whole input is requested in one round trip while
+// the number of workgroups, and so of atomics per buffer, stays small
+// (640 for an 80 MiB input).
+constexpr int kAmaxThreads = 512;
+constexpr int kVecPerThread = 16;
+
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a,
-                                                   float *b, const float *noop) {
-  __shared__ uint32_t lds4[4];
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a,
+                                                       float *b, const float *noop) {
+  __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  uint32_t m32 = 0;               // FP32: max of |x| bit patterns
-  ushort2_t m16 = {0, 0};         // BF16: max of 15-bit magnitudes, two lanes
-  auto take = [&](const uint4 &v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const uint64_t base = static_cast<uint64_t>(blockIdx.x) * (kAmaxThreads * kVecPerThread) + threadIdx.x;
+  uint4 v[kVecPerThread];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (DT == kBF16) {
-        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[k] & 0x7FFF7FFFu));
-      } else {
-        m32 = max(m32, w[k] & 0x7FFFFFFFu);
-      }
-    }
-  };
-  for (; i + 3 * stride < nvec; i += 4 * stride) {
-    uint4 v0 = *(x + i);
-    uint4 v1 = *(x + i + stride);
-    uint4 v2 = *(x + i + 2 * stride);
-    uint4 v3 = *(x + i + 3 * stride);
-    take(v0);
-    take(v1);
-    take(v2);
-    take(v3);
+  for (int k = 0; k < kVecPerThread; ++k) {
+    const uint64_t i = base + static_cast<uint64_t>(k) * kAmaxThreads;
+    v[k] = i < nvec ? x[i] : make_uint4(0, 0, 0, 0);
   }
-  for (; i < nvec; i += stride) take(x[i]);
+  uint32_t m32 = 0;        // FP32: max of |x| bit patterns
+  ushort2_t m16 = {0, 0};  // BF16: max of 15-bit magnitudes, two lanes
+#pragma unroll
+  for (int k = 0; k < kVecPerThread; ++k) {
+    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (DT == kBF16)
+        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[j] & 0x7FFF7FFFu));
+      else
+        m32 = max(m32, w[j] & 0x7FFFFFFFu);
+    }
+  }
   uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
-  m = block_umax(m, lds4);
+  m = block_umax<kAmaxThreads>(m, lds);
   if (threadIdx.x == 0) {
-    if (a) atomicMax(reinterpret_cast<unsigned int *>(a), m);
-    if (b && b != a) atomicMax(reinterpret_cast<unsigned int *>(b), m);
+    publish_max(a, m);
+    if (b != a) publish_max(b, m);
   }
 }
 
@@ -109,13 +126,13 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
 // takes VEC adjacent columns of one 16-row group: max|x| over the raw values,
 // max|t| over their 16-point transforms.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
+__global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
                                                        uint32_t mask, float *row_amax, float *col_amax,
                                                        const float *noop) {
   constexpr int VEC = DT == kBF16 ? 8 : 4;
-  __shared__ uint32_t lds4[4];
+  __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
-  const uint32_t c = (blockIdx.x * kThreads + threadIdx.x) * VEC;
+  const uint32_t c = (blockIdx.x * kAmaxThreads + threadIdx.x) * VEC;
   const uint32_t r0 = blockIdx.y * 16;
   uint32_t mx = 0, mt = 0;
   if (c < cols) {
@@ -130,12 +147,12 @@ __global__ __launch_bounds__(kThreads) void k_rht_amax(const void *__restrict__ 
       for (int r = 0; r < 16; ++r) mt = max(mt, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
     }
   }
-  mx = block_umax(mx, lds4);
+  mx = block_umax<kAmaxThreads>(mx, lds);
   __syncthreads();
-  mt = block_umax(mt, lds4);
+  mt = block_umax<kAmaxThreads>(mt, lds);
   if (threadIdx.x == 0) {
-    if (row_amax) atomicMax(reinterpret_cast<unsigned int *>(row_amax), mx);
-    if (col_amax) atomicMax(reinterpret_cast<unsigned int *>(col_amax), mt);
+    publish_max(row_amax, mx);
+    publish_max(col_amax, mt);
   }
 }
 
@@ -169,13 +186,12 @@ hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b,
                        hipStream_t s) {
   const uint64_t nvec = n * (dtype == kBF16 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
-  uint64_t blocks = (nvec + kThreads * 4 - 1) / (kThreads * 4);
-  if (blocks > 2048) blocks = 2048;
+  const uint64_t blocks = (nvec + kAmaxThreads * kVecPerThread - 1) / (kAmaxThreads * kVecPerThread);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_amax<kBF16>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(k_amax<kBF16>, dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
                        static_cast<const uint4 *>(x), nvec, a, b, noop);
   else
-    hipLaunchKernelGGL(k_amax<kFP32>, dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(k_amax<kFP32>, dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
                        static_cast<const uint4 *>(x), nvec, a, b, noop);
   return hipGetLastError();
 }
@@ -184,11 +200,13 @@ hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t col
                            float *row_amax, float *col_amax, const float *noop, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   const uint32_t vec = dtype == kBF16 ? 8 : 4;
-  dim3 grid((cols + kThreads * vec - 1) / (kThreads * vec), rows / 16);
+  dim3 grid((cols + kAmaxThreads * vec - 1) / (kAmaxThreads * vec), rows / 16);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_rht_amax<kBF16>, grid, dim3(kThreads), 0, s, x, rows, cols, mask, row_amax, col_amax, noop);
+    hipLaunchKernelGGL(k_rht_amax<kBF16>, grid, dim3(kAmaxThreads), 0, s, x, rows, cols, mask, row_amax, col_amax,
+                       noop);
   else
-    hipLaunchKernelGGL(k_rht_amax<kFP32>, grid, dim3(kThreads), 0, s, x, rows, cols, mask, row_amax, col_amax, noop);
+    hipLaunchKernelGGL(k_rht_amax<kFP32>, grid, dim3(kAmaxThreads), 0, s, x, rows, cols, mask, row_amax, col_amax,
+                       noop);
   return hipGetLastError();
 }
 

@@ -33,6 +33,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTC = 128;
 
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+
 template <int DT>
 struct Tile {
   static constexpr int kElem = DT == kBF16 ? 2 : 4;   // bytes per input element
@@ -73,24 +75,25 @@ __device__ __forceinline__ uint32_t max_abs_bits(const float (&v)[N]) {
 // (element 2i in the low nibble of byte i). byte0 = index of the first byte
 // in the orientation's data array (stochastic-rounding counter).
 template <bool SR>
-__device__ __forceinline__ uint32_t encode8(const float *v, float e, uint32_t key, uint32_t byte0) {
+__device__ __forceinline__ uint32_t encode8_scaled(const float *s, uint32_t key, uint32_t byte0) {
+  if (!SR) return e2m1_rne_x8(s);
   uint32_t word = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float a = v[2 * q] * e;
-    const float b = v[2 * q + 1] * e;
-    uint32_t lo, hi;
-    if (SR) {
-      const uint32_t r = fmix32(key ^ (byte0 + q));
-      lo = e2m1_sr(a, r & 0xFFFFu);
-      hi = e2m1_sr(b, r >> 16);
-    } else {
-      lo = e2m1_rne(a);
-      hi = e2m1_rne(b);
-    }
+    const uint32_t r = fmix32(key ^ (byte0 + q));
+    const uint32_t lo = e2m1_sr(s[2 * q], r & 0xFFFFu);
+    const uint32_t hi = e2m1_sr(s[2 * q + 1], r >> 16);
     word |= (lo | (hi << 4)) << (8 * q);
   }
   return word;
+}
+
+template <bool SR>
+__device__ __forceinline__ uint32_t encode8(const float *v, float e, uint32_t key, uint32_t byte0) {
+  float s[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s[k] = v[k] * e;
+  return encode8_scaled<SR>(s, key, byte0);
 }
 
 // Four scales (c .. c+3 of scale row r, c % 4 == 0) packed in `word`.
@@ -111,7 +114,7 @@ __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uin
 }
 
 template <int DT, bool B2D, bool RHT, bool SR>
-__global__ __launch_bounds__(kThreads) void k_cast(CastArgs p) {
+__global__ __launch_bounds__(kThreads) void k_cast_lds(CastArgs p) {
   using T = Tile<DT>;
   __shared__ __align__(16) uint8_t lds_tile[T::kTR * T::kStride * T::kElem];
   __shared__ __align__(4) uint8_t lds_cs[kTC][T::kNRB];  // column-wise scale codes
@@ -292,19 +295,343 @@ __global__ __launch_bounds__(kThreads) void k_cast(CastArgs p) {
   }
 }
 
-template <int DT, bool B2D, bool RHT, bool SR>
-hipError_t launch_one(const CastArgs &a, hipStream_t s) {
+// ---------------------------------------------------------------------------
+// Register-tile cast (1x16 or 16x16 blocks, no RHT).
+//
+// A workgroup owns a 128 x 128 tile; thread (ucol = tid % 16, rg = tid / 16)
+// owns the 8 x 8 sub-tile of rows 8rg..8rg+7 and columns 8ucol..8ucol+7, kept
+// in registers. Each load instruction of a wave reads 4 rows x 256 contiguous
+// bytes. With 8 consecutive rows in one thread, one conversion of the pair
+// (row 2i, row 2i+1) of a column gives a whole column-wise output byte, so the
+// column-wise side needs no transpose of the data through LDS:
+//   row-wise 1x16 block   = lanes (ucol, ucol ^ 1): DPP exchange,
+//   column-wise 1x16 block = lanes (rg, rg ^ 1) = lane ^ 16: swizzle exchange,
+//   16x16 block            = the four lanes of both pairs: one scale per thread.
+// The multiplier S / value(s) of every E4M3 code is computed once per
+// workgroup (one correctly rounded division per code) and looked up in LDS.
+// Scale codes and column-wise data words go through LDS so that they leave
+// as 32-bit scale words and 64 contiguous bytes per column.
+// ---------------------------------------------------------------------------
+constexpr int kRT = 128;  // register-tile edge
+
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xB1, 0xF, 0xF, false));
+}
+
+// lane ^ 16 (bit-mask swizzle: and 0x1F, or 0, xor 0x10)
+__device__ __forceinline__ uint32_t swz_xor16(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), 0x401F));
+}
+
+// lo ? a : b without letting the compiler turn a select between two array
+// elements into a lane-dependent index (which would move the array to scratch)
+__device__ __forceinline__ uint32_t pick(bool lo, uint32_t a, uint32_t b) {
+  const uint32_t mask = 0u - static_cast<uint32_t>(lo);
+  return b ^ ((a ^ b) & mask);
+}
+
+__device__ __forceinline__ uint32_t block_code(uint32_t m_bits, float S) {
+  const float q = __uint_as_float(m_bits) / 6.0f;
+  return e4m3_encode(q * S);
+}
+
+__device__ __forceinline__ float code_multiplier(uint32_t code, float S) {
+  return code == 0 ? 0.0f : fminf(S / e4m3_decode(code), kFltMax);
+}
+
+template <int DT>
+struct RT {
+  static constexpr int kElem = DT == kBF16 ? 2 : 4;
+  static constexpr int kWords = 8 * kElem / 4;  // 32-bit words per 8-element row piece
+};
+
+// value c (0..7) of a row piece
+template <int DT>
+__device__ __forceinline__ float piece_value(const uint32_t (&w)[RT<DT>::kWords], int c) {
+  if (DT == kBF16) return (c & 1) ? bf16_hi(w[c >> 1]) : bf16_lo(w[c >> 1]);
+  return __uint_as_float(w[c]);
+}
+
+// max |x| bit pattern of a row piece
+template <int DT>
+__device__ __forceinline__ uint32_t piece_max(const uint32_t (&w)[RT<DT>::kWords]) {
+  uint32_t m = 0;
+  if (DT == kBF16) {
+    ushort2_t h = {0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, w[q] & 0x7FFF7FFFu));
+    m = static_cast<uint32_t>(max(h.x, h.y)) << 16;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = max(m, w[q] & 0x7FFFFFFFu);
+  }
+  return m;
+}
+
+template <int DT, bool B2D, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
+  constexpr int W = RT<DT>::kWords;
+  __shared__ float lds_mult[2][128];                   // multiplier per E4M3 code (row, col)
+  __shared__ __align__(4) uint8_t lds_rs[kRT][8];      // row-wise codes [tile row][16-col block]
+  __shared__ __align__(4) uint8_t lds_cs[kRT][8];      // column-wise codes [tile col][16-row block]
+  __shared__ uint32_t lds_cw[16][kRT + 1];             // column-wise data words [row group][tile col]
+
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+
+  const int tid = threadIdx.x;
+  const int ucol = tid & 15;
+  const int rg = tid >> 4;
+  const uint32_t r0 = blockIdx.y * kRT;
+  const uint32_t c0 = blockIdx.x * kRT;
+  const uint32_t col = c0 + 8 * ucol;
+  const uint32_t rbase = r0 + 8 * rg;
+  const bool col_ok = col < p.cols;
+  const bool do_row = p.row_data != nullptr;
+  const bool do_col = p.col_data != nullptr;
+
+  uint32_t w[8][W];
+  auto load_piece = [&](int k) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.x) +
+                                                       (static_cast<uint64_t>(rbase + k) * p.cols + col) * RT<DT>::kElem);
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const uint4 t = src[q];
+      w[k][4 * q] = t.x;
+      w[k][4 * q + 1] = t.y;
+      w[k][4 * q + 2] = t.z;
+      w[k][4 * q + 3] = t.w;
+    }
+  };
+  if (r0 + kRT <= p.rows && c0 + kRT <= p.cols) {  // interior tile (uniform): no bounds checks
+#pragma unroll
+    for (int k = 0; k < 8; ++k) load_piece(k);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (col_ok && rbase + k < p.rows) {
+        load_piece(k);
+      } else {
+#pragma unroll
+        for (int q = 0; q < W; ++q) w[k][q] = 0;
+      }
+    }
+  }
+
+  const float S_row = do_row ? global_encode_scale(*p.row_amax) : 1.0f;
+  const float S_col = do_col ? global_encode_scale(*p.col_amax) : 1.0f;
+  if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
+  else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
+
+  // ---- block scale codes ----
+  uint32_t rcode[8], ccode[8];
+  if (B2D) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, piece_max<DT>(w[k]));
+    m = max(m, dpp_xor1(m));
+    m = max(m, swz_xor16(m));
+    const uint32_t cr = block_code(m, S_row);
+    const uint32_t cc = block_code(m, S_col);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rcode[k] = cr;
+      ccode[k] = cc;
+    }
+  } else {
+    if (do_row) {
+      // row k's block is this piece and the neighbour lane's piece; the two
+      // lanes split the eight divisions and swap results.
+      uint32_t mr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        mr[k] = piece_max<DT>(w[k]);
+        mr[k] = max(mr[k], dpp_xor1(mr[k]));
+      }
+      const bool lo = (ucol & 1) == 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mine = block_code(pick(lo, mr[j], mr[j + 4]), S_row);
+        const uint32_t other = dpp_xor1(mine);
+        rcode[j] = pick(lo, mine, other);
+        rcode[j + 4] = pick(lo, other, mine);
+      }
+    }
+    if (do_col) {
+      // column c's block is this thread's 8 rows and lane ^ 16's 8 rows.
+      uint32_t mc[8];
+      if (DT == kBF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ushort2_t h = {0, 0};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, w[k][q] & 0x7FFF7FFFu));
+          uint32_t both = __builtin_bit_cast(uint32_t, h);
+          both = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, both),
+                                                                        __builtin_bit_cast(ushort2_t, swz_xor16(both))));
+          mc[2 * q] = both << 16;
+          mc[2 * q + 1] = both & 0xFFFF0000u;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) m = max(m, w[k][c] & 0x7FFFFFFFu);
+          mc[c] = max(m, swz_xor16(m));
+        }
+      }
+      const bool lo = (rg & 1) == 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mine = block_code(pick(lo, mc[j], mc[j + 4]), S_col);
+        const uint32_t other = swz_xor16(mine);
+        ccode[j] = pick(lo, mine, other);
+        ccode[j + 4] = pick(lo, other, mine);
+      }
+    }
+  }
+  // codes to LDS (one writer per block and row / column)
+  if (do_row && (ucol & 1) == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lds_rs[8 * rg + k][ucol >> 1] = static_cast<uint8_t>(rcode[k]);
+  }
+  if (do_col && (rg & 1) == 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lds_cs[8 * ucol + c][rg >> 1] = static_cast<uint8_t>(ccode[c]);
+  }
+  __syncthreads();
+
+  float re[8], ce[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    re[k] = do_row ? lds_mult[0][rcode[k]] : 0.0f;
+    ce[k] = do_col ? lds_mult[1][ccode[k]] : 0.0f;
+  }
+
+  // ---- encode: row pairs (2i, 2i+1) ----
+  const uint32_t krow = SR ? sr_key(p.sr_seed, 0) : 0u;
+  const uint32_t kcol = SR ? sr_key(p.sr_seed, 1) : 0u;
+  const uint32_t half_cols = p.cols >> 1;
+  const uint32_t half_rows = p.rows >> 1;
+  // 16x16 blocks with equal row and column global scales share every product
+  // (a uniform branch: the scales come from the same two amax words in every lane)
+  const bool share = B2D && do_row && do_col && __builtin_amdgcn_readfirstlane(S_row == S_col);
+  uint32_t colw[8];  // byte i is written in row pair i; every byte is written
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v0[8], v1[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      v0[c] = piece_value<DT>(w[2 * i], c);
+      v1[c] = piece_value<DT>(w[2 * i + 1], c);
+    }
+    float s0[8], s1[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s0[c] = v0[c] * re[2 * i];
+      s1[c] = v1[c] * re[2 * i + 1];
+    }
+    if (do_row) {
+      const uint32_t row = rbase + 2 * i;
+      const uint32_t byte0 = row * half_cols + (col >> 1);
+      const uint32_t word0 = encode8_scaled<SR>(s0, krow, byte0);
+      const uint32_t word1 = encode8_scaled<SR>(s1, krow, byte0 + half_cols);
+      if (col_ok && row < p.rows) *reinterpret_cast<uint32_t *>(p.row_data + byte0) = word0;
+      if (col_ok && row + 1 < p.rows) *reinterpret_cast<uint32_t *>(p.row_data + byte0 + half_cols) = word1;
+    }
+    if (do_col) {
+      float t0[8], t1[8];
+      if (share) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          t0[c] = s0[c];
+          t1[c] = s1[c];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          t0[c] = v0[c] * ce[c];
+          t1[c] = v1[c] * ce[c];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float a = t0[c];
+        const float b = t1[c];
+        if (SR) {
+          const uint32_t byte = (col + c) * half_rows + (rbase >> 1) + i;
+          const uint32_t r = fmix32(kcol ^ byte);
+          const uint32_t pair = e2m1_sr(a, r & 0xFFFFu) | (e2m1_sr(b, r >> 16) << 4);
+          colw[c] = i == 0 ? pair : colw[c] | (pair << (8 * i));
+        } else {
+          colw[c] = e2m1_rne_pair_into(i == 0 ? __float_as_uint(a) : colw[c], a, b, i);
+        }
+      }
+    }
+  }
+  if (do_col) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) lds_cw[rg][8 * ucol + c] = colw[c];
+  }
+
+  if (do_col) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = tid + kThreads * it;
+      const int lc = e >> 2, h = e & 3;
+      const uint32_t j = c0 + lc;
+      const uint32_t rr = r0 + 32 * h;
+      if (j < p.cols && rr < p.rows) {
+        uint8_t *dst = p.col_data + j * half_rows + (rr >> 1);
+        if (rr + 32 <= p.rows)
+          *reinterpret_cast<uint4 *>(dst) = make_uint4(lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc], lds_cw[4 * h + 2][lc], lds_cw[4 * h + 3][lc]);
+        else
+          *reinterpret_cast<uint2 *>(dst) = make_uint2(lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc]);
+      }
+    }
+  }
+  // ---- scales: 128 rows (or columns) x 8 codes = one 32-bit word per thread ----
+  const int t_line = tid >> 1;
+  const int t_half = tid & 1;
+  if (do_row) {
+    const uint32_t row = r0 + t_line;
+    const uint32_t sc = (c0 >> 4) + 4 * t_half;
+    const uint32_t scale_cols = p.cols >> 4;
+    if (row < p.rows && sc < scale_cols)
+      store_scale_group(p.row_scales, row, sc, scale_cols, p.swizzled != 0,
+                        *reinterpret_cast<const uint32_t *>(&lds_rs[t_line][4 * t_half]));
+  }
+  if (do_col) {
+    const uint32_t j = c0 + t_line;
+    const uint32_t sc = (r0 >> 4) + 4 * t_half;
+    const uint32_t scale_cols = p.rows >> 4;
+    if (j < p.cols && sc < scale_cols)
+      store_scale_group(p.col_scales, j, sc, scale_cols, p.swizzled != 0,
+                        *reinterpret_cast<const uint32_t *>(&lds_cs[t_line][4 * t_half]));
+  }
+}
+
+template <int DT, bool B2D, bool SR>
+hipError_t launch_rt(const CastArgs &a, hipStream_t s) {
+  dim3 grid((a.cols + kRT - 1) / kRT, (a.rows + kRT - 1) / kRT);
+  hipLaunchKernelGGL((k_cast_rt<DT, B2D, SR>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, bool SR>
+hipError_t launch_rht(const CastArgs &a, hipStream_t s) {
   using T = Tile<DT>;
   dim3 grid((a.cols + kTC - 1) / kTC, (a.rows + T::kTR - 1) / T::kTR);
-  hipLaunchKernelGGL((k_cast<DT, B2D, RHT, SR>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_cast_lds<DT, false, true, SR>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dt(const CastArgs &a, bool block_2d, bool rht, bool sr, hipStream_t s) {
-  if (block_2d) return sr ? launch_one<DT, true, false, true>(a, s) : launch_one<DT, true, false, false>(a, s);
-  if (rht) return sr ? launch_one<DT, false, true, true>(a, s) : launch_one<DT, false, true, false>(a, s);
-  return sr ? launch_one<DT, false, false, true>(a, s) : launch_one<DT, false, false, false>(a, s);
+  if (rht) return sr ? launch_rht<DT, true>(a, s) : launch_rht<DT, false>(a, s);
+  if (block_2d) return sr ? launch_rt<DT, true, true>(a, s) : launch_rt<DT, true, false>(a, s);
+  return sr ? launch_rt<DT, false, true>(a, s) : launch_rt<DT, false, false>(a, s);
 }
 
 }  // namespace

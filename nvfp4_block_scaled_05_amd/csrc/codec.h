@@ -68,23 +68,38 @@ __device__ __forceinline__ BlockScale block_scale(float block_amax, float S) {
 }
 
 // ---------------------------------------------------------------------------
-// E2M1 encoding of an already scaled value v' (finite).
-// Magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6} are codes 0..7; bit 3 is the sign
-// bit of v'. Nearest even: a tie goes to the code with a zero low bit.
-// On non-negative binary32 values unsigned compares order like the values,
-// so the code is the number of decision points the magnitude passes.
+// E2M1 encoding of already scaled values v' (finite). Magnitudes
+// {0, .5, 1, 1.5, 2, 3, 4, 6} are codes 0..7; bit 3 is the sign bit of v'.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e2m1_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t c = (a > 0x3E800000u)     // > 0.25 (tie 0.25 -> 0)
-               + (a >= 0x3F400000u)  // >= 0.75 (tie -> 1.0)
-               + (a > 0x3FA00000u)   // > 1.25 (tie -> 1.0)
-               + (a >= 0x3FE00000u)  // >= 1.75 (tie -> 2.0)
-               + (a > 0x40200000u)   // > 2.5 (tie -> 2.0)
-               + (a >= 0x40600000u)  // >= 3.5 (tie -> 4.0)
-               + (a > 0x40A00000u);  // > 5 (tie -> 4.0); beyond 6 saturates at 7
-  return c | ((u >> 28) & 8u);
+
+// Nearest-even E2M1 codes of four pairs (a[2q], a[2q+1]) packed into one
+// 32-bit word, pair q in byte q, first element in the low nibble, with the
+// gfx950 conversion instruction at scale 1.0 (an exact no-op scale). The
+// instruction rounds to nearest even, saturates beyond 6 and keeps the sign
+// of zero and of values that round to zero (ties go to the code with a zero
+// low bit); the GPU tests compare it with the CPU definition on every BF16
+// value and on FP32 values around every decision point.
+__device__ __forceinline__ uint32_t e2m1_rne_x8(const float *a) {
+  // all four bytes are written, so any starting value will do; a[0]'s own
+  // register saves an initialising move
+  uint32_t w = __float_as_uint(a[0]);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[0], a[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[2], a[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[4], a[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a[6], a[7], 1.0f, 3);
+  return w;
+}
+
+// Nearest-even codes of the pair (a, b) written into byte `sel` (0..3) of w,
+// a in the low nibble; the other bytes of w are kept. `sel` must fold to a
+// constant (call it from unrolled loops).
+__device__ __forceinline__ uint32_t e2m1_rne_pair_into(uint32_t w, float a, float b, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 3);
+  }
 }
 
 // Stochastic rounding with 16 random bits r16: between grid neighbours

@@ -75,21 +75,18 @@ __device__ __forceinline__ void encode_unit(const Unit<DT> &u, bool valid, uint3
   m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
   const BlockScale bs = block_scale(__uint_as_float(m), S);
   const uint32_t byte0 = row * (p.cols >> 1) + uidx * 4;
-  uint32_t word = 0;
+  float s[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float a = v[2 * q] * bs.mult;
-    const float b = v[2 * q + 1] * bs.mult;
-    uint32_t lo, hi;
-    if (SR) {
+  for (int k = 0; k < 8; ++k) s[k] = v[k] * bs.mult;
+  uint32_t word = 0;
+  if (SR) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
       const uint32_t r = fmix32(key ^ (byte0 + q));
-      lo = e2m1_sr(a, r & 0xFFFFu);
-      hi = e2m1_sr(b, r >> 16);
-    } else {
-      lo = e2m1_rne(a);
-      hi = e2m1_rne(b);
+      word |= (e2m1_sr(s[2 * q], r & 0xFFFFu) | (e2m1_sr(s[2 * q + 1], r >> 16) << 4)) << (8 * q);
     }
-    word |= (lo | (hi << 4)) << (8 * q);
+  } else {
+    word = e2m1_rne_x8(s);
   }
   if (valid) *reinterpret_cast<uint32_t *>(p.data + byte0) = word;
   const uint32_t c1 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 2, 64));

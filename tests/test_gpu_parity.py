@@ -148,7 +148,8 @@ def test_sr_small(block_2d):
 # the block multiplier is exactly 1, so v' = v.
 # ---------------------------------------------------------------------------
 
-def _unit_multiplier_tensor(vals: np.ndarray) -> np.ndarray:
+def _unit_multiplier_tensor(vals: np.ndarray):
+    """Blocks [6, v0..v14], [6, v15..v29], ...; returns (x, number of such blocks)."""
     vals = vals[np.abs(vals) <= 6.0]
     n = (vals.size + 14) // 15
     blocks = np.zeros((n, 16), np.float32)
@@ -161,17 +162,17 @@ def _unit_multiplier_tensor(vals: np.ndarray) -> np.ndarray:
     rows = (rows + 15) // 16 * 16
     x = np.zeros(rows * cols, np.float32)
     x[:blocks.size] = blocks.ravel()
-    return x.reshape(rows, cols)
+    return x.reshape(rows, cols), n
 
 
 @pytest.mark.parametrize("stochastic", [False, True])
 def test_e2m1_every_bf16_value(stochastic):
     allv = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
     allv = allv[np.isfinite(allv)]
-    x = _unit_multiplier_tensor(allv)
+    x, nblocks = _unit_multiplier_tensor(allv)
     got = run_quantize(x, columnwise=False, stochastic=stochastic, sr_seed=77)
     ref = O.quantize(x, columnwise=False, stochastic=stochastic, sr_seed=77)
-    assert np.all(ref["row_scales"][:, 0] == 0x7E)
+    assert np.all(ref["row_scales"].ravel()[:nblocks] == 0x7E)  # e == 1 in every data block
     assert_matches(got, ref, what="e2m1 sweep")
 
 
@@ -180,7 +181,7 @@ def test_e2m1_fp32_near_decision_points():
     u = (pts.view(np.uint32)[:, None].astype(np.int64) + np.arange(-200, 201)[None, :]).ravel()
     v = u.astype(np.uint32).view(np.float32)
     v = np.concatenate([v, -v, np.float32([0.0, -0.0, 1e-40, -1e-40])])
-    x = _unit_multiplier_tensor(v)
+    x, _ = _unit_multiplier_tensor(v)
     check(x, columnwise=False, what="fp32 decision points")
     check(x, columnwise=False, stochastic=True, sr_seed=3, what="fp32 decision points sr")
 
