@@ -44,6 +44,118 @@ METRIC = "NVFP4 quantize HBM GB/s and % of peak, 8192x5120 BF16, row+col output"
 WORKLOAD = "8192x5120 BF16 N(0,1) x per-column 10^(-3+5u) (seed 1); 16x16 blocks; row+col FP4; " \
            "GEMM-swizzled E4M3 scales; RNE; per-tensor amax computed in the call"
 N_SETS = 4
+CAST_SOURCES = ("nvfp4_block_scaled_05_amd/csrc/cast.hip", "nvfp4_block_scaled_05_amd/csrc/codec.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_cast_2d_8192x5120.json")
+
+
+def cast_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in CAST_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per cast launch from the committed counter summary, or None
+    when the cast kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("source_sha256") != cast_source_hash():
+        return None
+    return t["bytes_per_launch"]
+
+
+# ---- rocprofv3 database summaries (rocpd SQLite) ---------------------------
+
+def _kernel_rows(db_path):
+    import re
+    import sqlite3
+
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select name, start, end from kernels order by start").fetchall()
+    out = []
+    for name, start, end in rows:
+        m = re.search(r"(k_\w+)(<[^>]*>)?", name)
+        out.append((m.group(1) + (m.group(2) or "") if m else name.split("(")[0][:60], start, end))
+    return out
+
+
+def summarize_trace(db_path):
+    import statistics as st
+
+    rows = _kernel_rows(db_path)
+    by = {}
+    for k, s, e in rows:
+        by.setdefault(k, []).append(e - s)
+    print(f"kernel durations from {os.path.basename(db_path)} (ns)")
+    print("| kernel | calls | average | median | min | max |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| {k} | {len(v)} | {st.mean(v):.0f} | {st.median(v):.0f} | {min(v)} | {max(v)} |")
+    spans = []
+    for i in range(len(rows) - 2):
+        a, b, c = rows[i], rows[i + 1], rows[i + 2]
+        if a[0].startswith("k_zero") and b[0].startswith("k_amax") and c[0].startswith("k_cast"):
+            spans.append(c[2] - a[1])
+    if spans:
+        med = st.median(spans)
+        print(f"\nper-call span, first kernel start to last kernel end: {len(spans)} calls, "
+              f"median {med / 1e3:.2f} us -> {B_ALG_CALL / med:.1f} GB/s algorithmic")
+
+
+def summarize_pmc(db_paths):
+    import collections
+    import sqlite3
+    import statistics as st
+
+    import re
+
+    for path in db_paths:
+        db = sqlite3.connect(path)
+        d = collections.defaultdict(list)
+        for name, cn, cv in db.execute("select name, counter_name, counter_value from pmc_events"):
+            m = re.search(r"(k_\w+)", name)
+            d[(m.group(1) if m else name.split("(")[0][:40], cn)].append(cv)
+        print(f"counters from {os.path.basename(os.path.dirname(path))}/{os.path.basename(path)} "
+              f"(median over dispatches; SQ counters are per instance)")
+        for (k, cn), v in sorted(d.items()):
+            print(f"  {k:40s} {cn:18s} n={len(v):4d} median={st.median(v):14.1f}")
+
+
+def _median_counter(db_path, kernel_substr, counter):
+    import sqlite3
+    import statistics as st
+
+    db = sqlite3.connect(db_path)
+    v = [cv for name, cn, cv in db.execute("select name, counter_name, counter_value from pmc_events")
+         if kernel_substr in name and cn == counter]
+    return st.median(v)
+
+
+def record_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db):
+    """Scale the cast kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
+    what the same counters read for a plain 80 MiB device copy, and store the
+    result with the hash of the cast kernel's sources."""
+    cf = _median_counter(copy_fetch_db, "copyBuffer", "FETCH_SIZE") * 1024.0
+    cw = _median_counter(copy_write_db, "copyBuffer", "WRITE_SIZE") * 1024.0
+    fetch_factor = INPUT_BYTES / cf
+    write_factor = INPUT_BYTES / cw
+    f = _median_counter(fetch_db, "k_cast", "FETCH_SIZE") * 1024.0 * fetch_factor
+    w = _median_counter(write_db, "k_cast", "WRITE_SIZE") * 1024.0 * write_factor
+    out = {"kernel": "k_cast_rt<bf16,16x16,rne>", "workload": "8192x5120 bf16 2d swizzled",
+           "fetch_bytes": round(f), "write_bytes": round(w), "bytes_per_launch": round(f + w),
+           "algorithmic_bytes_per_launch": B_ALG_CAST, "fetch_factor": round(fetch_factor, 5),
+           "write_factor": round(write_factor, 5), "source_sha256": cast_source_hash()}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(x_host, target_seconds: float = 12.0):
@@ -77,7 +189,17 @@ def main():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of the input size (80 MiB read + 80 MiB write), "
                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--summarize-trace", metavar="DB", help="print kernel stats of a rocprofv3 kernel trace")
+    p.add_argument("--summarize-pmc", nargs="+", metavar="DB", help="print counter medians of rocprofv3 --pmc runs")
+    p.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
+                   help="write the calibrated HBM traffic of the cast kernel to profiles/")
     args = p.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -159,9 +281,9 @@ def main():
                    "block": "16x16", "scales": "e4m3 gemm-swizzled", "rounding": "rne",
                    "bytes_per_call": B_ALG_CALL, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "buffer_sets_rotated": N_SETS},
-        "roofline": {"bound": "hbm", "kernel": "k_cast<bf16,16x16,rne> (fused cast-transpose)",
+        "roofline": {"bound": "hbm", "kernel": "k_cast_rt<bf16,16x16,rne> (fused cast-transpose)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": B_ALG_CAST, "avg_launch_ms": round(cast_ms, 6)},
     }
     if not args.no_cpu_baseline:
