@@ -158,6 +158,67 @@ def record_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db):
     print(json.dumps(out))
 
 
+# Other workloads (parity-test configurations; measured, not the headline).
+# bytes = algorithmic bytes of one call: each input read (two for a
+# per-tensor amax, one for the fused per-row path), every output written once.
+OTHER_WORKLOADS = {
+    "c1": dict(desc="1024x1024 BF16 N(0,1) (seed 0); 1x16 blocks; row+col; compact; RNE",
+               bytes=2 * 2 * 1024 * 1024 + 2 * (1024 * 1024 // 2 + 1024 * 1024 // 16) + 8),
+    "c3": dict(desc="1088x1024 FP32 (seed 2), max|x| 8; 1x16 blocks; row+col; compact; RNE; one output reused",
+               bytes=2 * 4 * 1088 * 1024 + 2 * (1088 * 1024 // 2 + 1088 * 1024 // 16) + 8),
+    "c4": dict(desc="4096x8192 BF16 N(0,1) x per-row exp(2n) (seed 3); per-row amax; row-wise only; compact; RNE",
+               bytes=2 * 4096 * 8192 + 4096 * 8192 // 2 + 4096 * 8192 // 16 + 4 * 4096),
+    "c5": dict(desc="8192x8192 BF16 N(0,1) + 0.1% at +-200 (seed 4); 1x16; row plain + col 16-point RHT; "
+                    "stochastic rounding (seed 5); compact",
+               bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
+}
+
+
+def run_other(name, steps, warmup):
+    import numpy as np
+    import torch
+
+    import nvfp4_block_scaled_05_amd as nv
+    import workloads
+
+    nv.load()
+    dev = torch.device("cuda:0")
+    w = OTHER_WORKLOADS[name]
+    if name == "c1":
+        x, cfg, rowwise, columnwise = workloads.c1(), nv.make_config(), True, True
+    elif name == "c3":
+        x, cfg, rowwise, columnwise = workloads.c3()[0], nv.make_config(), True, True
+    elif name == "c4":
+        x, cfg, rowwise, columnwise = workloads.c4(), nv.make_config(row_scaled=True), True, False
+    else:
+        x, mask, seed = workloads.c5()
+        cfg, rowwise, columnwise = nv.make_config(rht=True, rht_sign_mask=mask, stochastic=True, sr_seed=seed), True, True
+    xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16
+          else torch.from_numpy(x)).to(dev)
+    n_sets = 1 if name in ("c1", "c3") else N_SETS  # small inputs: one reused output, as in the pages' loop
+    sets = []
+    for _ in range(n_sets):
+        rows, cols = x.shape
+        row = nv.empty_orientation(rows, cols, dev, rows if cfg.row_scaled else 1) if rowwise else None
+        col = nv.empty_orientation(cols, rows, dev) if columnwise else None
+        sets.append((xd.clone() if n_sets > 1 else xd, row, col))
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        xs, row, col = sets[i % n_sets]
+        nv.nvfp4_quantize(xs, row, col, cfg, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        xs, row, col = sets[i % n_sets]
+        nv.nvfp4_quantize(xs, row, col, cfg, stream)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    print(json.dumps({"workload": name, "config": w["desc"], "us_per_call": round(us, 3),
+                      "bytes_per_call": w["bytes"], "GBps": round(w["bytes"] / us / 1e3, 1),
+                      "pct_of_hbm_peak": round(100 * w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
+                      "buffer_sets_rotated": n_sets}), flush=True)
+
+
 def cpu_baseline(x_host, target_seconds: float = 12.0):
     import numpy as np
 
@@ -189,6 +250,8 @@ def main():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of the input size (80 MiB read + 80 MiB write), "
                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--workload", default="c2", choices=["c2"] + sorted(OTHER_WORKLOADS),
+                   help="c2 (default) is the benchmark line; the others print their own timing line")
     p.add_argument("--summarize-trace", metavar="DB", help="print kernel stats of a rocprofv3 kernel trace")
     p.add_argument("--summarize-pmc", nargs="+", metavar="DB", help="print counter medians of rocprofv3 --pmc runs")
     p.add_argument("--record-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB"),
@@ -200,6 +263,10 @@ def main():
         return summarize_pmc(args.summarize_pmc)
     if args.record_traffic:
         return record_traffic(*args.record_traffic)
+    if args.workload != "c2":
+        if args.gpus != 1:
+            sys.exit(2)
+        return run_other(args.workload, args.steps, args.warmup)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)

@@ -34,6 +34,8 @@ constexpr int kThreads = 256;
 constexpr int kTC = 128;
 
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int DT>
 struct Tile {
@@ -100,12 +102,12 @@ __device__ __forceinline__ uint32_t encode8(const float *v, float e, uint32_t ke
 __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uint32_t c, uint32_t scale_cols,
                                                   bool swizzled, uint32_t word) {
   if (swizzled) {
-    *reinterpret_cast<uint32_t *>(base + swizzled_scale_offset(r, c, scale_cols)) = word;
+    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(base + swizzled_scale_offset(r, c, scale_cols)));
     return;
   }
   const uint64_t off = static_cast<uint64_t>(r) * scale_cols + c;
   if ((scale_cols & 3u) == 0 && c + 4 <= scale_cols) {
-    *reinterpret_cast<uint32_t *>(base + off) = word;
+    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(base + off));
   } else {
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i)
@@ -310,7 +312,9 @@ __global__ __launch_bounds__(kThreads) void k_cast_lds(CastArgs p) {
 // The multiplier S / value(s) of every E4M3 code is computed once per
 // workgroup (one correctly rounded division per code) and looked up in LDS.
 // Scale codes and column-wise data words go through LDS so that they leave
-// as 32-bit scale words and 64 contiguous bytes per column.
+// as 32-bit scale words and 64 contiguous bytes per column. The input is read
+// once and the outputs are not read back, so loads and stores are
+// non-temporal (streamed past the caches).
 // ---------------------------------------------------------------------------
 constexpr int kRT = 128;  // register-tile edge
 
@@ -391,11 +395,11 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
 
   uint32_t w[8][W];
   auto load_piece = [&](int k) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.x) +
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(p.x) +
                                                        (static_cast<uint64_t>(rbase + k) * p.cols + col) * RT<DT>::kElem);
 #pragma unroll
     for (int q = 0; q < W / 4; ++q) {
-      const uint4 t = src[q];
+      const u32x4 t = __builtin_nontemporal_load(src + q);
       w[k][4 * q] = t.x;
       w[k][4 * q + 1] = t.y;
       w[k][4 * q + 2] = t.z;
@@ -536,8 +540,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
       const uint32_t byte0 = row * half_cols + (col >> 1);
       const uint32_t word0 = encode8_scaled<SR>(s0, krow, byte0);
       const uint32_t word1 = encode8_scaled<SR>(s1, krow, byte0 + half_cols);
-      if (col_ok && row < p.rows) *reinterpret_cast<uint32_t *>(p.row_data + byte0) = word0;
-      if (col_ok && row + 1 < p.rows) *reinterpret_cast<uint32_t *>(p.row_data + byte0 + half_cols) = word1;
+      if (col_ok && row < p.rows)
+        __builtin_nontemporal_store(word0, reinterpret_cast<uint32_t *>(p.row_data + byte0));
+      if (col_ok && row + 1 < p.rows)
+        __builtin_nontemporal_store(word1, reinterpret_cast<uint32_t *>(p.row_data + byte0 + half_cols));
     }
     if (do_col) {
       float t0[8], t1[8];
@@ -585,9 +591,11 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
       if (j < p.cols && rr < p.rows) {
         uint8_t *dst = p.col_data + j * half_rows + (rr >> 1);
         if (rr + 32 <= p.rows)
-          *reinterpret_cast<uint4 *>(dst) = make_uint4(lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc], lds_cw[4 * h + 2][lc], lds_cw[4 * h + 3][lc]);
+          __builtin_nontemporal_store(
+              u32x4{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc], lds_cw[4 * h + 2][lc], lds_cw[4 * h + 3][lc]},
+              reinterpret_cast<u32x4 *>(dst));
         else
-          *reinterpret_cast<uint2 *>(dst) = make_uint2(lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc]);
+          __builtin_nontemporal_store(u32x2{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc]}, reinterpret_cast<u32x2 *>(dst));
       }
     }
   }
