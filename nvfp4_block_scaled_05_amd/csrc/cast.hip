@@ -376,8 +376,11 @@ template <int DT, bool B2D, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   constexpr int W = RT<DT>::kWords;
   __shared__ float lds_mult[2][128];                   // multiplier per E4M3 code (row, col)
-  __shared__ __align__(4) uint8_t lds_rs[kRT][8];      // row-wise codes [tile row][16-col block]
-  __shared__ __align__(4) uint8_t lds_cs[kRT][8];      // column-wise codes [tile col][16-row block]
+  // scale codes of the tile, row-wise [tile row][16-col block] and column-wise
+  // [tile col][16-row block]; compact: line * 8 + block; swizzled: the two
+  // 512-byte GEMM tiles that the 128 x 8 codes form, in memory order
+  __shared__ __align__(4) uint8_t lds_rs[kRT * 8];
+  __shared__ __align__(4) uint8_t lds_cs[kRT * 8];
   __shared__ uint32_t lds_cw[16][kRT + 1];             // column-wise data words [row group][tile col]
 
   if (p.noop != nullptr && *p.noop == 1.0f) return;
@@ -495,13 +498,17 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
     }
   }
   // codes to LDS (one writer per block and row / column)
+  const bool swz = p.swizzled != 0;
+  auto code_slot = [swz](int line, int blk) {
+    return swz ? ((blk >> 2) << 9) + ((line & 31) << 4) + ((line >> 5) << 2) + (blk & 3) : line * 8 + blk;
+  };
   if (do_row && (ucol & 1) == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) lds_rs[8 * rg + k][ucol >> 1] = static_cast<uint8_t>(rcode[k]);
+    for (int k = 0; k < 8; ++k) lds_rs[code_slot(8 * rg + k, ucol >> 1)] = static_cast<uint8_t>(rcode[k]);
   }
   if (do_col && (rg & 1) == 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) lds_cs[8 * ucol + c][rg >> 1] = static_cast<uint8_t>(ccode[c]);
+    for (int c = 0; c < 8; ++c) lds_cs[code_slot(8 * ucol + c, rg >> 1)] = static_cast<uint8_t>(ccode[c]);
   }
   __syncthreads();
 
@@ -600,6 +607,17 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
     }
   }
   // ---- scales: 128 rows (or columns) x 8 codes = one 32-bit word per thread ----
+  if (swz) {
+    // the tile's codes are two whole GEMM tiles, 1 KiB contiguous per orientation
+    // (swizzled shapes are multiples of 128, so every tile is complete)
+    if (do_row)
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(lds_rs)[tid],
+                                  reinterpret_cast<uint32_t *>(p.row_scales + swizzled_scale_offset(r0, c0 >> 4, p.cols >> 4)) + tid);
+    if (do_col)
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(lds_cs)[tid],
+                                  reinterpret_cast<uint32_t *>(p.col_scales + swizzled_scale_offset(c0, r0 >> 4, p.rows >> 4)) + tid);
+    return;
+  }
   const int t_line = tid >> 1;
   const int t_half = tid & 1;
   if (do_row) {
@@ -607,16 +625,16 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
     const uint32_t sc = (c0 >> 4) + 4 * t_half;
     const uint32_t scale_cols = p.cols >> 4;
     if (row < p.rows && sc < scale_cols)
-      store_scale_group(p.row_scales, row, sc, scale_cols, p.swizzled != 0,
-                        *reinterpret_cast<const uint32_t *>(&lds_rs[t_line][4 * t_half]));
+      store_scale_group(p.row_scales, row, sc, scale_cols, false,
+                        reinterpret_cast<const uint32_t *>(lds_rs)[tid]);
   }
   if (do_col) {
     const uint32_t j = c0 + t_line;
     const uint32_t sc = (r0 >> 4) + 4 * t_half;
     const uint32_t scale_cols = p.rows >> 4;
     if (j < p.cols && sc < scale_cols)
-      store_scale_group(p.col_scales, j, sc, scale_cols, p.swizzled != 0,
-                        *reinterpret_cast<const uint32_t *>(&lds_cs[t_line][4 * t_half]));
+      store_scale_group(p.col_scales, j, sc, scale_cols, false,
+                        reinterpret_cast<const uint32_t *>(lds_cs)[tid]);
   }
 }
 
