@@ -1,7 +1,7 @@
 // Fused NVFP4 cast-transpose for gfx950.
 //
-// One workgroup (256 threads, 4 waves of 64) owns a tile of TR x 128 input
-// elements (TR = 128 for BF16, 64 for FP32) and writes, for that tile:
+// One workgroup (256 threads, 4 waves of 64) owns a 128 x 128 tile of the
+// input and writes, for that tile:
 //   row-wise:    FP4 data [rows][cols/2] and E4M3 scales, 1x16 blocks along
 //                each input row (or the shared 16x16 block scale);
 //   column-wise: the same for the transposed tensor, 1x16 blocks along each
@@ -12,18 +12,15 @@
 // both orientations, and scales stored directly in the GEMM layout with one
 // 32-bit store per aligned group of four.
 //
-// Data flow per tile:
-//   1. each thread loads TR/16 row units of 8 elements with 128-bit loads
-//      (a wave reads 4 rows x 256 contiguous bytes per instruction) and, if
-//      the column-wise side is wanted, copies them to a padded LDS tile;
-//   2. 16x16 mode: block maxima via lane shuffles + LDS, one scale per block;
-//   3. row-wise: a 1x16 block is two adjacent lanes' units; the block max is
-//      one lane exchange; each lane writes one 32-bit word of 8 codes, and
-//      every 8th lane gathers four scales into one 32-bit store;
-//   4. column-wise: each thread reads 16 rows x 8 bytes from LDS (2 or 4
-//      columns), encodes each column block into 8 bytes (one 64-bit store),
-//      and the scales go through LDS so each column's run of scales leaves
-//      as 32-bit words.
+// Two kernels share this file:
+//   k_cast_rt   1x16 / 16x16 blocks: each thread keeps an 8 x 8 sub-tile in
+//               registers, so a column-wise byte (two consecutive rows of
+//               one column) is one hardware FP4 conversion;
+//   k_cast_rht  column-wise RHT: each thread keeps 16 rows x 4 columns, so a
+//               column's 16-row transform group is whole in one thread.
+// Both read the input once with non-temporal 128-bit (or 64-bit) loads, stage
+// output bytes and scale codes in LDS, and leave them as wide coalesced
+// non-temporal stores.
 #include "codec.h"
 #include "launch.h"
 
@@ -31,47 +28,13 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTC = 128;
 
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <int DT>
-struct Tile {
-  static constexpr int kElem = DT == kBF16 ? 2 : 4;   // bytes per input element
-  static constexpr int kTR = DT == kBF16 ? 128 : 64;  // tile rows
-  static constexpr int kUPT = kTR / 16;                // row units per thread
-  static constexpr int kUW = 8 * kElem / 4;            // 32-bit words per unit
-  static constexpr int kPad = 16 / kElem;              // 16 bytes of padding per LDS row
-  static constexpr int kStride = kTC + kPad;           // LDS row stride in elements
-  static constexpr int kCPT = 8 / kElem;               // columns per thread in the column phase
-  static constexpr int kNCQ = kTC / kCPT;              // column groups per tile
-  static constexpr int kNRB = kTR / 16;                // 16-row blocks per tile
-  static_assert(kNCQ * kNRB == kThreads, "column phase covers the tile");
-};
 
-template <int DT>
-__device__ __forceinline__ void unit_values(const uint32_t (&w)[Tile<DT>::kUW], float (&v)[8]) {
-  if (DT == kBF16) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = bf16_lo(w[k]);
-      v[2 * k + 1] = bf16_hi(w[k]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(w[k]);
-  }
-}
 
-template <int N>
-__device__ __forceinline__ uint32_t max_abs_bits(const float (&v)[N]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < N; ++k) m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
-  return m;
-}
 
 // Codes of 8 consecutive values of one output row, packed little-endian
 // (element 2i in the low nibble of byte i). byte0 = index of the first byte
@@ -112,188 +75,6 @@ __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uin
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i)
       if (c + i < scale_cols) base[off + i] = static_cast<uint8_t>(word >> (8 * i));
-  }
-}
-
-template <int DT, bool B2D, bool RHT, bool SR>
-__global__ __launch_bounds__(kThreads) void k_cast_lds(CastArgs p) {
-  using T = Tile<DT>;
-  __shared__ __align__(16) uint8_t lds_tile[T::kTR * T::kStride * T::kElem];
-  __shared__ __align__(4) uint8_t lds_cs[kTC][T::kNRB];  // column-wise scale codes
-  __shared__ uint32_t lds_m2d[4][T::kUPT][8];            // 16x16: per-wave partial block max
-  __shared__ uint32_t lds_s2d[2][T::kUPT][8];            // 16x16: codes (row, col)
-  __shared__ float lds_e2d[2][T::kUPT][8];               // 16x16: multipliers (row, col)
-
-  if (p.noop != nullptr && *p.noop == 1.0f) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int ucol = tid & 15;
-  const int rsub = tid >> 4;
-  const uint32_t r0 = blockIdx.y * T::kTR;
-  const uint32_t c0 = blockIdx.x * kTC;
-  const uint32_t col = c0 + ucol * 8;
-  const bool col_ok = col < p.cols;
-  const bool do_row = p.row_data != nullptr;
-  const bool do_col = p.col_data != nullptr;
-
-  // 1. load the tile's row units; stage them in LDS for the column phase.
-  uint32_t w[T::kUPT][T::kUW];
-#pragma unroll
-  for (int k = 0; k < T::kUPT; ++k) {
-    const uint32_t row = r0 + rsub + 16 * k;
-    if (col_ok && row < p.rows) {
-      const uint64_t off = static_cast<uint64_t>(row) * p.cols + col;
-      const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(p.x) + off * T::kElem);
-#pragma unroll
-      for (int q = 0; q < T::kUW / 4; ++q) {
-        const uint4 t = src[q];
-        w[k][4 * q] = t.x;
-        w[k][4 * q + 1] = t.y;
-        w[k][4 * q + 2] = t.z;
-        w[k][4 * q + 3] = t.w;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < T::kUW; ++q) w[k][q] = 0;
-    }
-  }
-  if (do_col) {
-#pragma unroll
-    for (int k = 0; k < T::kUPT; ++k) {
-      uint4 *dst = reinterpret_cast<uint4 *>(lds_tile + ((rsub + 16 * k) * T::kStride + ucol * 8) * T::kElem);
-#pragma unroll
-      for (int q = 0; q < T::kUW / 4; ++q)
-        dst[q] = make_uint4(w[k][4 * q], w[k][4 * q + 1], w[k][4 * q + 2], w[k][4 * q + 3]);
-    }
-  }
-
-  const float S_row = do_row ? global_encode_scale(*p.row_amax) : 1.0f;
-  const float S_col = do_col ? global_encode_scale(*p.col_amax) : 1.0f;
-
-  // 2. 16x16 blocks: block (k, b) covers tile rows 16k..16k+15 and columns
-  //    16b..16b+15, i.e. units held by lanes with ucol in {2b, 2b+1} over all
-  //    16 values of rsub (4 rows per wave, 4 waves).
-  if (B2D) {
-#pragma unroll
-    for (int k = 0; k < T::kUPT; ++k) {
-      float v[8];
-      unit_values<DT>(w[k], v);
-      uint32_t m = max_abs_bits(v);
-      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
-      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16, 64)));
-      m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32, 64)));
-      if (lane < 16 && (lane & 1) == 0) lds_m2d[wave][k][lane >> 1] = m;
-    }
-    __syncthreads();
-    if (tid < T::kUPT * 8) {
-      const int k = tid >> 3, b = tid & 7;
-      const uint32_t m = max(max(lds_m2d[0][k][b], lds_m2d[1][k][b]), max(lds_m2d[2][k][b], lds_m2d[3][k][b]));
-      const BlockScale br = block_scale(__uint_as_float(m), S_row);
-      const BlockScale bc = block_scale(__uint_as_float(m), S_col);
-      lds_s2d[0][k][b] = br.code;
-      lds_e2d[0][k][b] = br.mult;
-      lds_s2d[1][k][b] = bc.code;
-      lds_e2d[1][k][b] = bc.mult;
-    }
-    __syncthreads();
-  }
-
-  // 3. row-wise orientation.
-  if (do_row) {
-    const uint32_t key = SR ? sr_key(p.sr_seed, 0) : 0u;
-    const uint32_t half_cols = p.cols >> 1;
-    const uint32_t scale_cols = p.cols >> 4;
-#pragma unroll
-    for (int k = 0; k < T::kUPT; ++k) {
-      const uint32_t row = r0 + rsub + 16 * k;
-      float v[8];
-      unit_values<DT>(w[k], v);
-      uint32_t code;
-      float mult;
-      if (B2D) {
-        code = lds_s2d[0][k][ucol >> 1];
-        mult = lds_e2d[0][k][ucol >> 1];
-      } else {
-        uint32_t m = max_abs_bits(v);
-        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
-        const BlockScale bs = block_scale(__uint_as_float(m), S_row);
-        code = bs.code;
-        mult = bs.mult;
-      }
-      const bool valid = col_ok && row < p.rows;
-      const uint32_t byte0 = row * half_cols + (col >> 1);
-      const uint32_t word = encode8<SR>(v, mult, key, byte0);
-      if (valid) *reinterpret_cast<uint32_t *>(p.row_data + byte0) = word;
-      const uint32_t c1 = static_cast<uint32_t>(__shfl_down(static_cast<int>(code), 2, 64));
-      const uint32_t c2 = static_cast<uint32_t>(__shfl_down(static_cast<int>(code), 4, 64));
-      const uint32_t c3 = static_cast<uint32_t>(__shfl_down(static_cast<int>(code), 6, 64));
-      if (valid && (ucol & 7) == 0)
-        store_scale_group(p.row_scales, row, col >> 4, scale_cols, p.swizzled != 0,
-                          code | (c1 << 8) | (c2 << 16) | (c3 << 24));
-    }
-  }
-
-  // 4. column-wise orientation.
-  if (do_col) {
-    __syncthreads();
-    const uint32_t key = SR ? sr_key(p.sr_seed, 1) : 0u;
-    const int cq = tid % T::kNCQ;
-    const int rb = tid / T::kNCQ;
-    const int lc0 = cq * T::kCPT;
-    const uint32_t rr = r0 + rb * 16;
-    const bool rb_ok = rr < p.rows;
-    const uint32_t half_rows = p.rows >> 1;
-    uint2 raw[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      raw[i] = *reinterpret_cast<const uint2 *>(lds_tile + ((rb * 16 + i) * T::kStride + lc0) * T::kElem);
-#pragma unroll
-    for (int c = 0; c < T::kCPT; ++c) {
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (DT == kBF16) {
-          const uint32_t wd = (c < 2) ? raw[i].x : raw[i].y;
-          v[i] = (c & 1) ? bf16_hi(wd) : bf16_lo(wd);
-        } else {
-          v[i] = __uint_as_float(c == 0 ? raw[i].x : raw[i].y);
-        }
-      }
-      if (RHT) rht16(v, p.sign_mask);
-      uint32_t code;
-      float mult;
-      if (B2D) {
-        code = lds_s2d[1][rb][(lc0 + c) >> 4];
-        mult = lds_e2d[1][rb][(lc0 + c) >> 4];
-      } else {
-        const BlockScale bs = block_scale(__uint_as_float(max_abs_bits(v)), S_col);
-        code = bs.code;
-        mult = bs.mult;
-      }
-      const uint32_t j = c0 + lc0 + c;
-      const uint32_t byte0 = j * half_rows + (rr >> 1);
-      uint2 out;
-      out.x = encode8<SR>(v, mult, key, byte0);
-      out.y = encode8<SR>(v + 8, mult, key, byte0 + 4);
-      if (j < p.cols && rb_ok) *reinterpret_cast<uint2 *>(p.col_data + byte0) = out;
-      lds_cs[lc0 + c][rb] = static_cast<uint8_t>(code);
-    }
-    __syncthreads();
-    // column-wise scales: kTC columns x kNRB codes, one 32-bit word per thread
-    constexpr int kWordsPerCol = T::kNRB / 4;
-    if (tid < kTC * kWordsPerCol) {
-      const int lcol = tid / kWordsPerCol;
-      const int h = tid % kWordsPerCol;
-      const uint32_t j = c0 + lcol;
-      const uint32_t sc = (r0 >> 4) + 4 * h;
-      const uint32_t scale_cols = p.rows >> 4;
-      if (j < p.cols && sc < scale_cols) {
-        const uint32_t word = *reinterpret_cast<const uint32_t *>(&lds_cs[lcol][4 * h]);
-        store_scale_group(p.col_scales, j, sc, scale_cols, p.swizzled != 0, word);
-      }
-    }
   }
 }
 
@@ -638,6 +419,240 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Register-tile cast with the column-wise RHT.
+//
+// A workgroup owns a 128 x 128 tile; thread (cg = tid % 32, rq = tid / 32)
+// owns rows 16rq..16rq+15 of columns 4cg..4cg+3, so each column's 16-row
+// RHT group is whole in one thread: the transform, the block maximum and
+// the eight output bytes of that column need no lane exchange. A wave's load
+// reads 2 rows x 256 contiguous bytes. Row-wise (plain) 1x16 blocks are lane
+// quads (DPP). Row-wise and column-wise data bytes are staged in LDS and
+// leave as 16-byte stores (64 contiguous bytes per row / column).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_quad(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+// quad_perm controls: xor 1, xor 2, and broadcast of quad lane s
+constexpr int kQuadXor1 = 0xB1;  // [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // [2,3,0,1]
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x, int s) {
+  switch (s) {
+    case 0: return dpp_quad<0x00>(x);
+    case 1: return dpp_quad<0x55>(x);
+    case 2: return dpp_quad<0xAA>(x);
+    default: return dpp_quad<0xFF>(x);
+  }
+}
+
+template <int DT, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
+  constexpr int kElem = DT == kBF16 ? 2 : 4;
+  constexpr int W = kElem;  // 32-bit words per 4-column row piece: 2 (BF16) or 4 (FP32)
+  __shared__ float lds_mult[2][128];
+  __shared__ __align__(4) uint8_t lds_rs[kRT * 8];
+  __shared__ __align__(4) uint8_t lds_cs[kRT * 8];
+  __shared__ __align__(16) uint8_t lds_rd[kRT][64 + 16];  // row-wise data bytes (padded rows)
+  __shared__ __align__(16) uint8_t lds_cd[kRT][64 + 16];  // column-wise data bytes
+
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+
+  const int tid = threadIdx.x;
+  const int cg = tid & 31;
+  const int rq = tid >> 5;
+  const uint32_t r0 = blockIdx.y * kRT;
+  const uint32_t c0 = blockIdx.x * kRT;
+  const uint32_t col = c0 + 4 * cg;
+  const uint32_t rbase = r0 + 16 * rq;
+  const bool col_ok = col < p.cols;
+  const bool do_row = p.row_data != nullptr;
+  const bool do_col = p.col_data != nullptr;
+
+  uint32_t w[16][W];
+  auto load_piece = [&](int k) {
+    const uint8_t *src = static_cast<const uint8_t *>(p.x) + (static_cast<uint64_t>(rbase + k) * p.cols + col) * kElem;
+    if constexpr (DT == kBF16) {
+      const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(src));
+      w[k][0] = t.x;
+      w[k][1] = t.y;
+    } else {
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+      w[k][0] = t.x;
+      w[k][1] = t.y;
+      w[k][2] = t.z;
+      w[k][3] = t.w;
+    }
+  };
+  if (r0 + kRT <= p.rows && c0 + kRT <= p.cols) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) load_piece(k);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (col_ok && rbase + k < p.rows) {
+        load_piece(k);
+      } else {
+#pragma unroll
+        for (int q = 0; q < W; ++q) w[k][q] = 0;
+      }
+    }
+  }
+  auto value = [&](int k, int c) -> float {
+    if constexpr (DT == kBF16) return (c & 1) ? bf16_hi(w[k][c >> 1]) : bf16_lo(w[k][c >> 1]);
+    else return __uint_as_float(w[k][c]);
+  };
+
+  const float S_row = do_row ? global_encode_scale(*p.row_amax) : 1.0f;
+  const float S_col = do_col ? global_encode_scale(*p.col_amax) : 1.0f;
+  if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
+  else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
+  const bool swz = p.swizzled != 0;
+  auto code_slot = [swz](int line, int blk) {
+    return swz ? ((blk >> 2) << 9) + ((line & 31) << 4) + ((line >> 5) << 2) + (blk & 3) : line * 8 + blk;
+  };
+
+  // ---- row-wise block codes: row k's block is the lane quad's 16 values ----
+  uint32_t rcode[16];
+  if (do_row) {
+    const int q = cg & 3;
+    uint32_t mine[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine[j] = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) m = max(m, __float_as_uint(value(k, c)) & 0x7FFFFFFFu);
+      m = max(m, dpp_quad<kQuadXor1>(m));
+      m = max(m, dpp_quad<kQuadXor2>(m));
+      // quad lane q turns rows q, q+4, q+8, q+12 into codes
+      if ((k & 3) == 0) mine[k >> 2] = m;
+      else mine[k >> 2] = pick(q == (k & 3), m, mine[k >> 2]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine[j] = block_code(mine[j], S_row);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) rcode[k] = quad_bcast(mine[k >> 2], k & 3);
+    if (q == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) lds_rs[code_slot(16 * rq + k, cg >> 2)] = static_cast<uint8_t>(rcode[k]);
+    }
+  }
+  __syncthreads();  // multipliers ready
+
+  // ---- row-wise encode: 4 codes (2 bytes) per row ----
+  if (do_row) {
+    const uint32_t krow = SR ? sr_key(p.sr_seed, 0) : 0u;
+    const uint32_t half_cols = p.cols >> 1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float e = lds_mult[0][rcode[k]];
+      const float s0 = value(k, 0) * e, s1 = value(k, 1) * e, s2 = value(k, 2) * e, s3 = value(k, 3) * e;
+      uint32_t h;
+      if (SR) {
+        const uint32_t byte0 = (rbase + k) * half_cols + (col >> 1);
+        const uint32_t ra = fmix32(krow ^ byte0), rb = fmix32(krow ^ (byte0 + 1));
+        h = (e2m1_sr(s0, ra & 0xFFFFu) | (e2m1_sr(s1, ra >> 16) << 4)) |
+            ((e2m1_sr(s2, rb & 0xFFFFu) | (e2m1_sr(s3, rb >> 16) << 4)) << 8);
+      } else {
+        h = e2m1_rne_pair_into(__float_as_uint(s0), s0, s1, 0);
+        h = e2m1_rne_pair_into(h, s2, s3, 1);
+      }
+      *reinterpret_cast<uint16_t *>(&lds_rd[16 * rq + k][2 * cg]) = static_cast<uint16_t>(h);
+    }
+  }
+
+  // ---- column-wise: RHT of each 16-row column group, then encode ----
+  if (do_col) {
+    const uint32_t kcol = SR ? sr_key(p.sr_seed, 1) : 0u;
+    const uint32_t half_rows = p.rows >> 1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = value(k, c);
+      rht16(v, p.sign_mask);
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+      const uint32_t code = block_code(m, S_col);
+      const float e = lds_mult[1][code];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] *= e;
+      uint32_t lo, hi;
+      if (SR) {
+        const uint32_t byte0 = (col + c) * half_rows + (rbase >> 1);
+        lo = encode8_scaled<true>(v, kcol, byte0);
+        hi = encode8_scaled<true>(v + 8, kcol, byte0 + 4);
+      } else {
+        lo = e2m1_rne_x8(v);
+        hi = e2m1_rne_x8(v + 8);
+      }
+      *reinterpret_cast<u32x2 *>(&lds_cd[4 * cg + c][8 * rq]) = u32x2{lo, hi};
+      lds_cs[code_slot(4 * cg + c, rq)] = static_cast<uint8_t>(code);
+    }
+  }
+  __syncthreads();
+
+  // ---- data: 128 lines x 64 bytes per orientation, 16 bytes per store ----
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int e = tid + kThreads * it;
+    const int line = e >> 2, part = e & 3;
+    if (do_row) {
+      const uint32_t row = r0 + line;
+      const uint32_t cc = c0 + 32 * part;  // first column of this 16-byte piece
+      if (row < p.rows && cc < p.cols) {
+        uint8_t *dst = p.row_data + row * (p.cols >> 1) + (cc >> 1);
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(&lds_rd[line][16 * part]);
+        if (cc + 32 <= p.cols)
+          __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(dst));
+        else
+          __builtin_nontemporal_store(u32x2{val.x, val.y}, reinterpret_cast<u32x2 *>(dst));
+      }
+    }
+    if (do_col) {
+      const uint32_t j = c0 + line;
+      const uint32_t rr = r0 + 32 * part;
+      if (j < p.cols && rr < p.rows) {
+        uint8_t *dst = p.col_data + j * (p.rows >> 1) + (rr >> 1);
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(&lds_cd[line][16 * part]);
+        if (rr + 32 <= p.rows)
+          __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(dst));
+        else
+          __builtin_nontemporal_store(u32x2{val.x, val.y}, reinterpret_cast<u32x2 *>(dst));
+      }
+    }
+  }
+
+  // ---- scales ----
+  if (swz) {
+    if (do_row)
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(lds_rs)[tid],
+                                  reinterpret_cast<uint32_t *>(p.row_scales + swizzled_scale_offset(r0, c0 >> 4, p.cols >> 4)) + tid);
+    if (do_col)
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(lds_cs)[tid],
+                                  reinterpret_cast<uint32_t *>(p.col_scales + swizzled_scale_offset(c0, r0 >> 4, p.rows >> 4)) + tid);
+    return;
+  }
+  const int t_line = tid >> 1;
+  const int t_half = tid & 1;
+  if (do_row) {
+    const uint32_t row = r0 + t_line;
+    const uint32_t sc = (c0 >> 4) + 4 * t_half;
+    if (row < p.rows && sc < (p.cols >> 4))
+      store_scale_group(p.row_scales, row, sc, p.cols >> 4, false, reinterpret_cast<const uint32_t *>(lds_rs)[tid]);
+  }
+  if (do_col) {
+    const uint32_t j = c0 + t_line;
+    const uint32_t sc = (r0 >> 4) + 4 * t_half;
+    if (j < p.cols && sc < (p.rows >> 4))
+      store_scale_group(p.col_scales, j, sc, p.rows >> 4, false, reinterpret_cast<const uint32_t *>(lds_cs)[tid]);
+  }
+}
+
 template <int DT, bool B2D, bool SR>
 hipError_t launch_rt(const CastArgs &a, hipStream_t s) {
   dim3 grid((a.cols + kRT - 1) / kRT, (a.rows + kRT - 1) / kRT);
@@ -647,9 +662,8 @@ hipError_t launch_rt(const CastArgs &a, hipStream_t s) {
 
 template <int DT, bool SR>
 hipError_t launch_rht(const CastArgs &a, hipStream_t s) {
-  using T = Tile<DT>;
-  dim3 grid((a.cols + kTC - 1) / kTC, (a.rows + T::kTR - 1) / T::kTR);
-  hipLaunchKernelGGL((k_cast_lds<DT, false, true, SR>), grid, dim3(kThreads), 0, s, a);
+  dim3 grid((a.cols + kRT - 1) / kRT, (a.rows + kRT - 1) / kRT);
+  hipLaunchKernelGGL((k_cast_rht<DT, SR>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

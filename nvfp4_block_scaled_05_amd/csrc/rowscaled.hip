@@ -22,13 +22,17 @@ struct Unit {
   uint32_t w[kWords];
 };
 
-template <int DT>
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// NT: non-temporal (the part of a row that stays in registers is read once);
+// the part beyond that is read twice and goes through the caches.
+template <int DT, bool NT>
 __device__ __forceinline__ Unit<DT> load_unit(const void *x, uint64_t elem_off) {
   Unit<DT> u;
-  const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(x) + elem_off * (DT == kBF16 ? 2 : 4));
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(x) + elem_off * (DT == kBF16 ? 2 : 4));
 #pragma unroll
   for (int q = 0; q < Unit<DT>::kWords / 4; ++q) {
-    const uint4 t = src[q];
+    const u32x4 t = NT ? __builtin_nontemporal_load(src + q) : src[q];
     u.w[4 * q] = t.x;
     u.w[4 * q + 1] = t.y;
     u.w[4 * q + 2] = t.z;
@@ -88,7 +92,7 @@ __device__ __forceinline__ void encode_unit(const Unit<DT> &u, bool valid, uint3
   } else {
     word = e2m1_rne_x8(s);
   }
-  if (valid) *reinterpret_cast<uint32_t *>(p.data + byte0) = word;
+  if (valid) __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(p.data + byte0));
   const uint32_t c1 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 2, 64));
   const uint32_t c2 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 4, 64));
   const uint32_t c3 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 6, 64));
@@ -98,7 +102,7 @@ __device__ __forceinline__ void encode_unit(const Unit<DT> &u, bool valid, uint3
     const uint64_t off = static_cast<uint64_t>(row) * scale_cols + sc;
     const uint32_t group = bs.code | (c1 << 8) | (c2 << 16) | (c3 << 24);
     if ((scale_cols & 3u) == 0 && sc + 4 <= scale_cols) {
-      *reinterpret_cast<uint32_t *>(p.scales + off) = group;
+      __builtin_nontemporal_store(group, reinterpret_cast<uint32_t *>(p.scales + off));
     } else {
 #pragma unroll
       for (uint32_t i = 0; i < 4; ++i)
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
   for (int k = 0; k < kRegUnits; ++k) {
     const uint32_t u = tid + kThreads * k;
     if (u < units) {
-      reg[k] = load_unit<DT>(p.x, row_off + 8ull * u);
+      reg[k] = load_unit<DT, true>(p.x, row_off + 8ull * u);
       if (COMPUTE) m = max(m, unit_max_bits<DT>(reg[k]));
     } else {
 #pragma unroll
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
   float amax;
   if (COMPUTE) {
     for (uint32_t u = tid + kThreads * kRegUnits; u < units; u += kThreads)
-      m = max(m, unit_max_bits<DT>(load_unit<DT>(p.x, row_off + 8ull * u)));
+      m = max(m, unit_max_bits<DT>(load_unit<DT, false>(p.x, row_off + 8ull * u)));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 64)));
     if ((tid & 63) == 0) lds4[tid >> 6] = m;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
     const uint32_t u = base + tid;
     Unit<DT> cur;
     if (u < units) {
-      cur = load_unit<DT>(p.x, row_off + 8ull * u);
+      cur = load_unit<DT, false>(p.x, row_off + 8ull * u);
     } else {
 #pragma unroll
       for (int q = 0; q < Unit<DT>::kWords; ++q) cur.w[q] = 0;
