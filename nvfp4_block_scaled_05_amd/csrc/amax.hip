@@ -7,6 +7,8 @@
 // non-negative binary32 values an unsigned integer max of the bit patterns
 // is the float max, so each workgroup ends with one global_atomic_umax per
 // buffer on the +0.0 that the zeroing pass wrote.
+#include <type_traits>
+
 #include "codec.h"
 #include "launch.h"
 
@@ -60,12 +62,14 @@ __global__ void k_zero_amax(float *a, float *b, const float *noop) {
 // before reducing, so the whole input is requested in one round trip while
 // the number of workgroups, and so of atomics per buffer, stays small
 // (640 for an 80 MiB input).
+// Small inputs use fewer vectors per thread (VPT) so that they still spread
+// over many workgroups.
 constexpr int kAmaxThreads = 512;
-constexpr int kVecPerThread = 16;
 
-template <int DT>
+template <int DT, int VPT>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a,
                                                        float *b, const float *noop) {
+  constexpr int kVecPerThread = VPT;
   __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
   const uint64_t base = static_cast<uint64_t>(blockIdx.x) * (kAmaxThreads * kVecPerThread) + threadIdx.x;
@@ -186,13 +190,25 @@ hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b,
                        hipStream_t s) {
   const uint64_t nvec = n * (dtype == kBF16 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
-  const uint64_t blocks = (nvec + kAmaxThreads * kVecPerThread - 1) / (kAmaxThreads * kVecPerThread);
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_amax<kBF16>, dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
-                       static_cast<const uint4 *>(x), nvec, a, b, noop);
+  auto go = [&](auto vpt_tag) {
+    constexpr int VPT = decltype(vpt_tag)::value;
+    const uint64_t blocks = (nvec + kAmaxThreads * VPT - 1) / (kAmaxThreads * VPT);
+    if (dtype == kBF16)
+      hipLaunchKernelGGL((k_amax<kBF16, VPT>), dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
+                         static_cast<const uint4 *>(x), nvec, a, b, noop);
+    else
+      hipLaunchKernelGGL((k_amax<kFP32, VPT>), dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
+                         static_cast<const uint4 *>(x), nvec, a, b, noop);
+  };
+  // >= 512 workgroups at 16 vectors per thread; smaller inputs take 4 (tens to
+  // hundreds of workgroups: enough parallelism while the number of atomics,
+  // which serialize, stays small); tiny ones take 1.
+  if (nvec >= uint64_t{kAmaxThreads} * 16 * 512)
+    go(std::integral_constant<int, 16>{});
+  else if (nvec >= uint64_t{kAmaxThreads} * 4 * 16)
+    go(std::integral_constant<int, 4>{});
   else
-    hipLaunchKernelGGL(k_amax<kFP32>, dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
-                       static_cast<const uint4 *>(x), nvec, a, b, noop);
+    go(std::integral_constant<int, 1>{});
   return hipGetLastError();
 }
 

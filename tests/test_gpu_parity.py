@@ -384,3 +384,37 @@ def test_deterministic_across_runs():
     for k in ("row_data", "row_scales", "col_data", "col_scales", "amax_row", "amax_col"):
         assert np.array_equal(outs[0][k], outs[1][k]) and np.array_equal(outs[0][k], outs[2][k])
         assert np.array_equal(outs[3][k], outs[4][k])
+
+
+@pytest.mark.parametrize("mode", ["2d_swizzled", "1d_sr", "rht", "rowscaled"])
+def test_graph_capture_replays_match_eager(mode):
+    # The calls queue kernels only (no memset, no allocation, no sync), so a
+    # captured graph must reproduce the eager result on every replay, with
+    # other work and synchronizations between the replays.
+    x = W.c2(rows=256, cols=384, seed=81)
+    xd = to_device(x)
+    cfg = {"2d_swizzled": nv.make_config(block_2d=True, swizzled=True),
+           "1d_sr": nv.make_config(stochastic=True, sr_seed=3),
+           "rht": nv.make_config(rht=True, rht_sign_mask=0x9A5C),
+           "rowscaled": nv.make_config(row_scaled=True)}[mode]
+    rs = mode == "rowscaled"
+    row = nv.empty_orientation(256, 384, DEV, 256 if rs else 1)
+    col = None if rs else nv.empty_orientation(384, 256, DEV)
+    outs = [row.data, row.scales, row.amax] + ([] if col is None else [col.data, col.scales, col.amax])
+    nv.nvfp4_quantize(xd, row, col, cfg)
+    torch.cuda.synchronize()
+    eager = [host(t).copy() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        nv.nvfp4_quantize(xd, row, col, cfg, s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.view(torch.uint8).fill_(0x33 + rep)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, t in zip(eager, outs):
+            assert np.array_equal(e, host(t)), (mode, rep)
