@@ -2,8 +2,10 @@
 
 One step = one nvfp4_quantize call on the 8192x5120 BF16 workload with
 16x16 blocks, row-wise and column-wise output, GEMM-swizzled E4M3 scales,
-round to nearest even and a per-tensor amax computed inside the call
-(zeroing pass + amax reduction + fused cast-transpose). Inputs are resident
+round to nearest even and a per-tensor amax computed inside the call (amax
+pass storing per-workgroup maxima in a workspace, then the fused
+cast-transpose, which finishes the reduction and writes both amax buffers;
+two launches). Inputs are resident
 in HBM before timing starts; four input/output sets rotate so that no step
 finds its input in the 256 MB Infinity Cache from an earlier step.
 
@@ -12,8 +14,11 @@ outputs, both scale arrays, the amax pair) / seconds per call, in GB/s.
 
 The roofline entry covers the dominant kernel (the fused cast-transpose):
 its algorithmic bytes (one read of the input, both outputs and scales, the
-two amax reads) over its average duration, timed with HIP events on the
-stream it runs on, against the 8 TB/s HBM peak.
+two amax words) over its average duration, timed with HIP events on the
+stream it runs on, against the 8 TB/s HBM peak. Events cannot sit between
+the two kernels of one call, so the cast is timed in a split call (the
+amax computed by nvfp4_compute_amax first, then the cast alone reading it);
+the kernel trace of the same command shows the cast inside the real call.
 
 cpu_baseline times the CPU oracle (single thread) on the same workload.
 """
@@ -37,7 +42,7 @@ SCALE_BYTES = N // 16                     # per orientation
 AMAX_BYTES = 4
 # whole call: input read twice (amax pass + cast), both outputs, both scales, two amaxes
 B_ALG_CALL = 2 * INPUT_BYTES + 2 * FP4_BYTES + 2 * SCALE_BYTES + 2 * AMAX_BYTES
-# cast kernel alone: one input read, both outputs and scales, the two amax reads
+# cast kernel alone: one input read, both outputs and scales, the two amax words
 B_ALG_CAST = INPUT_BYTES + 2 * FP4_BYTES + 2 * SCALE_BYTES + 2 * AMAX_BYTES
 HBM_PEAK_GBS = 8000.0
 METRIC = "NVFP4 quantize HBM GB/s and % of peak, 8192x5120 BF16, row+col output"
@@ -98,11 +103,13 @@ def summarize_trace(db_path):
     print("|---|---:|---:|---:|---:|---:|")
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         print(f"| {k} | {len(v)} | {st.mean(v):.0f} | {st.median(v):.0f} | {min(v)} | {max(v)} |")
+    # one call with a workspace = k_amax k_cast_rt; the split call of the
+    # roofline timing (k_zero_amax k_amax, then k_cast_rt) is skipped
     spans = []
-    for i in range(len(rows) - 2):
-        a, b, c = rows[i], rows[i + 1], rows[i + 2]
-        if a[0].startswith("k_zero") and b[0].startswith("k_amax") and c[0].startswith("k_cast"):
-            spans.append(c[2] - a[1])
+    for i in range(len(rows) - 1):
+        a, b = rows[i], rows[i + 1]
+        if a[0].startswith("k_amax") and b[0].startswith("k_cast") and (i == 0 or not rows[i - 1][0].startswith("k_zero")):
+            spans.append(b[2] - a[1])
     if spans:
         med = st.median(spans)
         print(f"\nper-call span, first kernel start to last kernel end: {len(spans)} calls, "
@@ -193,6 +200,9 @@ def run_other(name, steps, warmup):
     else:
         x, mask, seed = workloads.c5()
         cfg, rowwise, columnwise = nv.make_config(rht=True, rht_sign_mask=mask, stochastic=True, sr_seed=seed), True, True
+    workspace = nv.empty_workspace(dev)
+    if not cfg.row_scaled:
+        cfg.workspace = workspace.data_ptr()
     xd = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16
           else torch.from_numpy(x)).to(dev)
     n_sets = 1 if name in ("c1", "c3") else N_SETS  # small inputs: one reused output, as in the pages' loop
@@ -297,7 +307,8 @@ def main():
         col = nv.empty_orientation(COLS, ROWS, dev)
         sets.append((x, row, col))
     del x0
-    cfg = nv.make_config(block_2d=True, swizzled=True)
+    workspace = nv.empty_workspace(dev)  # one stream: the calls never overlap
+    cfg = nv.make_config(block_2d=True, swizzled=True, workspace=workspace)
     cast_only = nv.make_config(block_2d=True, swizzled=True, compute_amax=False)
     stream = torch.cuda.current_stream()
 

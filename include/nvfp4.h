@@ -126,7 +126,24 @@ typedef struct {
   /* Device pointer or NULL. When *noop == 1.0f the call writes nothing, amax
    * buffers included ("Write both NVFP4 amax buffers", Changes). */
   const float *noop;
+  /* nvfp4_quantize with compute_amax == 1 and a per-tensor amax only (not
+   * row_scaled): NULL, or device memory of at least NVFP4_WORKSPACE_BYTES
+   * bytes, 16-byte aligned, owned by the caller. With a workspace the amax
+   * pass stores one maximum per workgroup there and the cast kernel
+   * finishes the reduction and writes the amax buffers, so the call needs
+   * neither the zeroing pass nor atomics (two launches instead of three).
+   * With NULL the amax buffers are zeroed and reduced with atomics. The
+   * contents on entry do not matter and are unspecified on return; calls
+   * that share a workspace must not run concurrently (queue them on one
+   * stream). Ignored by the other calls and paths. */
+  void *workspace;
 } nvfp4_config_t;
+
+/* Bytes of the optional quantize workspace (nvfp4_config_t.workspace). */
+#define NVFP4_WORKSPACE_BYTES 16384u
+
+/* NVFP4_WORKSPACE_BYTES, for bindings that cannot read the macro. */
+uint64_t nvfp4_workspace_bytes(void);
 
 /*
  * Amax reduction ("Write both NVFP4 amax buffers", Description and Changes).
@@ -156,8 +173,10 @@ nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t ro
  * E2M1(fl(v * e)), each step one correctly rounded FP32 operation.
  *
  * With compute_amax == 1 this queues the zeroing pass, the amax reduction
- * and the cast (row-scaled: one fused kernel); with compute_amax == 0 only
- * the cast, which reads the amax buffers as given.
+ * and the cast, or with a workspace the amax pass and the cast, which
+ * finishes the reduction (row-scaled: one fused kernel); with
+ * compute_amax == 0 only the cast, which reads the amax buffers as given.
+ * Either way the amax buffers hold the same values afterwards.
  */
 nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
                               const nvfp4_out_t *row, const nvfp4_out_t *col,

@@ -42,7 +42,7 @@ NVFP4_SCALE_E4M3 = 0
 NVFP4_SCALE_UE5M3 = 1
 
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
-            "nvfp4_debug_rht_colwise")
+            "nvfp4_workspace_bytes", "nvfp4_debug_rht_colwise")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -61,6 +61,7 @@ class nvfp4_config_t(ctypes.Structure):
         ("rht_sign_mask", ctypes.c_uint32),
         ("compute_amax", ctypes.c_uint32),
         ("noop", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
     ]
 
 
@@ -100,6 +101,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_out_t), I64, I64, U32, U32, P, P]
     lib.nvfp4_last_error.restype = ctypes.c_char_p
     lib.nvfp4_last_error.argtypes = []
+    lib.nvfp4_workspace_bytes.restype = ctypes.c_uint64
+    lib.nvfp4_workspace_bytes.argtypes = []
     lib.nvfp4_debug_rht_colwise.restype = I
     lib.nvfp4_debug_rht_colwise.argtypes = [P, I, I64, I64, U32, P, P]
     _lib = lib
@@ -137,11 +140,14 @@ def _shape2d(x: torch.Tensor):
 
 def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, stochastic=False, sr_seed=0,
                 row_scaled=False, rht=False, rht_sign_mask=0, compute_amax=True,
-                noop: Optional[torch.Tensor] = None) -> nvfp4_config_t:
+                noop: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> nvfp4_config_t:
+    """The config struct. The tensors named by noop and workspace must stay
+    alive while the config is used."""
     return nvfp4_config_t(int(block_2d), NVFP4_SCALES_GEMM_SWIZZLED if swizzled else NVFP4_SCALES_COMPACT,
                           int(scale_fmt), int(stochastic), int(sr_seed) & 0xFFFFFFFF, int(row_scaled), int(rht),
                           int(rht_sign_mask) & 0xFFFFFFFF, int(compute_amax),
-                          None if noop is None else noop.data_ptr())
+                          None if noop is None else noop.data_ptr(),
+                          None if workspace is None else workspace.data_ptr())
 
 
 @dataclasses.dataclass
@@ -157,6 +163,10 @@ class Orientation:
 
 def nvfp4_last_error() -> str:
     return load().nvfp4_last_error().decode()
+
+
+def nvfp4_workspace_bytes() -> int:
+    return int(load().nvfp4_workspace_bytes())
 
 
 def nvfp4_compute_amax(x: torch.Tensor, row_amax: Optional[torch.Tensor], col_amax: Optional[torch.Tensor],
@@ -198,12 +208,30 @@ def empty_orientation(n: int, k: int, device, amax_len: int = 1) -> Orientation:
                        torch.empty((amax_len,), dtype=torch.float32, device=device))
 
 
+def empty_workspace(device) -> torch.Tensor:
+    """An (uninitialized) quantize workspace; torch's allocator aligns it to 512 bytes."""
+    return torch.empty((nvfp4_workspace_bytes(),), dtype=torch.uint8, device=device)
+
+
 def quantize(x: torch.Tensor, *, rowwise=True, columnwise=True, cfg: Optional[nvfp4_config_t] = None,
-             stream=None):
-    """Allocate outputs for x [R][C] and run nvfp4_quantize. Returns (row, col)."""
+             stream=None, use_workspace: bool = True):
+    """Allocate outputs for x [R][C] and run nvfp4_quantize. Returns (row, col).
+
+    With use_workspace (and no workspace in cfg) a workspace is allocated for
+    the call, so a computed per-tensor amax takes two launches instead of
+    three; torch's stream-ordered allocator keeps it valid until the call's
+    work is done."""
     rows, cols = _shape2d(x)
     cfg = cfg if cfg is not None else make_config()
     row = empty_orientation(rows, cols, x.device, rows if cfg.row_scaled else 1) if rowwise else None
     col = empty_orientation(cols, rows, x.device) if columnwise else None
+    ws = None
+    if use_workspace and not cfg.workspace and cfg.compute_amax and not cfg.row_scaled:
+        ws = empty_workspace(x.device)
+        cfg = nvfp4_config_t.from_buffer_copy(cfg)
+        cfg.workspace = ws.data_ptr()
+        if stream is not None:  # keep the block from being reused before the call's stream is done
+            ws.record_stream(stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream)))
     nvfp4_quantize(x, row, col, cfg, stream)
+    del ws
     return row, col

@@ -6,7 +6,9 @@
 // copy and no second read are needed. Max is exact and order-free; on
 // non-negative binary32 values an unsigned integer max of the bit patterns
 // is the float max, so each workgroup ends with one global_atomic_umax per
-// buffer on the +0.0 that the zeroing pass wrote.
+// buffer on the +0.0 that the zeroing pass wrote. With a caller workspace
+// the workgroups store their maxima there instead and the cast kernel
+// reduces them, which needs neither the zeroing pass nor atomics.
 #include <type_traits>
 
 #include "codec.h"
@@ -56,47 +58,55 @@ __global__ void k_zero_amax(float *a, float *b, const float *noop) {
   }
 }
 
-// Per-tensor amax. nvec = number of 16-byte vectors of x. A workgroup of
-// kAmaxThreads (8 waves) owns one contiguous chunk of kAmaxThreads *
-// kVecPerThread vectors (128 KiB) and every thread issues all its loads
-// before reducing, so the whole input is requested in one round trip while
-// the number of workgroups, and so of atomics per buffer, stays small
-// (640 for an 80 MiB input).
-// Small inputs use fewer vectors per thread (VPT) so that they still spread
-// over many workgroups.
+// Per-tensor amax. nvec = number of 16-byte vectors of x, cut into nchunks
+// chunks of kAmaxThreads * VPT vectors (128 KiB at VPT 16). A workgroup of
+// kAmaxThreads (8 waves) reduces chunks blockIdx.x, blockIdx.x + gridDim.x,
+// ...; every thread issues all loads of a chunk before reducing, so a chunk
+// is requested in one round trip. Small inputs use fewer vectors per thread
+// so that they still spread over many workgroups.
+// The workgroup's maximum then goes either to partials[blockIdx.x] (plain
+// store; the cast kernel finishes the reduction) or, with partials == NULL,
+// into a and b by atomic max. The atomic form is launched with one chunk per
+// workgroup, which keeps the number of atomics per buffer small (640 for an
+// 80 MiB input).
 constexpr int kAmaxThreads = 512;
 
 template <int DT, int VPT>
-__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a,
-                                                       float *b, const float *noop) {
-  constexpr int kVecPerThread = VPT;
+__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, uint32_t nchunks,
+                                                       float *a, float *b, uint32_t *partials, const float *noop) {
   __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
-  const uint64_t base = static_cast<uint64_t>(blockIdx.x) * (kAmaxThreads * kVecPerThread) + threadIdx.x;
-  uint4 v[kVecPerThread];
-#pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
-    const uint64_t i = base + static_cast<uint64_t>(k) * kAmaxThreads;
-    v[k] = i < nvec ? x[i] : make_uint4(0, 0, 0, 0);
-  }
   uint32_t m32 = 0;        // FP32: max of |x| bit patterns
   ushort2_t m16 = {0, 0};  // BF16: max of 15-bit magnitudes, two lanes
+  for (uint32_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+    const uint64_t base = static_cast<uint64_t>(chunk) * (kAmaxThreads * VPT) + threadIdx.x;
+    uint4 v[VPT];
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k) {
-    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    for (int k = 0; k < VPT; ++k) {
+      const uint64_t i = base + static_cast<uint64_t>(k) * kAmaxThreads;
+      v[k] = i < nvec ? x[i] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (DT == kBF16)
-        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[j] & 0x7FFF7FFFu));
-      else
-        m32 = max(m32, w[j] & 0x7FFFFFFFu);
+    for (int k = 0; k < VPT; ++k) {
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (DT == kBF16)
+          m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[j] & 0x7FFF7FFFu));
+        else
+          m32 = max(m32, w[j] & 0x7FFFFFFFu);
+      }
     }
   }
   uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
   m = block_umax<kAmaxThreads>(m, lds);
   if (threadIdx.x == 0) {
-    publish_max(a, m);
-    if (b != a) publish_max(b, m);
+    if (partials != nullptr) {
+      partials[blockIdx.x] = m;
+    } else {
+      publish_max(a, m);
+      if (b != a) publish_max(b, m);
+    }
   }
 }
 
@@ -126,37 +136,48 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
   }
 }
 
-// RHT amax pair. Grid: (ceil(cols / (256 * VEC)), rows / 16). Each thread
-// takes VEC adjacent columns of one 16-row group: max|x| over the raw values,
-// max|t| over their 16-point transforms.
+// RHT amax pair. The input is cut into units of 16 rows x (kAmaxThreads *
+// VEC) columns, gx units across; a workgroup reduces units blockIdx.x,
+// blockIdx.x + gridDim.x, ... Each thread takes VEC adjacent columns of one
+// 16-row group: max|x| over the raw values, max|t| over their 16-point
+// transforms. Results go to partials[blockIdx.x] and
+// partials[kMaxPartials + blockIdx.x], or with partials == NULL (one unit per
+// workgroup) into row_amax and col_amax by atomic max.
 template <int DT>
 __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
-                                                       uint32_t mask, float *row_amax, float *col_amax,
-                                                       const float *noop) {
+                                                       uint32_t gx, uint32_t units, uint32_t mask, float *row_amax,
+                                                       float *col_amax, uint32_t *partials, const float *noop) {
   constexpr int VEC = DT == kBF16 ? 8 : 4;
   __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
-  const uint32_t c = (blockIdx.x * kAmaxThreads + threadIdx.x) * VEC;
-  const uint32_t r0 = blockIdx.y * 16;
   uint32_t mx = 0, mt = 0;
-  if (c < cols) {
-    float v[VEC][16];
-    load_strip<DT, VEC>(x, cols, r0, c, v);
+  for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const uint32_t by = u / gx;
+    const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * VEC;
+    if (c < cols) {
+      float v[VEC][16];
+      load_strip<DT, VEC>(x, cols, by * 16, c, v);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
+      for (int j = 0; j < VEC; ++j) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = max(mx, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
-      rht16(v[j], mask);
+        for (int r = 0; r < 16; ++r) mx = max(mx, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
+        rht16(v[j], mask);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = max(mt, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
+        for (int r = 0; r < 16; ++r) mt = max(mt, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
+      }
     }
   }
   mx = block_umax<kAmaxThreads>(mx, lds);
   __syncthreads();
   mt = block_umax<kAmaxThreads>(mt, lds);
   if (threadIdx.x == 0) {
-    publish_max(row_amax, mx);
-    publish_max(col_amax, mt);
+    if (partials != nullptr) {
+      partials[blockIdx.x] = mx;
+      partials[kMaxPartials + blockIdx.x] = mt;
+    } else {
+      publish_max(row_amax, mx);
+      publish_max(col_amax, mt);
+    }
   }
 }
 
@@ -186,21 +207,36 @@ hipError_t launch_zero_amax(float *a, float *b, const float *noop, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b, const float *noop,
-                       hipStream_t s) {
+namespace {
+
+// Grid of a reduction over `work` units: one unit per workgroup for the
+// atomic form; for the workspace form at most kMaxPartials workgroups, padded
+// to a multiple of kPartialsGrain (the extra workgroups store +0).
+uint32_t reduction_grid(uint64_t work, bool to_partials) {
+  if (!to_partials) return static_cast<uint32_t>(work);
+  const uint64_t g = (work + kPartialsGrain - 1) / kPartialsGrain * kPartialsGrain;
+  return static_cast<uint32_t>(g < kMaxPartials ? g : kMaxPartials);
+}
+
+}  // namespace
+
+hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b, uint32_t *partials,
+                       uint32_t *npartials, const float *noop, hipStream_t s) {
   const uint64_t nvec = n * (dtype == kBF16 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
   auto go = [&](auto vpt_tag) {
     constexpr int VPT = decltype(vpt_tag)::value;
-    const uint64_t blocks = (nvec + kAmaxThreads * VPT - 1) / (kAmaxThreads * VPT);
+    const uint64_t chunks = (nvec + kAmaxThreads * VPT - 1) / (kAmaxThreads * VPT);
+    const uint32_t grid = reduction_grid(chunks, partials != nullptr);
+    if (npartials) *npartials = grid;
     if (dtype == kBF16)
-      hipLaunchKernelGGL((k_amax<kBF16, VPT>), dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
-                         static_cast<const uint4 *>(x), nvec, a, b, noop);
+      hipLaunchKernelGGL((k_amax<kBF16, VPT>), dim3(grid), dim3(kAmaxThreads), 0, s, static_cast<const uint4 *>(x),
+                         nvec, static_cast<uint32_t>(chunks), a, b, partials, noop);
     else
-      hipLaunchKernelGGL((k_amax<kFP32, VPT>), dim3(static_cast<uint32_t>(blocks)), dim3(kAmaxThreads), 0, s,
-                         static_cast<const uint4 *>(x), nvec, a, b, noop);
+      hipLaunchKernelGGL((k_amax<kFP32, VPT>), dim3(grid), dim3(kAmaxThreads), 0, s, static_cast<const uint4 *>(x),
+                         nvec, static_cast<uint32_t>(chunks), a, b, partials, noop);
   };
-  // >= 512 workgroups at 16 vectors per thread; smaller inputs take 4 (tens to
+  // >= 512 chunks at 16 vectors per thread; smaller inputs take 4 (tens to
   // hundreds of workgroups: enough parallelism while the number of atomics,
   // which serialize, stays small); tiny ones take 1.
   if (nvec >= uint64_t{kAmaxThreads} * 16 * 512)
@@ -213,16 +249,20 @@ hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b,
 }
 
 hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t cols, uint32_t mask,
-                           float *row_amax, float *col_amax, const float *noop, hipStream_t s) {
+                           float *row_amax, float *col_amax, uint32_t *partials, uint32_t *npartials,
+                           const float *noop, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   const uint32_t vec = dtype == kBF16 ? 8 : 4;
-  dim3 grid((cols + kAmaxThreads * vec - 1) / (kAmaxThreads * vec), rows / 16);
+  const uint32_t gx = (cols + kAmaxThreads * vec - 1) / (kAmaxThreads * vec);
+  const uint32_t units = gx * (rows / 16);  // < 2^32: rows * cols < 2^32
+  const uint32_t grid = reduction_grid(units, partials != nullptr);
+  if (npartials) *npartials = grid;
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_rht_amax<kBF16>, grid, dim3(kAmaxThreads), 0, s, x, rows, cols, mask, row_amax, col_amax,
-                       noop);
+    hipLaunchKernelGGL(k_rht_amax<kBF16>, dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units, mask,
+                       row_amax, col_amax, partials, noop);
   else
-    hipLaunchKernelGGL(k_rht_amax<kFP32>, grid, dim3(kAmaxThreads), 0, s, x, rows, cols, mask, row_amax, col_amax,
-                       noop);
+    hipLaunchKernelGGL(k_rht_amax<kFP32>, dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units, mask,
+                       row_amax, col_amax, partials, noop);
   return hipGetLastError();
 }
 

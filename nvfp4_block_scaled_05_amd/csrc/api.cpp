@@ -73,6 +73,8 @@ nvfp4_status_t check_out(const nvfp4_out_t *o, const char *name, bool empty) {
 
 extern "C" const char *nvfp4_last_error(void) { return g_last_error.c_str(); }
 
+extern "C" uint64_t nvfp4_workspace_bytes(void) { return NVFP4_WORKSPACE_BYTES; }
+
 extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
                                              float *row_amax, float *col_amax, const nvfp4_config_t *cfg_in,
                                              void *stream) {
@@ -104,10 +106,11 @@ extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype,
   if (st != NVFP4_OK || rows * cols == 0) return st;
   if (cfg.rht)
     return hip_status(nvfp4::launch_rht_amax(x, dtype, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols),
-                                             cfg.rht_sign_mask, row_amax, col_amax, cfg.noop, s),
+                                             cfg.rht_sign_mask, row_amax, col_amax, nullptr, nullptr, cfg.noop, s),
                       "RHT amax launch");
-  return hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, cfg.noop, s),
-                    "amax launch");
+  return hip_status(
+      nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, nullptr, nullptr, cfg.noop, s),
+      "amax launch");
 }
 
 extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
@@ -127,6 +130,8 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", cfg.scale_layout);
   const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
+  if (cfg.workspace != nullptr && !aligned(cfg.workspace, 16))
+    return fail(NVFP4_ERR_ALIGN, "the workspace is not 16-byte aligned");
   if (cfg.row_scaled) {
     if (col) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 is row-wise only");
     if (cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 uses 1x16 blocks");
@@ -151,24 +156,44 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   }
   float *ra = row ? row->amax : nullptr;
   float *ca = col ? col->amax : nullptr;
+  // With a workspace the amax pass leaves per-workgroup maxima there and the
+  // cast kernel finishes the reduction. An empty input takes the zeroing
+  // pass, which is all it needs.
+  uint32_t *partials = nullptr;
+  uint32_t npartials = 0;
   if (cfg.compute_amax) {
     float *a = ra ? ra : ca;
     float *b = (ca == a) ? nullptr : ca;
-    st = hip_status(nvfp4::launch_zero_amax(a, b, cfg.noop, s), "zero amax launch");
-    if (st != NVFP4_OK) return st;
-    if (rows * cols > 0) {
+    if (cfg.workspace != nullptr && rows * cols > 0) {
+      partials = static_cast<uint32_t *>(cfg.workspace);
       if (cfg.rht)
-        st = hip_status(nvfp4::launch_rht_amax(x, dtype, R, C, cfg.rht_sign_mask, ra, ca, cfg.noop, s),
-                        "RHT amax launch");
+        st = hip_status(
+            nvfp4::launch_rht_amax(x, dtype, R, C, cfg.rht_sign_mask, ra, ca, partials, &npartials, cfg.noop, s),
+            "RHT amax launch");
       else
-        st = hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, cfg.noop, s),
+        st = hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, partials, &npartials,
+                                           cfg.noop, s),
                         "amax launch");
       if (st != NVFP4_OK) return st;
+    } else {
+      st = hip_status(nvfp4::launch_zero_amax(a, b, cfg.noop, s), "zero amax launch");
+      if (st != NVFP4_OK) return st;
+      if (rows * cols > 0) {
+        if (cfg.rht)
+          st = hip_status(
+              nvfp4::launch_rht_amax(x, dtype, R, C, cfg.rht_sign_mask, ra, ca, nullptr, nullptr, cfg.noop, s),
+              "RHT amax launch");
+        else
+          st = hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, nullptr, nullptr,
+                                             cfg.noop, s),
+                          "amax launch");
+        if (st != NVFP4_OK) return st;
+      }
     }
   }
   nvfp4::CastArgs a{x,  R,        C,    row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
-                    cfg.rht_sign_mask, cfg.noop};
+                    cfg.rht_sign_mask, cfg.noop, partials, npartials};
   return hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
 }
 

@@ -33,8 +33,81 @@ typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------------------
+// End of the per-tensor amax reduction. With a caller workspace the amax
+// pass leaves one maximum per workgroup (a multiple of four words, as float
+// bit patterns of non-negative values, so unsigned max == float max); every
+// cast workgroup reduces them itself, which costs a few cached 16-byte loads
+// per thread instead of a zeroing launch and atomics in the amax pass.
+// ---------------------------------------------------------------------------
+constexpr int kPartialVecs = kMaxPartials / 4 / kThreads;  // 16-byte loads per thread
 
+// Issued before the tile's loads, so that only these have to arrive before
+// the reduction. An index past the end is clamped to the last vector, which
+// cannot change a maximum.
+__device__ __forceinline__ void load_partials(const uint32_t *part, uint32_t n, int tid,
+                                              u32x4 (&v)[kPartialVecs]) {
+  const u32x4 *p4 = reinterpret_cast<const u32x4 *>(part);
+  const uint32_t last = n / 4 - 1;
+#pragma unroll
+  for (int i = 0; i < kPartialVecs; ++i) v[i] = p4[min(static_cast<uint32_t>(tid + i * kThreads), last)];
+}
 
+__device__ __forceinline__ uint32_t partials_max(const u32x4 (&v)[kPartialVecs]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kPartialVecs; ++i) m = max(m, max(max(v[i].x, v[i].y), max(v[i].z, v[i].w)));
+  return m;
+}
+
+constexpr int kWaves = kThreads / 64;
+
+// Workgroup maximum of N values per thread, returned to every thread.
+// Contains a barrier; lds holds N words per wave.
+template <int N>
+__device__ __forceinline__ void workgroup_max(uint32_t (&m)[N], uint32_t *lds) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) m[i] = max(m[i], static_cast<uint32_t>(__shfl_xor(static_cast<int>(m[i]), off, 64)));
+  }
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) lds[i * kWaves + (threadIdx.x >> 6)] = m[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    m[i] = lds[i * kWaves];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m[i] = max(m[i], lds[i * kWaves + w]);
+  }
+}
+
+// The amax pair of a cast workgroup: from the workspace (reduced here, and
+// stored to the amax buffers by workgroup (0, 0)) or read from the buffers.
+// TWO_ARRAYS: the column-wise amax has its own array (the RHT pair); else
+// both orientations take the one tensor amax.
+template <bool TWO_ARRAYS>
+__device__ __forceinline__ void amax_pair(const CastArgs &p, const u32x4 (&pr)[kPartialVecs],
+                                          const u32x4 (&pc)[kPartialVecs], uint32_t *lds, float &amax_row,
+                                          float &amax_col) {
+  if (p.partials != nullptr) {
+    uint32_t m[TWO_ARRAYS ? 2 : 1];
+    m[0] = partials_max(pr);
+    if constexpr (TWO_ARRAYS) m[1] = partials_max(pc);
+    workgroup_max(m, lds);
+    amax_row = __uint_as_float(m[0]);
+    amax_col = __uint_as_float(m[TWO_ARRAYS ? 1 : 0]);
+    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) {
+      if (p.row_amax) *p.row_amax = amax_row;
+      if (p.col_amax) *p.col_amax = amax_col;
+    }
+  } else {
+    amax_row = p.row_data != nullptr ? *p.row_amax : 0.0f;
+    amax_col = p.col_data != nullptr ? *p.col_amax : 0.0f;
+  }
+}
 
 // Codes of 8 consecutive values of one output row, packed little-endian
 // (element 2i in the low nibble of byte i). byte0 = index of the first byte
@@ -163,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   __shared__ __align__(4) uint8_t lds_rs[kRT * 8];
   __shared__ __align__(4) uint8_t lds_cs[kRT * 8];
   __shared__ uint32_t lds_cw[16][kRT + 1];             // column-wise data words [row group][tile col]
+  __shared__ uint32_t lds_red[kWaves];
 
   if (p.noop != nullptr && *p.noop == 1.0f) return;
 
@@ -176,6 +250,9 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   const bool col_ok = col < p.cols;
   const bool do_row = p.row_data != nullptr;
   const bool do_col = p.col_data != nullptr;
+
+  u32x4 part[kPartialVecs];
+  if (p.partials != nullptr) load_partials(p.partials, p.npartials, tid, part);
 
   uint32_t w[8][W];
   auto load_piece = [&](int k) {
@@ -205,8 +282,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
     }
   }
 
-  const float S_row = do_row ? global_encode_scale(*p.row_amax) : 1.0f;
-  const float S_col = do_col ? global_encode_scale(*p.col_amax) : 1.0f;
+  float amax_row, amax_col;
+  amax_pair<false>(p, part, part, lds_red, amax_row, amax_col);
+  const float S_row = do_row ? global_encode_scale(amax_row) : 1.0f;
+  const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
   if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
   else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
 
@@ -456,6 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   __shared__ __align__(4) uint8_t lds_cs[kRT * 8];
   __shared__ __align__(16) uint8_t lds_rd[kRT][64 + 16];  // row-wise data bytes (padded rows)
   __shared__ __align__(16) uint8_t lds_cd[kRT][64 + 16];  // column-wise data bytes
+  __shared__ uint32_t lds_red[2 * kWaves];
 
   if (p.noop != nullptr && *p.noop == 1.0f) return;
 
@@ -469,6 +549,12 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   const bool col_ok = col < p.cols;
   const bool do_row = p.row_data != nullptr;
   const bool do_col = p.col_data != nullptr;
+
+  u32x4 part_row[kPartialVecs], part_col[kPartialVecs];
+  if (p.partials != nullptr) {
+    load_partials(p.partials, p.npartials, tid, part_row);
+    load_partials(p.partials + kMaxPartials, p.npartials, tid, part_col);
+  }
 
   uint32_t w[16][W];
   auto load_piece = [&](int k) {
@@ -504,8 +590,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
     else return __uint_as_float(w[k][c]);
   };
 
-  const float S_row = do_row ? global_encode_scale(*p.row_amax) : 1.0f;
-  const float S_col = do_col ? global_encode_scale(*p.col_amax) : 1.0f;
+  float amax_row, amax_col;
+  amax_pair<true>(p, part_row, part_col, lds_red, amax_row, amax_col);
+  const float S_row = do_row ? global_encode_scale(amax_row) : 1.0f;
+  const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
   if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
   else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
   const bool swz = p.swizzled != 0;

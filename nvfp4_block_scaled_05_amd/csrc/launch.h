@@ -9,19 +9,33 @@ namespace nvfp4 {
 
 enum InType : int { kBF16 = 0, kFP32 = 1 };
 
+// Per-workgroup maxima of the amax pass in the caller's workspace: two arrays
+// of kMaxPartials words (the plain max|x|, then max|RHT(x)|), each holding a
+// non-negative float's bit pattern. The amax pass writes a multiple of
+// kPartialsGrain entries (workgroups without work write +0).
+constexpr uint32_t kMaxPartials = 2048;
+constexpr uint32_t kPartialsGrain = 4;
+static_assert(2 * kMaxPartials * 4 == 16384, "workspace size is part of the ABI");
+
 // Arguments of the fused cast(-transpose) kernels. A direction whose data
 // pointer is NULL is not written.
 struct CastArgs {
   const void *x;
   uint32_t rows, cols;
   uint8_t *row_data, *row_scales;
-  const float *row_amax;
+  float *row_amax;
   uint8_t *col_data, *col_scales;
-  const float *col_amax;
+  float *col_amax;
   uint32_t swizzled;
   uint32_t sr_seed;
   uint32_t sign_mask;
   const float *noop;
+  // NULL: the amax buffers hold the amax. Otherwise the workspace of the
+  // amax pass with npartials (a multiple of kPartialsGrain) entries per
+  // array: every workgroup reduces them and workgroup (0, 0) stores the
+  // result to the amax buffers.
+  const uint32_t *partials;
+  uint32_t npartials;
 };
 
 // Arguments of the row-scaled (per-row amax) kernel: row-wise output only.
@@ -35,10 +49,14 @@ struct RowScaledArgs {
 };
 
 hipError_t launch_zero_amax(float *a, float *b, const float *noop, hipStream_t s);
-hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b, const float *noop,
-                       hipStream_t s);
+// partials == NULL: atomic max into a and b (zeroed beforehand). Otherwise
+// store per-workgroup maxima to partials (a workspace as described above) and
+// their count to *npartials; a and b are not touched.
+hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b, uint32_t *partials,
+                       uint32_t *npartials, const float *noop, hipStream_t s);
 hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t cols, uint32_t mask,
-                           float *row_amax, float *col_amax, const float *noop, hipStream_t s);
+                           float *row_amax, float *col_amax, uint32_t *partials, uint32_t *npartials,
+                           const float *noop, hipStream_t s);
 hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);

@@ -113,7 +113,7 @@ __device__ __forceinline__ void encode_unit(const Unit<DT> &u, bool valid, uint3
 
 template <int DT, bool SR, bool COMPUTE>
 __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
-  __shared__ uint32_t lds4[4];
+  __shared__ uint32_t lds_w[kThreads / 64];
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   const uint32_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -139,9 +139,11 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
       m = max(m, unit_max_bits<DT>(load_unit<DT, false>(p.x, row_off + 8ull * u)));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 64)));
-    if ((tid & 63) == 0) lds4[tid >> 6] = m;
+    if ((tid & 63) == 0) lds_w[tid >> 6] = m;
     __syncthreads();
-    m = max(max(lds4[0], lds4[1]), max(lds4[2], lds4[3]));
+    m = lds_w[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = max(m, lds_w[w]);
     amax = __uint_as_float(m);
     if (tid == 0) p.amax[row] = amax;
   } else {

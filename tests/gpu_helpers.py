@@ -22,11 +22,13 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def run_quantize(x: np.ndarray, *, rowwise=True, columnwise=True, **cfg_kw):
-    """Quantize on the GPU; returns a dict shaped like oracle.quantize()'s."""
+def run_quantize(x: np.ndarray, *, rowwise=True, columnwise=True, use_workspace=True, **cfg_kw):
+    """Quantize on the GPU; returns a dict shaped like oracle.quantize()'s.
+    use_workspace: reduce a computed amax through a workspace (two launches)
+    rather than the zeroing pass and atomics (three)."""
     xd = to_device(x)
     cfg = nv.make_config(**cfg_kw)
-    row, col = nv.quantize(xd, rowwise=rowwise, columnwise=columnwise, cfg=cfg)
+    row, col = nv.quantize(xd, rowwise=rowwise, columnwise=columnwise, cfg=cfg, use_workspace=use_workspace)
     torch.cuda.synchronize()
     rows, cols = x.shape
     out = {"row_data": None, "row_scales": None, "col_data": None, "col_scales": None,

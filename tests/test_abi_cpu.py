@@ -7,6 +7,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -25,7 +26,7 @@ A2 = 0x500000
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:nvfp4_status_t|const char \*)\s*(nvfp4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status_t|const char \*|uint64_t)\s*(nvfp4_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -128,8 +129,29 @@ def test_debug_rht_rejections():
     assert lib.nvfp4_debug_rht_colwise(X, 0, 64, 64, 0, None, None) == nv.NVFP4_ERR_NULL
 
 
-def test_config_struct_matches_header_layout():
-    # 9 uint32 fields then one pointer, as declared in nvfp4_config_t
-    assert ctypes.sizeof(nv.nvfp4_config_t) == 9 * 4 + 4 + 8
-    assert nv.nvfp4_config_t.noop.offset == 40
-    assert ctypes.sizeof(nv.nvfp4_out_t) == 24
+def test_config_struct_matches_header_layout(tmp_path):
+    # compile the header with the host C compiler and compare sizes and offsets
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "nvfp4.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %u\\n", sizeof(nvfp4_config_t), '
+                   'offsetof(nvfp4_config_t, compute_amax), offsetof(nvfp4_config_t, noop), '
+                   'offsetof(nvfp4_config_t, workspace), sizeof(nvfp4_out_t), NVFP4_WORKSPACE_BYTES); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    size, compute_amax, noop, workspace, out_size, ws_bytes = map(int, subprocess.check_output([str(exe)]).split())
+    C = nv.nvfp4_config_t
+    assert (ctypes.sizeof(C), C.compute_amax.offset, C.noop.offset, C.workspace.offset) == \
+        (size, compute_amax, noop, workspace)
+    assert ctypes.sizeof(nv.nvfp4_out_t) == out_size
+    assert nv.nvfp4_workspace_bytes() == ws_bytes
+
+
+def test_workspace_must_be_aligned():
+    lib = nv.load()
+    r = nv.nvfp4_out_t(D, S, A)
+    c = nv.nvfp4_out_t(D + 0x10000, S + 0x10000, A2)
+    cfg = nv.make_config()
+    cfg.workspace = 0x600008
+    assert lib.nvfp4_quantize(X, 0, 64, 64, ctypes.byref(r), ctypes.byref(c), ctypes.byref(cfg), None) == \
+        nv.NVFP4_ERR_ALIGN
+    assert "workspace" in nv.nvfp4_last_error()

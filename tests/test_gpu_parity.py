@@ -37,9 +37,9 @@ def assert_matches(got, ref, *, swizzled=False, what=""):
 
 
 def check(x, *, rowwise=True, columnwise=True, swizzled=False, block_2d=False, stochastic=False, sr_seed=0,
-          row_scaled=False, what=""):
+          row_scaled=False, use_workspace=True, what=""):
     got = run_quantize(x, rowwise=rowwise, columnwise=columnwise, swizzled=swizzled, block_2d=block_2d,
-                       stochastic=stochastic, sr_seed=sr_seed, row_scaled=row_scaled)
+                       stochastic=stochastic, sr_seed=sr_seed, row_scaled=row_scaled, use_workspace=use_workspace)
     ref = O.quantize(x, rowwise=rowwise, columnwise=columnwise, block_2d=block_2d, stochastic=stochastic,
                      sr_seed=sr_seed, row_scaled=row_scaled)
     assert_matches(got, ref, swizzled=swizzled, what=what)
@@ -190,8 +190,9 @@ def test_e2m1_fp32_near_decision_points():
 # RHT column-wise side (workload c5) and its transform values
 # ---------------------------------------------------------------------------
 
-def _rht_compare(x, mask, stochastic, sr_seed):
-    got = run_quantize(x, rht=True, rht_sign_mask=mask, stochastic=stochastic, sr_seed=sr_seed)
+def _rht_compare(x, mask, stochastic, sr_seed, use_workspace=True):
+    got = run_quantize(x, rht=True, rht_sign_mask=mask, stochastic=stochastic, sr_seed=sr_seed,
+                       use_workspace=use_workspace)
     a_row, a_col = O.compute_amax(x, O.AMAX_RHT, mask)
     ref = O.quantize(x, rht=True, sign_mask=mask, stochastic=stochastic, sr_seed=sr_seed, amax_row=a_row,
                      amax_col=a_col)
@@ -386,17 +387,96 @@ def test_deterministic_across_runs():
         assert np.array_equal(outs[3][k], outs[4][k])
 
 
-@pytest.mark.parametrize("mode", ["2d_swizzled", "1d_sr", "rht", "rowscaled"])
+# ---------------------------------------------------------------------------
+# The two ways of reducing a computed per-tensor amax: zeroing pass + atomic
+# max (no workspace) and per-workgroup maxima in a workspace reduced by the
+# cast kernel. Both must give the oracle's bytes.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["1d", "2d_swizzled", "fp32_ragged", "row_only", "col_only", "sr"])
+@pytest.mark.parametrize("use_workspace", [True, False])
+def test_amax_reduction_paths(case, use_workspace):
+    if case == "1d":
+        x, kw = W.c1(), {}
+    elif case == "2d_swizzled":
+        x, kw = W.c2(rows=640, cols=768, seed=90), dict(block_2d=True, swizzled=True)
+    elif case == "fp32_ragged":
+        x, kw = W.gaussian_fp32(208, 1040, 91), {}
+    elif case == "row_only":
+        x, kw = W.randn_bf16(100, 272, 92), dict(columnwise=False)
+    elif case == "col_only":
+        x, kw = W.randn_bf16(96, 272, 93), dict(rowwise=False)
+    else:
+        x, kw = W.randn_bf16(256, 512, 94), dict(stochastic=True, sr_seed=11)
+    check(x, use_workspace=use_workspace, what=f"{case} workspace={use_workspace}", **kw)
+
+
+@pytest.mark.parametrize("use_workspace", [True, False])
+def test_rht_amax_reduction_paths(use_workspace):
+    _rht_compare(W.randn_bf16(512, 768, 95), W.rht_sign_mask(95), False, 0, use_workspace)
+
+
+def _quantize_with(xd, cfg, rowwise=True, columnwise=True):
+    rows, cols = xd.shape
+    row = nv.empty_orientation(rows, cols, DEV) if rowwise else None
+    col = nv.empty_orientation(cols, rows, DEV) if columnwise else None
+    nv.nvfp4_quantize(xd, row, col, cfg)
+    torch.cuda.synchronize()
+    return [host(t) for o in (row, col) if o is not None for t in (o.data, o.scales, o.amax)]
+
+
+def test_workspace_reuse_reads_only_this_calls_maxima():
+    # A call that leaves many large maxima in the workspace, then a smaller
+    # input with a smaller amax and fewer workgroups through the same workspace.
+    ws = nv.empty_workspace(DEV)
+    big = (W.randn_bf16(2048, 4096, 96), 2048, 4096)
+    small = W.randn_bf16(128, 256, 97)
+    cfg = nv.make_config(workspace=ws)
+    _quantize_with(to_device(big[0]) * 100.0, cfg)
+    got = _quantize_with(to_device(small), cfg)
+    ref = O.quantize(small)
+    for g, k in zip(got, ("row_data", "row_scales", "amax_row", "col_data", "col_scales", "amax_col")):
+        assert np.array_equal(g.ravel(), ref[k].ravel()), k
+
+
+@pytest.mark.parametrize("case", ["fp32_2112_chunks", "rht_2064_units"])
+def test_workspace_when_workgroups_loop(case):
+    # More reduction units than workspace entries (2048): workgroups of the
+    # amax pass take several units. The largest magnitude sits in the last
+    # unit. Compared with the atomic path (one unit per workgroup), bit for bit,
+    # and the plain amax with torch's max.
+    g = torch.Generator(device=DEV).manual_seed(98)
+    if case == "fp32_2112_chunks":
+        rows, cols = 8192, 8448  # 17.3M 16-byte vectors = 2112 chunks of 8192
+        xd = torch.randn((rows, cols), generator=g, device=DEV, dtype=torch.float32)
+        kw = {}
+    else:
+        rows, cols = 33024, 4096  # 2064 units of 16 rows x 4096 columns
+        xd = torch.randn((rows, cols), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+        kw = dict(rht=True, rht_sign_mask=0x5A3C)
+    xd[-1, -3] = -1000.0
+    ws = nv.empty_workspace(DEV)
+    with_ws = _quantize_with(xd, nv.make_config(workspace=ws, **kw))
+    atomic = _quantize_with(xd, nv.make_config(**kw))
+    for a, b in zip(with_ws, atomic):
+        assert np.array_equal(a, b)
+    assert with_ws[2][0] == 1000.0
+
+
+@pytest.mark.parametrize("mode", ["2d_swizzled", "1d_sr", "rht", "rowscaled", "2d_swizzled_ws", "rht_ws"])
 def test_graph_capture_replays_match_eager(mode):
     # The calls queue kernels only (no memset, no allocation, no sync), so a
     # captured graph must reproduce the eager result on every replay, with
     # other work and synchronizations between the replays.
     x = W.c2(rows=256, cols=384, seed=81)
     xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
     cfg = {"2d_swizzled": nv.make_config(block_2d=True, swizzled=True),
            "1d_sr": nv.make_config(stochastic=True, sr_seed=3),
            "rht": nv.make_config(rht=True, rht_sign_mask=0x9A5C),
-           "rowscaled": nv.make_config(row_scaled=True)}[mode]
+           "rowscaled": nv.make_config(row_scaled=True),
+           "2d_swizzled_ws": nv.make_config(block_2d=True, swizzled=True, workspace=ws),
+           "rht_ws": nv.make_config(rht=True, rht_sign_mask=0x9A5C, workspace=ws)}[mode]
     rs = mode == "rowscaled"
     row = nv.empty_orientation(256, 384, DEV, 256 if rs else 1)
     col = None if rs else nv.empty_orientation(384, 256, DEV)
@@ -411,7 +491,7 @@ def test_graph_capture_replays_match_eager(mode):
         nv.nvfp4_quantize(xd, row, col, cfg, s)
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in outs:
+        for t in outs + [ws]:
             t.view(torch.uint8).fill_(0x33 + rep)  # eager work between replays
         torch.cuda.synchronize()
         g.replay()
