@@ -62,15 +62,30 @@ __device__ __forceinline__ uint32_t partials_max(const u32x4 (&v)[kPartialVecs])
 
 constexpr int kWaves = kThreads / 64;
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over the wave, uniform: DPP steps leave each row of 16 lanes with
+// its maximum (quad xor 1, quad xor 2, half-row mirror, row mirror), then the
+// four rows are read out as scalars.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, dpp_mov<0xB1>(v));
+  v = max(v, dpp_mov<0x4E>(v));
+  v = max(v, dpp_mov<0x141>(v));
+  v = max(v, dpp_mov<0x140>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
 // Workgroup maximum of N values per thread, returned to every thread.
 // Contains a barrier; lds holds N words per wave.
 template <int N>
 __device__ __forceinline__ void workgroup_max(uint32_t (&m)[N], uint32_t *lds) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) m[i] = max(m[i], static_cast<uint32_t>(__shfl_xor(static_cast<int>(m[i]), off, 64)));
-  }
+  for (int i = 0; i < N; ++i) m[i] = wave_max(m[i]);
   if ((threadIdx.x & 63) == 0) {
 #pragma unroll
     for (int i = 0; i < N; ++i) lds[i * kWaves + (threadIdx.x >> 6)] = m[i];
@@ -254,10 +269,18 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   u32x4 part[kPartialVecs];
   if (p.partials != nullptr) load_partials(p.partials, p.npartials, tid, part);
 
+  // Every thread issues all its loads without a branch, so that the wait for
+  // the workspace loads above does not have to wait for these too. In an
+  // edge tile, pieces outside the input load from a clamped address and are
+  // zeroed afterwards.
+  const bool interior = r0 + kRT <= p.rows && c0 + kRT <= p.cols;  // uniform
+  const uint32_t lcol = col_ok ? col : 0u;
   uint32_t w[8][W];
-  auto load_piece = [&](int k) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t r = min(rbase + k, p.rows - 1);
     const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(p.x) +
-                                                       (static_cast<uint64_t>(rbase + k) * p.cols + col) * RT<DT>::kElem);
+                                                       (static_cast<uint64_t>(r) * p.cols + lcol) * RT<DT>::kElem);
 #pragma unroll
     for (int q = 0; q < W / 4; ++q) {
       const u32x4 t = __builtin_nontemporal_load(src + q);
@@ -265,20 +288,6 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
       w[k][4 * q + 1] = t.y;
       w[k][4 * q + 2] = t.z;
       w[k][4 * q + 3] = t.w;
-    }
-  };
-  if (r0 + kRT <= p.rows && c0 + kRT <= p.cols) {  // interior tile (uniform): no bounds checks
-#pragma unroll
-    for (int k = 0; k < 8; ++k) load_piece(k);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (col_ok && rbase + k < p.rows) {
-        load_piece(k);
-      } else {
-#pragma unroll
-        for (int q = 0; q < W; ++q) w[k][q] = 0;
-      }
     }
   }
 
@@ -288,6 +297,15 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
   if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
   else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
+  if (!interior) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (!(col_ok && rbase + k < p.rows)) {
+#pragma unroll
+        for (int q = 0; q < W; ++q) w[k][q] = 0;
+      }
+    }
+  }
 
   // ---- block scale codes ----
   uint32_t rcode[8], ccode[8];
@@ -556,9 +574,16 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
     load_partials(p.partials + kMaxPartials, p.npartials, tid, part_col);
   }
 
+  // Every thread issues all its loads without a branch (see k_cast_rt); in
+  // an edge tile, pieces outside the input load from a clamped address and
+  // are zeroed afterwards.
+  const bool interior = r0 + kRT <= p.rows && c0 + kRT <= p.cols;  // uniform
+  const uint32_t lcol = col_ok ? col : 0u;
   uint32_t w[16][W];
-  auto load_piece = [&](int k) {
-    const uint8_t *src = static_cast<const uint8_t *>(p.x) + (static_cast<uint64_t>(rbase + k) * p.cols + col) * kElem;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t r = min(rbase + k, p.rows - 1);
+    const uint8_t *src = static_cast<const uint8_t *>(p.x) + (static_cast<uint64_t>(r) * p.cols + lcol) * kElem;
     if constexpr (DT == kBF16) {
       const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(src));
       w[k][0] = t.x;
@@ -569,20 +594,6 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
       w[k][1] = t.y;
       w[k][2] = t.z;
       w[k][3] = t.w;
-    }
-  };
-  if (r0 + kRT <= p.rows && c0 + kRT <= p.cols) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) load_piece(k);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (col_ok && rbase + k < p.rows) {
-        load_piece(k);
-      } else {
-#pragma unroll
-        for (int q = 0; q < W; ++q) w[k][q] = 0;
-      }
     }
   }
   auto value = [&](int k, int c) -> float {
@@ -596,6 +607,15 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
   if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
   else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
+  if (!interior) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (!(col_ok && rbase + k < p.rows)) {
+#pragma unroll
+        for (int q = 0; q < W; ++q) w[k][q] = 0;
+      }
+    }
+  }
   const bool swz = p.swizzled != 0;
   auto code_slot = [swz](int line, int blk) {
     return swz ? ((blk >> 2) << 9) + ((line & 31) << 4) + ((line >> 5) << 2) + (blk & 3) : line * 8 + blk;
