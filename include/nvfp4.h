@@ -203,6 +203,21 @@ const char *nvfp4_last_error(void);
 nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t dtype, int64_t rows,
                                        int64_t cols, uint32_t sign_mask, float *t, void *stream);
 
+/* Flags of nvfp4_debug_e2m1_pack. */
+#define NVFP4_DEBUG_SR 1u       /* stochastic rounding (else nearest even) */
+#define NVFP4_DEBUG_PAIRWISE 2u /* the one-pair encoder (else the four-pair one) */
+
+/*
+ * Test hook: E2M1 codes of n pairs (v[2i], v[2i+1]) of already scaled FP32
+ * values, packed into out[i] (first value in the low nibble), by the same
+ * device encoders as the quantize kernels. With NVFP4_DEBUG_SR, r[i] is the
+ * pair's random word as in nvfp4_config_t.stochastic (low half for v[2i],
+ * high half for v[2i+1]); r may be NULL otherwise. v, r and out are device
+ * buffers; v and r 4-byte aligned. Values must be finite.
+ */
+nvfp4_status_t nvfp4_debug_e2m1_pack(const float *v, const uint32_t *r, uint8_t *out, int64_t n, uint32_t flags,
+                                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,8 +41,11 @@ NVFP4_SCALES_GEMM_SWIZZLED = 1
 NVFP4_SCALE_E4M3 = 0
 NVFP4_SCALE_UE5M3 = 1
 
+NVFP4_DEBUG_SR = 1
+NVFP4_DEBUG_PAIRWISE = 2
+
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
-            "nvfp4_workspace_bytes", "nvfp4_debug_rht_colwise")
+            "nvfp4_workspace_bytes", "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -105,6 +108,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_workspace_bytes.argtypes = []
     lib.nvfp4_debug_rht_colwise.restype = I
     lib.nvfp4_debug_rht_colwise.argtypes = [P, I, I64, I64, U32, P, P]
+    lib.nvfp4_debug_e2m1_pack.restype = I
+    lib.nvfp4_debug_e2m1_pack.argtypes = [P, P, P, I64, U32, P]
     _lib = lib
     return lib
 
@@ -197,6 +202,15 @@ def nvfp4_debug_rht_colwise(x: torch.Tensor, sign_mask: int, t: torch.Tensor, st
     rows, cols = _shape2d(x)
     _check(load().nvfp4_debug_rht_colwise(_ptr(x), _dtype_code(x), rows, cols, sign_mask & 0xFFFFFFFF, _ptr(t),
                                           _stream(stream)))
+
+
+def nvfp4_debug_e2m1_pack(v: torch.Tensor, r: Optional[torch.Tensor], out: torch.Tensor, flags: int,
+                          stream=None) -> None:
+    """v: float32 [2n]; r: int32/uint32 [n] or None; out: uint8 [n]."""
+    n = out.numel()
+    if v.numel() != 2 * n or (r is not None and r.numel() != n):
+        raise ValueError("v must hold 2n values and r n words for n output bytes")
+    _check(load().nvfp4_debug_e2m1_pack(_ptr(v), _ptr(r), _ptr(out), n, flags, _stream(stream)))
 
 
 # ---- allocation helpers (device memory only; no arithmetic) -----------------

@@ -231,3 +231,16 @@ extern "C" nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t d
                                             sign_mask, t, static_cast<hipStream_t>(stream)),
                     "RHT launch");
 }
+
+extern "C" nvfp4_status_t nvfp4_debug_e2m1_pack(const float *v, const uint32_t *r, uint8_t *out, int64_t n,
+                                                uint32_t flags, void *stream) {
+  if (n < 0 || n >= (int64_t{1} << 32)) return fail(NVFP4_ERR_SHAPE, "pair count %lld out of range", (long long)n);
+  if (flags & ~(NVFP4_DEBUG_SR | NVFP4_DEBUG_PAIRWISE)) return fail(NVFP4_ERR_UNSUPPORTED, "unknown flags %#x", flags);
+  const bool sr = (flags & NVFP4_DEBUG_SR) != 0;
+  if (n > 0 && (v == nullptr || out == nullptr || (sr && r == nullptr)))
+    return fail(NVFP4_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(v, 4) || !aligned(r, 4)) return fail(NVFP4_ERR_ALIGN, "v and r must be 4-byte aligned");
+  return hip_status(nvfp4::launch_debug_e2m1(v, r, out, static_cast<uint64_t>(n), sr, (flags & NVFP4_DEBUG_PAIRWISE) != 0,
+                                             static_cast<hipStream_t>(stream)),
+                    "debug e2m1 launch");
+}

@@ -130,15 +130,10 @@ __device__ __forceinline__ void amax_pair(const CastArgs &p, const u32x4 (&pr)[k
 template <bool SR>
 __device__ __forceinline__ uint32_t encode8_scaled(const float *s, uint32_t key, uint32_t byte0) {
   if (!SR) return e2m1_rne_x8(s);
-  uint32_t word = 0;
+  uint32_t r[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t r = fmix32(key ^ (byte0 + q));
-    const uint32_t lo = e2m1_sr(s[2 * q], r & 0xFFFFu);
-    const uint32_t hi = e2m1_sr(s[2 * q + 1], r >> 16);
-    word |= (lo | (hi << 4)) << (8 * q);
-  }
-  return word;
+  for (int q = 0; q < 4; ++q) r[q] = fmix32(key ^ (byte0 + q));
+  return e2m1_sr_x8(s, r);
 }
 
 template <bool SR>
@@ -451,9 +446,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
         const float b = t1[c];
         if (SR) {
           const uint32_t byte = (col + c) * half_rows + (rbase >> 1) + i;
-          const uint32_t r = fmix32(kcol ^ byte);
-          const uint32_t pair = e2m1_sr(a, r & 0xFFFFu) | (e2m1_sr(b, r >> 16) << 4);
-          colw[c] = i == 0 ? pair : colw[c] | (pair << (8 * i));
+          colw[c] = e2m1_sr_pair_into(i == 0 ? __float_as_uint(a) : colw[c], a, b, fmix32(kcol ^ byte), i);
         } else {
           colw[c] = e2m1_rne_pair_into(i == 0 ? __float_as_uint(a) : colw[c], a, b, i);
         }
@@ -661,9 +654,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
       uint32_t h;
       if (SR) {
         const uint32_t byte0 = (rbase + k) * half_cols + (col >> 1);
-        const uint32_t ra = fmix32(krow ^ byte0), rb = fmix32(krow ^ (byte0 + 1));
-        h = (e2m1_sr(s0, ra & 0xFFFFu) | (e2m1_sr(s1, ra >> 16) << 4)) |
-            ((e2m1_sr(s2, rb & 0xFFFFu) | (e2m1_sr(s3, rb >> 16) << 4)) << 8);
+        h = e2m1_sr_pair_into(__float_as_uint(s0), s0, s1, fmix32(krow ^ byte0), 0);
+        h = e2m1_sr_pair_into(h, s2, s3, fmix32(krow ^ (byte0 + 1)), 1);
       } else {
         h = e2m1_rne_pair_into(__float_as_uint(s0), s0, s1, 0);
         h = e2m1_rne_pair_into(h, s2, s3, 1);

@@ -82,13 +82,12 @@ __device__ __forceinline__ void encode_unit(const Unit<DT> &u, bool valid, uint3
   float s[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) s[k] = v[k] * bs.mult;
-  uint32_t word = 0;
+  uint32_t word;
   if (SR) {
+    uint32_t r[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t r = fmix32(key ^ (byte0 + q));
-      word |= (e2m1_sr(s[2 * q], r & 0xFFFFu) | (e2m1_sr(s[2 * q + 1], r >> 16) << 4)) << (8 * q);
-    }
+    for (int q = 0; q < 4; ++q) r[q] = fmix32(key ^ (byte0 + q));
+    word = e2m1_sr_x8(s, r);
   } else {
     word = e2m1_rne_x8(s);
   }

@@ -155,3 +155,11 @@ def test_workspace_must_be_aligned():
     assert lib.nvfp4_quantize(X, 0, 64, 64, ctypes.byref(r), ctypes.byref(c), ctypes.byref(cfg), None) == \
         nv.NVFP4_ERR_ALIGN
     assert "workspace" in nv.nvfp4_last_error()
+
+
+def test_debug_e2m1_rejections():
+    lib = nv.load()
+    assert lib.nvfp4_debug_e2m1_pack(D, S, A, -1, 0, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_debug_e2m1_pack(D, S, A, 8, 4, None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert lib.nvfp4_debug_e2m1_pack(D, None, A, 8, nv.NVFP4_DEBUG_SR, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_debug_e2m1_pack(D + 2, S, A, 8, 0, None) == nv.NVFP4_ERR_ALIGN
