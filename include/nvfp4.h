@@ -137,6 +137,12 @@ typedef struct {
    * that share a workspace must not run concurrently (queue them on one
    * stream). Ignored by the other calls and paths. */
   void *workspace;
+  /* nvfp4_quantize only: NULL, or the address of two hipEvent_t handles
+   * that the call records on its stream just before and just after the
+   * launch of its cast kernel (the row-scaled kernel on that path), so that
+   * the kernel can be timed inside a whole call. Not recorded when the call
+   * is rejected or the input is empty. */
+  void *const *cast_events;
 } nvfp4_config_t;
 
 /* Bytes of the optional quantize workspace (nvfp4_config_t.workspace). */

@@ -65,6 +65,7 @@ class nvfp4_config_t(ctypes.Structure):
         ("compute_amax", ctypes.c_uint32),
         ("noop", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
+        ("cast_events", ctypes.c_void_p),
     ]
 
 

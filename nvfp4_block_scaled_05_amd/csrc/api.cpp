@@ -121,6 +121,8 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   const nvfp4_config_t cfg = config_or_default(cfg_in);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (row == nullptr && col == nullptr) return fail(NVFP4_ERR_NULL, "neither a row-wise nor a column-wise output");
+  if (cfg.cast_events != nullptr && (cfg.cast_events[0] == nullptr || cfg.cast_events[1] == nullptr))
+    return fail(NVFP4_ERR_NULL, "cast_events holds a NULL event");
   const bool empty = rows * cols == 0;
   if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
   if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
@@ -150,9 +152,17 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
 
   const uint32_t R = static_cast<uint32_t>(rows), C = static_cast<uint32_t>(cols);
   const bool sr = cfg.stochastic != 0;
+  // optional events around the cast launch (rows * cols == 0 launches nothing)
+  const bool timed = cfg.cast_events != nullptr && rows * cols > 0;
+  auto record = [&](int i) -> nvfp4_status_t {
+    return timed ? hip_status(hipEventRecord(static_cast<hipEvent_t>(cfg.cast_events[i]), s), "cast event record")
+                 : NVFP4_OK;
+  };
   if (cfg.row_scaled) {
     nvfp4::RowScaledArgs a{x, R, C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop};
-    return hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
+    if ((st = record(0)) != NVFP4_OK) return st;
+    st = hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
+    return st != NVFP4_OK ? st : record(1);
   }
   float *ra = row ? row->amax : nullptr;
   float *ca = col ? col->amax : nullptr;
@@ -194,7 +204,9 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   nvfp4::CastArgs a{x,  R,        C,    row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
                     cfg.rht_sign_mask, cfg.noop, partials, npartials};
-  return hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
+  if ((st = record(0)) != NVFP4_OK) return st;
+  st = hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
+  return st != NVFP4_OK ? st : record(1);
 }
 
 extern "C" nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols, uint32_t scale_layout,

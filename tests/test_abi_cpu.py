@@ -133,15 +133,17 @@ def test_config_struct_matches_header_layout(tmp_path):
     # compile the header with the host C compiler and compare sizes and offsets
     src = tmp_path / "layout.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "nvfp4.h"\n'
-                   'int main(void) { printf("%zu %zu %zu %zu %zu %u\\n", sizeof(nvfp4_config_t), '
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %u %zu\\n", sizeof(nvfp4_config_t), '
                    'offsetof(nvfp4_config_t, compute_amax), offsetof(nvfp4_config_t, noop), '
-                   'offsetof(nvfp4_config_t, workspace), sizeof(nvfp4_out_t), NVFP4_WORKSPACE_BYTES); return 0; }\n')
+                   'offsetof(nvfp4_config_t, workspace), sizeof(nvfp4_out_t), NVFP4_WORKSPACE_BYTES, '
+                   'offsetof(nvfp4_config_t, cast_events)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
-    size, compute_amax, noop, workspace, out_size, ws_bytes = map(int, subprocess.check_output([str(exe)]).split())
+    size, compute_amax, noop, workspace, out_size, ws_bytes, events = \
+        map(int, subprocess.check_output([str(exe)]).split())
     C = nv.nvfp4_config_t
-    assert (ctypes.sizeof(C), C.compute_amax.offset, C.noop.offset, C.workspace.offset) == \
-        (size, compute_amax, noop, workspace)
+    assert (ctypes.sizeof(C), C.compute_amax.offset, C.noop.offset, C.workspace.offset, C.cast_events.offset) == \
+        (size, compute_amax, noop, workspace, events)
     assert ctypes.sizeof(nv.nvfp4_out_t) == out_size
     assert nv.nvfp4_workspace_bytes() == ws_bytes
 
@@ -163,3 +165,12 @@ def test_debug_e2m1_rejections():
     assert lib.nvfp4_debug_e2m1_pack(D, S, A, 8, 4, None) == nv.NVFP4_ERR_UNSUPPORTED
     assert lib.nvfp4_debug_e2m1_pack(D, None, A, 8, nv.NVFP4_DEBUG_SR, None) == nv.NVFP4_ERR_NULL
     assert lib.nvfp4_debug_e2m1_pack(D + 2, S, A, 8, 0, None) == nv.NVFP4_ERR_ALIGN
+
+
+def test_cast_events_must_not_hold_null():
+    lib = nv.load()
+    r = nv.nvfp4_out_t(D, S, A)
+    cfg = nv.make_config()
+    ev = (ctypes.c_void_p * 2)(0x1000, None)
+    cfg.cast_events = ctypes.cast(ev, ctypes.c_void_p)
+    assert lib.nvfp4_quantize(X, 0, 64, 64, ctypes.byref(r), None, ctypes.byref(cfg), None) == nv.NVFP4_ERR_NULL

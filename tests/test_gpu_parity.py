@@ -498,3 +498,31 @@ def test_graph_capture_replays_match_eager(mode):
         torch.cuda.synchronize()
         for e, t in zip(eager, outs):
             assert np.array_equal(e, host(t)), (mode, rep)
+
+
+@pytest.mark.parametrize("mode", ["2d_ws", "rowscaled"])
+def test_cast_events_bracket_the_cast_kernel(mode):
+    import ctypes
+
+    x = to_device(W.c2(rows=1024, cols=2048, seed=99))
+    rs = mode == "rowscaled"
+    ws = nv.empty_workspace(DEV)
+    cfg = nv.make_config(row_scaled=True) if rs else nv.make_config(block_2d=True, workspace=ws)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * 2)(ev[0].cuda_event, ev[1].cuda_event)
+    timed = nv.nvfp4_config_t.from_buffer_copy(cfg)
+    timed.cast_events = ctypes.cast(handles, ctypes.c_void_p).value
+    outs = []
+    for c in (cfg, timed):
+        row = nv.empty_orientation(1024, 2048, DEV, 1024 if rs else 1)
+        col = None if rs else nv.empty_orientation(2048, 1024, DEV)
+        nv.nvfp4_quantize(x, row, col, c)
+        torch.cuda.synchronize()
+        outs.append([host(t) for o in (row, col) if o is not None for t in (o.data, o.scales, o.amax)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    ms = ev[0].elapsed_time(ev[1])
+    assert 0.0 < ms < 100.0
