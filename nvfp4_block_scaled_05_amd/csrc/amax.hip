@@ -9,7 +9,6 @@
 // buffer on the +0.0 that the zeroing pass wrote. With a caller workspace
 // the workgroups store their maxima there instead and the cast kernel
 // reduces them, which needs neither the zeroing pass nor atomics.
-#include <type_traits>
 
 #include "codec.h"
 #include "launch.h"
@@ -58,32 +57,33 @@ __global__ void k_zero_amax(float *a, float *b, const float *noop) {
   }
 }
 
-// Per-tensor amax. nvec = number of 16-byte vectors of x, cut into nchunks
-// chunks of kAmaxThreads * VPT vectors (128 KiB at VPT 16). A workgroup of
-// kAmaxThreads (8 waves) reduces chunks blockIdx.x, blockIdx.x + gridDim.x,
-// ...; every thread issues all loads of a chunk before reducing, so a chunk
-// is requested in one round trip. Small inputs use fewer vectors per thread
-// so that they still spread over many workgroups.
+// Per-tensor amax. nvec = number of 16-byte vectors of x. The grid reads x
+// in passes of VPT grid-wide contiguous spans: in each pass thread t of the
+// grid loads vectors t, t + span, ..., t + (VPT - 1) * span (span = grid size
+// in threads), all issued before any is used, so every wave keeps VPT
+// 16-byte loads in flight and consecutive waves read consecutive memory.
 // The workgroup's maximum then goes either to partials[blockIdx.x] (plain
 // store; the cast kernel finishes the reduction) or, with partials == NULL,
-// into a and b by atomic max. The atomic form is launched with one chunk per
-// workgroup, which keeps the number of atomics per buffer small (640 for an
-// 80 MiB input).
-constexpr int kAmaxThreads = 512;
+// into a and b by atomic max.
+constexpr int kAmaxThreads = 512;     // RHT amax pair
+constexpr int kMaxThreads = 256;      // per-tensor amax
+constexpr int kMaxVecPerThread = 8;   // loads in flight per thread and pass
+constexpr uint32_t kMaxGrid = 1280;   // 5 workgroups per CU on 256 CUs
 
-template <int DT, int VPT>
-__global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, uint32_t nchunks,
-                                                       float *a, float *b, uint32_t *partials, const float *noop) {
-  __shared__ uint32_t lds[kAmaxThreads / 64];
+template <int DT>
+__global__ __launch_bounds__(kMaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a, float *b,
+                                                      uint32_t *partials, const float *noop) {
+  constexpr int VPT = kMaxVecPerThread;
+  __shared__ uint32_t lds[kMaxThreads / 64];
   if (noop_set(noop)) return;
   uint32_t m32 = 0;        // FP32: max of |x| bit patterns
   ushort2_t m16 = {0, 0};  // BF16: max of 15-bit magnitudes, two lanes
-  for (uint32_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-    const uint64_t base = static_cast<uint64_t>(chunk) * (kAmaxThreads * VPT) + threadIdx.x;
+  const uint64_t span = static_cast<uint64_t>(gridDim.x) * kMaxThreads;
+  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * kMaxThreads + threadIdx.x; i0 < nvec; i0 += span * VPT) {
     uint4 v[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const uint64_t i = base + static_cast<uint64_t>(k) * kAmaxThreads;
+      const uint64_t i = i0 + k * span;
       v[k] = i < nvec ? x[i] : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax(const uint4 *__restrict__
     }
   }
   uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
-  m = block_umax<kAmaxThreads>(m, lds);
+  m = block_umax<kMaxThreads>(m, lds);
   if (threadIdx.x == 0) {
     if (partials != nullptr) {
       partials[blockIdx.x] = m;
@@ -224,27 +224,18 @@ hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b,
                        uint32_t *npartials, const float *noop, hipStream_t s) {
   const uint64_t nvec = n * (dtype == kBF16 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
-  auto go = [&](auto vpt_tag) {
-    constexpr int VPT = decltype(vpt_tag)::value;
-    const uint64_t chunks = (nvec + kAmaxThreads * VPT - 1) / (kAmaxThreads * VPT);
-    const uint32_t grid = reduction_grid(chunks, partials != nullptr);
-    if (npartials) *npartials = grid;
-    if (dtype == kBF16)
-      hipLaunchKernelGGL((k_amax<kBF16, VPT>), dim3(grid), dim3(kAmaxThreads), 0, s, static_cast<const uint4 *>(x),
-                         nvec, static_cast<uint32_t>(chunks), a, b, partials, noop);
-    else
-      hipLaunchKernelGGL((k_amax<kFP32, VPT>), dim3(grid), dim3(kAmaxThreads), 0, s, static_cast<const uint4 *>(x),
-                         nvec, static_cast<uint32_t>(chunks), a, b, partials, noop);
-  };
-  // >= 512 chunks at 16 vectors per thread; smaller inputs take 4 (tens to
-  // hundreds of workgroups: enough parallelism while the number of atomics,
-  // which serialize, stays small); tiny ones take 1.
-  if (nvec >= uint64_t{kAmaxThreads} * 16 * 512)
-    go(std::integral_constant<int, 16>{});
-  else if (nvec >= uint64_t{kAmaxThreads} * 4 * 16)
-    go(std::integral_constant<int, 4>{});
+  // one pass of kMaxVecPerThread loads per thread covers the input when it
+  // fits; at most kMaxGrid workgroups (both forms: few atomics per buffer)
+  const uint64_t want = (nvec + kMaxThreads * kMaxVecPerThread - 1) / (kMaxThreads * kMaxVecPerThread);
+  uint32_t grid = static_cast<uint32_t>(want < kMaxGrid ? want : kMaxGrid);
+  if (partials != nullptr) grid = reduction_grid(grid, true);
+  if (npartials) *npartials = grid;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_amax<kBF16>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x), nvec, a, b,
+                       partials, noop);
   else
-    go(std::integral_constant<int, 1>{});
+    hipLaunchKernelGGL(k_amax<kFP32>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x), nvec, a, b,
+                       partials, noop);
   return hipGetLastError();
 }
 
