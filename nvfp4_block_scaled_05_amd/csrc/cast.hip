@@ -62,24 +62,6 @@ __device__ __forceinline__ uint32_t partials_max(const u32x4 (&v)[kPartialVecs])
 
 constexpr int kWaves = kThreads / 64;
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
-}
-
-// Maximum over the wave, uniform: DPP steps leave each row of 16 lanes with
-// its maximum (quad xor 1, quad xor 2, half-row mirror, row mirror), then the
-// four rows are read out as scalars.
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  v = max(v, dpp_mov<0xB1>(v));
-  v = max(v, dpp_mov<0x4E>(v));
-  v = max(v, dpp_mov<0x141>(v));
-  v = max(v, dpp_mov<0x140>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-
 // Workgroup maximum of N values per thread, returned to every thread.
 // Contains a barrier; lds holds N words per wave.
 template <int N>
@@ -181,10 +163,6 @@ __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uin
 // non-temporal (streamed past the caches).
 // ---------------------------------------------------------------------------
 constexpr int kRT = 128;  // register-tile edge
-
-__device__ __forceinline__ uint32_t dpp_xor1(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xB1, 0xF, 0xF, false));
-}
 
 // lane ^ 16 (bit-mask swizzle: and 0x1F, or 0, xor 0x10)
 __device__ __forceinline__ uint32_t swz_xor16(uint32_t x) {
@@ -308,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) m = max(m, piece_max<DT>(w[k]));
-    m = max(m, dpp_xor1(m));
+    m = max(m, dpp_mov<kQuadXor1>(m));
     m = max(m, swz_xor16(m));
     const uint32_t cr = block_code(m, S_row);
     const uint32_t cc = block_code(m, S_col);
@@ -325,13 +303,13 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         mr[k] = piece_max<DT>(w[k]);
-        mr[k] = max(mr[k], dpp_xor1(mr[k]));
+        mr[k] = max(mr[k], dpp_mov<kQuadXor1>(mr[k]));
       }
       const bool lo = (ucol & 1) == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t mine = block_code(pick(lo, mr[j], mr[j + 4]), S_row);
-        const uint32_t other = dpp_xor1(mine);
+        const uint32_t other = dpp_mov<kQuadXor1>(mine);
         rcode[j] = pick(lo, mine, other);
         rcode[j + 4] = pick(lo, other, mine);
       }
@@ -520,23 +498,6 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
 // quads (DPP). Row-wise and column-wise data bytes are staged in LDS and
 // leave as 16-byte stores (64 contiguous bytes per row / column).
 // ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_quad(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
-}
-
-// quad_perm controls: xor 1, xor 2, and broadcast of quad lane s
-constexpr int kQuadXor1 = 0xB1;  // [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;  // [2,3,0,1]
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t x, int s) {
-  switch (s) {
-    case 0: return dpp_quad<0x00>(x);
-    case 1: return dpp_quad<0x55>(x);
-    case 2: return dpp_quad<0xAA>(x);
-    default: return dpp_quad<0xFF>(x);
-  }
-}
-
 template <int DT, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   constexpr int kElem = DT == kBF16 ? 2 : 4;
@@ -626,8 +587,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
       uint32_t m = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) m = max(m, __float_as_uint(value(k, c)) & 0x7FFFFFFFu);
-      m = max(m, dpp_quad<kQuadXor1>(m));
-      m = max(m, dpp_quad<kQuadXor2>(m));
+      m = max(m, dpp_mov<kQuadXor1>(m));
+      m = max(m, dpp_mov<kQuadXor2>(m));
       // quad lane q turns rows q, q+4, q+8, q+12 into codes
       if ((k & 3) == 0) mine[k >> 2] = m;
       else mine[k >> 2] = pick(q == (k & 3), m, mine[k >> 2]);

@@ -220,6 +220,41 @@ __device__ __forceinline__ uint64_t swizzled_scale_offset(uint64_t r, uint64_t c
   return (tile << 9) + ((r & 31u) << 4) + (((r & 127u) >> 5) << 2) + (c & 3u);
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+
+// quad_perm controls: lane ^ 1 and lane ^ 2 within each group of four
+constexpr int kQuadXor1 = 0xB1;  // [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // [2,3,0,1]
+
+// Lane s (0..3) of each group of four, broadcast to the group; s constant.
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x, int s) {
+  switch (s) {
+    case 0: return dpp_mov<0x00>(x);
+    case 1: return dpp_mov<0x55>(x);
+    case 2: return dpp_mov<0xAA>(x);
+    default: return dpp_mov<0xFF>(x);
+  }
+}
+
+// Maximum over the wave, uniform: DPP steps leave each row of 16 lanes with
+// its maximum (quad xor 1, quad xor 2, half-row mirror, row mirror), then the
+// four rows are read out as scalars.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, dpp_mov<kQuadXor1>(v));
+  v = max(v, dpp_mov<kQuadXor2>(v));
+  v = max(v, dpp_mov<0x141>(v));
+  v = max(v, dpp_mov<0x140>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

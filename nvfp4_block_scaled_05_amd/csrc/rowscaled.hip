@@ -1,12 +1,19 @@
-// Row-scaled (per-token) NVFP4 quantize for gfx950: one workgroup per row.
+// Row-scaled (per-token) NVFP4 quantize for gfx950: one workgroup per two
+// rows.
 //
 // "Implement row-scaled NVFP4 fprop recipe" (Changes, Greptile summary): each
 // row gets its own FP32 amax and the E4M3 block scales are taken relative to
 // it; output is row-wise only with compact scales. There the row amax is a
 // separate kernel run before the quantize kernel. Here the two are one
-// kernel: a row of up to 256 x 4 units of 8 elements (8192 elements) stays
-// in registers between the reduction and the cast, so the input is read from
-// HBM once. Longer rows re-read the part beyond that from cache.
+// kernel: thread t keeps 1x16 blocks t and t + 256 of a row in registers (up
+// to 8192 elements per row) between the reduction and the cast, so the input
+// is read from HBM once; longer rows re-read the part beyond that from cache.
+//
+// With whole blocks per thread, a block's maximum needs no other lane; the
+// four scale codes of an aligned group (four consecutive threads) are
+// gathered with DPP, and the row maximum is a DPP wave reduction plus one
+// barrier. The second row's loads are issued with the first's, so they
+// overlap the first row's reduction, encode and stores.
 #include "codec.h"
 #include "launch.h"
 
@@ -14,135 +21,140 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRegUnits = 4;  // units of 8 elements kept in registers per thread
+constexpr int kWaves = kThreads / 64;
+constexpr int kRegBlocks = 2;  // 1x16 blocks per thread kept in registers
 
 template <int DT>
-struct Unit {
-  static constexpr int kWords = DT == kBF16 ? 4 : 8;
+struct Block {
+  static constexpr int kWords = DT == kBF16 ? 8 : 16;
   uint32_t w[kWords];
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 // NT: non-temporal (the part of a row that stays in registers is read once);
 // the part beyond that is read twice and goes through the caches.
 template <int DT, bool NT>
-__device__ __forceinline__ Unit<DT> load_unit(const void *x, uint64_t elem_off) {
-  Unit<DT> u;
+__device__ __forceinline__ Block<DT> load_block(const void *x, uint64_t elem_off) {
+  Block<DT> b;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(x) + elem_off * (DT == kBF16 ? 2 : 4));
 #pragma unroll
-  for (int q = 0; q < Unit<DT>::kWords / 4; ++q) {
+  for (int q = 0; q < Block<DT>::kWords / 4; ++q) {
     const u32x4 t = NT ? __builtin_nontemporal_load(src + q) : src[q];
-    u.w[4 * q] = t.x;
-    u.w[4 * q + 1] = t.y;
-    u.w[4 * q + 2] = t.z;
-    u.w[4 * q + 3] = t.w;
+    b.w[4 * q] = t.x;
+    b.w[4 * q + 1] = t.y;
+    b.w[4 * q + 2] = t.z;
+    b.w[4 * q + 3] = t.w;
   }
-  return u;
+  return b;
 }
 
 template <int DT>
-__device__ __forceinline__ void unit_values(const Unit<DT> &u, float (&v)[8]) {
+__device__ __forceinline__ void zero_block(Block<DT> &b) {
+#pragma unroll
+  for (int q = 0; q < Block<DT>::kWords; ++q) b.w[q] = 0;
+}
+
+// max |x| of a block as the bit pattern of a non-negative float
+template <int DT>
+__device__ __forceinline__ uint32_t block_max_bits(const Block<DT> &b) {
   if (DT == kBF16) {
+    ushort2_t h = {0, 0};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[2 * k] = bf16_lo(u.w[k]);
-      v[2 * k + 1] = bf16_hi(u.w[k]);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = __uint_as_float(u.w[k]);
+    for (int q = 0; q < 8; ++q) h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, b.w[q] & 0x7FFF7FFFu));
+    return static_cast<uint32_t>(max(h.x, h.y)) << 16;
   }
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t unit_max_bits(const Unit<DT> &u) {
-  float v[8];
-  unit_values<DT>(u, v);
   uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
+  for (int q = 0; q < 16; ++q) m = max(m, b.w[q] & 0x7FFFFFFFu);
   return m;
 }
 
-// Encode one unit (8 elements = half a 1x16 block; the other half is in the
-// neighbouring lane) and store its 4 data bytes and, on every 8th lane, the
-// group of 4 block scales. Executed by all lanes (shuffles), stores predicated.
+template <int DT>
+__device__ __forceinline__ float block_value(const Block<DT> &b, int k) {
+  if (DT == kBF16) return (k & 1) ? bf16_hi(b.w[k >> 1]) : bf16_lo(b.w[k >> 1]);
+  return __uint_as_float(b.w[k]);
+}
+
+// Encode block `blk` of `row` (16 elements, block max bits m) and store its 8
+// data bytes; lane 0 of each group of four stores the group's 4 scale codes.
+// Executed by all lanes (DPP), stores predicated on `valid`.
 template <int DT, bool SR>
-__device__ __forceinline__ void encode_unit(const Unit<DT> &u, bool valid, uint32_t uidx, uint32_t row,
-                                            const RowScaledArgs &p, float S, uint32_t key) {
-  float v[8];
-  unit_values<DT>(u, v);
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
-  m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
+__device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, bool valid, uint32_t blk, uint32_t row,
+                                             const RowScaledArgs &p, float S, uint32_t key) {
   const BlockScale bs = block_scale(__uint_as_float(m), S);
-  const uint32_t byte0 = row * (p.cols >> 1) + uidx * 4;
-  float s[8];
+  float s[16];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) s[k] = v[k] * bs.mult;
-  uint32_t word;
+  for (int k = 0; k < 16; ++k) s[k] = block_value<DT>(b, k) * bs.mult;
+  const uint64_t byte0 = static_cast<uint64_t>(row) * (p.cols >> 1) + 8ull * blk;
+  uint32_t lo, hi;
   if (SR) {
-    uint32_t r[4];
+    uint32_t r[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = fmix32(key ^ (byte0 + q));
-    word = e2m1_sr_x8(s, r);
+    for (int q = 0; q < 8; ++q) r[q] = fmix32(key ^ static_cast<uint32_t>(byte0 + q));
+    lo = e2m1_sr_x8(s, r);
+    hi = e2m1_sr_x8(s + 8, r + 4);
   } else {
-    word = e2m1_rne_x8(s);
+    lo = e2m1_rne_x8(s);
+    hi = e2m1_rne_x8(s + 8);
   }
-  if (valid) __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(p.data + byte0));
-  const uint32_t c1 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 2, 64));
-  const uint32_t c2 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 4, 64));
-  const uint32_t c3 = static_cast<uint32_t>(__shfl_down(static_cast<int>(bs.code), 6, 64));
-  if (valid && (uidx & 7u) == 0) {
+  if (valid) __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(p.data + byte0));
+  const uint32_t group = quad_bcast(bs.code, 0) | (quad_bcast(bs.code, 1) << 8) | (quad_bcast(bs.code, 2) << 16) |
+                         (quad_bcast(bs.code, 3) << 24);
+  if (valid && (blk & 3u) == 0) {
     const uint32_t scale_cols = p.cols >> 4;
-    const uint32_t sc = uidx >> 1;
-    const uint64_t off = static_cast<uint64_t>(row) * scale_cols + sc;
-    const uint32_t group = bs.code | (c1 << 8) | (c2 << 16) | (c3 << 24);
-    if ((scale_cols & 3u) == 0 && sc + 4 <= scale_cols) {
+    const uint64_t off = static_cast<uint64_t>(row) * scale_cols + blk;
+    if ((scale_cols & 3u) == 0 && blk + 4 <= scale_cols) {
       __builtin_nontemporal_store(group, reinterpret_cast<uint32_t *>(p.scales + off));
     } else {
 #pragma unroll
       for (uint32_t i = 0; i < 4; ++i)
-        if (sc + i < scale_cols) p.scales[off + i] = static_cast<uint8_t>(group >> (8 * i));
+        if (blk + i < scale_cols) p.scales[off + i] = static_cast<uint8_t>(group >> (8 * i));
     }
   }
 }
 
-template <int DT, bool SR, bool COMPUTE>
-__global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
-  __shared__ uint32_t lds_w[kThreads / 64];
-  if (p.noop != nullptr && *p.noop == 1.0f) return;
-  const uint32_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const uint32_t units = p.cols >> 3;
+// The register part of one row (blocks t, t + kThreads, ...), zero past the
+// row's end.
+template <int DT>
+__device__ __forceinline__ void load_row(const RowScaledArgs &p, uint32_t row, Block<DT> (&r)[kRegBlocks]) {
+  const uint32_t nblk = p.cols >> 4;
   const uint64_t row_off = static_cast<uint64_t>(row) * p.cols;
-
-  Unit<DT> reg[kRegUnits];
-  uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < kRegUnits; ++k) {
-    const uint32_t u = tid + kThreads * k;
-    if (u < units) {
-      reg[k] = load_unit<DT, true>(p.x, row_off + 8ull * u);
-      if (COMPUTE) m = max(m, unit_max_bits<DT>(reg[k]));
-    } else {
-#pragma unroll
-      for (int q = 0; q < Unit<DT>::kWords; ++q) reg[k].w[q] = 0;
-    }
+  for (int k = 0; k < kRegBlocks; ++k) {
+    const uint32_t blk = threadIdx.x + kThreads * k;
+    if (blk < nblk)
+      r[k] = load_block<DT, true>(p.x, row_off + 16ull * blk);
+    else
+      zero_block<DT>(r[k]);
   }
+}
+
+// One row: amax (or the given one), then encode and store.
+template <int DT, bool SR, bool COMPUTE>
+__device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row, const Block<DT> (&reg)[kRegBlocks],
+                                            uint32_t *lds_w, uint32_t key) {
+  const int tid = threadIdx.x;
+  const uint32_t nblk = p.cols >> 4;
+  const uint64_t row_off = static_cast<uint64_t>(row) * p.cols;
+  uint32_t bm[kRegBlocks];
+#pragma unroll
+  for (int k = 0; k < kRegBlocks; ++k) bm[k] = block_max_bits<DT>(reg[k]);
   float amax;
   if (COMPUTE) {
-    for (uint32_t u = tid + kThreads * kRegUnits; u < units; u += kThreads)
-      m = max(m, unit_max_bits<DT>(load_unit<DT, false>(p.x, row_off + 8ull * u)));
+    uint32_t m = bm[0];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 64)));
+    for (int k = 1; k < kRegBlocks; ++k) m = max(m, bm[k]);
+    for (uint32_t blk = tid + kThreads * kRegBlocks; blk < nblk; blk += kThreads)
+      m = max(m, block_max_bits<DT>(load_block<DT, false>(p.x, row_off + 16ull * blk)));
+    m = wave_max(m);
     if ((tid & 63) == 0) lds_w[tid >> 6] = m;
     __syncthreads();
     m = lds_w[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) m = max(m, lds_w[w]);
+    for (int w = 1; w < kWaves; ++w) m = max(m, lds_w[w]);
     amax = __uint_as_float(m);
     if (tid == 0) p.amax[row] = amax;
   } else {
@@ -151,28 +163,40 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
   if (p.data == nullptr) return;
 
   const float S = global_encode_scale(amax);
+#pragma unroll
+  for (int k = 0; k < kRegBlocks; ++k) {
+    const uint32_t blk = tid + kThreads * k;
+    encode_block<DT, SR>(reg[k], bm[k], blk < nblk, blk, row, p, S, key);
+  }
+  for (uint32_t base = kThreads * kRegBlocks; base < nblk; base += kThreads) {  // uniform loop
+    const uint32_t blk = base + tid;
+    Block<DT> cur;
+    if (blk < nblk)
+      cur = load_block<DT, false>(p.x, row_off + 16ull * blk);
+    else
+      zero_block<DT>(cur);
+    encode_block<DT, SR>(cur, block_max_bits<DT>(cur), blk < nblk, blk, row, p, S, key);
+  }
+}
+
+// Rows 2b and 2b + 1; their per-wave maxima use separate LDS slots.
+template <int DT, bool SR, bool COMPUTE>
+__global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
+  __shared__ uint32_t lds_w[2][kWaves];
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
   const uint32_t key = SR ? sr_key(p.sr_seed, 0) : 0u;
-#pragma unroll
-  for (int k = 0; k < kRegUnits; ++k) {
-    const uint32_t u = tid + kThreads * k;
-    encode_unit<DT, SR>(reg[k], u < units, u, row, p, S, key);
-  }
-  for (uint32_t base = kThreads * kRegUnits; base < units; base += kThreads) {
-    const uint32_t u = base + tid;
-    Unit<DT> cur;
-    if (u < units) {
-      cur = load_unit<DT, false>(p.x, row_off + 8ull * u);
-    } else {
-#pragma unroll
-      for (int q = 0; q < Unit<DT>::kWords; ++q) cur.w[q] = 0;
-    }
-    encode_unit<DT, SR>(cur, u < units, u, row, p, S, key);
-  }
+  const uint32_t r0 = blockIdx.x * 2;  // < rows
+  const bool two = r0 + 1 < p.rows;    // uniform
+  Block<DT> a[kRegBlocks], b[kRegBlocks];
+  load_row<DT>(p, r0, a);
+  if (two) load_row<DT>(p, r0 + 1, b);
+  process_row<DT, SR, COMPUTE>(p, r0, a, lds_w[0], key);
+  if (two) process_row<DT, SR, COMPUTE>(p, r0 + 1, b, lds_w[1], key);
 }
 
 template <int DT, bool SR, bool COMPUTE>
 hipError_t launch_one(const RowScaledArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((k_rowscaled<DT, SR, COMPUTE>), dim3(a.rows), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_rowscaled<DT, SR, COMPUTE>), dim3((a.rows + 1) / 2), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
