@@ -136,37 +136,81 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
   }
 }
 
-// RHT amax pair. The input is cut into units of 16 rows x (kAmaxThreads *
-// VEC) columns, gx units across; a workgroup reduces units blockIdx.x,
-// blockIdx.x + gridDim.x, ... Each thread takes VEC adjacent columns of one
-// 16-row group: max|x| over the raw values, max|t| over their 16-point
-// transforms. Results go to partials[blockIdx.x] and
-// partials[kMaxPartials + blockIdx.x], or with partials == NULL (one unit per
-// workgroup) into row_amax and col_amax by atomic max.
+// RHT amax pair. The input is cut into units of 16 rows x (kAmaxThreads * 4)
+// columns, gx units across; a workgroup reduces units blockIdx.x,
+// blockIdx.x + gridDim.x, ... Each thread loads 4 adjacent columns of one
+// 16-row group as raw words: max|x| comes from the words themselves, the
+// sign flips of the transform are applied to whole words (one sign per row),
+// and each column's 16 values then go through the unnormalized transform.
+// max|t| = fl(max|sum| / 4): scaling by 1/4 is exact up to rounding in the
+// denormal range, and rounding is monotonic, so this is the maximum of the
+// transformed values t = fl(sum / 4) themselves. Results go to
+// partials[blockIdx.x] and partials[kMaxPartials + blockIdx.x], or with
+// partials == NULL (one unit per workgroup) into row_amax and col_amax by
+// atomic max.
 template <int DT>
 __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
                                                        uint32_t gx, uint32_t units, uint32_t mask, float *row_amax,
                                                        float *col_amax, uint32_t *partials, const float *noop) {
-  constexpr int VEC = DT == kBF16 ? 8 : 4;
+  constexpr int VEC = 4;
+  constexpr int W = DT == kBF16 ? 2 : 4;  // 32-bit words per 4-column row piece
+  constexpr uint32_t kAbs = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+  constexpr uint32_t kSign = DT == kBF16 ? 0x80008000u : 0x80000000u;
   __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
-  uint32_t mx = 0, mt = 0;
+  ushort2_t mx16 = {0, 0};  // BF16 max|x|, two lanes
+  uint32_t mx32 = 0;        // FP32 max|x| bits
+  float ms = 0.0f;          // max |unnormalized transform|
   for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
     const uint32_t by = u / gx;
     const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * VEC;
     if (c < cols) {
-      float v[VEC][16];
-      load_strip<DT, VEC>(x, cols, by * 16, c, v);
+      uint32_t w[16][W];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint8_t *src = static_cast<const uint8_t *>(x) +
+                             (static_cast<uint64_t>(by * 16 + r) * cols + c) * (DT == kBF16 ? 2 : 4);
+        if constexpr (DT == kBF16) {
+          const uint2 t = *reinterpret_cast<const uint2 *>(src);
+          w[r][0] = t.x;
+          w[r][1] = t.y;
+        } else {
+          const uint4 t = *reinterpret_cast<const uint4 *>(src);
+          w[r][0] = t.x;
+          w[r][1] = t.y;
+          w[r][2] = t.z;
+          w[r][3] = t.w;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int q = 0; q < W; ++q) {
+          if constexpr (DT == kBF16)
+            mx16 = __builtin_elementwise_max(mx16, __builtin_bit_cast(ushort2_t, w[r][q] & kAbs));
+          else
+            mx32 = max(mx32, w[r][q] & kAbs);
+          w[r][q] ^= ((mask >> r) & 1u) ? kSign : 0u;  // uniform select
+        }
+      }
 #pragma unroll
       for (int j = 0; j < VEC; ++j) {
+        float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = max(mx, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
-        rht16(v[j], mask);
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (DT == kBF16)
+            v[r] = (j & 1) ? bf16_hi(w[r][j >> 1]) : bf16_lo(w[r][j >> 1]);
+          else
+            v[r] = __uint_as_float(w[r][j]);
+        }
+        fwht16(v);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = max(mt, __float_as_uint(v[j][r]) & 0x7FFFFFFFu);
+        for (int r = 0; r < 16; ++r) ms = fmaxf(ms, fabsf(v[r]));
       }
     }
   }
+  uint32_t mx = DT == kBF16 ? (static_cast<uint32_t>(max(mx16.x, mx16.y)) << 16) : mx32;
+  uint32_t mt = __float_as_uint(ms * 0.25f);
   mx = block_umax<kAmaxThreads>(mx, lds);
   __syncthreads();
   mt = block_umax<kAmaxThreads>(mt, lds);
@@ -243,8 +287,7 @@ hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t col
                            float *row_amax, float *col_amax, uint32_t *partials, uint32_t *npartials,
                            const float *noop, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  const uint32_t vec = dtype == kBF16 ? 8 : 4;
-  const uint32_t gx = (cols + kAmaxThreads * vec - 1) / (kAmaxThreads * vec);
+  const uint32_t gx = (cols + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
   const uint32_t units = gx * (rows / 16);  // < 2^32: rows * cols < 2^32
   const uint32_t grid = reduction_grid(units, partials != nullptr);
   if (npartials) *npartials = grid;

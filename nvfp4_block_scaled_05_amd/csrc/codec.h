@@ -192,9 +192,8 @@ __device__ __forceinline__ uint32_t sr_key(uint32_t seed, uint32_t orientation) 
 // an in-place fast Walsh-Hadamard transform (natural = Sylvester order), and
 // the orthonormal factor 1/4 (exact).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void rht16(float (&v)[16], uint32_t sign_mask) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(__float_as_uint(v[k]) ^ (((sign_mask >> k) & 1u) << 31));
+// Unnormalized 16-point fast Walsh-Hadamard transform, in place.
+__device__ __forceinline__ void fwht16(float (&v)[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -206,6 +205,12 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t sign_mask) {
       }
     }
   }
+}
+
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t sign_mask) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(__float_as_uint(v[k]) ^ (((sign_mask >> k) & 1u) << 31));
+  fwht16(v);
 #pragma unroll
   for (int k = 0; k < 16; ++k) v[k] *= 0.25f;
 }
