@@ -626,20 +626,30 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   }
 
   // ---- column-wise: RHT of each 16-row column group, then encode ----
+  // The transform's sign flips go on whole input words (one sign per row; the
+  // row-wise side is done with them), and its 1/4 is folded into the block
+  // max (exact: rounding is monotonic) and into the multiplier (exact: a
+  // power of two), so each column runs the unnormalized transform only.
   if (do_col) {
     const uint32_t kcol = SR ? sr_key(p.sr_seed, 1) : 0u;
     const uint32_t half_rows = p.rows >> 1;
+    constexpr uint32_t kSign = DT == kBF16 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+#pragma unroll
+      for (int q = 0; q < W; ++q) w[k][q] ^= ((p.sign_mask >> k) & 1u) ? kSign : 0u;  // uniform select
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float v[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = value(k, c);
-      rht16(v, p.sign_mask);
-      uint32_t m = 0;
+      fwht16(v);
+      float ms = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
-      const uint32_t code = block_code(m, S_col);
-      const float e = lds_mult[1][code];
+      for (int k = 0; k < 16; ++k) ms = fmaxf(ms, fabsf(v[k]));
+      const uint32_t code = block_code(__float_as_uint(ms * 0.25f), S_col);
+      const float e = lds_mult[1][code] * 0.25f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] *= e;
       uint32_t lo, hi;
