@@ -20,7 +20,7 @@
 //               column's 16-row transform group is whole in one thread.
 // Both read the input once with non-temporal 128-bit (or 64-bit) loads, stage
 // output bytes and scale codes in LDS, and leave them as wide coalesced
-// non-temporal stores.
+// stores (non-temporal, except the register-tile kernel's column-wise data).
 #include "codec.h"
 #include "launch.h"
 
@@ -159,8 +159,11 @@ __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uin
 // workgroup (one correctly rounded division per code) and looked up in LDS.
 // Scale codes and column-wise data words go through LDS so that they leave
 // as 32-bit scale words and 64 contiguous bytes per column. The input is read
-// once and the outputs are not read back, so loads and stores are
-// non-temporal (streamed past the caches).
+// once and the outputs are not read back, so loads and most stores are
+// non-temporal (streamed past the caches). Column-wise data is the exception:
+// a tile writes half of each 128-byte line it touches, the tile below it the
+// other half, and ordinary stores let the caches merge the two (measured
+// faster than streaming them).
 // ---------------------------------------------------------------------------
 constexpr int kRT = 128;  // register-tile edge
 
@@ -446,12 +449,13 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
       const uint32_t rr = r0 + 32 * h;
       if (j < p.cols && rr < p.rows) {
         uint8_t *dst = p.col_data + j * half_rows + (rr >> 1);
+        // cached stores: the 64-byte column pieces of vertically adjacent
+        // tiles share 128-byte lines, which the caches can merge
         if (rr + 32 <= p.rows)
-          __builtin_nontemporal_store(
-              u32x4{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc], lds_cw[4 * h + 2][lc], lds_cw[4 * h + 3][lc]},
-              reinterpret_cast<u32x4 *>(dst));
+          *reinterpret_cast<u32x4 *>(dst) =
+              u32x4{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc], lds_cw[4 * h + 2][lc], lds_cw[4 * h + 3][lc]};
         else
-          __builtin_nontemporal_store(u32x2{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc]}, reinterpret_cast<u32x2 *>(dst));
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc]};
       }
     }
   }
