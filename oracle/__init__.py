@@ -73,6 +73,7 @@ def _load():
         "oracle_quantize": (I, [P, I, I64, I64, I, I, I, U32, I, U32, P, P, P, P, P, P]),
         "oracle_swizzle_offset": (I64, [I64, I64, I64]),
         "oracle_swizzle_scales": (I, [P, I64, I64, P]),
+        "oracle_swizzle_scales_padded": (None, [P, I64, I64, P]),
         "oracle_dequantize": (None, [P, P, P, I, I64, I64, P]),
         "oracle_e2m1_rne_array": (None, [P, I64, P]),
         "oracle_e2m1_sr_array": (None, [P, P, I64, P]),
@@ -234,6 +235,20 @@ def swizzle_scales(compact) -> np.ndarray:
     out = np.empty(rows * sc, np.uint8)
     if _load().oracle_swizzle_scales(_ptr(compact), rows, sc, _ptr(out)) != 0:
         raise ValueError("swizzled layout needs rows % 128 == 0 and scale_cols % 4 == 0")
+    return out
+
+
+def swizzled_size(rows: int, scale_cols: int) -> int:
+    """Bytes of the zero-padded GEMM layout of a [rows][scale_cols] scale matrix."""
+    return (rows + 127) // 128 * 128 * ((scale_cols + 3) // 4 * 4)
+
+
+def swizzle_scales_padded(compact) -> np.ndarray:
+    """Compact [rows][scale_cols], any shape -> zero-padded GEMM-swizzled flat array."""
+    compact = np.ascontiguousarray(compact, np.uint8)
+    rows, sc = compact.shape
+    out = np.empty(swizzled_size(rows, sc), np.uint8)
+    _load().oracle_swizzle_scales_padded(_ptr(compact), rows, sc, _ptr(out))
     return out
 
 

@@ -432,6 +432,19 @@ int oracle_swizzle_scales(const uint8_t *compact, int64_t rows, int64_t scale_co
   return 0;
 }
 
+/* [P2] Description: shapes with partial scale tiles keep compact scales
+ * from the quantize call, and a separate pass after it produces the GEMM
+ * layout. Reading: that pass pads the scale matrix with zeros to whole
+ * 128 x 4 tiles, [ceil(rows/128)*128][ceil(scale_cols/4)*4], and lays the
+ * padded matrix out as above. swizzled holds that many bytes. */
+void oracle_swizzle_scales_padded(const uint8_t *compact, int64_t rows, int64_t scale_cols, uint8_t *swizzled) {
+  const int64_t prows = (rows + 127) / 128 * 128;
+  const int64_t pcols = (scale_cols + 3) / 4 * 4;
+  for (int64_t r = 0; r < prows; ++r)
+    for (int64_t c = 0; c < pcols; ++c)
+      swizzled[oracle_swizzle_offset(r, c, pcols)] = (r < rows && c < scale_cols) ? compact[r * scale_cols + c] : 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* Dequantize one direction (its own orientation, compact scales):      */
 /* y = (value(code) * value(s)) / S, the product being exact; S is the  */

@@ -473,6 +473,31 @@ def test_swizzle_groups_of_four_are_aligned_words():
         O.swizzle_scales(np.zeros((64, 8), np.uint8))
 
 
+def _reshape_swizzle(padded):
+    """The GEMM layout as an array reshape: 128x4 tiles in row-major tile
+    order, inside a tile [4 row groups of 32][32][4] -> [32][4][4]."""
+    pr, pc = padded.shape
+    t = padded.reshape(pr // 128, 128, pc // 4, 4).transpose(0, 2, 1, 3)
+    t = t.reshape(pr // 128, pc // 4, 4, 32, 4).transpose(0, 1, 3, 2, 4)
+    return t.reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [(1088, 64), (100, 7), (128, 4), (1, 1), (257, 130), (0, 5), (5, 0)])
+def test_padded_swizzle_is_the_layout_of_the_zero_padded_matrix(shape):
+    rows, sc = shape
+    rng = np.random.default_rng(rows * 1000 + sc)
+    compact = rng.integers(1, 256, size=shape, dtype=np.uint8)  # no zeros: padding stays visible
+    pr, pc = -(-rows // 128) * 128, -(-sc // 4) * 4
+    padded = np.zeros((pr, pc), np.uint8)
+    padded[:rows, :sc] = compact
+    got = O.swizzle_scales_padded(compact)
+    assert got.size == O.swizzled_size(rows, sc) == pr * pc
+    assert np.array_equal(got, _reshape_swizzle(padded))
+    assert np.count_nonzero(got) == rows * sc  # every value once; everything else is padding
+    if rows % 128 == 0 and sc % 4 == 0 and rows * sc > 0:
+        assert np.array_equal(got, O.swizzle_scales(compact))
+
+
 def test_rht_columnwise_is_plain_rowwise_of_the_transform():
     # The RHT path's column-wise output is the ordinary row-wise quantization
     # of the transformed tensor t[cols][rows], scaled by max|t|.
