@@ -198,6 +198,25 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
 nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols,
                                 uint32_t scale_layout, uint32_t row_scaled, float *y, void *stream);
 
+/*
+ * Compact -> GEMM-swizzled scales, for shapes with partial scale tiles
+ * ("Fuse NVFP4 scale swizzling ...", Description: such shapes keep compact
+ * scales from the quantize call and a separate pass lays them out for the
+ * GEMM). compact: device, [rows][scale_cols] bytes (scale_cols = k/16 of the
+ * orientation), 4-byte aligned. swizzled: device, 4-byte aligned,
+ * nvfp4_swizzled_scales_bytes(rows, scale_cols) bytes: the scale matrix
+ * padded with zeros to [ceil(rows/128)*128][ceil(scale_cols/4)*4] in the
+ * layout of NVFP4_SCALES_GEMM_SWIZZLED. Every byte of it is written. For
+ * rows % 128 == 0 and scale_cols % 4 == 0 the result equals the swizzled
+ * scales that nvfp4_quantize writes directly. rows * scale_cols < 2^32.
+ */
+nvfp4_status_t nvfp4_swizzle_scales(const uint8_t *compact, int64_t rows, int64_t scale_cols, uint8_t *swizzled,
+                                    void *stream);
+
+/* Size in bytes of the zero-padded swizzled scales of nvfp4_swizzle_scales
+ * (0 for a negative or empty shape). */
+uint64_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t scale_cols);
+
 /* Text for the last non-OK status returned on the calling thread ("" when
  * none). The pointer stays valid until the next call on that thread. */
 const char *nvfp4_last_error(void);

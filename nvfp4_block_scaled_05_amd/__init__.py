@@ -45,7 +45,8 @@ NVFP4_DEBUG_SR = 1
 NVFP4_DEBUG_PAIRWISE = 2
 
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
-            "nvfp4_workspace_bytes", "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack")
+            "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes",
+            "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -107,6 +108,10 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_workspace_bytes.restype = ctypes.c_uint64
     lib.nvfp4_workspace_bytes.argtypes = []
+    lib.nvfp4_swizzle_scales.restype = I
+    lib.nvfp4_swizzle_scales.argtypes = [P, I64, I64, P, P]
+    lib.nvfp4_swizzled_scales_bytes.restype = ctypes.c_uint64
+    lib.nvfp4_swizzled_scales_bytes.argtypes = [I64, I64]
     lib.nvfp4_debug_rht_colwise.restype = I
     lib.nvfp4_debug_rht_colwise.argtypes = [P, I, I64, I64, U32, P, P]
     lib.nvfp4_debug_e2m1_pack.restype = I
@@ -197,6 +202,19 @@ def nvfp4_dequantize(q: Orientation, rows: int, cols: int, scale_layout: int, ro
     qc = q.as_c()
     _check(load().nvfp4_dequantize(ctypes.byref(qc), rows, cols, scale_layout, int(row_scaled), _ptr(y),
                                    _stream(stream)))
+
+
+def nvfp4_swizzled_scales_bytes(rows: int, scale_cols: int) -> int:
+    return int(load().nvfp4_swizzled_scales_bytes(rows, scale_cols))
+
+
+def nvfp4_swizzle_scales(compact: torch.Tensor, rows: int, scale_cols: int, swizzled: torch.Tensor,
+                         stream=None) -> None:
+    """compact: uint8 with rows * scale_cols bytes; swizzled: uint8 with
+    nvfp4_swizzled_scales_bytes(rows, scale_cols) bytes."""
+    if compact.numel() != rows * scale_cols or swizzled.numel() != nvfp4_swizzled_scales_bytes(rows, scale_cols):
+        raise ValueError("buffer sizes do not match the scale shape")
+    _check(load().nvfp4_swizzle_scales(_ptr(compact), rows, scale_cols, _ptr(swizzled), _stream(stream)))
 
 
 def nvfp4_debug_rht_colwise(x: torch.Tensor, sign_mask: int, t: torch.Tensor, stream=None) -> None:

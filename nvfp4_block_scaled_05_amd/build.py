@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "amax.hip", "cast.hip", "rowscaled.hip", "dequant.hip", "hooks.hip"]
+SOURCES = ["api.cpp", "amax.hip", "cast.hip", "rowscaled.hip", "dequant.hip", "swizzle.hip", "hooks.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -75,6 +75,26 @@ extern "C" const char *nvfp4_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" uint64_t nvfp4_workspace_bytes(void) { return NVFP4_WORKSPACE_BYTES; }
 
+extern "C" uint64_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t scale_cols) {
+  if (rows <= 0 || scale_cols <= 0) return 0;
+  return nvfp4::swizzled_scales_bytes(static_cast<uint64_t>(rows), static_cast<uint64_t>(scale_cols));
+}
+
+extern "C" nvfp4_status_t nvfp4_swizzle_scales(const uint8_t *compact, int64_t rows, int64_t scale_cols,
+                                               uint8_t *swizzled, void *stream) {
+  if (rows < 0 || scale_cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape %lld x %lld", (long long)rows,
+                                              (long long)scale_cols);
+  if (rows > 0 && scale_cols > 0 && (rows + 127) / 128 * 128 * ((scale_cols + 3) / 4 * 4) >= (int64_t{1} << 34))
+    return fail(NVFP4_ERR_SHAPE, "scale matrix %lld x %lld is too large", (long long)rows, (long long)scale_cols);
+  if (rows * scale_cols == 0) return NVFP4_OK;
+  if (compact == nullptr || swizzled == nullptr) return fail(NVFP4_ERR_NULL, "a scale pointer is NULL");
+  if (!aligned(compact, 4) || !aligned(swizzled, 4))
+    return fail(NVFP4_ERR_ALIGN, "scale buffers must be 4-byte aligned");
+  return hip_status(nvfp4::launch_swizzle(compact, static_cast<uint32_t>(rows), static_cast<uint32_t>(scale_cols),
+                                          swizzled, static_cast<hipStream_t>(stream)),
+                    "swizzle launch");
+}
+
 extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
                                              float *row_amax, float *col_amax, const nvfp4_config_t *cfg_in,
                                              void *stream) {

@@ -62,6 +62,9 @@ hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bo
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *data, const uint8_t *scales, const float *amax, uint32_t rows,
                           uint32_t cols, bool swizzled, bool row_scaled, float *y, hipStream_t s);
+// zero-padded compact -> GEMM-swizzled scales; out holds swizzled_scales_bytes()
+uint64_t swizzled_scales_bytes(uint64_t rows, uint64_t scale_cols);
+hipError_t launch_swizzle(const uint8_t *compact, uint32_t rows, uint32_t scale_cols, uint8_t *out, hipStream_t s);
 hipError_t launch_debug_e2m1(const float *v, const uint32_t *r, uint8_t *out, uint64_t n, bool sr, bool pairwise,
                              hipStream_t s);
 hipError_t launch_debug_rht(const void *x, int dtype, uint32_t rows, uint32_t cols, uint32_t mask, float *t,

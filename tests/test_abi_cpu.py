@@ -174,3 +174,16 @@ def test_cast_events_must_not_hold_null():
     ev = (ctypes.c_void_p * 2)(0x1000, None)
     cfg.cast_events = ctypes.cast(ev, ctypes.c_void_p)
     assert lib.nvfp4_quantize(X, 0, 64, 64, ctypes.byref(r), None, ctypes.byref(cfg), None) == nv.NVFP4_ERR_NULL
+
+
+def test_swizzled_scales_size_and_rejections():
+    lib = nv.load()
+    assert nv.nvfp4_swizzled_scales_bytes(1088, 64) == 1152 * 64
+    assert nv.nvfp4_swizzled_scales_bytes(100, 7) == 128 * 8
+    assert nv.nvfp4_swizzled_scales_bytes(8192, 320) == 8192 * 320
+    assert nv.nvfp4_swizzled_scales_bytes(0, 8) == 0 and nv.nvfp4_swizzled_scales_bytes(-1, 8) == 0
+    assert lib.nvfp4_swizzle_scales(S, -1, 4, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_swizzle_scales(None, 128, 4, D, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_swizzle_scales(S + 2, 128, 4, D, None) == nv.NVFP4_ERR_ALIGN
+    assert lib.nvfp4_swizzle_scales(S, 1 << 30, 1 << 10, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_swizzle_scales(None, 0, 4, None, None) == nv.NVFP4_OK  # empty: nothing to do

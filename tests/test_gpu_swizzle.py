@@ -1,0 +1,80 @@
+"""GPU: the standalone compact -> GEMM-swizzled scale pass.
+
+- Against the oracle's zero-padded layout on shapes with partial tiles.
+- The pages' production-shape check: for the 128-aligned shapes of their
+  swizzle-fusion benchmark, 1D, 2D and RHT quantization with and without
+  stochastic rounding, the scales that nvfp4_quantize writes directly in the
+  GEMM layout equal the compact scales of the same call put through the
+  separate pass, and the FP4 data and both amaxes are the same
+  ("Fuse NVFP4 scale swizzling ...", validation footnote: 10 shapes x 6
+  modes, 60 cases).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_05_amd as nv
+import oracle as O
+from gpu_helpers import DEV, host
+
+pytestmark = pytest.mark.gpu
+
+
+def swizzle_on_gpu(compact: np.ndarray) -> np.ndarray:
+    rows, sc = compact.shape
+    src = torch.from_numpy(np.ascontiguousarray(compact)).to(DEV).reshape(-1)
+    out = torch.full((nv.nvfp4_swizzled_scales_bytes(rows, sc),), 0xA5, dtype=torch.uint8, device=DEV)
+    nv.nvfp4_swizzle_scales(src, rows, sc, out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("shape", [(1088, 64), (1088, 68), (100, 7), (129, 5), (128, 4), (8192, 320), (5120, 512),
+                                   (1, 1), (300, 33)])
+def test_swizzle_pass_matches_oracle(shape):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    compact = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    assert np.array_equal(swizzle_on_gpu(compact), O.swizzle_scales_padded(compact))
+
+
+def test_swizzle_pass_of_a_real_quantize_with_partial_tiles():
+    # 1088 x 1024: not 128-aligned, so the fused path rejects swizzled scales;
+    # compact scales + the separate pass give the oracle's padded layout
+    x = np.random.default_rng(5).standard_normal((1088, 1024)).astype(np.float32)
+    xd = torch.from_numpy(x).to(DEV)
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize(xd, cfg=nv.make_config(swizzled=True))
+    row, col = nv.quantize(xd)
+    ref = O.quantize(x)
+    assert np.array_equal(swizzle_on_gpu(host(row.scales).reshape(1088, 64)),
+                          O.swizzle_scales_padded(ref["row_scales"]))
+    assert np.array_equal(swizzle_on_gpu(host(col.scales).reshape(1024, 68)),
+                          O.swizzle_scales_padded(ref["col_scales"]))
+
+
+PRODUCTION_SHAPES = [(8192, 2560), (8192, 3584), (8192, 5120), (8192, 10240), (2560, 8192), (3584, 8192),
+                     (5120, 8192), (10240, 8192), (4096, 16384), (14336, 16384)]
+MODES = {"1d": {}, "1d_sr": dict(stochastic=True, sr_seed=9), "2d": dict(block_2d=True),
+         "2d_sr": dict(block_2d=True, stochastic=True, sr_seed=9), "rht": dict(rht=True, rht_sign_mask=0xB4D1),
+         "rht_sr": dict(rht=True, rht_sign_mask=0xB4D1, stochastic=True, sr_seed=9)}
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+@pytest.mark.parametrize("shape", PRODUCTION_SHAPES, ids=[f"{r}x{c}" for r, c in PRODUCTION_SHAPES])
+def test_fused_swizzle_equals_separate_pass(shape, mode):
+    rows, cols = shape
+    g = torch.Generator(device=DEV).manual_seed(rows + cols)
+    x = torch.randn(shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    fused_row, fused_col = nv.quantize(x, cfg=nv.make_config(swizzled=True, **MODES[mode]))
+    row, col = nv.quantize(x, cfg=nv.make_config(**MODES[mode]))
+    torch.cuda.synchronize()
+    for fused, plain, n, k in ((fused_row, row, rows, cols), (fused_col, col, cols, rows)):
+        assert torch.equal(fused.data, plain.data)
+        assert torch.equal(fused.amax, plain.amax)
+        out = torch.empty_like(fused.scales)
+        nv.nvfp4_swizzle_scales(plain.scales, n, k // 16, out)
+        assert torch.equal(fused.scales, out)
+    del x, fused_row, fused_col, row, col
