@@ -228,6 +228,53 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
             "amax_row": amax_row if rowwise else None, "amax_col": amax_col if columnwise else None}
 
 
+def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=False, rht=False, sign_mask=0,
+                     stochastic=False, sr_seed=0, amax_row=None, amax_col=None):
+    """Grouped quantize. The row-scaled page's changed files keep a grouped
+    tensor as one tensor per group with per-group amax offsets; reading: the
+    consecutive row slices x[s_g : s_g + m_g] (m_g = group_rows[g]) are each
+    quantized as a tensor of their own, with the same options (the same SR
+    seed, byte indices counted within the group's own arrays).
+
+    Returns flat arrays in group order: row_data (= [R][C/2]), row_scales
+    (= [R][C/16], compact), col_data (group g's [C][m_g/2] blocks one after
+    another), col_scales (group g's [C][m_g/16] blocks), amax_row [G],
+    amax_col [G]. amax_row / amax_col, when given, are per-group arrays.
+    """
+    x, _ = _input(x)
+    rows, cols = x.shape
+    group_rows = [int(m) for m in group_rows]
+    if sum(group_rows) != rows or min(group_rows) < 0:
+        raise ValueError("group rows must be non-negative and add up to the input's rows")
+    parts = {k: [] for k in ("row_data", "row_scales", "col_data", "col_scales", "amax_row", "amax_col")}
+    start = 0
+    for g, m in enumerate(group_rows):
+        xs = x[start:start + m]
+        start += m
+        if m == 0:
+            parts["amax_row"].append(np.zeros(1, np.float32))
+            parts["amax_col"].append(np.zeros(1, np.float32))
+            continue
+        given = {}
+        if amax_row is not None or amax_col is not None:
+            given = dict(amax_row=None if amax_row is None else np.asarray(amax_row, np.float32)[g:g + 1],
+                         amax_col=None if amax_col is None else np.asarray(amax_col, np.float32)[g:g + 1])
+        q = quantize(xs, rowwise=rowwise, columnwise=columnwise, block_2d=block_2d, rht=rht, sign_mask=sign_mask,
+                     stochastic=stochastic, sr_seed=sr_seed, **given)
+        for k in ("row_data", "row_scales", "col_data", "col_scales"):
+            if q[k] is not None:
+                parts[k].append(q[k].reshape(-1))
+        parts["amax_row"].append(q["amax_row"] if rowwise else np.zeros(1, np.float32))
+        parts["amax_col"].append(q["amax_col"] if columnwise else np.zeros(1, np.float32))
+    out = {}
+    for k in ("row_data", "row_scales", "col_data", "col_scales"):
+        on = rowwise if k.startswith("row") else columnwise
+        out[k] = (np.concatenate(parts[k]) if parts[k] else np.zeros(0, np.uint8)) if on else None
+    out["amax_row"] = np.concatenate(parts["amax_row"]).astype(np.float32) if rowwise else None
+    out["amax_col"] = np.concatenate(parts["amax_col"]).astype(np.float32) if columnwise else None
+    return out
+
+
 def swizzle_scales(compact) -> np.ndarray:
     """Compact [rows][scale_cols] -> GEMM-swizzled flat array (rows % 128, scale_cols % 4)."""
     compact = np.ascontiguousarray(compact, np.uint8)

@@ -527,3 +527,49 @@ def test_explicit_amax_is_used_as_given():
     assert not np.array_equal(q2["row_scales"], O.quantize(x)["row_scales"])
     for key in ("row_data", "row_scales", "col_data", "col_scales"):
         assert np.array_equal(q2[key], qh[key])
+
+
+# ----------------------------------------------------------------------------
+# Grouped quantize: each row slice is a tensor of its own.
+# ----------------------------------------------------------------------------
+
+def test_grouped_single_group_is_plain_quantize():
+    x = W.randn_bf16(64, 96, 41)
+    g = O.quantize_grouped(x, [64], stochastic=True, sr_seed=3)
+    q = O.quantize(x, stochastic=True, sr_seed=3)
+    for k in ("row_data", "row_scales", "col_data", "col_scales", "amax_row", "amax_col"):
+        assert np.array_equal(g[k], q[k].reshape(-1)), k
+
+
+def test_grouped_scaling_one_group_changes_only_its_amax():
+    # power-of-two invariance per group: codes and scales stay, that group's
+    # amax scales by exactly 2^k, the other groups do not move at all
+    x = W.gaussian_fp32(96, 64, 42)
+    sizes = [32, 48, 16]
+    base = O.quantize_grouped(x, sizes, block_2d=True)
+    y = x.copy()
+    y[32:80] *= np.float32(2.0 ** 7)
+    moved = O.quantize_grouped(y, sizes, block_2d=True)
+    for k in ("row_data", "row_scales", "col_data", "col_scales"):
+        assert np.array_equal(base[k], moved[k]), k
+    assert np.array_equal(moved["amax_row"], base["amax_row"] * np.float32([1, 128, 1]))
+    assert np.array_equal(moved["amax_col"], base["amax_col"] * np.float32([1, 128, 1]))
+
+
+def test_grouped_blocks_follow_group_order():
+    # swapping two groups swaps their blocks in every output array
+    x = W.randn_bf16(64, 48, 43)
+    a = O.quantize_grouped(x, [16, 48])
+    xs = np.concatenate([x[16:], x[:16]])
+    b = O.quantize_grouped(xs, [48, 16])
+    assert np.array_equal(b["row_data"], np.concatenate([a["row_data"][16 * 24:], a["row_data"][:16 * 24]]))
+    assert np.array_equal(b["col_data"], np.concatenate([a["col_data"][48 * 8:], a["col_data"][:48 * 8]]))
+    assert np.array_equal(b["col_scales"], np.concatenate([a["col_scales"][48 * 1:], a["col_scales"][:48 * 1]]))
+    assert np.array_equal(b["amax_row"], a["amax_row"][::-1])
+
+
+def test_grouped_empty_group_has_zero_amax_and_no_bytes():
+    x = W.randn_bf16(32, 32, 44)
+    g = O.quantize_grouped(x, [16, 0, 16])
+    assert g["amax_row"][1] == 0 and g["amax_col"][1] == 0
+    assert g["row_data"].size == 32 * 16 and g["col_data"].size == 2 * 32 * 8
