@@ -188,6 +188,34 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
                               const nvfp4_out_t *row, const nvfp4_out_t *col,
                               const nvfp4_config_t *cfg, void *stream);
 
+/* Most groups of one nvfp4_quantize_grouped call. */
+#define NVFP4_MAX_GROUPS 256
+
+/*
+ * Grouped quantize (the row-scaled page's grouped tensor storage: one tensor
+ * per group with its own amax, "Implement row-scaled NVFP4 fprop recipe",
+ * changed files). x is R x C with R = group_rows[0] + ... +
+ * group_rows[G-1] (1 <= G <= NVFP4_MAX_GROUPS; group_rows is a host array;
+ * a group may be empty). Group g is the slice of group_rows[g] rows starting
+ * at row s_g = group_rows[0] + ... + group_rows[g-1]. Each group is
+ * quantized exactly as nvfp4_quantize would quantize that slice on its own
+ * with the same config (stochastic-rounding byte indices counted within
+ * the group's own arrays), in three launches for all groups:
+ *   row  data [R][C/2] and scales (compact [R][C/16], or each group's
+ *        swizzled block at byte s_g * C/16), amax [G];
+ *   col  group g's column-wise tensor [C][group_rows[g]]: data at byte
+ *        C * s_g / 2, scales at byte C * s_g / 16 (compact or swizzled
+ *        block), amax [G].
+ * Each group_rows[g] must be a multiple of 16 for column-wise output, 16x16
+ * blocks or the RHT, and of 128 for swizzled scales (C too). Row-scaled
+ * configs are rejected (per-row scaling already treats rows on their own:
+ * use nvfp4_quantize). A computed amax is zeroed and reduced with atomics;
+ * the workspace is not used.
+ */
+nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_t num_groups,
+                                      const int64_t *group_rows, int64_t cols, const nvfp4_out_t *row,
+                                      const nvfp4_out_t *col, const nvfp4_config_t *cfg, void *stream);
+
 /*
  * Dequantize one orientation q (n = rows, k = cols in q's own orientation,
  * k % 16 == 0) into y [rows][cols] FP32 (device, 4-byte aligned):

@@ -44,8 +44,10 @@ NVFP4_SCALE_UE5M3 = 1
 NVFP4_DEBUG_SR = 1
 NVFP4_DEBUG_PAIRWISE = 2
 
+NVFP4_MAX_GROUPS = 256
+
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
-            "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes",
+            "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes", "nvfp4_quantize_grouped",
             "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack")
 
 
@@ -108,6 +110,10 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_workspace_bytes.restype = ctypes.c_uint64
     lib.nvfp4_workspace_bytes.argtypes = []
+    lib.nvfp4_quantize_grouped.restype = I
+    lib.nvfp4_quantize_grouped.argtypes = [P, I, I64, ctypes.POINTER(ctypes.c_int64), I64,
+                                           ctypes.POINTER(nvfp4_out_t), ctypes.POINTER(nvfp4_out_t),
+                                           ctypes.POINTER(nvfp4_config_t), P]
     lib.nvfp4_swizzle_scales.restype = I
     lib.nvfp4_swizzle_scales.argtypes = [P, I64, I64, P, P]
     lib.nvfp4_swizzled_scales_bytes.restype = ctypes.c_uint64
@@ -202,6 +208,38 @@ def nvfp4_dequantize(q: Orientation, rows: int, cols: int, scale_layout: int, ro
     qc = q.as_c()
     _check(load().nvfp4_dequantize(ctypes.byref(qc), rows, cols, scale_layout, int(row_scaled), _ptr(y),
                                    _stream(stream)))
+
+
+def nvfp4_quantize_grouped(x: torch.Tensor, group_rows, row: Optional[Orientation], col: Optional[Orientation],
+                           cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
+    """x [sum(group_rows)][C]; row/col hold the concatenated per-group outputs
+    (data and scales flat or shaped, amax [G])."""
+    rows, cols = _shape2d(x)
+    g = (ctypes.c_int64 * len(group_rows))(*[int(m) for m in group_rows])
+    r = row.as_c() if row is not None else None
+    c = col.as_c() if col is not None else None
+    _check(load().nvfp4_quantize_grouped(_ptr(x), _dtype_code(x), len(group_rows), g, cols,
+                                         None if r is None else ctypes.byref(r), None if c is None else ctypes.byref(c),
+                                         None if cfg is None else ctypes.byref(cfg), _stream(stream)))
+
+
+def quantize_grouped(x: torch.Tensor, group_rows, *, rowwise=True, columnwise=True,
+                     cfg: Optional[nvfp4_config_t] = None, stream=None):
+    """Allocate the concatenated per-group outputs and run nvfp4_quantize_grouped.
+    Returns (row, col) with flat data and scales and amax [G]."""
+    rows, cols = _shape2d(x)
+    G = len(group_rows)
+    dev = x.device
+
+    def orient():
+        return Orientation(torch.empty((rows * cols // 2,), dtype=torch.uint8, device=dev),
+                           torch.empty((rows * cols // 16,), dtype=torch.uint8, device=dev),
+                           torch.empty((G,), dtype=torch.float32, device=dev))
+
+    row = orient() if rowwise else None
+    col = orient() if columnwise else None
+    nvfp4_quantize_grouped(x, group_rows, row, col, cfg, stream)
+    return row, col
 
 
 def nvfp4_swizzled_scales_bytes(rows: int, scale_cols: int) -> int:

@@ -148,14 +148,88 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
 // partials[blockIdx.x] and partials[kMaxPartials + blockIdx.x], or with
 // partials == NULL (one unit per workgroup) into row_amax and col_amax by
 // atomic max.
+// One RHT amax unit: this thread's 4 columns c .. c+3 of rows 16 by .. +15.
+// Accumulates max|x| (mx16 / mx32 by input type) and max|unnormalized
+// transform| (ms).
 template <int DT>
-__global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
-                                                       uint32_t gx, uint32_t units, uint32_t mask, float *row_amax,
-                                                       float *col_amax, uint32_t *partials, const float *noop) {
+__device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32_t cols, uint32_t by, uint32_t c,
+                                              uint32_t mask, ushort2_t &mx16, uint32_t &mx32, float &ms) {
   constexpr int VEC = 4;
   constexpr int W = DT == kBF16 ? 2 : 4;  // 32-bit words per 4-column row piece
   constexpr uint32_t kAbs = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
   constexpr uint32_t kSign = DT == kBF16 ? 0x80008000u : 0x80000000u;
+  uint32_t w[16][W];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint8_t *src = static_cast<const uint8_t *>(x) +
+                         (static_cast<uint64_t>(by * 16 + r) * cols + c) * (DT == kBF16 ? 2 : 4);
+    if constexpr (DT == kBF16) {
+      const uint2 t = *reinterpret_cast<const uint2 *>(src);
+      w[r][0] = t.x;
+      w[r][1] = t.y;
+    } else {
+      const uint4 t = *reinterpret_cast<const uint4 *>(src);
+      w[r][0] = t.x;
+      w[r][1] = t.y;
+      w[r][2] = t.z;
+      w[r][3] = t.w;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      if constexpr (DT == kBF16)
+        mx16 = __builtin_elementwise_max(mx16, __builtin_bit_cast(ushort2_t, w[r][q] & kAbs));
+      else
+        mx32 = max(mx32, w[r][q] & kAbs);
+      w[r][q] ^= ((mask >> r) & 1u) ? kSign : 0u;  // uniform select
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (DT == kBF16)
+        v[r] = (j & 1) ? bf16_hi(w[r][j >> 1]) : bf16_lo(w[r][j >> 1]);
+      else
+        v[r] = __uint_as_float(w[r][j]);
+    }
+    fwht16(v);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ms = fmaxf(ms, fabsf(v[r]));
+  }
+}
+
+// Workgroup maxima of an RHT amax pass: (max|x|, max|t|) as float bits, in
+// every thread.
+template <int DT>
+__device__ __forceinline__ void rht_amax_finish(ushort2_t mx16, uint32_t mx32, float ms, uint32_t *lds, uint32_t &mx,
+                                                uint32_t &mt) {
+  mx = DT == kBF16 ? (static_cast<uint32_t>(max(mx16.x, mx16.y)) << 16) : mx32;
+  mt = __float_as_uint(ms * 0.25f);
+  mx = block_umax<kAmaxThreads>(mx, lds);
+  __syncthreads();
+  mt = block_umax<kAmaxThreads>(mt, lds);
+}
+
+// RHT amax pair. The input is cut into units of 16 rows x (kAmaxThreads * 4)
+// columns, gx units across; a workgroup reduces units blockIdx.x,
+// blockIdx.x + gridDim.x, ... Each thread loads 4 adjacent columns of one
+// 16-row group as raw words: max|x| comes from the words themselves, the
+// sign flips of the transform are applied to whole words (one sign per row),
+// and each column's 16 values then go through the unnormalized transform.
+// max|t| = fl(max|sum| / 4): scaling by 1/4 is exact up to rounding in the
+// denormal range, and rounding is monotonic, so this is the maximum of the
+// transformed values t = fl(sum / 4) themselves. Results go to
+// partials[blockIdx.x] and partials[kMaxPartials + blockIdx.x], or with
+// partials == NULL (one unit per workgroup) into row_amax and col_amax by
+// atomic max.
+template <int DT>
+__global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
+                                                       uint32_t gx, uint32_t units, uint32_t mask, float *row_amax,
+                                                       float *col_amax, uint32_t *partials, const float *noop) {
   __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
   ushort2_t mx16 = {0, 0};  // BF16 max|x|, two lanes
@@ -163,57 +237,11 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restric
   float ms = 0.0f;          // max |unnormalized transform|
   for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
     const uint32_t by = u / gx;
-    const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * VEC;
-    if (c < cols) {
-      uint32_t w[16][W];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint8_t *src = static_cast<const uint8_t *>(x) +
-                             (static_cast<uint64_t>(by * 16 + r) * cols + c) * (DT == kBF16 ? 2 : 4);
-        if constexpr (DT == kBF16) {
-          const uint2 t = *reinterpret_cast<const uint2 *>(src);
-          w[r][0] = t.x;
-          w[r][1] = t.y;
-        } else {
-          const uint4 t = *reinterpret_cast<const uint4 *>(src);
-          w[r][0] = t.x;
-          w[r][1] = t.y;
-          w[r][2] = t.z;
-          w[r][3] = t.w;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int q = 0; q < W; ++q) {
-          if constexpr (DT == kBF16)
-            mx16 = __builtin_elementwise_max(mx16, __builtin_bit_cast(ushort2_t, w[r][q] & kAbs));
-          else
-            mx32 = max(mx32, w[r][q] & kAbs);
-          w[r][q] ^= ((mask >> r) & 1u) ? kSign : 0u;  // uniform select
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (DT == kBF16)
-            v[r] = (j & 1) ? bf16_hi(w[r][j >> 1]) : bf16_lo(w[r][j >> 1]);
-          else
-            v[r] = __uint_as_float(w[r][j]);
-        }
-        fwht16(v);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ms = fmaxf(ms, fabsf(v[r]));
-      }
-    }
+    const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * 4;
+    if (c < cols) rht_amax_unit<DT>(x, cols, by, c, mask, mx16, mx32, ms);
   }
-  uint32_t mx = DT == kBF16 ? (static_cast<uint32_t>(max(mx16.x, mx16.y)) << 16) : mx32;
-  uint32_t mt = __float_as_uint(ms * 0.25f);
-  mx = block_umax<kAmaxThreads>(mx, lds);
-  __syncthreads();
-  mt = block_umax<kAmaxThreads>(mt, lds);
+  uint32_t mx, mt;
+  rht_amax_finish<DT>(mx16, mx32, ms, lds, mx, mt);
   if (threadIdx.x == 0) {
     if (partials != nullptr) {
       partials[blockIdx.x] = mx;
@@ -222,6 +250,79 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restric
       publish_max(row_amax, mx);
       publish_max(col_amax, mt);
     }
+  }
+}
+
+// Grouped RHT amax pair: one unit per workgroup, units of group g
+// unit_start[g] .. unit_start[g + 1] - 1 (gx across, m_g / 16 down); atomic
+// max into the group's slots.
+template <int DT>
+__global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *__restrict__ x, uint32_t cols,
+                                                               uint32_t gx, GroupTable t, uint32_t mask,
+                                                               float *row_amax, float *col_amax, const float *noop) {
+  __shared__ uint32_t lds[kAmaxThreads / 64];
+  if (noop_set(noop)) return;
+  const uint32_t g = group_of(t, blockIdx.x);
+  const uint32_t u = blockIdx.x - t.unit_start[g];
+  const uint32_t by = u / gx;
+  const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * 4;
+  const void *xg = static_cast<const uint8_t *>(x) + static_cast<uint64_t>(t.row_start[g]) * cols * (DT == kBF16 ? 2 : 4);
+  ushort2_t mx16 = {0, 0};
+  uint32_t mx32 = 0;
+  float ms = 0.0f;
+  if (c < cols) rht_amax_unit<DT>(xg, cols, by, c, mask, mx16, mx32, ms);
+  uint32_t mx, mt;
+  rht_amax_finish<DT>(mx16, mx32, ms, lds, mx, mt);
+  if (threadIdx.x == 0) {
+    if (row_amax) publish_max(row_amax + g, mx);
+    if (col_amax) publish_max(col_amax + g, mt);
+  }
+}
+
+// Grouped per-tensor amax: chunks of kMaxThreads * kMaxVecPerThread vectors
+// within each group, one per workgroup; the chunks of group g are
+// unit_start[g] .. unit_start[g + 1] - 1. Atomic max into the group's slots.
+template <int DT>
+__global__ __launch_bounds__(kMaxThreads) void k_amax_grouped(const uint4 *__restrict__ x, uint32_t vec_per_row,
+                                                              GroupTable t, float *a, float *b, const float *noop) {
+  constexpr int VPT = kMaxVecPerThread;
+  __shared__ uint32_t lds[kMaxThreads / 64];
+  if (noop_set(noop)) return;
+  const uint32_t g = group_of(t, blockIdx.x);
+  const uint64_t first = static_cast<uint64_t>(t.row_start[g]) * vec_per_row;
+  const uint64_t nvec = static_cast<uint64_t>(t.row_start[g + 1] - t.row_start[g]) * vec_per_row;
+  const uint64_t base = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * (kMaxThreads * VPT) + threadIdx.x;
+  // all loads in flight at once: past the group's end the index is clamped
+  // to its last vector (nvec >= 1), which cannot change a maximum
+  uint4 v[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) v[k] = x[first + min(base + static_cast<uint64_t>(k) * kMaxThreads, nvec - 1)];
+  uint32_t m32 = 0;
+  ushort2_t m16 = {0, 0};
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (DT == kBF16)
+        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[j] & 0x7FFF7FFFu));
+      else
+        m32 = max(m32, w[j] & 0x7FFFFFFFu);
+    }
+  }
+  uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
+  m = block_umax<kMaxThreads>(m, lds);
+  if (threadIdx.x == 0) {
+    if (a) publish_max(a + g, m);
+    if (b && b != a) publish_max(b + g, m);
+  }
+}
+
+__global__ void k_zero_amax_n(float *a, float *b, uint32_t n, const float *noop) {
+  if (noop_set(noop)) return;
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    if (a) a[i] = 0.0f;
+    if (b) b[i] = 0.0f;
   }
 }
 
@@ -297,6 +398,50 @@ hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t col
   else
     hipLaunchKernelGGL(k_rht_amax<kFP32>, dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units, mask,
                        row_amax, col_amax, partials, noop);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_amax_n(float *a, float *b, uint32_t n, const float *noop, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_amax_n, dim3(1), dim3(256), 0, s, a, b, n, noop);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start, uint32_t ngroups,
+                               float *a, float *b, const float *noop, hipStream_t s) {
+  GroupTable t{};
+  t.ngroups = ngroups;
+  const uint32_t vec_per_row = cols * (dtype == kBF16 ? 2 : 4) / 16;
+  const uint64_t chunk = kMaxThreads * kMaxVecPerThread;
+  for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
+  for (uint32_t g = 0; g < ngroups; ++g) {
+    const uint64_t nvec = static_cast<uint64_t>(row_start[g + 1] - row_start[g]) * vec_per_row;
+    t.unit_start[g + 1] = t.unit_start[g] + static_cast<uint32_t>((nvec + chunk - 1) / chunk);
+  }
+  if (t.unit_start[ngroups] == 0) return hipSuccess;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_amax_grouped<kBF16>, dim3(t.unit_start[ngroups]), dim3(kMaxThreads), 0, s,
+                       static_cast<const uint4 *>(x), vec_per_row, t, a, b, noop);
+  else
+    hipLaunchKernelGGL(k_amax_grouped<kFP32>, dim3(t.unit_start[ngroups]), dim3(kMaxThreads), 0, s,
+                       static_cast<const uint4 *>(x), vec_per_row, t, a, b, noop);
+  return hipGetLastError();
+}
+
+hipError_t launch_rht_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start,
+                                   uint32_t ngroups, uint32_t mask, float *row_amax, float *col_amax,
+                                   const float *noop, hipStream_t s) {
+  GroupTable t{};
+  t.ngroups = ngroups;
+  const uint32_t gx = (cols + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
+  for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
+  for (uint32_t g = 0; g < ngroups; ++g) t.unit_start[g + 1] = t.unit_start[g] + gx * ((row_start[g + 1] - row_start[g]) / 16);
+  if (t.unit_start[ngroups] == 0) return hipSuccess;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_rht_amax_grouped<kBF16>, dim3(t.unit_start[ngroups]), dim3(kAmaxThreads), 0, s, x, cols, gx,
+                       t, mask, row_amax, col_amax, noop);
+  else
+    hipLaunchKernelGGL(k_rht_amax_grouped<kFP32>, dim3(t.unit_start[ngroups]), dim3(kAmaxThreads), 0, s, x, cols, gx,
+                       t, mask, row_amax, col_amax, noop);
   return hipGetLastError();
 }
 

@@ -229,6 +229,71 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   return st != NVFP4_OK ? st : record(1);
 }
 
+extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_t num_groups,
+                                                 const int64_t *group_rows, int64_t cols, const nvfp4_out_t *row,
+                                                 const nvfp4_out_t *col, const nvfp4_config_t *cfg_in,
+                                                 void *stream) {
+  if (num_groups < 1 || num_groups > NVFP4_MAX_GROUPS)
+    return fail(NVFP4_ERR_SHAPE, "num_groups = %lld must be in [1, %d]", (long long)num_groups, NVFP4_MAX_GROUPS);
+  if (group_rows == nullptr) return fail(NVFP4_ERR_NULL, "group_rows is NULL");
+  int64_t rows = 0;
+  for (int64_t g = 0; g < num_groups; ++g) {
+    if (group_rows[g] < 0) return fail(NVFP4_ERR_SHAPE, "group %lld has %lld rows", (long long)g, (long long)group_rows[g]);
+    rows += group_rows[g];
+    if (rows >= (int64_t{1} << 32)) return fail(NVFP4_ERR_SHAPE, "too many rows");
+  }
+  nvfp4_status_t st = check_input(x, dtype, rows, cols);
+  if (st != NVFP4_OK) return st;
+  const nvfp4_config_t cfg = config_or_default(cfg_in);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (row == nullptr && col == nullptr) return fail(NVFP4_ERR_NULL, "neither a row-wise nor a column-wise output");
+  const bool empty = rows * cols == 0;
+  if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
+  if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
+  if (cfg.row_scaled) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled grouped quantize: use nvfp4_quantize");
+  if (cfg.scale_fmt != NVFP4_SCALE_E4M3) return fail(NVFP4_ERR_UNSUPPORTED, "only E4M3 block scales are supported");
+  if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", cfg.scale_layout);
+  const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
+  if (cfg.rht && cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "the RHT is defined for 1x16 blocks only");
+  if (cfg.rht && row && col && row->amax == col->amax)
+    return fail(NVFP4_ERR_UNSUPPORTED, "the RHT quantize needs distinct row-wise and column-wise amax buffers");
+  const int64_t mult = swz ? 128 : ((col || cfg.block_2d || cfg.rht) ? 16 : 1);
+  for (int64_t g = 0; g < num_groups; ++g)
+    if (group_rows[g] % mult != 0)
+      return fail(NVFP4_ERR_SHAPE, "group %lld: %lld rows is not a multiple of %lld", (long long)g,
+                  (long long)group_rows[g], (long long)mult);
+  if (swz && cols % 128 != 0)
+    return fail(NVFP4_ERR_SHAPE, "GEMM-swizzled scales need cols %% 128 == 0 (got %lld)", (long long)cols);
+
+  uint32_t row_start[nvfp4::kMaxGroups + 1];
+  row_start[0] = 0;
+  for (int64_t g = 0; g < num_groups; ++g) row_start[g + 1] = row_start[g] + static_cast<uint32_t>(group_rows[g]);
+  const uint32_t G = static_cast<uint32_t>(num_groups), C = static_cast<uint32_t>(cols);
+  const bool sr = cfg.stochastic != 0;
+  float *ra = row ? row->amax : nullptr;
+  float *ca = col ? col->amax : nullptr;
+  if (cfg.compute_amax) {
+    float *a = ra ? ra : ca;
+    float *b = (ca == a) ? nullptr : ca;
+    if ((st = hip_status(nvfp4::launch_zero_amax_n(a, b, G, cfg.noop, s), "zero amax launch")) != NVFP4_OK) return st;
+    if (!empty) {
+      if (cfg.rht)
+        st = hip_status(nvfp4::launch_rht_amax_grouped(x, dtype, C, row_start, G, cfg.rht_sign_mask, ra, ca, cfg.noop, s),
+                        "RHT amax launch");
+      else
+        st = hip_status(nvfp4::launch_amax_grouped(x, dtype, C, row_start, G, a, b, cfg.noop, s), "amax launch");
+      if (st != NVFP4_OK) return st;
+    }
+  }
+  if (empty) return NVFP4_OK;
+  nvfp4::CastArgs a{x, static_cast<uint32_t>(rows), C, row ? row->data : nullptr, row ? row->scales : nullptr, ra,
+                    col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
+                    cfg.rht_sign_mask, cfg.noop, nullptr, 0};
+  return hip_status(nvfp4::launch_cast_grouped(a, row_start, G, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s),
+                    "grouped quantize launch");
+}
+
 extern "C" nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols, uint32_t scale_layout,
                                            uint32_t row_scaled, float *y, void *stream) {
   if (q == nullptr || y == nullptr) return fail(NVFP4_ERR_NULL, "NULL quantized tensor or output");

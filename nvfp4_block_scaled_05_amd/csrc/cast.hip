@@ -218,7 +218,7 @@ __device__ __forceinline__ uint32_t piece_max(const uint32_t (&w)[RT<DT>::kWords
 }
 
 template <int DT, bool B2D, bool SR>
-__global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
+__device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
   constexpr int W = RT<DT>::kWords;
   __shared__ float lds_mult[2][128];                   // multiplier per E4M3 code (row, col)
   // scale codes of the tile, row-wise [tile row][16-col block] and column-wise
@@ -234,8 +234,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   const int tid = threadIdx.x;
   const int ucol = tid & 15;
   const int rg = tid >> 4;
-  const uint32_t r0 = blockIdx.y * kRT;
-  const uint32_t c0 = blockIdx.x * kRT;
+  const uint32_t r0 = ty * kRT;
+  const uint32_t c0 = tx * kRT;
   const uint32_t col = c0 + 8 * ucol;
   const uint32_t rbase = r0 + 8 * rg;
   const bool col_ok = col < p.cols;
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
 // leave as 16-byte stores (64 contiguous bytes per row / column).
 // ---------------------------------------------------------------------------
 template <int DT, bool SR>
-__global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
+__device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
   constexpr int kElem = DT == kBF16 ? 2 : 4;
   constexpr int W = kElem;  // 32-bit words per 4-column row piece: 2 (BF16) or 4 (FP32)
   __shared__ float lds_mult[2][128];
@@ -518,8 +518,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   const int tid = threadIdx.x;
   const int cg = tid & 31;
   const int rq = tid >> 5;
-  const uint32_t r0 = blockIdx.y * kRT;
-  const uint32_t c0 = blockIdx.x * kRT;
+  const uint32_t r0 = ty * kRT;
+  const uint32_t c0 = tx * kRT;
   const uint32_t col = c0 + 4 * cg;
   const uint32_t rbase = r0 + 16 * rq;
   const bool col_ok = col < p.cols;
@@ -729,6 +729,56 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
 }
 
 template <int DT, bool B2D, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
+  cast_rt_tile<DT, B2D, SR>(p, blockIdx.x, blockIdx.y);
+}
+
+template <int DT, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
+  cast_rht_tile<DT, SR>(p, blockIdx.x, blockIdx.y);
+}
+
+// The arguments of group g's own tensor: its rows of the input, its blocks
+// of the concatenated outputs, its amax slots.
+template <int DT>
+__device__ __forceinline__ CastArgs group_args(const CastArgs &p, const GroupTable &t, uint32_t g) {
+  CastArgs q = p;
+  const uint64_t r0 = t.row_start[g];
+  q.rows = t.row_start[g + 1] - t.row_start[g];
+  q.x = static_cast<const uint8_t *>(p.x) + r0 * p.cols * RT<DT>::kElem;
+  if (p.row_data != nullptr) {
+    q.row_data = p.row_data + r0 * (p.cols >> 1);
+    q.row_scales = p.row_scales + r0 * (p.cols >> 4);
+  }
+  if (p.col_data != nullptr) {
+    q.col_data = p.col_data + p.cols * r0 / 2;
+    q.col_scales = p.col_scales + p.cols * r0 / 16;
+  }
+  if (p.row_amax != nullptr) q.row_amax = p.row_amax + g;
+  if (p.col_amax != nullptr) q.col_amax = p.col_amax + g;
+  q.partials = nullptr;
+  return q;
+}
+
+// One workgroup per 128 x 128 tile of some group; the tiles of group g are
+// unit_start[g] .. unit_start[g + 1] - 1, row-major over that group.
+template <int DT, bool B2D, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rt_grouped(CastArgs p, GroupTable t) {
+  const uint32_t g = group_of(t, blockIdx.x);
+  const uint32_t local = blockIdx.x - t.unit_start[g];
+  const uint32_t tiles_x = (p.cols + kRT - 1) / kRT;
+  cast_rt_tile<DT, B2D, SR>(group_args<DT>(p, t, g), local % tiles_x, local / tiles_x);
+}
+
+template <int DT, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rht_grouped(CastArgs p, GroupTable t) {
+  const uint32_t g = group_of(t, blockIdx.x);
+  const uint32_t local = blockIdx.x - t.unit_start[g];
+  const uint32_t tiles_x = (p.cols + kRT - 1) / kRT;
+  cast_rht_tile<DT, SR>(group_args<DT>(p, t, g), local % tiles_x, local / tiles_x);
+}
+
+template <int DT, bool B2D, bool SR>
 hipError_t launch_rt(const CastArgs &a, hipStream_t s) {
   dim3 grid((a.cols + kRT - 1) / kRT, (a.rows + kRT - 1) / kRT);
   hipLaunchKernelGGL((k_cast_rt<DT, B2D, SR>), grid, dim3(kThreads), 0, s, a);
@@ -749,7 +799,43 @@ hipError_t launch_dt(const CastArgs &a, bool block_2d, bool rht, bool sr, hipStr
   return sr ? launch_rt<DT, false, true>(a, s) : launch_rt<DT, false, false>(a, s);
 }
 
+template <int DT>
+hipError_t launch_grouped_dt(const CastArgs &a, const GroupTable &t, bool block_2d, bool rht, bool sr, hipStream_t s) {
+  const dim3 grid(t.unit_start[t.ngroups]), block(kThreads);
+  if (rht) {
+    if (sr)
+      hipLaunchKernelGGL((k_cast_rht_grouped<DT, true>), grid, block, 0, s, a, t);
+    else
+      hipLaunchKernelGGL((k_cast_rht_grouped<DT, false>), grid, block, 0, s, a, t);
+  } else if (block_2d) {
+    if (sr)
+      hipLaunchKernelGGL((k_cast_rt_grouped<DT, true, true>), grid, block, 0, s, a, t);
+    else
+      hipLaunchKernelGGL((k_cast_rt_grouped<DT, true, false>), grid, block, 0, s, a, t);
+  } else {
+    if (sr)
+      hipLaunchKernelGGL((k_cast_rt_grouped<DT, false, true>), grid, block, 0, s, a, t);
+    else
+      hipLaunchKernelGGL((k_cast_rt_grouped<DT, false, false>), grid, block, 0, s, a, t);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
+                               bool block_2d, bool rht, bool sr, hipStream_t s) {
+  GroupTable t{};
+  t.ngroups = ngroups;
+  const uint32_t tiles_x = (a.cols + kRT - 1) / kRT;
+  for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
+  t.unit_start[0] = 0;
+  for (uint32_t g = 0; g < ngroups; ++g)
+    t.unit_start[g + 1] = t.unit_start[g] + (row_start[g + 1] - row_start[g] + kRT - 1) / kRT * tiles_x;
+  if (t.unit_start[ngroups] == 0) return hipSuccess;
+  return dtype == kBF16 ? launch_grouped_dt<kBF16>(a, t, block_2d, rht, sr, s)
+                        : launch_grouped_dt<kFP32>(a, t, block_2d, rht, sr, s);
+}
 
 hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s) {
   if (a.rows == 0 || a.cols == 0) return hipSuccess;

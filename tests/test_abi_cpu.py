@@ -187,3 +187,26 @@ def test_swizzled_scales_size_and_rejections():
     assert lib.nvfp4_swizzle_scales(S + 2, 128, 4, D, None) == nv.NVFP4_ERR_ALIGN
     assert lib.nvfp4_swizzle_scales(S, 1 << 30, 1 << 10, D, None) == nv.NVFP4_ERR_SHAPE
     assert lib.nvfp4_swizzle_scales(None, 0, 4, None, None) == nv.NVFP4_OK  # empty: nothing to do
+
+
+def test_grouped_rejections():
+    lib = nv.load()
+    r = nv.nvfp4_out_t(D, S, A)
+    c = nv.nvfp4_out_t(D + 0x100000, S + 0x100000, A2)
+    G = ctypes.c_int64 * 3
+
+    def call(groups, cols=64, cfg=None, row=r, col=c):
+        arr = G(*groups) if len(groups) == 3 else (ctypes.c_int64 * len(groups))(*groups)
+        return lib.nvfp4_quantize_grouped(X, 0, len(groups), arr, cols, ctypes.byref(row) if row else None,
+                                          ctypes.byref(col) if col else None,
+                                          None if cfg is None else ctypes.byref(cfg), None)
+
+    assert lib.nvfp4_quantize_grouped(X, 0, 0, None, 64, ctypes.byref(r), None, None, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_quantize_grouped(X, 0, 257, None, 64, ctypes.byref(r), None, None, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_quantize_grouped(X, 0, 2, None, 64, ctypes.byref(r), None, None, None) == nv.NVFP4_ERR_NULL
+    assert call([16, -16, 16]) == nv.NVFP4_ERR_SHAPE
+    assert call([16, 8, 16]) == nv.NVFP4_ERR_SHAPE              # column-wise output needs multiples of 16
+    assert call([128, 64, 128], cols=128, cfg=nv.make_config(swizzled=True)) == nv.NVFP4_ERR_SHAPE
+    assert call([16, 16, 16], cfg=nv.make_config(row_scaled=True), col=None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call([16, 16, 16], cfg=nv.make_config(rht=True, block_2d=True)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call([16, 16, 16], cols=40) == nv.NVFP4_ERR_SHAPE

@@ -1,0 +1,145 @@
+"""GPU: grouped quantize (consecutive row slices, each a tensor of its own)
+against the oracle's grouped quantize, and against one nvfp4_quantize call
+per group."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_05_amd as nv
+import oracle as O
+import workloads as W
+from gpu_helpers import DEV, codes, e2m1_step_distance, host, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_grouped(x, groups, rowwise=True, columnwise=True, **kw):
+    row, col = nv.quantize_grouped(to_device(x), groups, rowwise=rowwise, columnwise=columnwise,
+                                   cfg=nv.make_config(**kw))
+    torch.cuda.synchronize()
+    out = {}
+    for side, o in (("row", row), ("col", col)):
+        out[f"{side}_data"] = None if o is None else host(o.data)
+        out[f"{side}_scales"] = None if o is None else host(o.scales)
+        out[f"amax_{side}"] = None if o is None else host(o.amax)
+    return out
+
+
+def swizzle_groups(compact, groups, cols, columnwise):
+    """Per-group oracle swizzle of a concatenated compact scale array."""
+    parts, off = [], 0
+    for m in groups:
+        n, k = (cols, m) if columnwise else (m, cols)
+        blk = compact[off:off + n * k // 16].reshape(n, k // 16)
+        off += n * k // 16
+        if m:
+            parts.append(O.swizzle_scales(blk))
+    return np.concatenate(parts)
+
+
+CASES = {
+    "bf16_1d": (lambda: W.c2(rows=400, cols=400, seed=51), [128, 0, 48, 16, 208], {}),
+    "fp32_2d": (lambda: W.gaussian_fp32(320, 272, 52, 4.0), [16, 256, 48], dict(block_2d=True)),
+    "bf16_sr": (lambda: W.randn_bf16(192, 336, 53), [64, 64, 0, 64], dict(stochastic=True, sr_seed=7)),
+    "fp32_2d_sr": (lambda: W.gaussian_fp32(144, 208, 54), [96, 48], dict(block_2d=True, stochastic=True, sr_seed=8)),
+    "single": (lambda: W.randn_bf16(272, 400, 55), [272], {}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_grouped_matches_oracle(case):
+    make, groups, kw = CASES[case]
+    x = make()
+    got = run_grouped(x, groups, **kw)
+    ref = O.quantize_grouped(x, groups, **kw)
+    for k in ("row_data", "row_scales", "col_data", "col_scales", "amax_row", "amax_col"):
+        assert np.array_equal(got[k].ravel(), ref[k].ravel()), k
+
+
+@pytest.mark.parametrize("orient", ["row", "col"])
+def test_grouped_one_orientation(orient):
+    x = W.randn_bf16(96, 160, 56)
+    groups = [5, 17, 0, 74] if orient == "row" else [16, 0, 80]  # row-only: any group size
+    rw, cw = orient == "row", orient == "col"
+    got = run_grouped(x, groups, rowwise=rw, columnwise=cw)
+    ref = O.quantize_grouped(x, groups, rowwise=rw, columnwise=cw)
+    for k in (f"{orient}_data", f"{orient}_scales", f"amax_{orient}"):
+        assert np.array_equal(got[k].ravel(), ref[k].ravel()), k
+
+
+def test_grouped_swizzled():
+    x = W.c2(rows=896, cols=512, seed=57)
+    groups = [256, 128, 0, 384, 128]
+    got = run_grouped(x, groups, swizzled=True, block_2d=True)
+    ref = O.quantize_grouped(x, groups, block_2d=True)
+    assert np.array_equal(got["row_data"].ravel(), ref["row_data"])
+    assert np.array_equal(got["col_data"].ravel(), ref["col_data"])
+    assert np.array_equal(got["row_scales"], swizzle_groups(ref["row_scales"], groups, 512, False))
+    assert np.array_equal(got["col_scales"], swizzle_groups(ref["col_scales"], groups, 512, True))
+    assert np.array_equal(got["amax_row"], ref["amax_row"]) and np.array_equal(got["amax_col"], ref["amax_col"])
+
+
+@pytest.mark.parametrize("stochastic", [False, True])
+def test_grouped_rht(stochastic):
+    x, _, _ = W.c5(rows=320, cols=512)
+    mask = W.rht_sign_mask(58)
+    groups = [64, 0, 128, 128]
+    kw = dict(rht=True, rht_sign_mask=mask, stochastic=stochastic, sr_seed=9)
+    got = run_grouped(x, groups, **kw)
+    ref = O.quantize_grouped(x, groups, rht=True, sign_mask=mask, stochastic=stochastic, sr_seed=9)
+    assert np.array_equal(got["row_data"].ravel(), ref["row_data"])
+    assert np.array_equal(got["row_scales"].ravel(), ref["row_scales"])
+    assert np.array_equal(got["amax_row"], ref["amax_row"])
+    np.testing.assert_allclose(got["amax_col"], ref["amax_col"], rtol=1e-5)
+    d = e2m1_step_distance(np.stack([got["col_data"] & 0xF, got["col_data"] >> 4], -1).ravel(),
+                           np.stack([ref["col_data"] & 0xF, ref["col_data"] >> 4], -1).ravel())
+    assert d.max() <= 1 and np.count_nonzero(d) <= max(1, 1e-4 * d.size)
+    gs, rs = got["col_scales"].astype(np.int32), ref["col_scales"].astype(np.int32)
+    assert np.abs(gs - rs).max() <= 1 and np.count_nonzero(gs != rs) <= max(1, 1e-4 * gs.size)
+
+
+def test_grouped_equals_one_call_per_group():
+    # an MoE-like split: 32 groups of 0..640 rows, multiples of 128 (swizzled)
+    rng = np.random.default_rng(59)
+    groups = [int(m) for m in rng.integers(0, 6, 32) * 128]
+    R, C = sum(groups), 1024
+    g = torch.Generator(device=DEV).manual_seed(60)
+    x = (torch.randn((R, C), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    cfg = nv.make_config(swizzled=True, stochastic=True, sr_seed=4)
+    row, col = nv.quantize_grouped(x, groups, cfg=cfg)
+    s = 0
+    for i, m in enumerate(groups):
+        if m:
+            r1, c1 = nv.quantize(x[s:s + m], cfg=cfg)
+            assert torch.equal(row.data[s * C // 2:(s + m) * C // 2], r1.data.reshape(-1))
+            assert torch.equal(row.scales[s * C // 16:(s + m) * C // 16], r1.scales)
+            assert torch.equal(col.data[s * C // 2:(s + m) * C // 2], c1.data.reshape(-1))
+            assert torch.equal(col.scales[s * C // 16:(s + m) * C // 16], c1.scales)
+            assert row.amax[i] == r1.amax[0] and col.amax[i] == c1.amax[0]
+        else:
+            assert row.amax[i] == 0 and col.amax[i] == 0
+        s += m
+
+
+def test_grouped_noop_and_given_amax():
+    x = W.randn_bf16(64, 96, 61)
+    xd = to_device(x)
+    groups = [16, 48]
+    row, col = nv.quantize_grouped(xd, groups)
+    torch.cuda.synchronize()
+    before = [host(t).copy() for t in (row.data, row.scales, row.amax, col.data, col.scales, col.amax)]
+    noop = torch.ones(1, dtype=torch.float32, device=DEV)
+    nv.nvfp4_quantize_grouped(xd * 3, groups, row, col, nv.make_config(noop=noop))
+    torch.cuda.synchronize()
+    for b, t in zip(before, (row.data, row.scales, row.amax, col.data, col.scales, col.amax)):
+        assert np.array_equal(b, host(t))
+    # given per-group amaxes: twice the true ones
+    row.amax.copy_(torch.from_numpy(before[2] * 2))
+    col.amax.copy_(torch.from_numpy(before[5] * 2))
+    nv.nvfp4_quantize_grouped(xd, groups, row, col, nv.make_config(compute_amax=False))
+    torch.cuda.synchronize()
+    ref = O.quantize_grouped(x, groups, amax_row=before[2] * 2, amax_col=before[5] * 2)
+    assert np.array_equal(host(row.data), ref["row_data"]) and np.array_equal(host(col.scales), ref["col_scales"])
