@@ -184,6 +184,12 @@ OTHER_WORKLOADS = {
     "c5": dict(desc="8192x8192 BF16 N(0,1) + 0.1% at +-200 (seed 4); 1x16; row plain + col 16-point RHT; "
                     "stochastic rounding (seed 5); compact",
                bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
+    "grouped": dict(desc="grouped quantize, MoE-like: 64 groups of 0..512 rows (multiples of 128, seed 6; 16768 rows) "
+                         "x 4096 BF16 N(0,1) (seed 7); 1x16; row+col; compact; RNE; per-group amax",
+                    bytes=2 * 2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64),
+    "swizzle": dict(desc="separate compact -> GEMM-swizzled scale pass, both orientations of 1088x1024 "
+                         "(partial tiles: 1088x64 -> 1152x64 and 1024x68 -> 1024x68 padded to 72)",
+                    bytes=1088 * 64 + 1152 * 64 + 1024 * 68 + 1024 * 72),
 }
 
 
@@ -197,6 +203,10 @@ def run_other(name, steps, warmup):
     nv.load()
     dev = torch.device("cuda:0")
     w = OTHER_WORKLOADS[name]
+    if name == "swizzle":
+        return run_swizzle(nv, torch, dev, w, steps, warmup)
+    if name == "grouped":
+        return run_grouped(nv, torch, dev, w, steps, warmup)
     if name == "c1":
         x, cfg, rowwise, columnwise = workloads.c1(), nv.make_config(), True, True
     elif name == "c3":
@@ -233,6 +243,94 @@ def run_other(name, steps, warmup):
                       "bytes_per_call": w["bytes"], "GBps": round(w["bytes"] / us / 1e3, 1),
                       "pct_of_hbm_peak": round(100 * w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
                       "buffer_sets_rotated": n_sets}), flush=True)
+
+
+def grouped_rows():
+    import numpy as np
+
+    return [int(m) for m in np.random.default_rng(6).integers(0, 5, 64) * 128]
+
+
+def run_grouped(nv, torch, dev, w, steps, warmup):
+    """Grouped quantize of an MoE-like split (one call: amax pass and cast
+    with a workspace), and for comparison the same call without a workspace
+    (zeroing, atomic amax, cast) and the same work as one nvfp4_quantize
+    call per group."""
+    groups = grouped_rows()
+    R, C = sum(groups), 4096
+    assert R == 16768, R
+    g = torch.Generator(device=dev).manual_seed(7)
+    sets = []
+    for _ in range(N_SETS):
+        x = torch.randn((R, C), generator=g, device=dev).to(torch.bfloat16)
+        sets.append((x,) + nv.quantize_grouped(x, groups))
+    stream = torch.cuda.current_stream()
+    ws = nv.empty_workspace(dev)
+    cfg_ws = nv.make_config(workspace=ws)
+    cfg_atomic = nv.make_config()
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps
+
+    def grouped_call(i, cfg=cfg_ws):
+        x, row, col = sets[i % N_SETS]
+        nv.nvfp4_quantize_grouped(x, groups, row, col, cfg, stream)
+
+    per_group = []
+    for x, _, _ in sets:
+        outs, s0 = [], 0
+        for m in groups:
+            if m:
+                outs.append((x[s0:s0 + m], nv.empty_orientation(m, C, dev), nv.empty_orientation(C, m, dev)))
+            s0 += m
+        per_group.append(outs)
+
+    def per_group_calls(i):
+        for xs, row, col in per_group[i % N_SETS]:
+            nv.nvfp4_quantize(xs, row, col, cfg_ws, stream)
+
+    us = timed(grouped_call)
+    us_atomic = timed(lambda i: grouped_call(i, cfg_atomic))
+    us_sep = timed(per_group_calls)
+    print(json.dumps({"workload": "grouped", "config": w["desc"], "us_per_call": round(us, 3),
+                      "bytes_per_call": w["bytes"], "GBps": round(w["bytes"] / us / 1e3, 1),
+                      "pct_of_hbm_peak": round(100 * w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
+                      "nonempty_groups": sum(1 for m in groups if m),
+                      "no_workspace_us": round(us_atomic, 3), "one_call_per_group_us": round(us_sep, 3),
+                      "buffer_sets_rotated": N_SETS}), flush=True)
+
+
+def run_swizzle(nv, torch, dev, w, steps, warmup):
+    """The separate scale pass on the scales of a 1088x1024 quantize (partial
+    tiles in both orientations), both orientations per call."""
+    x = torch.randn((1088, 1024), generator=torch.Generator().manual_seed(2)).to(dev)
+    row, col = nv.quantize(x)
+    jobs = []
+    for q, n, k in ((row, 1088, 1024), (col, 1024, 1088)):
+        out = torch.empty((nv.nvfp4_swizzled_scales_bytes(n, k // 16),), dtype=torch.uint8, device=dev)
+        jobs.append((q.scales, n, k // 16, out))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for j in jobs:
+            nv.nvfp4_swizzle_scales(*j, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for j in jobs:
+            nv.nvfp4_swizzle_scales(*j, stream)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    print(json.dumps({"workload": "swizzle", "config": w["desc"], "us_per_call": round(us, 3),
+                      "bytes_per_call": w["bytes"], "GBps": round(w["bytes"] / us / 1e3, 1),
+                      "pct_of_hbm_peak": round(100 * w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
+                      "launches_per_call": 2}), flush=True)
 
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000

@@ -200,7 +200,7 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
  * at row s_g = group_rows[0] + ... + group_rows[g-1]. Each group is
  * quantized exactly as nvfp4_quantize would quantize that slice on its own
  * with the same config (stochastic-rounding byte indices counted within
- * the group's own arrays), in three launches for all groups:
+ * the group's own arrays), in at most three launches for all groups:
  *   row  data [R][C/2] and scales (compact [R][C/16], or each group's
  *        swizzled block at byte s_g * C/16), amax [G];
  *   col  group g's column-wise tensor [C][group_rows[g]]: data at byte
@@ -209,8 +209,12 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
  * Each group_rows[g] must be a multiple of 16 for column-wise output, 16x16
  * blocks or the RHT, and of 128 for swizzled scales (C too). Row-scaled
  * configs are rejected (per-row scaling already treats rows on their own:
- * use nvfp4_quantize). A computed amax is zeroed and reduced with atomics;
- * the workspace is not used.
+ * use nvfp4_quantize). A computed amax takes two launches (amax pass, cast)
+ * with a workspace, each group's workgroup maxima in a range of it that the
+ * group's cast tiles reduce (the slots of empty groups are written +0);
+ * without one it is zeroed and reduced by atomic max (three launches). The
+ * same workspace rule holds as for nvfp4_quantize: one call at a time per
+ * workspace, in stream order.
  */
 nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_t num_groups,
                                       const int64_t *group_rows, int64_t cols, const nvfp4_out_t *row,

@@ -253,68 +253,103 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restric
   }
 }
 
-// Grouped RHT amax pair: one unit per workgroup, units of group g
-// unit_start[g] .. unit_start[g + 1] - 1 (gx across, m_g / 16 down); atomic
-// max into the group's slots.
+// Slots of empty groups: in the workspace form no cast tile writes them.
+__device__ __forceinline__ void zero_empty_groups(const GroupTable &t, float *a, float *b) {
+  for (uint32_t g = threadIdx.x; g < t.ngroups; g += blockDim.x) {
+    if (t.row_start[g + 1] == t.row_start[g]) {
+      if (a) a[g] = 0.0f;
+      if (b) b[g] = 0.0f;
+    }
+  }
+}
+
+// Grouped RHT amax pair. Workgroup b of group g (b in unit_start[g] ..
+// unit_start[g + 1] - 1) takes `per_wg` consecutive units of that group
+// (gx across, m_g / 16 down; units past the group's end are empty). Results
+// go to partials[b] and partials[kMaxPartials + b], or with partials == NULL
+// into the group's slots by atomic max.
 template <int DT>
 __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *__restrict__ x, uint32_t cols,
-                                                               uint32_t gx, GroupTable t, uint32_t mask,
-                                                               float *row_amax, float *col_amax, const float *noop) {
+                                                               uint32_t gx, GroupTable t, uint32_t per_wg,
+                                                               uint32_t mask, float *row_amax, float *col_amax,
+                                                               uint32_t *partials, const float *noop) {
   __shared__ uint32_t lds[kAmaxThreads / 64];
   if (noop_set(noop)) return;
+  if (partials != nullptr && blockIdx.x == 0) zero_empty_groups(t, row_amax, col_amax);
   const uint32_t g = group_of(t, blockIdx.x);
-  const uint32_t u = blockIdx.x - t.unit_start[g];
-  const uint32_t by = u / gx;
-  const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * 4;
+  const uint32_t units = gx * ((t.row_start[g + 1] - t.row_start[g]) / 16);
   const void *xg = static_cast<const uint8_t *>(x) + static_cast<uint64_t>(t.row_start[g]) * cols * (DT == kBF16 ? 2 : 4);
   ushort2_t mx16 = {0, 0};
   uint32_t mx32 = 0;
   float ms = 0.0f;
-  if (c < cols) rht_amax_unit<DT>(xg, cols, by, c, mask, mx16, mx32, ms);
+  const uint32_t u0 = (blockIdx.x - t.unit_start[g]) * per_wg;
+  for (uint32_t u = u0; u < u0 + per_wg && u < units; ++u) {
+    const uint32_t by = u / gx;
+    const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * 4;
+    if (c < cols) rht_amax_unit<DT>(xg, cols, by, c, mask, mx16, mx32, ms);
+  }
   uint32_t mx, mt;
   rht_amax_finish<DT>(mx16, mx32, ms, lds, mx, mt);
   if (threadIdx.x == 0) {
-    if (row_amax) publish_max(row_amax + g, mx);
-    if (col_amax) publish_max(col_amax + g, mt);
+    if (partials != nullptr) {
+      partials[blockIdx.x] = mx;
+      partials[kMaxPartials + blockIdx.x] = mt;
+    } else {
+      if (row_amax) publish_max(row_amax + g, mx);
+      if (col_amax) publish_max(col_amax + g, mt);
+    }
   }
 }
 
-// Grouped per-tensor amax: chunks of kMaxThreads * kMaxVecPerThread vectors
-// within each group, one per workgroup; the chunks of group g are
-// unit_start[g] .. unit_start[g + 1] - 1. Atomic max into the group's slots.
+// Grouped per-tensor amax. Workgroup b of group g takes chunk
+// b - unit_start[g] of that group: `passes` x kMaxThreads x kMaxVecPerThread
+// consecutive vectors of its rows (chunks past the group's end are empty).
+// Result to partials[b], or with partials == NULL into the group's slots by
+// atomic max.
 template <int DT>
 __global__ __launch_bounds__(kMaxThreads) void k_amax_grouped(const uint4 *__restrict__ x, uint32_t vec_per_row,
-                                                              GroupTable t, float *a, float *b, const float *noop) {
+                                                              GroupTable t, uint32_t passes, float *a, float *b,
+                                                              uint32_t *partials, const float *noop) {
   constexpr int VPT = kMaxVecPerThread;
   __shared__ uint32_t lds[kMaxThreads / 64];
   if (noop_set(noop)) return;
+  if (partials != nullptr && blockIdx.x == 0) zero_empty_groups(t, a, b);
   const uint32_t g = group_of(t, blockIdx.x);
   const uint64_t first = static_cast<uint64_t>(t.row_start[g]) * vec_per_row;
   const uint64_t nvec = static_cast<uint64_t>(t.row_start[g + 1] - t.row_start[g]) * vec_per_row;
-  const uint64_t base = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * (kMaxThreads * VPT) + threadIdx.x;
-  // all loads in flight at once: past the group's end the index is clamped
-  // to its last vector (nvec >= 1), which cannot change a maximum
-  uint4 v[VPT];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) v[k] = x[first + min(base + static_cast<uint64_t>(k) * kMaxThreads, nvec - 1)];
+  const uint64_t chunk0 = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * passes;
   uint32_t m32 = 0;
   ushort2_t m16 = {0, 0};
+  for (uint32_t pass = 0; pass < passes; ++pass) {
+    const uint64_t start = (chunk0 + pass) * (kMaxThreads * VPT);  // uniform
+    if (start >= nvec) break;
+    // all loads in flight at once: past the group's end the index is
+    // clamped to its last vector, which cannot change a maximum
+    uint4 v[VPT];
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    for (int k = 0; k < VPT; ++k)
+      v[k] = x[first + min(start + threadIdx.x + static_cast<uint64_t>(k) * kMaxThreads, nvec - 1)];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (DT == kBF16)
-        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[j] & 0x7FFF7FFFu));
-      else
-        m32 = max(m32, w[j] & 0x7FFFFFFFu);
+    for (int k = 0; k < VPT; ++k) {
+      const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (DT == kBF16)
+          m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(ushort2_t, w[j] & 0x7FFF7FFFu));
+        else
+          m32 = max(m32, w[j] & 0x7FFFFFFFu);
+      }
     }
   }
   uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
   m = block_umax<kMaxThreads>(m, lds);
   if (threadIdx.x == 0) {
-    if (a) publish_max(a + g, m);
-    if (b && b != a) publish_max(b + g, m);
+    if (partials != nullptr) {
+      partials[blockIdx.x] = m;
+    } else {
+      if (a) publish_max(a + g, m);
+      if (b && b != a) publish_max(b + g, m);
+    }
   }
 }
 
@@ -406,42 +441,75 @@ hipError_t launch_zero_amax_n(float *a, float *b, uint32_t n, const float *noop,
   return hipGetLastError();
 }
 
+namespace {
+
+// Work units per group for a grouped amax pass: `work[g]` units of group g,
+// `per` of them per workgroup. The atomic form takes per = 1. The workspace
+// form doubles `per` until every group's workgroup count, padded to a
+// multiple of kPartialsGrain, fits kMaxPartials in total.
+uint32_t plan_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, GroupTable &t) {
+  uint32_t per = 1;
+  for (;;) {
+    uint64_t total = 0;
+    t.unit_start[0] = 0;
+    for (uint32_t g = 0; g < ngroups; ++g) {
+      uint64_t n = (work[g] + per - 1) / per;
+      if (to_partials) n = (n + kPartialsGrain - 1) / kPartialsGrain * kPartialsGrain;
+      total += n;
+      t.unit_start[g + 1] = static_cast<uint32_t>(total < 0xFFFFFFFFull ? total : 0xFFFFFFFFull);
+    }
+    if (!to_partials || total <= kMaxPartials) return per;
+    per *= 2;
+  }
+}
+
+}  // namespace
+
 hipError_t launch_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start, uint32_t ngroups,
-                               float *a, float *b, const float *noop, hipStream_t s) {
+                               float *a, float *b, uint32_t *partials, uint32_t *part_start, const float *noop,
+                               hipStream_t s) {
   GroupTable t{};
   t.ngroups = ngroups;
   const uint32_t vec_per_row = cols * (dtype == kBF16 ? 2 : 4) / 16;
   const uint64_t chunk = kMaxThreads * kMaxVecPerThread;
+  uint64_t work[kMaxGroups];
   for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
-  for (uint32_t g = 0; g < ngroups; ++g) {
-    const uint64_t nvec = static_cast<uint64_t>(row_start[g + 1] - row_start[g]) * vec_per_row;
-    t.unit_start[g + 1] = t.unit_start[g] + static_cast<uint32_t>((nvec + chunk - 1) / chunk);
-  }
-  if (t.unit_start[ngroups] == 0) return hipSuccess;
+  for (uint32_t g = 0; g < ngroups; ++g)
+    work[g] = (static_cast<uint64_t>(row_start[g + 1] - row_start[g]) * vec_per_row + chunk - 1) / chunk;
+  const uint32_t passes = plan_groups(work, ngroups, partials != nullptr, t);
+  if (part_start)
+    for (uint32_t g = 0; g <= ngroups; ++g) part_start[g] = t.unit_start[g];
+  const uint32_t grid = t.unit_start[ngroups] > 0 ? t.unit_start[ngroups] : (partials ? 1u : 0u);
+  if (grid == 0) return hipSuccess;
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_amax_grouped<kBF16>, dim3(t.unit_start[ngroups]), dim3(kMaxThreads), 0, s,
-                       static_cast<const uint4 *>(x), vec_per_row, t, a, b, noop);
+    hipLaunchKernelGGL(k_amax_grouped<kBF16>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x),
+                       vec_per_row, t, passes, a, b, partials, noop);
   else
-    hipLaunchKernelGGL(k_amax_grouped<kFP32>, dim3(t.unit_start[ngroups]), dim3(kMaxThreads), 0, s,
-                       static_cast<const uint4 *>(x), vec_per_row, t, a, b, noop);
+    hipLaunchKernelGGL(k_amax_grouped<kFP32>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x),
+                       vec_per_row, t, passes, a, b, partials, noop);
   return hipGetLastError();
 }
 
 hipError_t launch_rht_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start,
                                    uint32_t ngroups, uint32_t mask, float *row_amax, float *col_amax,
-                                   const float *noop, hipStream_t s) {
+                                   uint32_t *partials, uint32_t *part_start, const float *noop, hipStream_t s) {
   GroupTable t{};
   t.ngroups = ngroups;
   const uint32_t gx = (cols + kAmaxThreads * 4 - 1) / (kAmaxThreads * 4);
+  uint64_t work[kMaxGroups];
   for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
-  for (uint32_t g = 0; g < ngroups; ++g) t.unit_start[g + 1] = t.unit_start[g] + gx * ((row_start[g + 1] - row_start[g]) / 16);
-  if (t.unit_start[ngroups] == 0) return hipSuccess;
+  for (uint32_t g = 0; g < ngroups; ++g) work[g] = static_cast<uint64_t>(gx) * ((row_start[g + 1] - row_start[g]) / 16);
+  const uint32_t per_wg = plan_groups(work, ngroups, partials != nullptr, t);
+  if (part_start)
+    for (uint32_t g = 0; g <= ngroups; ++g) part_start[g] = t.unit_start[g];
+  const uint32_t grid = t.unit_start[ngroups] > 0 ? t.unit_start[ngroups] : (partials ? 1u : 0u);
+  if (grid == 0) return hipSuccess;
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_rht_amax_grouped<kBF16>, dim3(t.unit_start[ngroups]), dim3(kAmaxThreads), 0, s, x, cols, gx,
-                       t, mask, row_amax, col_amax, noop);
+    hipLaunchKernelGGL(k_rht_amax_grouped<kBF16>, dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t, per_wg, mask,
+                       row_amax, col_amax, partials, noop);
   else
-    hipLaunchKernelGGL(k_rht_amax_grouped<kFP32>, dim3(t.unit_start[ngroups]), dim3(kAmaxThreads), 0, s, x, cols, gx,
-                       t, mask, row_amax, col_amax, noop);
+    hipLaunchKernelGGL(k_rht_amax_grouped<kFP32>, dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t, per_wg, mask,
+                       row_amax, col_amax, partials, noop);
   return hipGetLastError();
 }
 

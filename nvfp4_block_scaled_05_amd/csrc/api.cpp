@@ -255,6 +255,8 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", cfg.scale_layout);
   const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
+  if (cfg.workspace != nullptr && !aligned(cfg.workspace, 16))
+    return fail(NVFP4_ERR_ALIGN, "the workspace is not 16-byte aligned");
   if (cfg.rht && cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "the RHT is defined for 1x16 blocks only");
   if (cfg.rht && row && col && row->amax == col->amax)
     return fail(NVFP4_ERR_UNSUPPORTED, "the RHT quantize needs distinct row-wise and column-wise amax buffers");
@@ -273,24 +275,35 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   const bool sr = cfg.stochastic != 0;
   float *ra = row ? row->amax : nullptr;
   float *ca = col ? col->amax : nullptr;
+  // With a workspace each group's amax workgroups leave their maxima in a
+  // range of it (part_start) that the group's cast tiles reduce; without
+  // one, the slots are zeroed and reduced by atomic max.
+  uint32_t *partials = nullptr;
+  uint32_t part_start[nvfp4::kMaxGroups + 1];
   if (cfg.compute_amax) {
     float *a = ra ? ra : ca;
     float *b = (ca == a) ? nullptr : ca;
-    if ((st = hip_status(nvfp4::launch_zero_amax_n(a, b, G, cfg.noop, s), "zero amax launch")) != NVFP4_OK) return st;
+    if (cfg.workspace != nullptr && !empty) partials = static_cast<uint32_t *>(cfg.workspace);
+    else if ((st = hip_status(nvfp4::launch_zero_amax_n(a, b, G, cfg.noop, s), "zero amax launch")) != NVFP4_OK)
+      return st;
     if (!empty) {
+      uint32_t *ps = partials ? part_start : nullptr;
       if (cfg.rht)
-        st = hip_status(nvfp4::launch_rht_amax_grouped(x, dtype, C, row_start, G, cfg.rht_sign_mask, ra, ca, cfg.noop, s),
+        st = hip_status(nvfp4::launch_rht_amax_grouped(x, dtype, C, row_start, G, cfg.rht_sign_mask, ra, ca, partials,
+                                                       ps, cfg.noop, s),
                         "RHT amax launch");
       else
-        st = hip_status(nvfp4::launch_amax_grouped(x, dtype, C, row_start, G, a, b, cfg.noop, s), "amax launch");
+        st = hip_status(nvfp4::launch_amax_grouped(x, dtype, C, row_start, G, a, b, partials, ps, cfg.noop, s),
+                        "amax launch");
       if (st != NVFP4_OK) return st;
     }
   }
   if (empty) return NVFP4_OK;
   nvfp4::CastArgs a{x, static_cast<uint32_t>(rows), C, row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
-                    cfg.rht_sign_mask, cfg.noop, nullptr, 0};
-  return hip_status(nvfp4::launch_cast_grouped(a, row_start, G, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s),
+                    cfg.rht_sign_mask, cfg.noop, partials, 0};
+  return hip_status(nvfp4::launch_cast_grouped(a, row_start, partials ? part_start : nullptr, G, dtype,
+                                               cfg.block_2d != 0, cfg.rht != 0, sr, s),
                     "grouped quantize launch");
 }
 

@@ -82,13 +82,14 @@ __device__ __forceinline__ void workgroup_max(uint32_t (&m)[N], uint32_t *lds) {
 }
 
 // The amax pair of a cast workgroup: from the workspace (reduced here, and
-// stored to the amax buffers by workgroup (0, 0)) or read from the buffers.
+// stored to the amax buffers by the workgroup of tile (0, 0), `writer`) or
+// read from the buffers.
 // TWO_ARRAYS: the column-wise amax has its own array (the RHT pair); else
 // both orientations take the one tensor amax.
 template <bool TWO_ARRAYS>
 __device__ __forceinline__ void amax_pair(const CastArgs &p, const u32x4 (&pr)[kPartialVecs],
-                                          const u32x4 (&pc)[kPartialVecs], uint32_t *lds, float &amax_row,
-                                          float &amax_col) {
+                                          const u32x4 (&pc)[kPartialVecs], uint32_t *lds, bool writer,
+                                          float &amax_row, float &amax_col) {
   if (p.partials != nullptr) {
     uint32_t m[TWO_ARRAYS ? 2 : 1];
     m[0] = partials_max(pr);
@@ -96,7 +97,7 @@ __device__ __forceinline__ void amax_pair(const CastArgs &p, const u32x4 (&pr)[k
     workgroup_max(m, lds);
     amax_row = __uint_as_float(m[0]);
     amax_col = __uint_as_float(m[TWO_ARRAYS ? 1 : 0]);
-    if ((blockIdx.x | blockIdx.y | threadIdx.x) == 0) {
+    if (writer && threadIdx.x == 0) {
       if (p.row_amax) *p.row_amax = amax_row;
       if (p.col_amax) *p.col_amax = amax_col;
     }
@@ -268,7 +269,7 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
   }
 
   float amax_row, amax_col;
-  amax_pair<false>(p, part, part, lds_red, amax_row, amax_col);
+  amax_pair<false>(p, part, part, lds_red, (tx | ty) == 0, amax_row, amax_col);
   const float S_row = do_row ? global_encode_scale(amax_row) : 1.0f;
   const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
   if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
@@ -560,7 +561,7 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
   };
 
   float amax_row, amax_col;
-  amax_pair<true>(p, part_row, part_col, lds_red, amax_row, amax_col);
+  amax_pair<true>(p, part_row, part_col, lds_red, (tx | ty) == 0, amax_row, amax_col);
   const float S_row = do_row ? global_encode_scale(amax_row) : 1.0f;
   const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
   if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
@@ -756,7 +757,10 @@ __device__ __forceinline__ CastArgs group_args(const CastArgs &p, const GroupTab
   }
   if (p.row_amax != nullptr) q.row_amax = p.row_amax + g;
   if (p.col_amax != nullptr) q.col_amax = p.col_amax + g;
-  q.partials = nullptr;
+  if (p.partials != nullptr) {  // the group's own maxima (a multiple of four, 16-byte aligned)
+    q.partials = p.partials + t.part_start[g];
+    q.npartials = t.part_start[g + 1] - t.part_start[g];
+  }
   return q;
 }
 
@@ -823,12 +827,15 @@ hipError_t launch_grouped_dt(const CastArgs &a, const GroupTable &t, bool block_
 
 }  // namespace
 
-hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
-                               bool block_2d, bool rht, bool sr, hipStream_t s) {
+hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, const uint32_t *part_start,
+                               uint32_t ngroups, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s) {
   GroupTable t{};
   t.ngroups = ngroups;
   const uint32_t tiles_x = (a.cols + kRT - 1) / kRT;
-  for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
+  for (uint32_t g = 0; g <= ngroups; ++g) {
+    t.row_start[g] = row_start[g];
+    t.part_start[g] = part_start ? part_start[g] : 0;
+  }
   t.unit_start[0] = 0;
   for (uint32_t g = 0; g < ngroups; ++g)
     t.unit_start[g + 1] = t.unit_start[g] + (row_start[g + 1] - row_start[g] + kRT - 1) / kRT * tiles_x;

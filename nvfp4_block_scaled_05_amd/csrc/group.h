@@ -14,6 +14,7 @@ struct GroupTable {
   uint32_t ngroups;
   uint32_t row_start[kMaxGroups + 1];   // first input row of group g; [ngroups] = total rows
   uint32_t unit_start[kMaxGroups + 1];  // first work unit (tile, chunk) of group g; [ngroups] = total units
+  uint32_t part_start[kMaxGroups + 1];  // first workspace maximum of group g (multiples of 4)
 };
 
 // The group that owns work unit `unit` (< unit_start[ngroups]): the g with

@@ -64,16 +64,21 @@ hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bo
 // Grouped forms. row_start: host array of ngroups + 1 prefix sums of the
 // groups' row counts (validated by the caller). `a` describes the whole
 // input and the base pointers of the concatenated outputs; amax buffers hold
-// one float per group. No workspace: the amaxes are zeroed and reduced with
-// atomics.
+// one float per group.
+// Amax with partials == NULL: atomic max into the zeroed slots. Otherwise
+// per-workgroup maxima in the workspace, group g's at part_start[g] ..
+// part_start[g + 1] - 1 (filled in here, host array of ngroups + 1), and the
+// slots of empty groups set to +0; the cast then takes a->partials and
+// part_start.
 hipError_t launch_zero_amax_n(float *a, float *b, uint32_t n, const float *noop, hipStream_t s);
 hipError_t launch_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start, uint32_t ngroups,
-                               float *a, float *b, const float *noop, hipStream_t s);
+                               float *a, float *b, uint32_t *partials, uint32_t *part_start, const float *noop,
+                               hipStream_t s);
 hipError_t launch_rht_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start,
                                    uint32_t ngroups, uint32_t mask, float *row_amax, float *col_amax,
-                                   const float *noop, hipStream_t s);
-hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
-                               bool block_2d, bool rht, bool sr, hipStream_t s);
+                                   uint32_t *partials, uint32_t *part_start, const float *noop, hipStream_t s);
+hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, const uint32_t *part_start,
+                               uint32_t ngroups, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *data, const uint8_t *scales, const float *amax, uint32_t rows,

@@ -16,9 +16,10 @@ from gpu_helpers import DEV, codes, e2m1_step_distance, host, to_device
 pytestmark = pytest.mark.gpu
 
 
-def run_grouped(x, groups, rowwise=True, columnwise=True, **kw):
+def run_grouped(x, groups, rowwise=True, columnwise=True, ws=False, **kw):
+    workspace = nv.empty_workspace(DEV).fill_(0xA5) if ws else None  # stale contents must not matter
     row, col = nv.quantize_grouped(to_device(x), groups, rowwise=rowwise, columnwise=columnwise,
-                                   cfg=nv.make_config(**kw))
+                                   cfg=nv.make_config(workspace=workspace, **kw))
     torch.cuda.synchronize()
     out = {}
     for side, o in (("row", row), ("col", col)):
@@ -49,11 +50,12 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["atomic", "workspace"])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_grouped_matches_oracle(case):
+def test_grouped_matches_oracle(case, ws):
     make, groups, kw = CASES[case]
     x = make()
-    got = run_grouped(x, groups, **kw)
+    got = run_grouped(x, groups, ws=ws, **kw)
     ref = O.quantize_grouped(x, groups, **kw)
     for k in ("row_data", "row_scales", "col_data", "col_scales", "amax_row", "amax_col"):
         assert np.array_equal(got[k].ravel(), ref[k].ravel()), k
@@ -82,13 +84,14 @@ def test_grouped_swizzled():
     assert np.array_equal(got["amax_row"], ref["amax_row"]) and np.array_equal(got["amax_col"], ref["amax_col"])
 
 
+@pytest.mark.parametrize("ws", [False, True], ids=["atomic", "workspace"])
 @pytest.mark.parametrize("stochastic", [False, True])
-def test_grouped_rht(stochastic):
+def test_grouped_rht(stochastic, ws):
     x, _, _ = W.c5(rows=320, cols=512)
     mask = W.rht_sign_mask(58)
     groups = [64, 0, 128, 128]
     kw = dict(rht=True, rht_sign_mask=mask, stochastic=stochastic, sr_seed=9)
-    got = run_grouped(x, groups, **kw)
+    got = run_grouped(x, groups, ws=ws, **kw)
     ref = O.quantize_grouped(x, groups, rht=True, sign_mask=mask, stochastic=stochastic, sr_seed=9)
     assert np.array_equal(got["row_data"].ravel(), ref["row_data"])
     assert np.array_equal(got["row_scales"].ravel(), ref["row_scales"])
@@ -109,7 +112,8 @@ def test_grouped_equals_one_call_per_group():
     g = torch.Generator(device=DEV).manual_seed(60)
     x = (torch.randn((R, C), generator=g, device=DEV) * 3).to(torch.bfloat16)
     cfg = nv.make_config(swizzled=True, stochastic=True, sr_seed=4)
-    row, col = nv.quantize_grouped(x, groups, cfg=cfg)
+    row, col = nv.quantize_grouped(x, groups, cfg=nv.make_config(swizzled=True, stochastic=True, sr_seed=4,
+                                                                 workspace=nv.empty_workspace(DEV)))
     s = 0
     for i, m in enumerate(groups):
         if m:
@@ -121,6 +125,45 @@ def test_grouped_equals_one_call_per_group():
             assert row.amax[i] == r1.amax[0] and col.amax[i] == c1.amax[0]
         else:
             assert row.amax[i] == 0 and col.amax[i] == 0
+        s += m
+
+
+@pytest.mark.parametrize("rht", [False, True], ids=["plain", "rht"])
+def test_grouped_workspace_many_groups(rht):
+    # 256 groups with more amax work than the workspace has slots, so that
+    # each amax workgroup takes several units; every amax slot starts stale
+    rng = np.random.default_rng(62 + rht)
+    groups = [int(m) for m in rng.integers(0, 17, 256) * 16]
+    groups[3] = 0
+    R, C = sum(groups), 2048
+    g = torch.Generator(device=DEV).manual_seed(63)
+    x = (torch.randn((R, C), generator=g, device=DEV) * 2).to(torch.bfloat16)
+    x[7, 5] = 300.0  # an outlier inside group 0
+    kw = dict(rht=rht, rht_sign_mask=W.rht_sign_mask(64) if rht else 0, stochastic=True, sr_seed=5)
+
+    def outputs():
+        o = [nv.Orientation(torch.empty(R * C // 2, dtype=torch.uint8, device=DEV),
+                            torch.empty(R * C // 16, dtype=torch.uint8, device=DEV),
+                            torch.full((256,), 7.0, dtype=torch.float32, device=DEV)) for _ in range(2)]
+        return o[0], o[1]
+
+    row, col = outputs()
+    nv.nvfp4_quantize_grouped(x, groups, row, col, nv.make_config(workspace=nv.empty_workspace(DEV), **kw))
+    ref_row, ref_col = outputs()
+    nv.nvfp4_quantize_grouped(x, groups, ref_row, ref_col, nv.make_config(**kw))  # zero + atomics
+    torch.cuda.synchronize()
+    for a, b in zip((row, col), (ref_row, ref_col)):
+        assert torch.equal(a.amax, b.amax) and torch.equal(a.data, b.data) and torch.equal(a.scales, b.scales)
+    empty = torch.tensor([m == 0 for m in groups], device=DEV)
+    assert torch.all(row.amax[empty] == 0) and torch.all(col.amax[empty] == 0)
+    s = 0
+    ws = nv.empty_workspace(DEV)
+    for i, m in enumerate(groups[:24]):  # spot check against single-tensor calls
+        if m:
+            r1, c1 = nv.quantize(x[s:s + m], cfg=nv.make_config(workspace=ws, **kw))
+            assert row.amax[i] == r1.amax[0] and col.amax[i] == c1.amax[0], i
+            assert torch.equal(row.data[s * C // 2:(s + m) * C // 2], r1.data.reshape(-1))
+            assert torch.equal(col.data[s * C // 2:(s + m) * C // 2], c1.data.reshape(-1))
         s += m
 
 
