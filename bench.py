@@ -90,7 +90,7 @@ def _kernel_rows(db_path):
     return out
 
 
-def summarize_trace(db_path):
+def summarize_trace(db_path, workload="c2"):
     import statistics as st
 
     rows = _kernel_rows(db_path)
@@ -102,24 +102,33 @@ def summarize_trace(db_path):
     print("|---|---:|---:|---:|---:|---:|")
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         print(f"| {k} | {len(v)} | {st.mean(v):.0f} | {st.median(v):.0f} | {min(v)} | {max(v)} |")
-    # one call with a workspace = k_amax k_cast_rt; in the roofline pass the
-    # library records timing events between the two, which leaves a gap
+    # one call with a workspace = amax pass then cast, with no zeroing pass
+    # right before; in c2's roofline pass the library records timing events
+    # between the two, which leaves a gap. The grouped workload also runs the
+    # no-workspace form and single-tensor calls: only its grouped pairs count.
+    call_bytes = B_ALG_CALL if workload == "c2" else OTHER_WORKLOADS[workload]["bytes"]
+    grouped = workload == "grouped"
     spans, plain, evented = [], [], []
     for i in range(len(rows) - 1):
         a, b = rows[i], rows[i + 1]
-        if a[0].startswith("k_amax") and b[0].startswith("k_cast"):
-            if b[1] - a[2] < 1000:
-                plain.append(b[2] - b[1])
-                spans.append(b[2] - a[1])
-            else:
-                evented.append(b[2] - b[1])
+        if not (a[0].startswith(("k_amax", "k_rht_amax")) and b[0].startswith("k_cast")):
+            continue
+        if grouped != ("grouped" in a[0] and "grouped" in b[0]):
+            continue
+        if i > 0 and rows[i - 1][0].startswith("k_zero") and a[1] - rows[i - 1][2] < 1000:
+            continue
+        if b[1] - a[2] < 1000:
+            plain.append(b[2] - b[1])
+            spans.append(b[2] - a[1])
+        else:
+            evented.append(b[2] - b[1])
     for name, v in (("k_cast in calls without timing events", plain), ("k_cast in calls with timing events", evented)):
         if v:
             print(f"\n{name}: {len(v)} launches, average {st.mean(v):.0f} ns, median {st.median(v):.0f} ns")
     if spans:
         med = st.median(spans)
-        print(f"\nper-call span (calls without timing events), first kernel start to last kernel end: {len(spans)} calls, "
-              f"median {med / 1e3:.2f} us -> {B_ALG_CALL / med:.1f} GB/s algorithmic")
+        print(f"\nper-call span (calls with a workspace, without timing events), first kernel start to last kernel "
+              f"end: {len(spans)} calls, median {med / 1e3:.2f} us -> {call_bytes / med:.1f} GB/s algorithmic")
 
 
 def summarize_pmc(db_paths):
@@ -412,7 +421,7 @@ def main():
                    help="write the calibrated HBM traffic of the cast kernel to profiles/")
     args = p.parse_args()
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace)
+        return summarize_trace(args.summarize_trace, args.workload)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
     if args.record_traffic:

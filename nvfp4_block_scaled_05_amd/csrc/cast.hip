@@ -128,6 +128,10 @@ __device__ __forceinline__ uint32_t encode8(const float *v, float e, uint32_t ke
 }
 
 // Four scales (c .. c+3 of scale row r, c % 4 == 0) packed in `word`.
+// Compact scales take ordinary (cached) stores: a tile owns only 8 bytes of
+// each scale row, and streamed 4-byte pieces reach HBM as partial writes
+// (in a measurement they doubled the cast time); in L2 the pieces of
+// neighbouring tiles merge into whole lines first.
 __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uint32_t c, uint32_t scale_cols,
                                                   bool swizzled, uint32_t word) {
   if (swizzled) {
@@ -136,7 +140,7 @@ __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uin
   }
   const uint64_t off = static_cast<uint64_t>(r) * scale_cols + c;
   if ((scale_cols & 3u) == 0 && c + 4 <= scale_cols) {
-    __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(base + off));
+    *reinterpret_cast<uint32_t *>(base + off) = word;
   } else {
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i)
@@ -729,14 +733,29 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
   }
 }
 
+// Tile order. Workgroups go to the 8 XCDs round-robin (workgroup i to XCD
+// i % 8). With compact scales a tile owns 8 bytes of each scale row, and the
+// pieces of horizontally adjacent tiles share lines, so each XCD takes a
+// contiguous run of the row-major tile order (i -> its position within
+// the run of XCD i % 8): neighbours then run together on one XCD and L2
+// merges their pieces. With swizzled scales each tile writes whole blocks,
+// and the launch order measured faster.
+__device__ __forceinline__ uint32_t tile_index(const CastArgs &p, uint32_t i, uint32_t n) {
+  if (p.swizzled) return i;
+  const uint32_t x = i & 7u, q = n >> 3, r = n & 7u;
+  return x * q + min(x, r) + (i >> 3);
+}
+
 template <int DT, bool B2D, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
-  cast_rt_tile<DT, B2D, SR>(p, blockIdx.x, blockIdx.y);
+  const uint32_t t = tile_index(p, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  cast_rt_tile<DT, B2D, SR>(p, t % gridDim.x, t / gridDim.x);
 }
 
 template <int DT, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
-  cast_rht_tile<DT, SR>(p, blockIdx.x, blockIdx.y);
+  const uint32_t t = tile_index(p, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  cast_rht_tile<DT, SR>(p, t % gridDim.x, t / gridDim.x);
 }
 
 // The arguments of group g's own tensor: its rows of the input, its blocks
@@ -765,19 +784,22 @@ __device__ __forceinline__ CastArgs group_args(const CastArgs &p, const GroupTab
 }
 
 // One workgroup per 128 x 128 tile of some group; the tiles of group g are
-// unit_start[g] .. unit_start[g + 1] - 1, row-major over that group.
+// unit_start[g] .. unit_start[g + 1] - 1 (in tile_index order), row-major
+// over that group.
 template <int DT, bool B2D, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rt_grouped(CastArgs p, GroupTable t) {
-  const uint32_t g = group_of(t, blockIdx.x);
-  const uint32_t local = blockIdx.x - t.unit_start[g];
+  const uint32_t u = tile_index(p, blockIdx.x, gridDim.x);
+  const uint32_t g = group_of(t, u);
+  const uint32_t local = u - t.unit_start[g];
   const uint32_t tiles_x = (p.cols + kRT - 1) / kRT;
   cast_rt_tile<DT, B2D, SR>(group_args<DT>(p, t, g), local % tiles_x, local / tiles_x);
 }
 
 template <int DT, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rht_grouped(CastArgs p, GroupTable t) {
-  const uint32_t g = group_of(t, blockIdx.x);
-  const uint32_t local = blockIdx.x - t.unit_start[g];
+  const uint32_t u = tile_index(p, blockIdx.x, gridDim.x);
+  const uint32_t g = group_of(t, u);
+  const uint32_t local = u - t.unit_start[g];
   const uint32_t tiles_x = (p.cols + kRT - 1) / kRT;
   cast_rht_tile<DT, SR>(group_args<DT>(p, t, g), local % tiles_x, local / tiles_x);
 }
