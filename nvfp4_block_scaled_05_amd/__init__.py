@@ -227,9 +227,10 @@ def nvfp4_quantize_grouped(x: torch.Tensor, group_rows, row: Optional[Orientatio
 
 
 def quantize_grouped(x: torch.Tensor, group_rows, *, rowwise=True, columnwise=True,
-                     cfg: Optional[nvfp4_config_t] = None, stream=None):
+                     cfg: Optional[nvfp4_config_t] = None, stream=None, use_workspace: bool = True):
     """Allocate the concatenated per-group outputs and run nvfp4_quantize_grouped.
-    Returns (row, col) with flat data and scales and amax [G]."""
+    Returns (row, col) with flat data and scales and amax [G]. A workspace
+    is allocated for the call as in quantize()."""
     rows, cols = _shape2d(x)
     G = len(group_rows)
     dev = x.device
@@ -241,7 +242,16 @@ def quantize_grouped(x: torch.Tensor, group_rows, *, rowwise=True, columnwise=Tr
 
     row = orient() if rowwise else None
     col = orient() if columnwise else None
+    cfg = cfg if cfg is not None else make_config()
+    ws = None
+    if use_workspace and not cfg.workspace and cfg.compute_amax:
+        ws = empty_workspace(dev)
+        cfg = nvfp4_config_t.from_buffer_copy(cfg)
+        cfg.workspace = ws.data_ptr()
+        if stream is not None:
+            ws.record_stream(stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream)))
     nvfp4_quantize_grouped(x, group_rows, row, col, cfg, stream)
+    del ws
     return row, col
 
 

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 def run_grouped(x, groups, rowwise=True, columnwise=True, ws=False, **kw):
     workspace = nv.empty_workspace(DEV).fill_(0xA5) if ws else None  # stale contents must not matter
     row, col = nv.quantize_grouped(to_device(x), groups, rowwise=rowwise, columnwise=columnwise,
-                                   cfg=nv.make_config(workspace=workspace, **kw))
+                                   cfg=nv.make_config(workspace=workspace, **kw), use_workspace=False)
     torch.cuda.synchronize()
     out = {}
     for side, o in (("row", row), ("col", col)):
