@@ -69,6 +69,8 @@ def _load():
         "oracle_sr_word": (U32, [U32, I, U32]),
         "oracle_rht16": (None, [P, U32, P]),
         "oracle_rht_colwise": (None, [P, I, I64, I64, U32, P]),
+        "oracle_rht_colwise_ex": (None, [P, I, I64, I64, U32, I, P]),
+        "oracle_round_bf16": (F, [F]),
         "oracle_compute_amax": (None, [P, I, I64, I64, I, U32, P, P]),
         "oracle_quantize": (I, [P, I, I64, I64, I, I, I, U32, I, U32, P, P, P, P, P, P]),
         "oracle_swizzle_offset": (I64, [I64, I64, I64]),
@@ -171,18 +173,27 @@ def swizzle_offset(r: int, c: int, scale_cols: int) -> int:
 
 # ---- whole-tensor steps -------------------------------------------------
 
-def rht_colwise(x, sign_mask: int) -> np.ndarray:
-    """Column-wise RHT image t[cols][rows] of x[rows][cols] (rows % 16 == 0)."""
+def round_bf16(v) -> np.ndarray:
+    """Each binary32 value rounded to BF16 (nearest, ties to even), as binary32."""
+    v = np.asarray(v, np.float32)
+    f = _load().oracle_round_bf16
+    return np.array([f(float(a)) for a in v.ravel()], np.float32).reshape(v.shape)
+
+
+def rht_colwise(x, sign_mask: int, bf16: bool = False) -> np.ndarray:
+    """Column-wise RHT image t[cols][rows] of x[rows][cols] (rows % 16 == 0);
+    bf16 rounds every transformed value to BF16."""
     x, dt = _input(x)
     rows, cols = x.shape
     t = np.empty((cols, rows), np.float32)
-    _load().oracle_rht_colwise(_ptr(x), dt, rows, cols, sign_mask, _ptr(t))
+    _load().oracle_rht_colwise_ex(_ptr(x), dt, rows, cols, sign_mask, int(bf16), _ptr(t))
     return t
 
 
 AMAX_PER_TENSOR = 0
 AMAX_PER_ROW = 1
 AMAX_RHT = 2
+AMAX_RHT_BF16 = 3
 
 
 def compute_amax(x, mode: int = AMAX_PER_TENSOR, sign_mask: int = 0):
@@ -200,8 +211,10 @@ def compute_amax(x, mode: int = AMAX_PER_TENSOR, sign_mask: int = 0):
 
 
 def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=False, rht=False,
-             sign_mask=0, stochastic=False, sr_seed=0, amax_row=None, amax_col=None):
-    """Quantize with the given amaxes (computed here when None).
+             sign_mask=0, stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False):
+    """Quantize with the given amaxes (computed here when None). rht_bf16
+    (with rht): the transformed values are rounded to BF16 before the
+    column-wise amax, block scales and codes.
 
     Returns a dict with ``row_data``, ``row_scales``, ``col_data``,
     ``col_scales`` (compact; absent directions are None), ``amax_row``,
@@ -210,7 +223,7 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
     x, dt = _input(x)
     rows, cols = x.shape
     if amax_row is None and amax_col is None:
-        mode = AMAX_PER_ROW if row_scaled else (AMAX_RHT if rht else AMAX_PER_TENSOR)
+        mode = AMAX_PER_ROW if row_scaled else ((AMAX_RHT_BF16 if rht_bf16 else AMAX_RHT) if rht else AMAX_PER_TENSOR)
         amax_row, amax_col = compute_amax(x, mode, sign_mask)
     amax_row = None if amax_row is None else np.ascontiguousarray(amax_row, np.float32)
     amax_col = None if amax_col is None else np.ascontiguousarray(amax_col, np.float32)
@@ -219,7 +232,7 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
     cd = np.empty((cols, rows // 2), np.uint8) if columnwise else None
     cs = np.empty((cols, rows // 16), np.uint8) if columnwise else None
     rc = _load().oracle_quantize(
-        _ptr(x), dt, rows, cols, int(block_2d), int(row_scaled), int(rht), sign_mask,
+        _ptr(x), dt, rows, cols, int(block_2d), int(row_scaled), (2 if rht_bf16 else 1) if rht else 0, sign_mask,
         int(stochastic), sr_seed, _ptr(amax_row) if rowwise else None,
         _ptr(amax_col) if columnwise else None, _ptr(rd), _ptr(rs), _ptr(cd), _ptr(cs))
     if rc != 0:
@@ -229,7 +242,7 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
 
 
 def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=False, rht=False, sign_mask=0,
-                     stochastic=False, sr_seed=0, amax_row=None, amax_col=None):
+                     stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False):
     """Grouped quantize. The row-scaled page's changed files keep a grouped
     tensor as one tensor per group with per-group amax offsets; reading: the
     consecutive row slices x[s_g : s_g + m_g] (m_g = group_rows[g]) are each
@@ -260,7 +273,7 @@ def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=F
             given = dict(amax_row=None if amax_row is None else np.asarray(amax_row, np.float32)[g:g + 1],
                          amax_col=None if amax_col is None else np.asarray(amax_col, np.float32)[g:g + 1])
         q = quantize(xs, rowwise=rowwise, columnwise=columnwise, block_2d=block_2d, rht=rht, sign_mask=sign_mask,
-                     stochastic=stochastic, sr_seed=sr_seed, **given)
+                     stochastic=stochastic, sr_seed=sr_seed, rht_bf16=rht_bf16, **given)
         for k in ("row_data", "row_scales", "col_data", "col_scales"):
             if q[k] is not None:
                 parts[k].append(q[k].reshape(-1))

@@ -231,17 +231,46 @@ void oracle_rht16(const float w_in[16], uint32_t sign_mask, float t_out[16]) {
   }
 }
 
-/* Column-wise RHT image of x: t[j][i] for column j, row i (rows % 16 == 0). */
-void oracle_rht_colwise(const void *x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask,
-                        float *t /* [cols][rows] */) {
+/* ------------------------------------------------------------------ */
+/* BF16 rounding of a binary32 value (round to nearest, ties to the     */
+/* even significand), for the variant whose transformed values are      */
+/* BF16. [P1] review thread: the post-RHT amaxes printed there (5.03125, */
+/* 16.875) are BF16 values, which suggests BF16 transformed values; the */
+/* page does not say so, so this is an opt-in reading. A BF16 value is  */
+/* a binary32 value whose low 16 bits are zero; x lies between the two  */
+/* such values lo (x's bits with the low half cleared) and the next one */
+/* away from zero, and the low half of x's bits says which is nearer.   */
+/* ------------------------------------------------------------------ */
+float oracle_round_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  uint32_t lo = u & 0xFFFF0000u, rest = u & 0xFFFFu;
+  uint32_t r;
+  if (rest < 0x8000u) r = lo;
+  else if (rest > 0x8000u) r = lo + 0x10000u;
+  else r = (lo & 0x10000u) ? lo + 0x10000u : lo; /* tie: the even significand */
+  float y;
+  memcpy(&y, &r, 4);
+  return y;
+}
+
+/* Column-wise RHT image of x: t[j][i] for column j, row i (rows % 16 == 0);
+ * bf16 != 0 rounds every transformed value to BF16. */
+void oracle_rht_colwise_ex(const void *x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask, int bf16,
+                           float *t /* [cols][rows] */) {
   float w[16], out[16];
   for (int64_t j = 0; j < cols; ++j) {
     for (int64_t g = 0; g < rows / 16; ++g) {
       for (int k = 0; k < 16; ++k) w[k] = oracle_load(x, dtype, (g * 16 + k) * cols + j);
       oracle_rht16(w, sign_mask, out);
-      for (int r = 0; r < 16; ++r) t[j * rows + g * 16 + r] = out[r];
+      for (int r = 0; r < 16; ++r) t[j * rows + g * 16 + r] = bf16 ? oracle_round_bf16(out[r]) : out[r];
     }
   }
+}
+
+void oracle_rht_colwise(const void *x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask,
+                        float *t /* [cols][rows] */) {
+  oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, 0, t);
 }
 
 /* ------------------------------------------------------------------ */
@@ -251,7 +280,8 @@ void oracle_rht_colwise(const void *x, int dtype, int64_t rows, int64_t cols, ui
 /* recipe keeps one amax per row. [P1] GPU-work table / review table:   */
 /* the RHT path reduces max|x| for the row-wise side and max|RHT(x)|    */
 /* for the column-wise side in one op.                                 */
-/* mode 0: per tensor, mode 1: per row, mode 2: RHT pair.              */
+/* mode 0: per tensor, mode 1: per row, mode 2: RHT pair, mode 3: RHT  */
+/* pair with BF16 transformed values.                                  */
 /* amax_row / amax_col may be NULL (that buffer is not requested).     */
 /* ------------------------------------------------------------------ */
 void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, int mode,
@@ -271,11 +301,11 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
     if (amax_col) amax_col[0] = a;
     return;
   }
-  /* mode 2: RHT pair */
+  /* modes 2 and 3: RHT pair */
   if (amax_row) amax_row[0] = a;
   if (amax_col) {
     float *t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
-    oracle_rht_colwise(x, dtype, rows, cols, sign_mask, t);
+    oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, mode == 3, t);
     float b = 0.0f;
     for (int64_t n = 0; n < rows * cols; ++n) b = fmaxf(b, fabsf(t[n]));
     free(t);
@@ -319,7 +349,8 @@ static void encode_row(const float *vals, const float *e_per_block, int64_t n, i
 /* amax_col[0]; each direction's global scale comes from its own amax. */
 /* block_2d: one scale per 16x16 block shared by both directions        */
 /* ([P2] Changes: the 2D path); otherwise 1x16 blocks along each        */
-/* direction's rows. rht: column-wise values are the RHT image.        */
+/* direction's rows. rht: column-wise values are the RHT image (rht == */
+/* 2: the image rounded to BF16).                                      */
 /* Returns 0, or -1 on an unsupported combination.                     */
 /* ------------------------------------------------------------------ */
 int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int block_2d, int row_scaled,
@@ -379,7 +410,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
     float *t = NULL;
     if (rht) {
       t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
-      oracle_rht_colwise(x, dtype, rows, cols, sign_mask, t);
+      oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, rht == 2, t);
     }
     float S = oracle_global_encode_scale(amax_col[0]);
     float *v = (float *)malloc(sizeof(float) * (size_t)rows);

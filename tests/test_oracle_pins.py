@@ -573,3 +573,77 @@ def test_grouped_empty_group_has_zero_amax_and_no_bytes():
     g = O.quantize_grouped(x, [16, 0, 16])
     assert g["amax_row"][1] == 0 and g["amax_col"][1] == 0
     assert g["row_data"].size == 32 * 16 and g["col_data"].size == 2 * 32 * 8
+
+
+# ----------------------------------------------------------------------------
+# BF16 transformed values (opt-in RHT variant): the rounding itself against
+# torch's BF16 cast, closed forms, and the order of rounding and maximum.
+# ----------------------------------------------------------------------------
+
+def _torch_bf16(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def test_round_bf16_matches_torch_cast():
+    rng = np.random.default_rng(71)
+    bits = rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]  # finite values only
+    # every tie and its neighbours, in both parities of the kept bit
+    hi = rng.integers(0, 2 ** 16, 4096, dtype=np.uint64).astype(np.uint32) << 16
+    hi = hi[(hi & 0x7F800000) != 0x7F800000]
+    ties = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi, hi | 0xFFFF])
+    ties = ties[((ties & 0x7F800000) != 0x7F800000)]
+    v = np.concatenate([bits, ties, np.uint32([0, 0x80000000, 1, 0x8000, 0x18000, 0x7F7F7FFF])]).view(np.float32)
+    got = O.round_bf16(v)
+    ref = _torch_bf16(v)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_rht_bf16_closed_form():
+    # one group [1, 2^-9, 0 x 14], mask 0: t_r = (1 +- 2^-9) / 4, the sign
+    # from (-1)^popcount(r & 1). 1 + 2^-9 is below the BF16 midpoint above 1,
+    # and 1 - 2^-9 is the tie between 1 - 2^-8 and 1 (even: 1), so every
+    # BF16 value is exactly 1/4.
+    x = np.zeros((16, 16), np.float32)
+    x[0, 3], x[1, 3] = 1.0, 2.0 ** -9
+    t32 = O.rht_colwise(x, 0)[3]
+    t16 = O.rht_colwise(x, 0, bf16=True)[3]
+    r = np.arange(16)
+    expect32 = np.float32(0.25) * np.where(r % 2 == 0, np.float32(1 + 2 ** -9), np.float32(1 - 2 ** -9))
+    assert np.array_equal(t32, expect32)
+    assert np.all(t16 == np.float32(0.25))
+    a32 = O.compute_amax(x, O.AMAX_RHT, 0)[1][0]
+    a16 = O.compute_amax(x, O.AMAX_RHT_BF16, 0)[1][0]
+    assert a32 == np.float32(0.25 * (1 + 2 ** -9)) and a16 == np.float32(0.25)
+    # the BF16 column: 16 equal values at the amax -> s = 448 (0x7E), e = 24, v' = 6
+    q = O.quantize(x, rht=True, rht_bf16=True, rowwise=False)
+    assert q["amax_col"][0] == 0.25
+    assert q["col_scales"][3, 0] == 0x7E and np.all(q["col_data"][3] == 0x77)
+    assert np.all(q["col_data"][:3] == 0) and np.all(q["col_scales"][:3] == 0)
+
+
+def test_rht_bf16_amax_is_the_rounded_fp32_amax():
+    # rounding is monotonic, so max|bf16(t)| == bf16(max|t|), and it is a BF16 value
+    for seed in range(5):
+        x = W.randn_bf16(64, 96, 72 + seed)
+        mask = W.rht_sign_mask(seed)
+        a32 = O.compute_amax(x, O.AMAX_RHT, mask)[1][0]
+        a16 = O.compute_amax(x, O.AMAX_RHT_BF16, mask)[1][0]
+        assert a16 == _torch_bf16([a32])[0]
+        assert np.float32(a16).view(np.uint32) & 0xFFFF == 0
+
+
+def test_rht_bf16_columnwise_is_plain_rowwise_of_the_rounded_transform():
+    x = W.randn_bf16(64, 48, 76)
+    mask = 0x2D3B
+    q = O.quantize(x, rht=True, rht_bf16=True, sign_mask=mask, stochastic=True, sr_seed=4)
+    t = _torch_bf16(O.rht_colwise(x, mask))
+    qt = O.quantize(t, columnwise=False, stochastic=True, sr_seed=4)
+    # the SR byte indices of the column side use direction 1, so compare RNE codes
+    qr = O.quantize(x, rht=True, rht_bf16=True, sign_mask=mask)
+    qtr = O.quantize(t, columnwise=False)
+    assert q["amax_col"][0] == np.abs(t).max()
+    assert np.array_equal(qr["col_data"], qtr["row_data"])
+    assert np.array_equal(q["col_scales"], qt["row_scales"])
+    # the row-wise side does not see the rounding
+    assert np.array_equal(q["row_data"], O.quantize(x, rht=True, sign_mask=mask, stochastic=True, sr_seed=4)["row_data"])
