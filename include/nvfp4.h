@@ -118,7 +118,15 @@ typedef struct {
    * work per quantize call and review thread). The row-wise orientation and
    * row->amax stay plain. Needs block_2d == 0. */
   uint32_t rht;
-  uint32_t rht_sign_mask;
+  uint32_t rht_sign_mask; /* bits 0..15; higher bits are ignored */
+  /* With rht == 1 only (else NVFP4_ERR_UNSUPPORTED). 1: every transformed
+   * value t is rounded to BF16 (nearest, ties to even) before col->amax,
+   * the column-wise block scales and the codes are taken from it. The
+   * post-RHT amaxes printed in the review thread of "Write both NVFP4 amax
+   * buffers" are BF16 values, which suggests BF16 transformed values; the
+   * page does not say so, so this is an option and 0 (binary32 t) the
+   * default. */
+  uint32_t rht_bf16;
   /* nvfp4_quantize only. 1: zero the amax buffers and reduce them inside the
    * call. 0: use the amax buffers as they are (for instance after a MAX
    * all-reduce across devices). */
@@ -256,6 +264,8 @@ const char *nvfp4_last_error(void);
 /*
  * Test hook: the column-wise RHT image t [cols][rows] FP32 (device) of x,
  * computed by the same device code as the quantize kernels. R % 16 == 0.
+ * sign_mask bits 0..15 are the signs; bit 16 set rounds every value to
+ * BF16 as rht_bf16 does; higher bits are ignored.
  */
 nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t dtype, int64_t rows,
                                        int64_t cols, uint32_t sign_mask, float *t, void *stream);

@@ -65,6 +65,7 @@ class nvfp4_config_t(ctypes.Structure):
         ("row_scaled", ctypes.c_uint32),
         ("rht", ctypes.c_uint32),
         ("rht_sign_mask", ctypes.c_uint32),
+        ("rht_bf16", ctypes.c_uint32),
         ("compute_amax", ctypes.c_uint32),
         ("noop", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
@@ -157,13 +158,14 @@ def _shape2d(x: torch.Tensor):
 
 def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, stochastic=False, sr_seed=0,
                 row_scaled=False, rht=False, rht_sign_mask=0, compute_amax=True,
-                noop: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> nvfp4_config_t:
+                noop: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                rht_bf16=False) -> nvfp4_config_t:
     """The config struct. It holds references to the noop and workspace
     tensors (a copy made with from_buffer_copy does not: keep them alive
     while such a copy is used)."""
     cfg = nvfp4_config_t(int(block_2d), NVFP4_SCALES_GEMM_SWIZZLED if swizzled else NVFP4_SCALES_COMPACT,
                          int(scale_fmt), int(stochastic), int(sr_seed) & 0xFFFFFFFF, int(row_scaled), int(rht),
-                         int(rht_sign_mask) & 0xFFFFFFFF, int(compute_amax),
+                         int(rht_sign_mask) & 0xFFFFFFFF, int(rht_bf16), int(compute_amax),
                          None if noop is None else noop.data_ptr(),
                          None if workspace is None else workspace.data_ptr())
     cfg._tensors = (noop, workspace)

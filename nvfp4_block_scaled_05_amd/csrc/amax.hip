@@ -205,10 +205,15 @@ __device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32
 // Workgroup maxima of an RHT amax pass: (max|x|, max|t|) as float bits, in
 // every thread.
 template <int DT>
-__device__ __forceinline__ void rht_amax_finish(ushort2_t mx16, uint32_t mx32, float ms, uint32_t *lds, uint32_t &mx,
-                                                uint32_t &mt) {
+__device__ __forceinline__ void rht_amax_finish(ushort2_t mx16, uint32_t mx32, float ms, uint32_t mask, uint32_t *lds,
+                                                uint32_t &mx, uint32_t &mt) {
   mx = DT == kBF16 ? (static_cast<uint32_t>(max(mx16.x, mx16.y)) << 16) : mx32;
-  mt = __float_as_uint(ms * 0.25f);
+  float t = ms * 0.25f;
+  if (mask & kRhtBf16) {  // rounding is monotonic: max|bf16(t)| == bf16(max|t|)
+    float unused = 0.0f;
+    bf16_round_pair(t, unused);
+  }
+  mt = __float_as_uint(t);
   mx = block_umax<kAmaxThreads>(mx, lds);
   __syncthreads();
   mt = block_umax<kAmaxThreads>(mt, lds);
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restric
     if (c < cols) rht_amax_unit<DT>(x, cols, by, c, mask, mx16, mx32, ms);
   }
   uint32_t mx, mt;
-  rht_amax_finish<DT>(mx16, mx32, ms, lds, mx, mt);
+  rht_amax_finish<DT>(mx16, mx32, ms, mask, lds, mx, mt);
   if (threadIdx.x == 0) {
     if (partials != nullptr) {
       partials[blockIdx.x] = mx;
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *_
     if (c < cols) rht_amax_unit<DT>(xg, cols, by, c, mask, mx16, mx32, ms);
   }
   uint32_t mx, mt;
-  rht_amax_finish<DT>(mx16, mx32, ms, lds, mx, mt);
+  rht_amax_finish<DT>(mx16, mx32, ms, mask, lds, mx, mt);
   if (threadIdx.x == 0) {
     if (partials != nullptr) {
       partials[blockIdx.x] = mx;
@@ -374,6 +379,7 @@ __global__ __launch_bounds__(kThreads) void k_debug_rht(const void *__restrict__
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
     rht16(v[j], mask);
+    if (mask & kRhtBf16) bf16_round16(v[j]);
     float4 *dst = reinterpret_cast<float4 *>(t + static_cast<uint64_t>(c + j) * rows + r0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[j][4 * q], v[j][4 * q + 1], v[j][4 * q + 2], v[j][4 * q + 3]);

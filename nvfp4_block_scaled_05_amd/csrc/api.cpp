@@ -40,6 +40,11 @@ nvfp4_config_t config_or_default(const nvfp4_config_t *cfg) {
   return c;
 }
 
+// The RHT kernels' mask word: the 16 sign bits, and the BF16 option above them.
+uint32_t rht_word(const nvfp4_config_t &c) {
+  return (c.rht_sign_mask & 0xFFFFu) | (c.rht_bf16 ? nvfp4::kRhtBf16 : 0u);
+}
+
 nvfp4_status_t hip_status(hipError_t e, const char *what) {
   if (e == hipSuccess) return NVFP4_OK;
   return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -106,6 +111,7 @@ extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype,
   if ((row_amax && !aligned(row_amax, 4)) || (col_amax && !aligned(col_amax, 4)))
     return fail(NVFP4_ERR_ALIGN, "amax pointers must be 4-byte aligned");
   if (cfg.row_scaled && cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled amax cannot be combined with the RHT");
+  if (cfg.rht_bf16 && !cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "rht_bf16 needs rht");
   if (cfg.row_scaled) {
     if (col_amax != nullptr)
       return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled amax is row-wise only: col_amax must be NULL");
@@ -126,7 +132,7 @@ extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype,
   if (st != NVFP4_OK || rows * cols == 0) return st;
   if (cfg.rht)
     return hip_status(nvfp4::launch_rht_amax(x, dtype, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols),
-                                             cfg.rht_sign_mask, row_amax, col_amax, nullptr, nullptr, cfg.noop, s),
+                                             rht_word(cfg), row_amax, col_amax, nullptr, nullptr, cfg.noop, s),
                       "RHT amax launch");
   return hip_status(
       nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, nullptr, nullptr, cfg.noop, s),
@@ -161,6 +167,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
     if (swz) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 keeps compact scales");
   }
   if (cfg.rht && cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "the RHT is defined for 1x16 blocks only");
+  if (cfg.rht_bf16 && !cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "rht_bf16 needs rht");
   if (cfg.rht && row && col && row->amax == col->amax)
     return fail(NVFP4_ERR_UNSUPPORTED, "the RHT quantize needs distinct row-wise and column-wise amax buffers");
   if ((col || cfg.block_2d) && rows % 16 != 0)
@@ -198,7 +205,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
       partials = static_cast<uint32_t *>(cfg.workspace);
       if (cfg.rht)
         st = hip_status(
-            nvfp4::launch_rht_amax(x, dtype, R, C, cfg.rht_sign_mask, ra, ca, partials, &npartials, cfg.noop, s),
+            nvfp4::launch_rht_amax(x, dtype, R, C, rht_word(cfg), ra, ca, partials, &npartials, cfg.noop, s),
             "RHT amax launch");
       else
         st = hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, partials, &npartials,
@@ -211,7 +218,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
       if (rows * cols > 0) {
         if (cfg.rht)
           st = hip_status(
-              nvfp4::launch_rht_amax(x, dtype, R, C, cfg.rht_sign_mask, ra, ca, nullptr, nullptr, cfg.noop, s),
+              nvfp4::launch_rht_amax(x, dtype, R, C, rht_word(cfg), ra, ca, nullptr, nullptr, cfg.noop, s),
               "RHT amax launch");
         else
           st = hip_status(nvfp4::launch_amax(x, dtype, static_cast<uint64_t>(rows * cols), a, b, nullptr, nullptr,
@@ -223,7 +230,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   }
   nvfp4::CastArgs a{x,  R,        C,    row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
-                    cfg.rht_sign_mask, cfg.noop, partials, npartials};
+                    rht_word(cfg), cfg.noop, partials, npartials};
   if ((st = record(0)) != NVFP4_OK) return st;
   st = hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
   return st != NVFP4_OK ? st : record(1);
@@ -258,6 +265,7 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   if (cfg.workspace != nullptr && !aligned(cfg.workspace, 16))
     return fail(NVFP4_ERR_ALIGN, "the workspace is not 16-byte aligned");
   if (cfg.rht && cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "the RHT is defined for 1x16 blocks only");
+  if (cfg.rht_bf16 && !cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "rht_bf16 needs rht");
   if (cfg.rht && row && col && row->amax == col->amax)
     return fail(NVFP4_ERR_UNSUPPORTED, "the RHT quantize needs distinct row-wise and column-wise amax buffers");
   const int64_t mult = swz ? 128 : ((col || cfg.block_2d || cfg.rht) ? 16 : 1);
@@ -289,7 +297,7 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
     if (!empty) {
       uint32_t *ps = partials ? part_start : nullptr;
       if (cfg.rht)
-        st = hip_status(nvfp4::launch_rht_amax_grouped(x, dtype, C, row_start, G, cfg.rht_sign_mask, ra, ca, partials,
+        st = hip_status(nvfp4::launch_rht_amax_grouped(x, dtype, C, row_start, G, rht_word(cfg), ra, ca, partials,
                                                        ps, cfg.noop, s),
                         "RHT amax launch");
       else
@@ -301,7 +309,7 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   if (empty) return NVFP4_OK;
   nvfp4::CastArgs a{x, static_cast<uint32_t>(rows), C, row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
-                    cfg.rht_sign_mask, cfg.noop, partials, 0};
+                    rht_word(cfg), cfg.noop, partials, 0};
   return hip_status(nvfp4::launch_cast_grouped(a, row_start, partials ? part_start : nullptr, G, dtype,
                                                cfg.block_2d != 0, cfg.rht != 0, sr, s),
                     "grouped quantize launch");
@@ -338,7 +346,8 @@ extern "C" nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t d
   if (rows * cols > 0 && t == nullptr) return fail(NVFP4_ERR_NULL, "output pointer is NULL");
   if (t != nullptr && !aligned(t, 16)) return fail(NVFP4_ERR_ALIGN, "output must be 16-byte aligned");
   return hip_status(nvfp4::launch_debug_rht(x, dtype, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols),
-                                            sign_mask, t, static_cast<hipStream_t>(stream)),
+                                            sign_mask & (0xFFFFu | nvfp4::kRhtBf16), t,
+                                            static_cast<hipStream_t>(stream)),
                     "RHT launch");
 }
 

@@ -654,6 +654,9 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = value(k, c);
       fwht16(v);
+      // BF16 transformed values: bf16(4t) == 4 bf16(t), so the unnormalized
+      // values are rounded and the folding of 1/4 below stays as it is
+      if (p.sign_mask & kRhtBf16) bf16_round16(v);
       float ms = 0.0f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) ms = fmaxf(ms, fabsf(v[k]));

@@ -207,6 +207,18 @@ __device__ __forceinline__ void fwht16(float (&v)[16]) {
   }
 }
 
+// Two binary32 values rounded to BF16 (nearest, ties to even) and widened
+// back; the pair becomes one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ void bf16_round_pair(float &a, float &b) {
+  a = static_cast<float>(static_cast<__bf16>(a));
+  b = static_cast<float>(static_cast<__bf16>(b));
+}
+
+__device__ __forceinline__ void bf16_round16(float (&v)[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) bf16_round_pair(v[k], v[k + 1]);
+}
+
 __device__ __forceinline__ void rht16(float (&v)[16], uint32_t sign_mask) {
 #pragma unroll
   for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(__float_as_uint(v[k]) ^ (((sign_mask >> k) & 1u) << 31));

@@ -16,6 +16,10 @@ enum InType : int { kBF16 = 0, kFP32 = 1 };
 // non-negative float's bit pattern. The amax pass writes a multiple of
 // kPartialsGrain entries (workgroups without work write +0).
 constexpr uint32_t kMaxPartials = 2048;
+
+// Bit of the internal sign-mask word (above the 16 sign bits) that asks the
+// RHT kernels to round the transformed values to BF16.
+constexpr uint32_t kRhtBf16 = 1u << 16;
 constexpr uint32_t kPartialsGrain = 4;
 static_assert(2 * kMaxPartials * 4 == 16384, "workspace size is part of the ABI");
 

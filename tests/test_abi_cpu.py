@@ -130,22 +130,38 @@ def test_debug_rht_rejections():
 
 
 def test_config_struct_matches_header_layout(tmp_path):
-    # compile the header with the host C compiler and compare sizes and offsets
+    # compile the header with the host C compiler and compare sizes and every field's offset
+    C = nv.nvfp4_config_t
+    names = [f[0] for f in C._fields_]
+    offs = ", ".join(f"offsetof(nvfp4_config_t, {n})" for n in names)
     src = tmp_path / "layout.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "nvfp4.h"\n'
-                   'int main(void) { printf("%zu %zu %zu %zu %zu %u %zu\\n", sizeof(nvfp4_config_t), '
-                   'offsetof(nvfp4_config_t, compute_amax), offsetof(nvfp4_config_t, noop), '
-                   'offsetof(nvfp4_config_t, workspace), sizeof(nvfp4_out_t), NVFP4_WORKSPACE_BYTES, '
-                   'offsetof(nvfp4_config_t, cast_events)); return 0; }\n')
+                   'int main(void) { printf("%zu %zu %u' + " %zu" * len(names) + '\\n", sizeof(nvfp4_config_t), '
+                   'sizeof(nvfp4_out_t), NVFP4_WORKSPACE_BYTES, ' + offs + '); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
-    size, compute_amax, noop, workspace, out_size, ws_bytes, events = \
-        map(int, subprocess.check_output([str(exe)]).split())
-    C = nv.nvfp4_config_t
-    assert (ctypes.sizeof(C), C.compute_amax.offset, C.noop.offset, C.workspace.offset, C.cast_events.offset) == \
-        (size, compute_amax, noop, workspace, events)
+    size, out_size, ws_bytes, *field_offsets = map(int, subprocess.check_output([str(exe)]).split())
+    assert ctypes.sizeof(C) == size
+    assert [getattr(C, n).offset for n in names] == field_offsets
     assert ctypes.sizeof(nv.nvfp4_out_t) == out_size
     assert nv.nvfp4_workspace_bytes() == ws_bytes
+
+
+def test_rht_bf16_needs_rht():
+    # every call below fails validation, so nothing is launched
+    lib = nv.load()
+    cfg = nv.make_config(rht_bf16=True)
+    assert lib.nvfp4_compute_amax(X, 0, 64, 64, A, A2, ctypes.byref(cfg), None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert "rht_bf16" in nv.nvfp4_last_error()
+    r = nv.nvfp4_out_t(D, S, A)
+    c = nv.nvfp4_out_t(D + 0x10000, S + 0x10000, A2)
+    assert lib.nvfp4_quantize(X, 0, 64, 64, ctypes.byref(r), ctypes.byref(c), ctypes.byref(cfg), None) == \
+        nv.NVFP4_ERR_UNSUPPORTED
+    assert "rht_bf16" in nv.nvfp4_last_error()
+    groups = (ctypes.c_int64 * 2)(32, 32)
+    assert lib.nvfp4_quantize_grouped(X, 0, 2, groups, 64, ctypes.byref(r), ctypes.byref(c), ctypes.byref(cfg),
+                                      None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert "rht_bf16" in nv.nvfp4_last_error()
 
 
 def test_workspace_must_be_aligned():
