@@ -193,6 +193,8 @@ OTHER_WORKLOADS = {
     "c5": dict(desc="8192x8192 BF16 N(0,1) + 0.1% at +-200 (seed 4); 1x16; row plain + col 16-point RHT; "
                     "stochastic rounding (seed 5); compact",
                bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
+    "c5_bf16": dict(desc="as c5, with the transformed values rounded to BF16 (rht_bf16)",
+                    bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
     "grouped": dict(desc="grouped quantize, MoE-like: 64 groups of 0..512 rows (multiples of 128, seed 6; 16768 rows) "
                          "x 4096 BF16 N(0,1) (seed 7); 1x16; row+col; compact; RNE; per-group amax",
                     bytes=2 * 2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64),
@@ -224,7 +226,8 @@ def run_other(name, steps, warmup):
         x, cfg, rowwise, columnwise = workloads.c4(), nv.make_config(row_scaled=True), True, False
     else:
         x, mask, seed = workloads.c5()
-        cfg, rowwise, columnwise = nv.make_config(rht=True, rht_sign_mask=mask, stochastic=True, sr_seed=seed), True, True
+        cfg = nv.make_config(rht=True, rht_sign_mask=mask, stochastic=True, sr_seed=seed, rht_bf16=name == "c5_bf16")
+        rowwise, columnwise = True, True
     workspace = nv.empty_workspace(dev)
     if not cfg.row_scaled:
         cfg.workspace = workspace.data_ptr()

@@ -306,15 +306,15 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *_
   }
 }
 
-// Grouped per-tensor amax. Workgroup b of group g takes chunk
-// b - unit_start[g] of that group: `passes` x kMaxThreads x kMaxVecPerThread
-// consecutive vectors of its rows (chunks past the group's end are empty).
-// Result to partials[b], or with partials == NULL into the group's slots by
-// atomic max.
+// Grouped per-tensor amax. The n_g = unit_start[g + 1] - unit_start[g]
+// workgroups of group g read its rows as k_amax reads a tensor: grid-wide
+// (here group-wide) contiguous spans, kMaxVecPerThread loads per thread in
+// flight. Result to partials[b], or with partials == NULL into the group's
+// slots by atomic max.
 template <int DT>
 __global__ __launch_bounds__(kMaxThreads) void k_amax_grouped(const uint4 *__restrict__ x, uint32_t vec_per_row,
-                                                              GroupTable t, uint32_t passes, float *a, float *b,
-                                                              uint32_t *partials, const float *noop) {
+                                                              GroupTable t, float *a, float *b, uint32_t *partials,
+                                                              const float *noop) {
   constexpr int VPT = kMaxVecPerThread;
   __shared__ uint32_t lds[kMaxThreads / 64];
   if (noop_set(noop)) return;
@@ -322,18 +322,16 @@ __global__ __launch_bounds__(kMaxThreads) void k_amax_grouped(const uint4 *__res
   const uint32_t g = group_of(t, blockIdx.x);
   const uint64_t first = static_cast<uint64_t>(t.row_start[g]) * vec_per_row;
   const uint64_t nvec = static_cast<uint64_t>(t.row_start[g + 1] - t.row_start[g]) * vec_per_row;
-  const uint64_t chunk0 = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * passes;
+  const uint64_t span = static_cast<uint64_t>(t.unit_start[g + 1] - t.unit_start[g]) * kMaxThreads;
   uint32_t m32 = 0;
   ushort2_t m16 = {0, 0};
-  for (uint32_t pass = 0; pass < passes; ++pass) {
-    const uint64_t start = (chunk0 + pass) * (kMaxThreads * VPT);  // uniform
-    if (start >= nvec) break;
+  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * kMaxThreads + threadIdx.x; i0 < nvec;
+       i0 += span * VPT) {
     // all loads in flight at once: past the group's end the index is
     // clamped to its last vector, which cannot change a maximum
     uint4 v[VPT];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k)
-      v[k] = x[first + min(start + threadIdx.x + static_cast<uint64_t>(k) * kMaxThreads, nvec - 1)];
+    for (int k = 0; k < VPT; ++k) v[k] = x[first + min(i0 + k * span, nvec - 1)];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
@@ -469,6 +467,29 @@ uint32_t plan_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, G
   }
 }
 
+// Workgroups per group for the per-tensor amax: shares of about kMaxGrid
+// in proportion to each group's chunks (at least one, at most its chunk
+// count), so that the whole pass runs as one k_amax over the tensor would.
+// The workspace form pads each share to a multiple of kPartialsGrain and
+// lowers the target so that the sum stays within kMaxPartials:
+// sum <= target + ngroups (rounding up) + 3 ngroups (padding).
+void share_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, GroupTable &t) {
+  uint64_t total = 0;
+  for (uint32_t g = 0; g < ngroups; ++g) total += work[g];
+  uint64_t target = kMaxGrid;
+  if (to_partials && target + 4ull * ngroups > kMaxPartials) target = kMaxPartials - 4ull * ngroups;
+  t.unit_start[0] = 0;
+  for (uint32_t g = 0; g < ngroups; ++g) {
+    uint64_t n = 0;
+    if (work[g] > 0) {
+      n = (target * work[g] + total - 1) / total;
+      n = n < 1 ? 1 : (n > work[g] ? work[g] : n);
+      if (to_partials) n = (n + kPartialsGrain - 1) / kPartialsGrain * kPartialsGrain;
+    }
+    t.unit_start[g + 1] = t.unit_start[g] + static_cast<uint32_t>(n);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_amax_grouped(const void *x, int dtype, uint32_t cols, const uint32_t *row_start, uint32_t ngroups,
@@ -482,17 +503,17 @@ hipError_t launch_amax_grouped(const void *x, int dtype, uint32_t cols, const ui
   for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
   for (uint32_t g = 0; g < ngroups; ++g)
     work[g] = (static_cast<uint64_t>(row_start[g + 1] - row_start[g]) * vec_per_row + chunk - 1) / chunk;
-  const uint32_t passes = plan_groups(work, ngroups, partials != nullptr, t);
+  share_groups(work, ngroups, partials != nullptr, t);
   if (part_start)
     for (uint32_t g = 0; g <= ngroups; ++g) part_start[g] = t.unit_start[g];
   const uint32_t grid = t.unit_start[ngroups] > 0 ? t.unit_start[ngroups] : (partials ? 1u : 0u);
   if (grid == 0) return hipSuccess;
   if (dtype == kBF16)
     hipLaunchKernelGGL(k_amax_grouped<kBF16>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x),
-                       vec_per_row, t, passes, a, b, partials, noop);
+                       vec_per_row, t, a, b, partials, noop);
   else
     hipLaunchKernelGGL(k_amax_grouped<kFP32>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x),
-                       vec_per_row, t, passes, a, b, partials, noop);
+                       vec_per_row, t, a, b, partials, noop);
   return hipGetLastError();
 }
 
