@@ -186,3 +186,50 @@ def test_grouped_noop_and_given_amax():
     torch.cuda.synchronize()
     ref = O.quantize_grouped(x, groups, amax_row=before[2] * 2, amax_col=before[5] * 2)
     assert np.array_equal(host(row.data), ref["row_data"]) and np.array_equal(host(col.scales), ref["col_scales"])
+
+
+@pytest.mark.parametrize("mode", ["ws", "atomic", "rht_bf16_ws"])
+def test_grouped_graph_capture_replays_match_eager(mode):
+    # The grouped call queues kernels only (the group table travels in the
+    # kernel arguments), so a captured graph reproduces the eager result on
+    # every replay, with other work and synchronizations between replays.
+    x = W.randn_bf16(320, 256, 65)
+    xd = to_device(x)
+    groups = [64, 0, 128, 16, 112]
+    ws = nv.empty_workspace(DEV)
+    kw = dict(rht=True, rht_sign_mask=0x6C1D, rht_bf16=True, stochastic=True, sr_seed=2) if mode.startswith("rht") \
+        else dict(stochastic=True, sr_seed=2)
+    cfg = nv.make_config(workspace=None if mode == "atomic" else ws, **kw)
+    row, col = nv.quantize_grouped(xd, groups, cfg=cfg, use_workspace=False)
+    torch.cuda.synchronize()
+    outs = [row.data, row.scales, row.amax, col.data, col.scales, col.amax]
+    eager = [host(t).copy() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        nv.nvfp4_quantize_grouped(xd, groups, row, col, cfg, s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs + [ws]:
+            t.view(torch.uint8).fill_(0x5A + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, t in zip(eager, outs):
+            assert np.array_equal(e, host(t)), (mode, rep)
+
+
+def test_grouped_noop_with_workspace_writes_nothing():
+    x = W.randn_bf16(96, 128, 66)
+    xd = to_device(x)
+    groups = [32, 0, 64]
+    ws = nv.empty_workspace(DEV)
+    row, col = nv.quantize_grouped(xd, groups, cfg=nv.make_config(workspace=ws), use_workspace=False)
+    torch.cuda.synchronize()
+    before = [host(t).copy() for t in (row.data, row.scales, row.amax, col.data, col.scales, col.amax)]
+    noop = torch.ones(1, dtype=torch.float32, device=DEV)
+    nv.nvfp4_quantize_grouped(xd * 5, groups, row, col, nv.make_config(noop=noop, workspace=ws))
+    torch.cuda.synchronize()
+    for b, t in zip(before, (row.data, row.scales, row.amax, col.data, col.scales, col.amax)):
+        assert np.array_equal(b, host(t))
