@@ -65,7 +65,7 @@ __global__ void k_zero_amax(float *a, float *b, const float *noop) {
 // The workgroup's maximum then goes either to partials[blockIdx.x] (plain
 // store; the cast kernel finishes the reduction) or, with partials == NULL,
 // into a and b by atomic max.
-constexpr int kAmaxThreads = 512;     // RHT amax pair
+constexpr int kAmaxThreads = 256;     // RHT amax pair (512 and 1024 measured slower, 64 and 128 the same)
 constexpr int kMaxThreads = 256;      // per-tensor amax
 constexpr int kMaxVecPerThread = 8;   // loads in flight per thread and pass
 constexpr uint32_t kMaxGrid = 1280;   // 5 workgroups per CU on 256 CUs

@@ -451,7 +451,7 @@ def test_workspace_when_workgroups_loop(case):
         xd = torch.randn((rows, cols), generator=g, device=DEV, dtype=torch.float32)
         kw = {}
     else:
-        rows, cols = 33024, 4096  # 2064 units of 16 rows x 4096 columns
+        rows, cols = 33024, 4096  # 2064 groups of 16 rows, several RHT amax units each
         xd = torch.randn((rows, cols), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
         kw = dict(rht=True, rht_sign_mask=0x5A3C)
     xd[-1, -3] = -1000.0
