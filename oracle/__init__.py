@@ -73,6 +73,14 @@ def _load():
         "oracle_round_bf16": (F, [F]),
         "oracle_compute_amax": (None, [P, I, I64, I64, I, U32, P, P]),
         "oracle_quantize": (I, [P, I, I64, I64, I, I, I, U32, I, U32, P, P, P, P, P, P]),
+        "oracle_quantize_fmt": (I, [P, I, I64, I64, I, I, I, U32, I, U32, P, P, P, P, P, P, I]),
+        "oracle_ue5m3_value": (ctypes.c_double, [U8]),
+        "oracle_ue5m3_rne_satfinite": (U8, [F]),
+        "oracle_ue5m3_array": (None, [P, I64, P]),
+        "oracle_global_encode_scale_fmt": (F, [F, I]),
+        "oracle_block_scale_fmt": (U8, [F, F, I]),
+        "oracle_block_encode_multiplier_fmt": (F, [U8, F, I]),
+        "oracle_dequantize_fmt": (None, [P, P, P, I, I64, I64, P, I]),
         "oracle_swizzle_offset": (I64, [I64, I64, I64]),
         "oracle_swizzle_scales": (I, [P, I64, I64, P]),
         "oracle_swizzle_scales_padded": (None, [P, I64, I64, P]),
@@ -136,16 +144,32 @@ def e4m3_value(code: int) -> float:
     return _load().oracle_e4m3_value(code)
 
 
-def global_encode_scale(amax: float) -> float:
-    return _load().oracle_global_encode_scale(amax)
+def ue5m3(v) -> np.ndarray:
+    """UE5M3 codes (nearest even, saturating to 61440) of non-negative values."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_ue5m3_array(_ptr(v), v.size, _ptr(out))
+    return out
 
 
-def block_scale(block_amax: float, S: float) -> int:
-    return _load().oracle_block_scale(block_amax, S)
+def ue5m3_value(code: int) -> float:
+    return _load().oracle_ue5m3_value(code)
 
 
-def block_encode_multiplier(s: int, S: float) -> float:
-    return _load().oracle_block_encode_multiplier(s, S)
+SCALE_E4M3 = 0
+SCALE_UE5M3 = 1
+
+
+def global_encode_scale(amax: float, scale_fmt: int = SCALE_E4M3) -> float:
+    return _load().oracle_global_encode_scale_fmt(amax, scale_fmt)
+
+
+def block_scale(block_amax: float, S: float, scale_fmt: int = SCALE_E4M3) -> int:
+    return _load().oracle_block_scale_fmt(block_amax, S, scale_fmt)
+
+
+def block_encode_multiplier(s: int, S: float, scale_fmt: int = SCALE_E4M3) -> float:
+    return _load().oracle_block_encode_multiplier_fmt(s, S, scale_fmt)
 
 
 def fmix32(h) -> np.ndarray:
@@ -211,7 +235,8 @@ def compute_amax(x, mode: int = AMAX_PER_TENSOR, sign_mask: int = 0):
 
 
 def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=False, rht=False,
-             sign_mask=0, stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False):
+             sign_mask=0, stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False,
+             scale_fmt=SCALE_E4M3):
     """Quantize with the given amaxes (computed here when None). rht_bf16
     (with rht): the transformed values are rounded to BF16 before the
     column-wise amax, block scales and codes.
@@ -231,10 +256,10 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
     rs = np.empty((rows, cols // 16), np.uint8) if rowwise else None
     cd = np.empty((cols, rows // 2), np.uint8) if columnwise else None
     cs = np.empty((cols, rows // 16), np.uint8) if columnwise else None
-    rc = _load().oracle_quantize(
+    rc = _load().oracle_quantize_fmt(
         _ptr(x), dt, rows, cols, int(block_2d), int(row_scaled), (2 if rht_bf16 else 1) if rht else 0, sign_mask,
         int(stochastic), sr_seed, _ptr(amax_row) if rowwise else None,
-        _ptr(amax_col) if columnwise else None, _ptr(rd), _ptr(rs), _ptr(cd), _ptr(cs))
+        _ptr(amax_col) if columnwise else None, _ptr(rd), _ptr(rs), _ptr(cd), _ptr(cs), int(scale_fmt))
     if rc != 0:
         raise ValueError("unsupported oracle configuration")
     return {"row_data": rd, "row_scales": rs, "col_data": cd, "col_scales": cs,
@@ -242,7 +267,8 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
 
 
 def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=False, rht=False, sign_mask=0,
-                     stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False):
+                     stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False,
+                     scale_fmt=SCALE_E4M3):
     """Grouped quantize. The row-scaled page's changed files keep a grouped
     tensor as one tensor per group with per-group amax offsets; reading: the
     consecutive row slices x[s_g : s_g + m_g] (m_g = group_rows[g]) are each
@@ -273,7 +299,7 @@ def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=F
             given = dict(amax_row=None if amax_row is None else np.asarray(amax_row, np.float32)[g:g + 1],
                          amax_col=None if amax_col is None else np.asarray(amax_col, np.float32)[g:g + 1])
         q = quantize(xs, rowwise=rowwise, columnwise=columnwise, block_2d=block_2d, rht=rht, sign_mask=sign_mask,
-                     stochastic=stochastic, sr_seed=sr_seed, rht_bf16=rht_bf16, **given)
+                     stochastic=stochastic, sr_seed=sr_seed, rht_bf16=rht_bf16, scale_fmt=scale_fmt, **given)
         for k in ("row_data", "row_scales", "col_data", "col_scales"):
             if q[k] is not None:
                 parts[k].append(q[k].reshape(-1))
@@ -312,11 +338,13 @@ def swizzle_scales_padded(compact) -> np.ndarray:
     return out
 
 
-def dequantize(data, scales, amax, rows: int, cols: int, row_scaled: bool = False) -> np.ndarray:
+def dequantize(data, scales, amax, rows: int, cols: int, row_scaled: bool = False,
+               scale_fmt: int = SCALE_E4M3) -> np.ndarray:
     """One direction, its own orientation [rows][cols], compact scales."""
     data = np.ascontiguousarray(data, np.uint8)
     scales = np.ascontiguousarray(scales, np.uint8)
     amax = np.ascontiguousarray(amax, np.float32)
     y = np.empty((rows, cols), np.float32)
-    _load().oracle_dequantize(_ptr(data), _ptr(scales), _ptr(amax), int(row_scaled), rows, cols, _ptr(y))
+    _load().oracle_dequantize_fmt(_ptr(data), _ptr(scales), _ptr(amax), int(row_scaled), rows, cols, _ptr(y),
+                                  int(scale_fmt))
     return y

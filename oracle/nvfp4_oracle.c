@@ -149,36 +149,88 @@ uint8_t oracle_e4m3_rne_satfinite(float sd) {
 }
 
 /* ------------------------------------------------------------------ */
+/* UE5M3 block scales (opt-in; "parity unpinned" against the pages).   */
+/* [P2] Changes and Validation test "E4M3/UE5M3" block scales but do   */
+/* not define UE5M3. Reading: an unsigned float, 5 exponent bits with  */
+/* bias 15 and 3 mantissa bits; exponent 0 holds the subnormals        */
+/* m * 2^-17; exponent 31 (codes 0xF8..0xFF) is reserved, as in the    */
+/* IEEE-style 5-bit-exponent formats, so the largest finite value is   */
+/* 1.875 * 2^15 = 61440 (code 0xF7). Encoding: nearest value, ties to  */
+/* the even code, saturating to 61440.                                 */
+/* ------------------------------------------------------------------ */
+double oracle_ue5m3_value(uint8_t code) {
+  int e = code >> 3;
+  int m = code & 7;
+  return (e == 0) ? ldexp((double)m, -17) : ldexp(1.0 + m / 8.0, e - 15);
+}
+
+static double ue5m3_table[0xF8];
+static int ue5m3_table_ready = 0;
+
+uint8_t oracle_ue5m3_rne_satfinite(float sd) {
+  if (!ue5m3_table_ready) { /* the decoded values of codes 0x00..0xF7, once */
+    for (int k = 0; k < 0xF8; ++k) ue5m3_table[k] = oracle_ue5m3_value((uint8_t)k);
+    ue5m3_table_ready = 1;
+  }
+  double a = (double)sd;
+  for (int k = 0; k < 0xF7; ++k) {
+    double lo = ue5m3_table[k];
+    double hi = ue5m3_table[k + 1];
+    double mid = 0.5 * (lo + hi); /* exact in binary64 */
+    if (a < mid) return (uint8_t)k;
+    if (a == mid) return (uint8_t)((k % 2 == 0) ? k : k + 1);
+  }
+  return 0xF7;
+}
+
+/* Decoded value and nearest-even encoding of a block scale in format fmt
+ * (0: E4M3, 1: UE5M3), and the largest finite value of that format. */
+static double scale_value(uint8_t code, int fmt) {
+  return fmt ? oracle_ue5m3_value(code) : oracle_e4m3_value(code);
+}
+
+static uint8_t scale_encode(float sd, int fmt) {
+  return fmt ? oracle_ue5m3_rne_satfinite(sd) : oracle_e4m3_rne_satfinite(sd);
+}
+
+/* ------------------------------------------------------------------ */
 /* Two-level scaling.                                                  */
 /* [P3] Greptile summary: block-level FP8 scales are computed relative */
 /* to a tensor-level (or row-level) FP32 amax, with zero-guard handling */
 /* in the reference quantizer. The formula is not printed on the pages; */
 /* the reading used: the global encode scale maps amax onto the largest */
-/* product of the two formats, 6 (E2M1) * 448 (E4M3) = 2688.           */
+/* product of the two formats, 6 (E2M1) * 448 (E4M3) = 2688; with      */
+/* UE5M3 block scales 6 * 61440 = 368640.                              */
 /* ------------------------------------------------------------------ */
-float oracle_global_encode_scale(float amax) {
+float oracle_global_encode_scale_fmt(float amax, int fmt) {
   if (amax == 0.0f) return 1.0f; /* zero guard */
-  float s = 2688.0f / amax;
+  float s = (fmt ? 368640.0f : 2688.0f) / amax;
   if (s > FLT_MAX) s = FLT_MAX; /* amax so small that the quotient overflows */
   return s;
 }
 
-/* Block decode scale: sd = (m / 6) * S, stored as E4M3. */
-uint8_t oracle_block_scale(float block_amax, float S) {
+float oracle_global_encode_scale(float amax) { return oracle_global_encode_scale_fmt(amax, 0); }
+
+/* Block decode scale: sd = (m / 6) * S, stored in the scale format. */
+uint8_t oracle_block_scale_fmt(float block_amax, float S, int fmt) {
   float q = block_amax / 6.0f;
   float sd = q * S;
-  return oracle_e4m3_rne_satfinite(sd);
+  return scale_encode(sd, fmt);
 }
+
+uint8_t oracle_block_scale(float block_amax, float S) { return oracle_block_scale_fmt(block_amax, S, 0); }
 
 /* Block encode multiplier: e = S / value(s), or 0 when the stored scale is
  * zero (every value of the block then encodes as a signed zero). */
-float oracle_block_encode_multiplier(uint8_t s, float S) {
+float oracle_block_encode_multiplier_fmt(uint8_t s, float S, int fmt) {
   if (s == 0) return 0.0f;
-  float sf = (float)oracle_e4m3_value(s);
+  float sf = (float)scale_value(s, fmt);
   float e = S / sf;
   if (e > FLT_MAX) e = FLT_MAX;
   return e;
 }
+
+float oracle_block_encode_multiplier(uint8_t s, float S) { return oracle_block_encode_multiplier_fmt(s, S, 0); }
 
 /* ------------------------------------------------------------------ */
 /* Counter-based random bits for stochastic rounding.                  */
@@ -353,10 +405,10 @@ static void encode_row(const float *vals, const float *e_per_block, int64_t n, i
 /* 2: the image rounded to BF16).                                      */
 /* Returns 0, or -1 on an unsupported combination.                     */
 /* ------------------------------------------------------------------ */
-int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int block_2d, int row_scaled,
-                    int rht, uint32_t sign_mask, int stochastic, uint32_t sr_seed, const float *amax_row,
-                    const float *amax_col, uint8_t *row_data, uint8_t *row_scales, uint8_t *col_data,
-                    uint8_t *col_scales) {
+int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, int block_2d, int row_scaled,
+                        int rht, uint32_t sign_mask, int stochastic, uint32_t sr_seed, const float *amax_row,
+                        const float *amax_col, uint8_t *row_data, uint8_t *row_scales, uint8_t *col_data,
+                        uint8_t *col_scales, int scale_fmt) {
   int want_row = row_data != NULL;
   int want_col = col_data != NULL;
   if (cols % 16 != 0) return -1;
@@ -388,7 +440,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
     float *e = (float *)malloc(sizeof(float) * (size_t)(cols / 16));
     for (int64_t i = 0; i < rows; ++i) {
       const float *v = xv + i * cols;
-      float S = oracle_global_encode_scale(row_scaled ? amax_row[i] : amax_row[0]);
+      float S = oracle_global_encode_scale_fmt(row_scaled ? amax_row[i] : amax_row[0], scale_fmt);
       for (int64_t b = 0; b < cols / 16; ++b) {
         float m = 0.0f;
         if (block_2d) {
@@ -396,8 +448,8 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
         } else {
           for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(v[b * 16 + k]));
         }
-        uint8_t s = oracle_block_scale(m, S);
-        e[b] = oracle_block_encode_multiplier(s, S);
+        uint8_t s = oracle_block_scale_fmt(m, S, scale_fmt);
+        e[b] = oracle_block_encode_multiplier_fmt(s, S, scale_fmt);
         row_scales[i * (cols / 16) + b] = s;
       }
       encode_row(v, e, cols, stochastic, sr_seed, 0, i * (cols / 2), row_data + i * (cols / 2));
@@ -412,7 +464,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
       t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
       oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, rht == 2, t);
     }
-    float S = oracle_global_encode_scale(amax_col[0]);
+    float S = oracle_global_encode_scale_fmt(amax_col[0], scale_fmt);
     float *v = (float *)malloc(sizeof(float) * (size_t)rows);
     float *e = (float *)malloc(sizeof(float) * (size_t)(rows / 16));
     for (int64_t j = 0; j < cols; ++j) {
@@ -424,8 +476,8 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
         } else {
           for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(v[b * 16 + k]));
         }
-        uint8_t s = oracle_block_scale(m, S);
-        e[b] = oracle_block_encode_multiplier(s, S);
+        uint8_t s = oracle_block_scale_fmt(m, S, scale_fmt);
+        e[b] = oracle_block_encode_multiplier_fmt(s, S, scale_fmt);
         col_scales[j * (rows / 16) + b] = s;
       }
       encode_row(v, e, rows, stochastic, sr_seed, 1, j * (rows / 2), col_data + j * (rows / 2));
@@ -438,6 +490,14 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
   free(xv);
   free(m2d);
   return 0;
+}
+
+int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int block_2d, int row_scaled,
+                    int rht, uint32_t sign_mask, int stochastic, uint32_t sr_seed, const float *amax_row,
+                    const float *amax_col, uint8_t *row_data, uint8_t *row_scales, uint8_t *col_data,
+                    uint8_t *col_scales) {
+  return oracle_quantize_fmt(x, dtype, rows, cols, block_2d, row_scaled, rht, sign_mask, stochastic, sr_seed,
+                             amax_row, amax_col, row_data, row_scales, col_data, col_scales, 0);
 }
 
 /* ------------------------------------------------------------------ */
@@ -483,18 +543,23 @@ void oracle_swizzle_scales_padded(const uint8_t *compact, int64_t rows, int64_t 
 /* row_scaled ([P3] Changes: dequantization picks the row's amax for    */
 /* row-scaled tensors).                                                */
 /* ------------------------------------------------------------------ */
-void oracle_dequantize(const uint8_t *data, const uint8_t *scales, const float *amax, int row_scaled,
-                       int64_t rows, int64_t cols, float *y) {
+void oracle_dequantize_fmt(const uint8_t *data, const uint8_t *scales, const float *amax, int row_scaled,
+                           int64_t rows, int64_t cols, float *y, int scale_fmt) {
   for (int64_t i = 0; i < rows; ++i) {
-    float S = oracle_global_encode_scale(row_scaled ? amax[i] : amax[0]);
+    float S = oracle_global_encode_scale_fmt(row_scaled ? amax[i] : amax[0], scale_fmt);
     for (int64_t j = 0; j < cols; ++j) {
       uint8_t byte = data[i * (cols / 2) + j / 2];
       uint8_t code = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-      float sf = (float)oracle_e4m3_value(scales[i * (cols / 16) + j / 16]);
+      float sf = (float)scale_value(scales[i * (cols / 16) + j / 16], scale_fmt);
       float p = (float)oracle_e2m1_value(code) * sf;
       y[i * cols + j] = p / S;
     }
   }
+}
+
+void oracle_dequantize(const uint8_t *data, const uint8_t *scales, const float *amax, int row_scaled,
+                       int64_t rows, int64_t cols, float *y) {
+  oracle_dequantize_fmt(data, scales, amax, row_scaled, rows, cols, y, 0);
 }
 
 /* Bit helpers exported for the tests' hand-worked checks. */
@@ -514,6 +579,10 @@ void oracle_e2m1_sr_array(const float *v, const uint16_t *r16, int64_t n, uint8_
 
 void oracle_e4m3_array(const float *v, int64_t n, uint8_t *codes) {
   for (int64_t i = 0; i < n; ++i) codes[i] = oracle_e4m3_rne_satfinite(v[i]);
+}
+
+void oracle_ue5m3_array(const float *v, int64_t n, uint8_t *codes) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = oracle_ue5m3_rne_satfinite(v[i]);
 }
 
 void oracle_fmix32_array(const uint32_t *h, int64_t n, uint32_t *out) {

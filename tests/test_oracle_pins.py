@@ -647,3 +647,88 @@ def test_rht_bf16_columnwise_is_plain_rowwise_of_the_rounded_transform():
     assert np.array_equal(q["col_scales"], qt["row_scales"])
     # the row-wise side does not see the rounding
     assert np.array_equal(q["row_data"], O.quantize(x, rht=True, sign_mask=mask, stochastic=True, sr_seed=4)["row_data"])
+
+
+# ----------------------------------------------------------------------------
+# UE5M3 block scales (opt-in reading; the pages name the format without
+# defining it, so these pin the oracle to the stated definition only).
+# ----------------------------------------------------------------------------
+
+def test_ue5m3_values_are_the_fp16_values_with_three_mantissa_bits():
+    # unsigned, 5 exponent bits (bias 15), 3 mantissa bits: code c is the
+    # binary16 number with bits c << 7 (sign 0, low 7 mantissa bits zero)
+    codes = np.arange(0xF8, dtype=np.uint16)
+    f16 = (codes << 7).view(np.float16).astype(np.float64)
+    got = np.array([O.ue5m3_value(int(c)) for c in codes])
+    assert np.array_equal(got, f16)
+    assert O.ue5m3_value(0xF7) == 61440.0 and O.ue5m3_value(1) == 2.0 ** -17 and O.ue5m3_value(8) == 2.0 ** -14
+
+
+def _nearest_even_code(x: float, values) -> int:
+    """Exact rational nearest-value search over a sorted grid, ties to the even code."""
+    fx = Fraction(x)
+    best, best_d = None, None
+    for k, v in enumerate(values):
+        d = abs(fx - Fraction(v))
+        if best is None or d < best_d or (d == best_d and k % 2 == 0):
+            best, best_d = k, d
+    return best
+
+
+def test_ue5m3_encoding_nearest_even_saturating():
+    values = [O.ue5m3_value(c) for c in range(0xF8)]
+    probes = []
+    for k in range(0xF7):
+        mid = np.float32((values[k] + values[k + 1]) / 2)
+        probes += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(np.inf)), np.float32(values[k])]
+    rng = np.random.default_rng(91)
+    probes += list((2.0 ** rng.uniform(-20, 16, 3000)).astype(np.float32))
+    probes = np.array(probes, np.float32)
+    got = O.ue5m3(probes)
+    want = np.array([_nearest_even_code(float(p), values) for p in probes])
+    assert np.array_equal(got, want)
+    # beyond the largest value, and +inf, saturate to 61440
+    assert np.all(O.ue5m3(np.float32([61440, 63488, 65536, 1e30, np.inf])) == 0xF7)
+    assert O.ue5m3(np.float32([0.0]))[0] == 0
+
+
+def test_ue5m3_hand_worked_block():
+    # 1x32, E4M3's hand-worked blocks with UE5M3 scales: amax 6, S = 368640 / 6 = 61440.
+    # Block 0 = [6, 0 x 15]: sd = 61440 -> 0xF7, e = 1, codes 7, 0, ...
+    # Block 1 = [1, .5, .25, .125, -1, -.5, -.25, -.125, 0 x 8]: sd = fl(fl(1/6) * 61440)
+    # = 10240 = 1.25 * 2^13 -> code (28 << 3) | 2 = 0xE2, e = 6; v' = 6, 3, 1.5, .75
+    # -> codes 7, 5, 3, 2 (0.75 is the tie between 0.5 and 1: even code 2).
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 6.0
+    x[0, 16:24] = [1, .5, .25, .125, -1, -.5, -.25, -.125]
+    q = O.quantize(x, columnwise=False, scale_fmt=O.SCALE_UE5M3)
+    assert O.global_encode_scale(6.0, O.SCALE_UE5M3) == 61440.0
+    assert list(q["row_scales"][0]) == [0xF7, 0xE2]
+    assert bytes(q["row_data"][0]).hex() == "0700000000000000" + "5723dfab00000000"
+    y = O.dequantize(q["row_data"], q["row_scales"], q["amax_row"], 1, 32, scale_fmt=O.SCALE_UE5M3)
+    assert y[0, 16] == 1.0 and y[0, 0] == 6.0  # 6 * 10240 / 61440 and 6 * 61440 / 61440
+
+
+def test_ue5m3_keeps_blocks_that_e4m3_flushes():
+    # a block 2^-20 below the tensor amax: E4M3's sd = 448 * 2^-20 is under
+    # half its smallest subnormal (2^-10), so its codes are all zero; UE5M3's
+    # sd = 61440 * 2^-20 is a normal value and the block keeps its codes
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 1.0
+    x[0, 16:20] = np.float32([2.0 ** -20, 2.0 ** -21, -(2.0 ** -20), 2.0 ** -22])
+    e4 = O.quantize(x, columnwise=False)
+    ue = O.quantize(x, columnwise=False, scale_fmt=O.SCALE_UE5M3)
+    assert e4["row_scales"][0, 1] == 0 and not np.any(e4["row_data"][0, 8:] & 0x77)
+    assert ue["row_scales"][0, 1] != 0
+    assert list(O.dequantize(ue["row_data"], ue["row_scales"], ue["amax_row"], 1, 32,
+                             scale_fmt=O.SCALE_UE5M3)[0, 16:20]) == [2.0 ** -20, 2.0 ** -21, -(2.0 ** -20), 2.0 ** -22]
+
+
+@pytest.mark.parametrize("k", [-9, 5])
+def test_ue5m3_power_of_two_invariance(k):
+    x = W.gaussian_fp32(32, 64, 92, 3.0)
+    a = O.quantize(x, block_2d=True, scale_fmt=O.SCALE_UE5M3)
+    b = O.quantize((x * np.float32(2.0 ** k)).astype(np.float32), block_2d=True, scale_fmt=O.SCALE_UE5M3)
+    for key in ("row_data", "row_scales", "col_data", "col_scales"):
+        assert np.array_equal(a[key], b[key]), key
+    assert b["amax_row"][0] == a["amax_row"][0] * np.float32(2.0 ** k)
