@@ -193,6 +193,8 @@ OTHER_WORKLOADS = {
     "c5": dict(desc="8192x8192 BF16 N(0,1) + 0.1% at +-200 (seed 4); 1x16; row plain + col 16-point RHT; "
                     "stochastic rounding (seed 5); compact",
                bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
+    "c2_ue5m3": dict(desc="as the bench workload (8192x5120 BF16, 16x16, swizzled, RNE), with UE5M3 block scales",
+                     bytes=2 * 2 * 8192 * 5120 + 2 * (8192 * 5120 // 2 + 8192 * 5120 // 16) + 8),
     "c5_bf16": dict(desc="as c5, with the transformed values rounded to BF16 (rht_bf16)",
                     bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
     "grouped": dict(desc="grouped quantize, MoE-like: 64 groups of 0..512 rows (multiples of 128, seed 6; 16768 rows) "
@@ -224,6 +226,9 @@ def run_other(name, steps, warmup):
         x, cfg, rowwise, columnwise = workloads.c3()[0], nv.make_config(), True, True
     elif name == "c4":
         x, cfg, rowwise, columnwise = workloads.c4(), nv.make_config(row_scaled=True), True, False
+    elif name == "c2_ue5m3":
+        x = workloads.c2()
+        cfg, rowwise, columnwise = nv.make_config(block_2d=True, swizzled=True, scale_fmt=nv.NVFP4_SCALE_UE5M3), True, True
     else:
         x, mask, seed = workloads.c5()
         cfg = nv.make_config(rht=True, rht_sign_mask=mask, stochastic=True, sr_seed=seed, rht_bf16=name == "c5_bf16")
@@ -434,7 +439,7 @@ def main():
             sys.exit(2)
         return run_other(args.workload, args.steps, args.warmup)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU: --gpus must be 1"}))
         sys.exit(2)
 
     import numpy as np

@@ -67,8 +67,11 @@ typedef enum {
 
 typedef enum {
   NVFP4_SCALE_E4M3 = 0, /* OCP E4M3 (bias 7, max 448), round to nearest even, saturating */
-  NVFP4_SCALE_UE5M3 = 1 /* named on "Fuse NVFP4 scale swizzling ..." (Changes) but not
-                           defined there: rejected with NVFP4_ERR_UNSUPPORTED */
+  NVFP4_SCALE_UE5M3 = 1 /* named on "Fuse NVFP4 scale swizzling ..." (Changes, Validation)
+                           but not defined there. Reading: unsigned, 5 exponent bits
+                           (bias 15), 3 mantissa bits, subnormals m * 2^-17, exponent 31
+                           reserved, max 61440 (code 0xF7); round to nearest even,
+                           saturating. The global scale numerator becomes 6 * 61440. */
 } nvfp4_scale_fmt_t;
 
 /* One orientation of an NVFP4 tensor. For the row-wise orientation of an
@@ -181,8 +184,9 @@ nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t ro
  * into the requested orientations; row or col may be NULL, not both. The
  * column-wise orientation needs R % 16 == 0.
  *
- * Per orientation: S = 2688 / amax (1 when amax == 0, at most FLT_MAX);
- * per block of 16 (or 16x16): m = max|v|, scale s = E4M3(fl(m / 6) * S),
+ * Per orientation: S = 2688 / amax (368640 / amax with UE5M3 scales; 1
+ * when amax == 0, at most FLT_MAX); per block of 16 (or 16x16): m = max|v|,
+ * scale s = E4M3(fl(m / 6) * S) (or UE5M3),
  * multiplier e = S / s (0 when s == 0, at most FLT_MAX), code =
  * E2M1(fl(v * e)), each step one correctly rounded FP32 operation.
  *
@@ -233,10 +237,11 @@ nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_
  * k % 16 == 0) into y [rows][cols] FP32 (device, 4-byte aligned):
  * y = (value(code) * value(s)) / S, S from q->amax[0], or q->amax[i] for
  * row i when row_scaled ("Implement row-scaled NVFP4 fprop recipe",
- * Changes: the dequantize kernel selects the row's amax).
+ * Changes: the dequantize kernel selects the row's amax). scale_layout and
+ * scale_fmt (nvfp4_scale_fmt_t) are those the tensor was quantized with.
  */
-nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols,
-                                uint32_t scale_layout, uint32_t row_scaled, float *y, void *stream);
+nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols, uint32_t scale_layout,
+                                uint32_t scale_fmt, uint32_t row_scaled, float *y, void *stream);
 
 /*
  * Compact -> GEMM-swizzled scales, for shapes with partial scale tiles

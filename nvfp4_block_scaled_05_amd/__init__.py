@@ -106,7 +106,7 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_quantize.argtypes = [P, I, I64, I64, ctypes.POINTER(nvfp4_out_t), ctypes.POINTER(nvfp4_out_t),
                                    ctypes.POINTER(nvfp4_config_t), P]
     lib.nvfp4_dequantize.restype = I
-    lib.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_out_t), I64, I64, U32, U32, P, P]
+    lib.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_out_t), I64, I64, U32, U32, U32, P, P]
     lib.nvfp4_last_error.restype = ctypes.c_char_p
     lib.nvfp4_last_error.argtypes = []
     lib.nvfp4_workspace_bytes.restype = ctypes.c_uint64
@@ -209,9 +209,9 @@ def nvfp4_quantize(x: torch.Tensor, row: Optional[Orientation], col: Optional[Or
 
 
 def nvfp4_dequantize(q: Orientation, rows: int, cols: int, scale_layout: int, row_scaled: bool, y: torch.Tensor,
-                     stream=None) -> None:
+                     stream=None, scale_fmt: int = 0) -> None:
     qc = q.as_c()
-    _check(load().nvfp4_dequantize(ctypes.byref(qc), rows, cols, scale_layout, int(row_scaled), _ptr(y),
+    _check(load().nvfp4_dequantize(ctypes.byref(qc), rows, cols, scale_layout, scale_fmt, int(row_scaled), _ptr(y),
                                    _stream(stream)))
 
 

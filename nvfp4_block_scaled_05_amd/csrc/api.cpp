@@ -152,9 +152,8 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   const bool empty = rows * cols == 0;
   if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
   if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
-  if (cfg.scale_fmt == NVFP4_SCALE_UE5M3)
-    return fail(NVFP4_ERR_UNSUPPORTED, "UE5M3 block scales are not supported (not defined on the pages)");
-  if (cfg.scale_fmt != NVFP4_SCALE_E4M3) return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale format %u", cfg.scale_fmt);
+  if (cfg.scale_fmt != NVFP4_SCALE_E4M3 && cfg.scale_fmt != NVFP4_SCALE_UE5M3)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale format %u", cfg.scale_fmt);
   if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", cfg.scale_layout);
   const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
@@ -187,6 +186,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   };
   if (cfg.row_scaled) {
     nvfp4::RowScaledArgs a{x, R, C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop};
+    a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
     if ((st = record(0)) != NVFP4_OK) return st;
     st = hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
     return st != NVFP4_OK ? st : record(1);
@@ -231,6 +231,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   nvfp4::CastArgs a{x,  R,        C,    row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
                     rht_word(cfg), cfg.noop, partials, npartials};
+  a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
   if ((st = record(0)) != NVFP4_OK) return st;
   st = hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
   return st != NVFP4_OK ? st : record(1);
@@ -258,7 +259,8 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
   if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
   if (cfg.row_scaled) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled grouped quantize: use nvfp4_quantize");
-  if (cfg.scale_fmt != NVFP4_SCALE_E4M3) return fail(NVFP4_ERR_UNSUPPORTED, "only E4M3 block scales are supported");
+  if (cfg.scale_fmt != NVFP4_SCALE_E4M3 && cfg.scale_fmt != NVFP4_SCALE_UE5M3)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale format %u", cfg.scale_fmt);
   if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", cfg.scale_layout);
   const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
@@ -310,13 +312,14 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   nvfp4::CastArgs a{x, static_cast<uint32_t>(rows), C, row ? row->data : nullptr, row ? row->scales : nullptr, ra,
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
                     rht_word(cfg), cfg.noop, partials, 0};
+  a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
   return hip_status(nvfp4::launch_cast_grouped(a, row_start, partials ? part_start : nullptr, G, dtype,
                                                cfg.block_2d != 0, cfg.rht != 0, sr, s),
                     "grouped quantize launch");
 }
 
 extern "C" nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols, uint32_t scale_layout,
-                                           uint32_t row_scaled, float *y, void *stream) {
+                                           uint32_t scale_fmt, uint32_t row_scaled, float *y, void *stream) {
   if (q == nullptr || y == nullptr) return fail(NVFP4_ERR_NULL, "NULL quantized tensor or output");
   if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
   if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 16", (long long)cols);
@@ -328,12 +331,15 @@ extern "C" nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, i
   if (!aligned(y, 16)) return fail(NVFP4_ERR_ALIGN, "output must be 16-byte aligned");
   if (scale_layout != NVFP4_SCALES_COMPACT && scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale layout %u", scale_layout);
+  if (scale_fmt != NVFP4_SCALE_E4M3 && scale_fmt != NVFP4_SCALE_UE5M3)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale format %u", scale_fmt);
   const bool swz = scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
   if (swz && (rows % 128 != 0 || cols % 128 != 0))
     return fail(NVFP4_ERR_SHAPE, "GEMM-swizzled scales need rows and cols that are multiples of 128");
   if (row_scaled && swz) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 keeps compact scales");
   return hip_status(nvfp4::launch_dequant(q->data, q->scales, q->amax, static_cast<uint32_t>(rows),
-                                          static_cast<uint32_t>(cols), swz, row_scaled != 0, y,
+                                          static_cast<uint32_t>(cols), swz, row_scaled != 0,
+                                          scale_fmt == NVFP4_SCALE_UE5M3, y,
                                           static_cast<hipStream_t>(stream)),
                     "dequantize launch");
 }

@@ -184,13 +184,27 @@ __device__ __forceinline__ uint32_t pick(bool lo, uint32_t a, uint32_t b) {
   return b ^ ((a ^ b) & mask);
 }
 
-__device__ __forceinline__ uint32_t block_code(uint32_t m_bits, float S) {
+__device__ __forceinline__ uint32_t block_code(uint32_t m_bits, float S, bool ue5m3) {
   const float q = __uint_as_float(m_bits) / 6.0f;
-  return e4m3_encode(q * S);
+  return scale_encode(q * S, ue5m3);
 }
 
-__device__ __forceinline__ float code_multiplier(uint32_t code, float S) {
-  return code == 0 ? 0.0f : fminf(S / e4m3_decode(code), kFltMax);
+__device__ __forceinline__ float code_multiplier(uint32_t code, float S, bool ue5m3) {
+  return code == 0 ? 0.0f : fminf(S / scale_decode(code, ue5m3), kFltMax);
+}
+
+// The multiplier of every scale code of both orientations, in LDS: E4M3
+// has 127 finite non-negative codes (one division per thread), UE5M3 248
+// (two per thread). Codes past the format's last one are never looked up.
+__device__ __forceinline__ void fill_multipliers(float (&lds)[2][256], int tid, float S_row, float S_col,
+                                                 bool ue5m3) {
+  if (!ue5m3) {
+    if (tid < 127) lds[0][tid] = code_multiplier(tid, S_row, false);
+    else if (tid >= 128 && tid < 255) lds[1][tid - 128] = code_multiplier(tid - 128, S_col, false);
+  } else if (tid < 248) {
+    lds[0][tid] = code_multiplier(tid, S_row, true);
+    lds[1][tid] = code_multiplier(tid, S_col, true);
+  }
 }
 
 template <int DT>
@@ -225,7 +239,7 @@ __device__ __forceinline__ uint32_t piece_max(const uint32_t (&w)[RT<DT>::kWords
 template <int DT, bool B2D, bool SR>
 __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
   constexpr int W = RT<DT>::kWords;
-  __shared__ float lds_mult[2][128];                   // multiplier per E4M3 code (row, col)
+  __shared__ float lds_mult[2][256];                   // multiplier per scale code (row, col)
   // scale codes of the tile, row-wise [tile row][16-col block] and column-wise
   // [tile col][16-row block]; compact: line * 8 + block; swizzled: the two
   // 512-byte GEMM tiles that the 128 x 8 codes form, in memory order
@@ -274,10 +288,10 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
 
   float amax_row, amax_col;
   amax_pair<false>(p, part, part, lds_red, (tx | ty) == 0, amax_row, amax_col);
-  const float S_row = do_row ? global_encode_scale(amax_row) : 1.0f;
-  const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
-  if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
-  else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
+  const bool ue = p.ue5m3 != 0;
+  const float S_row = do_row ? global_encode_scale(amax_row, ue) : 1.0f;
+  const float S_col = do_col ? global_encode_scale(amax_col, ue) : 1.0f;
+  fill_multipliers(lds_mult, tid, S_row, S_col, ue);
   if (!interior) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -296,8 +310,8 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
     for (int k = 0; k < 8; ++k) m = max(m, piece_max<DT>(w[k]));
     m = max(m, dpp_mov<kQuadXor1>(m));
     m = max(m, swz_xor16(m));
-    const uint32_t cr = block_code(m, S_row);
-    const uint32_t cc = block_code(m, S_col);
+    const uint32_t cr = block_code(m, S_row, ue);
+    const uint32_t cc = block_code(m, S_col, ue);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       rcode[k] = cr;
@@ -316,7 +330,7 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
       const bool lo = (ucol & 1) == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t mine = block_code(pick(lo, mr[j], mr[j + 4]), S_row);
+        const uint32_t mine = block_code(pick(lo, mr[j], mr[j + 4]), S_row, ue);
         const uint32_t other = dpp_mov<kQuadXor1>(mine);
         rcode[j] = pick(lo, mine, other);
         rcode[j + 4] = pick(lo, other, mine);
@@ -349,7 +363,7 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
       const bool lo = (rg & 1) == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t mine = block_code(pick(lo, mc[j], mc[j + 4]), S_col);
+        const uint32_t mine = block_code(pick(lo, mc[j], mc[j + 4]), S_col, ue);
         const uint32_t other = swz_xor16(mine);
         ccode[j] = pick(lo, mine, other);
         ccode[j + 4] = pick(lo, other, mine);
@@ -511,7 +525,7 @@ template <int DT, bool SR>
 __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
   constexpr int kElem = DT == kBF16 ? 2 : 4;
   constexpr int W = kElem;  // 32-bit words per 4-column row piece: 2 (BF16) or 4 (FP32)
-  __shared__ float lds_mult[2][128];
+  __shared__ float lds_mult[2][256];
   __shared__ __align__(4) uint8_t lds_rs[kRT * 8];
   __shared__ __align__(4) uint8_t lds_cs[kRT * 8];
   __shared__ __align__(16) uint8_t lds_rd[kRT][64 + 16];  // row-wise data bytes (padded rows)
@@ -566,10 +580,10 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
 
   float amax_row, amax_col;
   amax_pair<true>(p, part_row, part_col, lds_red, (tx | ty) == 0, amax_row, amax_col);
-  const float S_row = do_row ? global_encode_scale(amax_row) : 1.0f;
-  const float S_col = do_col ? global_encode_scale(amax_col) : 1.0f;
-  if (tid < 127) lds_mult[0][tid] = code_multiplier(tid, S_row);
-  else if (tid >= 128 && tid < 255) lds_mult[1][tid - 128] = code_multiplier(tid - 128, S_col);
+  const bool ue = p.ue5m3 != 0;
+  const float S_row = do_row ? global_encode_scale(amax_row, ue) : 1.0f;
+  const float S_col = do_col ? global_encode_scale(amax_col, ue) : 1.0f;
+  fill_multipliers(lds_mult, tid, S_row, S_col, ue);
   if (!interior) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -603,7 +617,7 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
       else mine[k >> 2] = pick(q == (k & 3), m, mine[k >> 2]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mine[j] = block_code(mine[j], S_row);
+    for (int j = 0; j < 4; ++j) mine[j] = block_code(mine[j], S_row, ue);
 #pragma unroll
     for (int k = 0; k < 16; ++k) rcode[k] = quad_bcast(mine[k >> 2], k & 3);
     if (q == 0) {
@@ -660,7 +674,7 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
       float ms = 0.0f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) ms = fmaxf(ms, fabsf(v[k]));
-      const uint32_t code = block_code(__float_as_uint(ms * 0.25f), S_col);
+      const uint32_t code = block_code(__float_as_uint(ms * 0.25f), S_col, ue);
       const float e = lds_mult[1][code] * 0.25f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] *= e;

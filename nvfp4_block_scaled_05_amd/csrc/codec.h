@@ -13,18 +13,20 @@
 namespace nvfp4 {
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
-// Largest E2M1 magnitude times largest E4M3 magnitude: 6 * 448.
+// Largest E2M1 magnitude times the largest block-scale magnitude: 6 * 448
+// with E4M3 scales, 6 * 61440 with UE5M3 scales.
 constexpr float kGlobalScaleNumerator = 2688.0f;
+constexpr float kGlobalScaleNumeratorUe5m3 = 368640.0f;
 
 // ---------------------------------------------------------------------------
 // Two-level scaling ("Implement row-scaled NVFP4 fprop recipe", Greptile
 // summary: FP8 block scales relative to a per-tensor or per-row FP32 amax,
 // with a zero guard).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float global_encode_scale(float amax) {
+__device__ __forceinline__ float global_encode_scale(float amax, bool ue5m3) {
   if (amax == 0.0f) return 1.0f;
-  float s = kGlobalScaleNumerator / amax;  // IEEE division (HIP default)
-  return fminf(s, kFltMax);                 // an overflow to +inf clamps
+  float s = (ue5m3 ? kGlobalScaleNumeratorUe5m3 : kGlobalScaleNumerator) / amax;  // IEEE division
+  return fminf(s, kFltMax);  // an overflow to +inf clamps
 }
 
 // E4M3 (bias 7, max 448) of a non-negative value, nearest even, saturating.
@@ -52,18 +54,56 @@ __device__ __forceinline__ float e4m3_decode(uint32_t code) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
+// UE5M3 block scales: unsigned, 5 exponent bits (bias 15), 3 mantissa
+// bits, subnormals m * 2^-17, exponent 31 reserved, so the largest value is
+// 61440 (code 0xF7); nearest even, saturating. The format is named but not
+// defined in "Fuse NVFP4 scale swizzling on SM120 and SM121" (Changes); this
+// is the reading the library takes.
+__device__ __forceinline__ uint32_t ue5m3_encode(float sd) {
+  if (!(sd < 61440.0f)) return 0xF7u;  // 61440 and above (incl. +inf) saturate
+  if (sd < 6.103515625e-05f) {
+    // subnormal range (below 2^-14), quantum 2^-17: the nearest-even
+    // integer multiple (a result of 8 is the smallest normal, code 0x08)
+    return static_cast<uint32_t>(__builtin_rintf(sd * 131072.0f));
+  }
+  uint32_t u = __float_as_uint(sd);
+  uint32_t exp5 = (u >> 23) - 127u + 15u;  // 1..30
+  uint32_t man = u & 0x7FFFFFu;
+  uint32_t keep = man >> 20;
+  uint32_t rest = man & 0xFFFFFu;
+  uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & keep);
+  uint32_t code = (exp5 << 3) + keep + up;  // a mantissa carry bumps the exponent
+  return code > 0xF7u ? 0xF7u : code;
+}
+
+__device__ __forceinline__ float ue5m3_decode(uint32_t code) {
+  uint32_t e = (code >> 3) & 0x1Fu;
+  uint32_t m = code & 7u;
+  if (e == 0) return static_cast<float>(m) * 7.62939453125e-06f;  // m * 2^-17
+  return __uint_as_float(((e + 112u) << 23) | (m << 20));
+}
+
+// The block-scale format of a call: E4M3 (default) or UE5M3 (uniform flag).
+__device__ __forceinline__ uint32_t scale_encode(float sd, bool ue5m3) {
+  return ue5m3 ? ue5m3_encode(sd) : e4m3_encode(sd);
+}
+
+__device__ __forceinline__ float scale_decode(uint32_t code, bool ue5m3) {
+  return ue5m3 ? ue5m3_decode(code) : e4m3_decode(code);
+}
+
 struct BlockScale {
-  uint32_t code;  // E4M3 byte
+  uint32_t code;  // scale byte
   float mult;     // encode multiplier e
 };
 
 // sd = fl(fl(m / 6) * S); e = fl(S / value(s)), 0 when s == 0.
-__device__ __forceinline__ BlockScale block_scale(float block_amax, float S) {
+__device__ __forceinline__ BlockScale block_scale(float block_amax, float S, bool ue5m3) {
   float q = block_amax / 6.0f;
   float sd = q * S;
   BlockScale b;
-  b.code = e4m3_encode(sd);
-  b.mult = b.code == 0 ? 0.0f : fminf(S / e4m3_decode(b.code), kFltMax);
+  b.code = scale_encode(sd, ue5m3);
+  b.mult = b.code == 0 ? 0.0f : fminf(S / scale_decode(b.code, ue5m3), kFltMax);
   return b;
 }
 

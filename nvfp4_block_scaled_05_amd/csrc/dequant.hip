@@ -25,17 +25,18 @@ __device__ __forceinline__ float e2m1_value(uint32_t code) {
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict__ data,
                                                       const uint8_t *__restrict__ scales,
                                                       const float *__restrict__ amax, uint32_t rows, uint32_t cols,
-                                                      uint32_t swizzled, uint32_t row_scaled, float *__restrict__ y) {
+                                                      uint32_t swizzled, uint32_t row_scaled, uint32_t ue5m3,
+                                                      float *__restrict__ y) {
   const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const uint32_t units_per_row = cols >> 3;
   if (i >= static_cast<uint64_t>(rows) * units_per_row) return;
   const uint32_t r = static_cast<uint32_t>(i / units_per_row);
   const uint32_t c = static_cast<uint32_t>(i % units_per_row) * 8;
-  const float S = global_encode_scale(amax[row_scaled ? r : 0]);
+  const float S = global_encode_scale(amax[row_scaled ? r : 0], ue5m3 != 0);
   const uint32_t scale_cols = cols >> 4;
   const uint64_t soff = swizzled ? swizzled_scale_offset(r, c >> 4, scale_cols)
                                  : static_cast<uint64_t>(r) * scale_cols + (c >> 4);
-  const float sf = e4m3_decode(scales[soff]);
+  const float sf = scale_decode(scales[soff], ue5m3 != 0);
   const uint32_t word = *reinterpret_cast<const uint32_t *>(data + static_cast<uint64_t>(r) * (cols >> 1) + (c >> 1));
   float out[8];
 #pragma unroll
@@ -48,12 +49,12 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t *__restrict_
 }  // namespace
 
 hipError_t launch_dequant(const uint8_t *data, const uint8_t *scales, const float *amax, uint32_t rows,
-                          uint32_t cols, bool swizzled, bool row_scaled, float *y, hipStream_t s) {
+                          uint32_t cols, bool swizzled, bool row_scaled, bool ue5m3, float *y, hipStream_t s) {
   const uint64_t units = static_cast<uint64_t>(rows) * (cols >> 3);
   if (units == 0) return hipSuccess;
   const uint32_t blocks = static_cast<uint32_t>((units + kThreads - 1) / kThreads);
   hipLaunchKernelGGL(k_dequant, dim3(blocks), dim3(kThreads), 0, s, data, scales, amax, rows, cols,
-                     swizzled ? 1u : 0u, row_scaled ? 1u : 0u, y);
+                     swizzled ? 1u : 0u, row_scaled ? 1u : 0u, ue5m3 ? 1u : 0u, y);
   return hipGetLastError();
 }
 

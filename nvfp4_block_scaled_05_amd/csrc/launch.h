@@ -42,6 +42,7 @@ struct CastArgs {
   // result to the amax buffers.
   const uint32_t *partials;
   uint32_t npartials;
+  uint32_t ue5m3;  // block scales in UE5M3 rather than E4M3
 };
 
 // Arguments of the row-scaled (per-row amax) kernel: row-wise output only.
@@ -52,6 +53,7 @@ struct RowScaledArgs {
   float *amax;             // [rows]
   uint32_t sr_seed;
   const float *noop;
+  uint32_t ue5m3;  // block scales in UE5M3 rather than E4M3
 };
 
 hipError_t launch_zero_amax(float *a, float *b, const float *noop, hipStream_t s);
@@ -86,7 +88,7 @@ hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, con
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *data, const uint8_t *scales, const float *amax, uint32_t rows,
-                          uint32_t cols, bool swizzled, bool row_scaled, float *y, hipStream_t s);
+                          uint32_t cols, bool swizzled, bool row_scaled, bool ue5m3, float *y, hipStream_t s);
 // zero-padded compact -> GEMM-swizzled scales; out holds swizzled_scales_bytes()
 uint64_t swizzled_scales_bytes(uint64_t rows, uint64_t scale_cols);
 hipError_t launch_swizzle(const uint8_t *compact, uint32_t rows, uint32_t scale_cols, uint8_t *out, hipStream_t s);

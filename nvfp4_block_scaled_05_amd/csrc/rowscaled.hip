@@ -82,7 +82,7 @@ __device__ __forceinline__ float block_value(const Block<DT> &b, int k) {
 template <int DT, bool SR>
 __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, bool valid, uint32_t blk, uint32_t row,
                                              const RowScaledArgs &p, float S, uint32_t key) {
-  const BlockScale bs = block_scale(__uint_as_float(m), S);
+  const BlockScale bs = block_scale(__uint_as_float(m), S, p.ue5m3 != 0);
   float s[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) s[k] = block_value<DT>(b, k) * bs.mult;
@@ -160,7 +160,7 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
   }
   if (p.data == nullptr) return;
 
-  const float S = global_encode_scale(amax);
+  const float S = global_encode_scale(amax, p.ue5m3 != 0);
 #pragma unroll
   for (int k = 0; k < kRegBlocks; ++k) {
     const uint32_t blk = tid + kThreads * k;

@@ -96,10 +96,16 @@ def test_rht_gates():
     assert _q(128, 128, row=_out(), col=_out(), cfg=nv.make_config(rht=True)) == nv.NVFP4_ERR_UNSUPPORTED
 
 
-def test_ue5m3_is_unsupported():
-    cfg = nv.make_config(scale_fmt=nv.NVFP4_SCALE_UE5M3)
+def test_unknown_scale_format_is_unsupported():
+    # E4M3 (0) and UE5M3 (1) are the formats; every call below fails validation
+    cfg = nv.make_config(scale_fmt=2)
     assert _q(128, 128, row=_out(), cfg=cfg) == nv.NVFP4_ERR_UNSUPPORTED
-    assert "UE5M3" in nv.nvfp4_last_error()
+    assert "scale format" in nv.nvfp4_last_error()
+    lib = nv.load()
+    groups = (ctypes.c_int64 * 1)(128)
+    r = _out()
+    assert lib.nvfp4_quantize_grouped(X, 0, 1, groups, 128, ctypes.byref(r), None, ctypes.byref(cfg), None) == \
+        nv.NVFP4_ERR_UNSUPPORTED
 
 
 def test_compute_amax_rejections():
@@ -116,11 +122,13 @@ def test_compute_amax_rejections():
 def test_dequantize_rejections():
     lib = nv.load()
     q = _out()
-    assert lib.nvfp4_dequantize(None, 64, 64, 0, 0, D, None) == nv.NVFP4_ERR_NULL
-    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 40, 0, 0, D, None) == nv.NVFP4_ERR_SHAPE
-    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 1, 0, D, None) == nv.NVFP4_ERR_SHAPE
-    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 0, 0, D + 4, None) == nv.NVFP4_ERR_ALIGN
-    assert lib.nvfp4_dequantize(ctypes.byref(q), 128, 128, 1, 1, D, None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert lib.nvfp4_dequantize(None, 64, 64, 0, 0, 0, D, None) == nv.NVFP4_ERR_NULL
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 40, 0, 0, 0, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 1, 0, 0, D, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 0, 0, 0, D + 4, None) == nv.NVFP4_ERR_ALIGN
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 128, 128, 1, 0, 1, D, None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert lib.nvfp4_dequantize(ctypes.byref(q), 64, 64, 0, 2, 0, D, None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert "scale format" in nv.nvfp4_last_error()
 
 
 def test_debug_rht_rejections():
