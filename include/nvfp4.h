@@ -259,7 +259,7 @@ nvfp4_status_t nvfp4_swizzle_scales(const uint8_t *compact, int64_t rows, int64_
                                     void *stream);
 
 /* Size in bytes of the zero-padded swizzled scales of nvfp4_swizzle_scales
- * (0 for a negative or empty shape). */
+ * (0 for a negative or empty shape, or 2^32 or more rows or scale columns). */
 uint64_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t scale_cols);
 
 /* Text for the last non-OK status returned on the calling thread ("" when

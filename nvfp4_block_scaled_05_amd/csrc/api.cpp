@@ -50,14 +50,21 @@ nvfp4_status_t hip_status(hipError_t e, const char *what) {
   return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// a * b >= limit for non-negative a, b, without overflow (limit <= 2^63).
+bool product_at_least(int64_t a, int64_t b, uint64_t limit) {
+  if (a == 0 || b == 0) return false;
+  if (a >= (int64_t{1} << 32) || b >= (int64_t{1} << 32)) return true;
+  return static_cast<uint64_t>(a) * static_cast<uint64_t>(b) >= limit;
+}
+
 // Shared checks of an input matrix.
 nvfp4_status_t check_input(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols) {
   if (dtype != NVFP4_IN_BF16 && dtype != NVFP4_IN_FP32)
     return fail(NVFP4_ERR_UNSUPPORTED, "input dtype %d is not BF16 (0) or FP32 (1)", static_cast<int>(dtype));
   if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape %lld x %lld", (long long)rows, (long long)cols);
   if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 16", (long long)cols);
-  if (rows > 0 && cols > 0 && rows * cols >= (int64_t{1} << 32))
-    return fail(NVFP4_ERR_SHAPE, "rows * cols = %lld must be below 2^32", (long long)(rows * cols));
+  if (product_at_least(rows, cols, uint64_t{1} << 32))
+    return fail(NVFP4_ERR_SHAPE, "rows * cols (%lld x %lld) must be below 2^32", (long long)rows, (long long)cols);
   if (rows * cols > 0 && x == nullptr) return fail(NVFP4_ERR_NULL, "input pointer is NULL");
   if (x != nullptr && !aligned(x, 16)) return fail(NVFP4_ERR_ALIGN, "input pointer is not 16-byte aligned");
   return NVFP4_OK;
@@ -81,7 +88,7 @@ extern "C" const char *nvfp4_last_error(void) { return g_last_error.c_str(); }
 extern "C" uint64_t nvfp4_workspace_bytes(void) { return NVFP4_WORKSPACE_BYTES; }
 
 extern "C" uint64_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t scale_cols) {
-  if (rows <= 0 || scale_cols <= 0) return 0;
+  if (rows <= 0 || scale_cols <= 0 || rows >= (int64_t{1} << 32) || scale_cols >= (int64_t{1} << 32)) return 0;
   return nvfp4::swizzled_scales_bytes(static_cast<uint64_t>(rows), static_cast<uint64_t>(scale_cols));
 }
 
@@ -89,7 +96,7 @@ extern "C" nvfp4_status_t nvfp4_swizzle_scales(const uint8_t *compact, int64_t r
                                                uint8_t *swizzled, void *stream) {
   if (rows < 0 || scale_cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape %lld x %lld", (long long)rows,
                                               (long long)scale_cols);
-  if (rows > 0 && scale_cols > 0 && (rows + 127) / 128 * 128 * ((scale_cols + 3) / 4 * 4) >= (int64_t{1} << 34))
+  if (product_at_least((rows + 127) / 128 * 128, (scale_cols + 3) / 4 * 4, uint64_t{1} << 34))
     return fail(NVFP4_ERR_SHAPE, "scale matrix %lld x %lld is too large", (long long)rows, (long long)scale_cols);
   if (rows * scale_cols == 0) return NVFP4_OK;
   if (compact == nullptr || swizzled == nullptr) return fail(NVFP4_ERR_NULL, "a scale pointer is NULL");
@@ -246,7 +253,8 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   if (group_rows == nullptr) return fail(NVFP4_ERR_NULL, "group_rows is NULL");
   int64_t rows = 0;
   for (int64_t g = 0; g < num_groups; ++g) {
-    if (group_rows[g] < 0) return fail(NVFP4_ERR_SHAPE, "group %lld has %lld rows", (long long)g, (long long)group_rows[g]);
+    if (group_rows[g] < 0 || group_rows[g] >= (int64_t{1} << 32))
+      return fail(NVFP4_ERR_SHAPE, "group %lld has %lld rows", (long long)g, (long long)group_rows[g]);
     rows += group_rows[g];
     if (rows >= (int64_t{1} << 32)) return fail(NVFP4_ERR_SHAPE, "too many rows");
   }
@@ -323,7 +331,7 @@ extern "C" nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, i
   if (q == nullptr || y == nullptr) return fail(NVFP4_ERR_NULL, "NULL quantized tensor or output");
   if (rows < 0 || cols < 0) return fail(NVFP4_ERR_SHAPE, "negative shape");
   if (cols % 16 != 0) return fail(NVFP4_ERR_SHAPE, "cols = %lld is not a multiple of 16", (long long)cols);
-  if (rows * cols >= (int64_t{1} << 32)) return fail(NVFP4_ERR_SHAPE, "rows * cols must be below 2^32");
+  if (product_at_least(rows, cols, uint64_t{1} << 32)) return fail(NVFP4_ERR_SHAPE, "rows * cols must be below 2^32");
   if (rows * cols == 0) return NVFP4_OK;
   if (q->data == nullptr || q->scales == nullptr || q->amax == nullptr)
     return fail(NVFP4_ERR_NULL, "quantized tensor has a NULL data, scales or amax pointer");

@@ -234,3 +234,20 @@ def test_grouped_rejections():
     assert call([16, 16, 16], cfg=nv.make_config(row_scaled=True), col=None) == nv.NVFP4_ERR_UNSUPPORTED
     assert call([16, 16, 16], cfg=nv.make_config(rht=True, block_2d=True)) == nv.NVFP4_ERR_UNSUPPORTED
     assert call([16, 16, 16], cols=40) == nv.NVFP4_ERR_SHAPE
+
+
+def test_size_limits_are_checked_without_overflow():
+    # products that overflow 64 bits, and the exact 2^32 limit, are refused
+    # before anything is queued (nothing here launches)
+    lib = nv.load()
+    r = _out()
+    for rows, cols in ((1 << 40, 1 << 40), (1 << 62, 16), (65536, 65536), (1 << 32, 16)):
+        assert _q(rows, cols, row=r) == nv.NVFP4_ERR_SHAPE, (rows, cols)
+        assert lib.nvfp4_compute_amax(X, 0, rows, cols, A, None, None, None) == nv.NVFP4_ERR_SHAPE
+        assert lib.nvfp4_dequantize(ctypes.byref(r), rows, cols, 0, 0, 0, D, None) == nv.NVFP4_ERR_SHAPE
+    groups = (ctypes.c_int64 * 2)(16, 1 << 62)
+    assert lib.nvfp4_quantize_grouped(X, 0, 2, groups, 64, ctypes.byref(r), None, None, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_swizzle_scales(S, 1 << 40, 1 << 40, S, None) == nv.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_swizzle_scales(S, 1 << 17, 1 << 17, S, None) == nv.NVFP4_ERR_SHAPE
+    assert nv.nvfp4_swizzled_scales_bytes(1 << 40, 4) == 0
+    assert nv.nvfp4_swizzled_scales_bytes(4, 1 << 33) == 0
