@@ -151,9 +151,26 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _shape2d(x: torch.Tensor):
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
+    if x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous 2-D CUDA tensor")
     return x.shape[0], x.shape[1]
+
+
+# The C ABI takes plain pointers and cannot see buffer sizes; the binding
+# checks every tensor it passes against what the call will touch.
+def _need(t: Optional[torch.Tensor], n: int, dtypes, what: str) -> None:
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t is None or not t.is_cuda or not t.is_contiguous() or t.dtype not in dtypes or t.numel() < n:
+        raise ValueError(f"{what} must be a contiguous CUDA tensor of {'/'.join(str(d) for d in dtypes)} "
+                         f"with at least {n} elements")
+
+
+def _need_orientation(o, n: int, k: int, amax_len: int, what: str) -> None:
+    if o is None:
+        return
+    _need(o.data, n * k // 2, torch.uint8, f"{what} data")
+    _need(o.scales, n * k // 16, torch.uint8, f"{what} scales")
+    _need(o.amax, amax_len, torch.float32, f"{what} amax")
 
 
 def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, stochastic=False, sr_seed=0,
@@ -163,6 +180,11 @@ def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, s
     """The config struct. It holds references to the noop and workspace
     tensors (a copy made with from_buffer_copy does not: keep them alive
     while such a copy is used)."""
+    if noop is not None:
+        _need(noop, 1, torch.float32, "noop")
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()
+                                  or workspace.numel() * workspace.element_size() < nvfp4_workspace_bytes()):
+        raise ValueError(f"workspace must be contiguous CUDA memory of at least {nvfp4_workspace_bytes()} bytes")
     cfg = nvfp4_config_t(int(block_2d), NVFP4_SCALES_GEMM_SWIZZLED if swizzled else NVFP4_SCALES_COMPACT,
                          int(scale_fmt), int(stochastic), int(sr_seed) & 0xFFFFFFFF, int(row_scaled), int(rht),
                          int(rht_sign_mask) & 0xFFFFFFFF, int(rht_bf16), int(compute_amax),
@@ -194,6 +216,10 @@ def nvfp4_workspace_bytes() -> int:
 def nvfp4_compute_amax(x: torch.Tensor, row_amax: Optional[torch.Tensor], col_amax: Optional[torch.Tensor],
                        cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
     rows, cols = _shape2d(x)
+    if row_amax is not None:
+        _need(row_amax, rows if (cfg is not None and cfg.row_scaled) else 1, torch.float32, "row_amax")
+    if col_amax is not None:
+        _need(col_amax, 1, torch.float32, "col_amax")
     _check(load().nvfp4_compute_amax(_ptr(x), _dtype_code(x), rows, cols, _ptr(row_amax), _ptr(col_amax),
                                      None if cfg is None else ctypes.byref(cfg), _stream(stream)))
 
@@ -201,6 +227,8 @@ def nvfp4_compute_amax(x: torch.Tensor, row_amax: Optional[torch.Tensor], col_am
 def nvfp4_quantize(x: torch.Tensor, row: Optional[Orientation], col: Optional[Orientation],
                    cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
     rows, cols = _shape2d(x)
+    _need_orientation(row, rows, cols, rows if (cfg is not None and cfg.row_scaled) else 1, "row-wise")
+    _need_orientation(col, cols, rows, 1, "column-wise")
     r = row.as_c() if row is not None else None
     c = col.as_c() if col is not None else None
     _check(load().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, None if r is None else ctypes.byref(r),
@@ -210,6 +238,8 @@ def nvfp4_quantize(x: torch.Tensor, row: Optional[Orientation], col: Optional[Or
 
 def nvfp4_dequantize(q: Orientation, rows: int, cols: int, scale_layout: int, row_scaled: bool, y: torch.Tensor,
                      stream=None, scale_fmt: int = 0) -> None:
+    _need_orientation(q, rows, cols, rows if row_scaled else 1, "quantized tensor")
+    _need(y, rows * cols, torch.float32, "y")
     qc = q.as_c()
     _check(load().nvfp4_dequantize(ctypes.byref(qc), rows, cols, scale_layout, scale_fmt, int(row_scaled), _ptr(y),
                                    _stream(stream)))
@@ -220,6 +250,8 @@ def nvfp4_quantize_grouped(x: torch.Tensor, group_rows, row: Optional[Orientatio
     """x [sum(group_rows)][C]; row/col hold the concatenated per-group outputs
     (data and scales flat or shaped, amax [G])."""
     rows, cols = _shape2d(x)
+    _need_orientation(row, rows, cols, len(group_rows), "row-wise")
+    _need_orientation(col, cols, rows, len(group_rows), "column-wise")
     g = (ctypes.c_int64 * len(group_rows))(*[int(m) for m in group_rows])
     r = row.as_c() if row is not None else None
     c = col.as_c() if col is not None else None
@@ -265,13 +297,14 @@ def nvfp4_swizzle_scales(compact: torch.Tensor, rows: int, scale_cols: int, swiz
                          stream=None) -> None:
     """compact: uint8 with rows * scale_cols bytes; swizzled: uint8 with
     nvfp4_swizzled_scales_bytes(rows, scale_cols) bytes."""
-    if compact.numel() != rows * scale_cols or swizzled.numel() != nvfp4_swizzled_scales_bytes(rows, scale_cols):
-        raise ValueError("buffer sizes do not match the scale shape")
+    _need(compact, rows * scale_cols, torch.uint8, "compact")
+    _need(swizzled, nvfp4_swizzled_scales_bytes(rows, scale_cols), torch.uint8, "swizzled")
     _check(load().nvfp4_swizzle_scales(_ptr(compact), rows, scale_cols, _ptr(swizzled), _stream(stream)))
 
 
 def nvfp4_debug_rht_colwise(x: torch.Tensor, sign_mask: int, t: torch.Tensor, stream=None) -> None:
     rows, cols = _shape2d(x)
+    _need(t, rows * cols, torch.float32, "t")
     _check(load().nvfp4_debug_rht_colwise(_ptr(x), _dtype_code(x), rows, cols, sign_mask & 0xFFFFFFFF, _ptr(t),
                                           _stream(stream)))
 
@@ -280,8 +313,10 @@ def nvfp4_debug_e2m1_pack(v: torch.Tensor, r: Optional[torch.Tensor], out: torch
                           stream=None) -> None:
     """v: float32 [2n]; r: int32/uint32 [n] or None; out: uint8 [n]."""
     n = out.numel()
-    if v.numel() != 2 * n or (r is not None and r.numel() != n):
-        raise ValueError("v must hold 2n values and r n words for n output bytes")
+    _need(out, n, torch.uint8, "out")
+    _need(v, 2 * n, torch.float32, "v")
+    if r is not None:
+        _need(r, n, (torch.int32, torch.uint32), "r")
     _check(load().nvfp4_debug_e2m1_pack(_ptr(v), _ptr(r), _ptr(out), n, flags, _stream(stream)))
 
 

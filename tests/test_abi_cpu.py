@@ -10,6 +10,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import nvfp4_block_scaled_05_amd as nv
 
@@ -251,3 +252,25 @@ def test_size_limits_are_checked_without_overflow():
     assert lib.nvfp4_swizzle_scales(S, 1 << 17, 1 << 17, S, None) == nv.NVFP4_ERR_SHAPE
     assert nv.nvfp4_swizzled_scales_bytes(1 << 40, 4) == 0
     assert nv.nvfp4_swizzled_scales_bytes(4, 1 << 33) == 0
+
+
+def test_binding_refuses_host_tensors_and_short_buffers():
+    # the binding checks every tensor before calling the library; host
+    # tensors stand in for mistakes here (nothing reaches a GPU)
+    x = torch.zeros((32, 64), dtype=torch.bfloat16)
+    o = nv.Orientation(torch.zeros(32 * 32, dtype=torch.uint8), torch.zeros(32 * 4, dtype=torch.uint8),
+                       torch.zeros(1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="CUDA"):
+        nv.nvfp4_quantize(x, o, None)
+    with pytest.raises(ValueError, match="CUDA"):
+        nv.quantize(x)
+    with pytest.raises(ValueError, match="CUDA"):
+        nv.quantize_grouped(x, [16, 16])
+    with pytest.raises(ValueError, match="noop"):
+        nv.make_config(noop=torch.ones(1))
+    with pytest.raises(ValueError, match="workspace"):
+        nv.make_config(workspace=torch.zeros(16384, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="quantized tensor data"):
+        nv.nvfp4_dequantize(o, 32, 64, 0, False, torch.zeros(32 * 64))
+    with pytest.raises(ValueError, match="compact"):
+        nv.nvfp4_swizzle_scales(torch.zeros(128 * 4, dtype=torch.uint8), 128, 4, torch.zeros(512, dtype=torch.uint8))
