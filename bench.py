@@ -48,17 +48,23 @@ METRIC = "NVFP4 quantize HBM GB/s and % of peak, 8192x5120 BF16, row+col output"
 WORKLOAD = "8192x5120 BF16 N(0,1) x per-column 10^(-3+5u) (seed 1); 16x16 blocks; row+col FP4; " \
            "GEMM-swizzled E4M3 scales; RNE; per-tensor amax computed in the call"
 N_SETS = 4
-CAST_SOURCES = ("nvfp4_block_scaled_05_amd/csrc/cast.hip", "nvfp4_block_scaled_05_amd/csrc/codec.h")
+CAST_SOURCES = ("nvfp4_block_scaled_05_amd/csrc/cast.hip", "nvfp4_block_scaled_05_amd/csrc/codec.h",
+                "nvfp4_block_scaled_05_amd/csrc/launch.h", "nvfp4_block_scaled_05_amd/csrc/group.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_cast_2d_8192x5120.json")
 
 
 def cast_source_hash() -> str:
+    """Hash of the cast kernel's code: its sources with // comments and
+    blank lines dropped, so that a comment edit does not void the counters."""
     import hashlib
 
     h = hashlib.sha256()
     for rel in CAST_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

@@ -1,5 +1,7 @@
 // Amax kernels: the zeroing pass, the per-tensor max|x| reduction that fills
-// both amax buffers, and the RHT pair (max|x| and max|RHT(x)|) from one read.
+// both amax buffers, and the RHT pair (max|x| and max|RHT(x)|) from one read;
+// each also in a grouped form (one amax per row slice of the input, group
+// table in the kernel arguments).
 //
 // "Write both NVFP4 amax buffers" (Description, Changes): the zeroing kernel
 // clears both buffers and every block applies its atomic max to both, so no

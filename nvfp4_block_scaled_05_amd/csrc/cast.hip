@@ -2,8 +2,9 @@
 //
 // One workgroup (256 threads, 4 waves of 64) owns a 128 x 128 tile of the
 // input and writes, for that tile:
-//   row-wise:    FP4 data [rows][cols/2] and E4M3 scales, 1x16 blocks along
-//                each input row (or the shared 16x16 block scale);
+//   row-wise:    FP4 data [rows][cols/2] and E4M3 (or UE5M3) scales, 1x16
+//                blocks along each input row (or the shared 16x16 block
+//                scale);
 //   column-wise: the same for the transposed tensor, 1x16 blocks along each
 //                input column, optionally after a 16-point RHT of each
 //                16-row column group.
@@ -20,7 +21,9 @@
 //               column's 16-row transform group is whole in one thread.
 // Both read the input once with non-temporal 128-bit (or 64-bit) loads, stage
 // output bytes and scale codes in LDS, and leave them as wide coalesced
-// stores (non-temporal, except the register-tile kernel's column-wise data).
+// stores (non-temporal, except the register-tile kernel's column-wise data
+// and compact scales, which merge in L2). Grouped forms of both run the
+// same tile code on the tiles of several row slices, one tensor per slice.
 #include "codec.h"
 #include "launch.h"
 
