@@ -203,6 +203,10 @@ OTHER_WORKLOADS = {
                      bytes=2 * 2 * 8192 * 5120 + 2 * (8192 * 5120 // 2 + 8192 * 5120 // 16) + 8),
     "c5_bf16": dict(desc="as c5, with the transformed values rounded to BF16 (rht_bf16)",
                     bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
+    "pages": dict(desc="the pages' shape grid: 1024x1024 ... 5120x8192 BF16 torch.randn (device generator, seed 0), "
+                       "row+col, RNE; 1D and 2D with compact or swizzled scales, RHT with swizzled scales; "
+                       "one input reused, as the pages' q(x) loop does",
+                  bytes=None),
     "grouped": dict(desc="grouped quantize, MoE-like: 64 groups of 0..512 rows (multiples of 128, seed 6; 16768 rows) "
                          "x 4096 BF16 N(0,1) (seed 7); 1x16; row+col; compact; RNE; per-group amax",
                     bytes=2 * 2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64),
@@ -224,6 +228,8 @@ def run_other(name, steps, warmup):
     w = OTHER_WORKLOADS[name]
     if name == "swizzle":
         return run_swizzle(nv, torch, dev, w, steps, warmup)
+    if name == "pages":
+        return run_pages(nv, torch, dev, w, steps, warmup)
     if name == "grouped":
         return run_grouped(nv, torch, dev, w, steps, warmup)
     if name == "c1":
@@ -328,6 +334,49 @@ def run_grouped(nv, torch, dev, w, steps, warmup):
                       "nonempty_groups": sum(1 for m in groups if m),
                       "no_workspace_us": round(us_atomic, 3), "one_call_per_group_us": round(us_sep, 3),
                       "buffer_sets_rotated": N_SETS}), flush=True)
+
+
+# Host wall-clock time per quantize call printed on the pages for an RTX 5050
+# (BF16 torch.randn input, row- and column-wise output), for context only:
+# "Write both NVFP4 amax buffers", Time per quantize call, optimize_for_gemm
+# False (this PR's column), and "Fuse NVFP4 scale swizzling on SM120 and
+# SM121", Time per quantize call, optimize_for_gemm True (this PR's column).
+PAGES_SHAPES = ((1024, 1024), (2048, 2048), (4096, 4096), (8192, 5120), (5120, 8192))
+PAGES_US = {
+    ("1D", False): (19.2, 28.6, 290.6, 724.3, 728.5),
+    ("2D", False): (19.1, 34.1, 294.8, 751.8, 782.4),
+    ("1D", True): (20.9, 29.1, 291.4, 724.6, 725.5),
+    ("2D", True): (21.2, 35.4, 292.7, 729.6, 731.1),
+    ("RHT", True): (21.0, 56.2, 318.0, 754.0, 755.6),
+}
+
+
+def run_pages(nv, torch, dev, w, steps, warmup):
+    """The pages' quantizer x shape x layout grid on this GPU: host
+    wall-clock per call over a loop of calls on one reused input."""
+    stream = torch.cuda.current_stream()
+    ws = nv.empty_workspace(dev)
+    for si, (R, C) in enumerate(PAGES_SHAPES):
+        g = torch.Generator(device=dev).manual_seed(0)
+        x = torch.randn((R, C), generator=g, device=dev).to(torch.bfloat16)
+        row, col = nv.empty_orientation(R, C, dev), nv.empty_orientation(C, R, dev)
+        for (quantizer, swizzled), page_us in PAGES_US.items():
+            cfg = nv.make_config(block_2d=quantizer == "2D", rht=quantizer == "RHT", swizzled=swizzled,
+                                 rht_sign_mask=0x5A5A if quantizer == "RHT" else 0, workspace=ws)
+            for _ in range(warmup):
+                nv.nvfp4_quantize(x, row, col, cfg, stream)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                nv.nvfp4_quantize(x, row, col, cfg, stream)
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / steps
+            nbytes = 2 * 2 * R * C + 2 * (R * C // 2 + R * C // 16) + 8
+            print(json.dumps({"workload": "pages", "quantizer": quantizer, "shape": f"{R}x{C}",
+                              "optimize_for_gemm": swizzled, "us_per_call": round(us, 3),
+                              "GBps": round(nbytes / us / 1e3, 1), "pages_rtx5050_us": page_us[si],
+                              "ratio_pages_over_this": round(page_us[si] / us, 1)}), flush=True)
+        del x, row, col
 
 
 def run_swizzle(nv, torch, dev, w, steps, warmup):
