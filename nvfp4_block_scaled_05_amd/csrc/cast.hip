@@ -766,16 +766,43 @@ __device__ __forceinline__ uint32_t tile_index(const CastArgs &p, uint32_t i, ui
   return x * q + min(x, r) + (i >> 3);
 }
 
+// Tile (tx, ty) at position L of a tx_n x ty_n tile grid. Swizzled scales:
+// row-major. Compact scales: row-major over 8 x 8 blocks of tiles (edge
+// blocks partial), row-major inside a block, so that one XCD's run covers
+// tiles that are neighbours both across (row-wise scale pieces) and down
+// (column-wise scale pieces): 5120x8192 2D compact 41.6 -> 38.2 us.
+__device__ __forceinline__ void tile_xy(const CastArgs &p, uint32_t L, uint32_t tx_n, uint32_t ty_n, uint32_t &tx,
+                                        uint32_t &ty) {
+  if (p.swizzled) {
+    ty = L / tx_n;
+    tx = L - ty * tx_n;
+    return;
+  }
+  constexpr uint32_t B = 8;
+  const uint32_t by = L / (B * tx_n);
+  const uint32_t rem = L - by * B * tx_n;
+  const uint32_t h = min(B, ty_n - B * by);            // rows of this block row
+  const uint32_t bx = min(rem / (B * h), (tx_n - 1) / B);  // full-width blocks come first
+  const uint32_t rem2 = rem - bx * B * h;
+  const uint32_t w = min(B, tx_n - B * bx);            // columns of this block
+  ty = B * by + rem2 / w;
+  tx = B * bx + rem2 % w;
+}
+
 template <int DT, bool B2D, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   const uint32_t t = tile_index(p, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
-  cast_rt_tile<DT, B2D, SR>(p, t % gridDim.x, t / gridDim.x);
+  uint32_t tx, ty;
+  tile_xy(p, t, gridDim.x, gridDim.y, tx, ty);
+  cast_rt_tile<DT, B2D, SR>(p, tx, ty);
 }
 
 template <int DT, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   const uint32_t t = tile_index(p, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
-  cast_rht_tile<DT, SR>(p, t % gridDim.x, t / gridDim.x);
+  uint32_t tx, ty;
+  tile_xy(p, t, gridDim.x, gridDim.y, tx, ty);
+  cast_rht_tile<DT, SR>(p, tx, ty);
 }
 
 // The arguments of group g's own tensor: its rows of the input, its blocks
@@ -804,15 +831,18 @@ __device__ __forceinline__ CastArgs group_args(const CastArgs &p, const GroupTab
 }
 
 // One workgroup per 128 x 128 tile of some group; the tiles of group g are
-// unit_start[g] .. unit_start[g + 1] - 1 (in tile_index order), row-major
-// over that group.
+// unit_start[g] .. unit_start[g + 1] - 1 (in tile_index order), in tile_xy
+// order over that group's own tile grid.
 template <int DT, bool B2D, bool SR>
 __global__ __launch_bounds__(kThreads) void k_cast_rt_grouped(CastArgs p, GroupTable t) {
   const uint32_t u = tile_index(p, blockIdx.x, gridDim.x);
   const uint32_t g = group_of(t, u);
   const uint32_t local = u - t.unit_start[g];
   const uint32_t tiles_x = (p.cols + kRT - 1) / kRT;
-  cast_rt_tile<DT, B2D, SR>(group_args<DT>(p, t, g), local % tiles_x, local / tiles_x);
+  const CastArgs q = group_args<DT>(p, t, g);
+  uint32_t tx, ty;
+  tile_xy(p, local, tiles_x, (q.rows + kRT - 1) / kRT, tx, ty);
+  cast_rt_tile<DT, B2D, SR>(q, tx, ty);
 }
 
 template <int DT, bool SR>
@@ -821,7 +851,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht_grouped(CastArgs p, Group
   const uint32_t g = group_of(t, u);
   const uint32_t local = u - t.unit_start[g];
   const uint32_t tiles_x = (p.cols + kRT - 1) / kRT;
-  cast_rht_tile<DT, SR>(group_args<DT>(p, t, g), local % tiles_x, local / tiles_x);
+  const CastArgs q = group_args<DT>(p, t, g);
+  uint32_t tx, ty;
+  tile_xy(p, local, tiles_x, (q.rows + kRT - 1) / kRT, tx, ty);
+  cast_rht_tile<DT, SR>(q, tx, ty);
 }
 
 template <int DT, bool B2D, bool SR>
