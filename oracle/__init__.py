@@ -268,7 +268,7 @@ def quantize(x, *, rowwise=True, columnwise=True, block_2d=False, row_scaled=Fal
 
 def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=False, rht=False, sign_mask=0,
                      stochastic=False, sr_seed=0, amax_row=None, amax_col=None, rht_bf16=False,
-                     scale_fmt=SCALE_E4M3):
+                     scale_fmt=SCALE_E4M3, row_scaled=False):
     """Grouped quantize. The row-scaled page's changed files keep a grouped
     tensor as one tensor per group with per-group amax offsets; reading: the
     consecutive row slices x[s_g : s_g + m_g] (m_g = group_rows[g]) are each
@@ -279,7 +279,12 @@ def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=F
     (= [R][C/16], compact), col_data (group g's [C][m_g/2] blocks one after
     another), col_scales (group g's [C][m_g/16] blocks), amax_row [G],
     amax_col [G]. amax_row / amax_col, when given, are per-group arrays.
+    row_scaled (row-wise only): each group's amax has one entry per row, so
+    amax_row is [R] (the same page's grouped storage sizes it as the sum of
+    the groups' rows); a given amax_row is then [R] too.
     """
+    if row_scaled:
+        columnwise = False
     x, _ = _input(x)
     rows, cols = x.shape
     group_rows = [int(m) for m in group_rows]
@@ -291,15 +296,19 @@ def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=F
         xs = x[start:start + m]
         start += m
         if m == 0:
-            parts["amax_row"].append(np.zeros(1, np.float32))
+            if not row_scaled:
+                parts["amax_row"].append(np.zeros(1, np.float32))
             parts["amax_col"].append(np.zeros(1, np.float32))
             continue
         given = {}
-        if amax_row is not None or amax_col is not None:
+        if row_scaled and amax_row is not None:
+            given = dict(amax_row=np.asarray(amax_row, np.float32)[start - m:start])
+        elif amax_row is not None or amax_col is not None:
             given = dict(amax_row=None if amax_row is None else np.asarray(amax_row, np.float32)[g:g + 1],
                          amax_col=None if amax_col is None else np.asarray(amax_col, np.float32)[g:g + 1])
         q = quantize(xs, rowwise=rowwise, columnwise=columnwise, block_2d=block_2d, rht=rht, sign_mask=sign_mask,
-                     stochastic=stochastic, sr_seed=sr_seed, rht_bf16=rht_bf16, scale_fmt=scale_fmt, **given)
+                     stochastic=stochastic, sr_seed=sr_seed, rht_bf16=rht_bf16, scale_fmt=scale_fmt,
+                     row_scaled=row_scaled, **given)
         for k in ("row_data", "row_scales", "col_data", "col_scales"):
             if q[k] is not None:
                 parts[k].append(q[k].reshape(-1))
@@ -309,7 +318,8 @@ def quantize_grouped(x, group_rows, *, rowwise=True, columnwise=True, block_2d=F
     for k in ("row_data", "row_scales", "col_data", "col_scales"):
         on = rowwise if k.startswith("row") else columnwise
         out[k] = (np.concatenate(parts[k]) if parts[k] else np.zeros(0, np.uint8)) if on else None
-    out["amax_row"] = np.concatenate(parts["amax_row"]).astype(np.float32) if rowwise else None
+    out["amax_row"] = (np.concatenate(parts["amax_row"]).astype(np.float32) if parts["amax_row"]
+                       else np.zeros(0, np.float32)) if rowwise else None
     out["amax_col"] = np.concatenate(parts["amax_col"]).astype(np.float32) if columnwise else None
     return out
 

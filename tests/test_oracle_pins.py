@@ -732,3 +732,20 @@ def test_ue5m3_power_of_two_invariance(k):
     for key in ("row_data", "row_scales", "col_data", "col_scales"):
         assert np.array_equal(a[key], b[key]), key
     assert b["amax_row"][0] == a["amax_row"][0] * np.float32(2.0 ** k)
+
+
+def test_grouped_rowscaled_with_nearest_even_is_one_rowscaled_call():
+    # per-row scaling treats every row on its own, so with nearest-even
+    # rounding (no byte-index dependence) the grouping cannot change a byte;
+    # with stochastic rounding only the byte indices restart per group
+    x = W.c4(rows=80, cols=96, seed=45)
+    groups = [16, 0, 48, 16]
+    g = O.quantize_grouped(x, groups, row_scaled=True)
+    q = O.quantize(x, columnwise=False, row_scaled=True)
+    assert g["col_data"] is None and g["amax_row"].shape == (80,)
+    for k in ("row_data", "row_scales", "amax_row"):
+        assert np.array_equal(g[k], q[k].reshape(-1)), k
+    gs = O.quantize_grouped(x, groups, row_scaled=True, stochastic=True, sr_seed=6)
+    last = O.quantize(x[64:], columnwise=False, row_scaled=True, stochastic=True, sr_seed=6)
+    assert np.array_equal(gs["row_data"][64 * 48:], last["row_data"].reshape(-1))
+    assert np.array_equal(gs["row_scales"], q["row_scales"].reshape(-1))  # scales are always nearest even
