@@ -220,8 +220,12 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
  *        block), amax [G].
  * Each group_rows[g] must be a multiple of 16 for column-wise output, 16x16
  * blocks or the RHT, and of 128 for swizzled scales (C too). Row-scaled
- * configs are rejected (per-row scaling already treats rows on their own:
- * use nvfp4_quantize). A computed amax takes two launches (amax pass, cast)
+ * configs (row-wise only, 1x16, compact, no RHT) run as one fused launch:
+ * row->amax then holds one entry per row, [R] (the same page's grouped
+ * storage sizes it as the sum of the groups' rows), and nearest-even
+ * results equal a single nvfp4_quantize over all rows; stochastic rounding
+ * counts its byte indices within each group. Otherwise a computed amax
+ * takes two launches (amax pass, cast)
  * with a workspace, each group's workgroup maxima in a range of it that the
  * group's cast tiles reduce (the slots of empty groups are written +0);
  * without one it is zeroed and reduced by atomic max (three launches). The

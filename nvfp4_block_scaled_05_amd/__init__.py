@@ -250,7 +250,7 @@ def nvfp4_quantize_grouped(x: torch.Tensor, group_rows, row: Optional[Orientatio
     """x [sum(group_rows)][C]; row/col hold the concatenated per-group outputs
     (data and scales flat or shaped, amax [G])."""
     rows, cols = _shape2d(x)
-    _need_orientation(row, rows, cols, len(group_rows), "row-wise")
+    _need_orientation(row, rows, cols, rows if (cfg is not None and cfg.row_scaled) else len(group_rows), "row-wise")
     _need_orientation(col, cols, rows, len(group_rows), "column-wise")
     g = (ctypes.c_int64 * len(group_rows))(*[int(m) for m in group_rows])
     r = row.as_c() if row is not None else None
@@ -263,22 +263,23 @@ def nvfp4_quantize_grouped(x: torch.Tensor, group_rows, row: Optional[Orientatio
 def quantize_grouped(x: torch.Tensor, group_rows, *, rowwise=True, columnwise=True,
                      cfg: Optional[nvfp4_config_t] = None, stream=None, use_workspace: bool = True):
     """Allocate the concatenated per-group outputs and run nvfp4_quantize_grouped.
-    Returns (row, col) with flat data and scales and amax [G]. A workspace
-    is allocated for the call as in quantize()."""
+    Returns (row, col) with flat data and scales and amax [G] ([R] for a
+    row-scaled config). A workspace is allocated for the call as in
+    quantize()."""
     rows, cols = _shape2d(x)
     G = len(group_rows)
     dev = x.device
+    cfg = cfg if cfg is not None else make_config()
 
-    def orient():
+    def orient(amax_len):
         return Orientation(torch.empty((rows * cols // 2,), dtype=torch.uint8, device=dev),
                            torch.empty((rows * cols // 16,), dtype=torch.uint8, device=dev),
-                           torch.empty((G,), dtype=torch.float32, device=dev))
+                           torch.empty((amax_len,), dtype=torch.float32, device=dev))
 
-    row = orient() if rowwise else None
-    col = orient() if columnwise else None
-    cfg = cfg if cfg is not None else make_config()
+    row = orient(rows if cfg.row_scaled else G) if rowwise else None
+    col = orient(G) if columnwise else None
     ws = None
-    if use_workspace and not cfg.workspace and cfg.compute_amax:
+    if use_workspace and not cfg.workspace and cfg.compute_amax and not cfg.row_scaled:
         ws = empty_workspace(dev)
         cfg = nvfp4_config_t.from_buffer_copy(cfg)
         cfg.workspace = ws.data_ptr()

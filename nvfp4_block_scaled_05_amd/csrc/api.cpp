@@ -266,7 +266,13 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   const bool empty = rows * cols == 0;
   if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
   if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
-  if (cfg.row_scaled) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled grouped quantize: use nvfp4_quantize");
+  if (cfg.row_scaled) {
+    if (col) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 is row-wise only");
+    if (cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 uses 1x16 blocks");
+    if (cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 cannot be combined with the RHT");
+    if (cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED)
+      return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 keeps compact scales");
+  }
   if (cfg.scale_fmt != NVFP4_SCALE_E4M3 && cfg.scale_fmt != NVFP4_SCALE_UE5M3)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown scale format %u", cfg.scale_fmt);
   if (cfg.scale_layout != NVFP4_SCALES_COMPACT && cfg.scale_layout != NVFP4_SCALES_GEMM_SWIZZLED)
@@ -291,6 +297,12 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   for (int64_t g = 0; g < num_groups; ++g) row_start[g + 1] = row_start[g] + static_cast<uint32_t>(group_rows[g]);
   const uint32_t G = static_cast<uint32_t>(num_groups), C = static_cast<uint32_t>(cols);
   const bool sr = cfg.stochastic != 0;
+  if (cfg.row_scaled) {  // one fused launch over all rows; amax has one entry per row
+    nvfp4::RowScaledArgs a{x, static_cast<uint32_t>(rows), C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop};
+    a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
+    return hip_status(nvfp4::launch_rowscaled_grouped(a, row_start, G, dtype, sr, cfg.compute_amax != 0, s),
+                      "grouped row-scaled quantize launch");
+  }
   float *ra = row ? row->amax : nullptr;
   float *ca = col ? col->amax : nullptr;
   // With a workspace each group's amax workgroups leave their maxima in a

@@ -87,6 +87,10 @@ hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, con
                                uint32_t ngroups, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
+// grouped form: row_start[0..ngroups] are the groups' first rows (stochastic
+// rounding counts byte indices per group)
+hipError_t launch_rowscaled_grouped(const RowScaledArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
+                                    bool sr, bool compute_amax, hipStream_t s);
 hipError_t launch_dequant(const uint8_t *data, const uint8_t *scales, const float *amax, uint32_t rows,
                           uint32_t cols, bool swizzled, bool row_scaled, bool ue5m3, float *y, hipStream_t s);
 // zero-padded compact -> GEMM-swizzled scales; out holds swizzled_scales_bytes()

@@ -81,7 +81,7 @@ __device__ __forceinline__ float block_value(const Block<DT> &b, int k) {
 // Executed by all lanes (DPP), stores predicated on `valid`.
 template <int DT, bool SR>
 __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, bool valid, uint32_t blk, uint32_t row,
-                                             const RowScaledArgs &p, float S, uint32_t key) {
+                                             const RowScaledArgs &p, float S, uint32_t key, uint64_t sr_base) {
   const BlockScale bs = block_scale(__uint_as_float(m), S, p.ue5m3 != 0);
   float s[16];
 #pragma unroll
@@ -91,7 +91,7 @@ __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, boo
   if (SR) {
     uint32_t r[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) r[q] = fmix32(key ^ static_cast<uint32_t>(byte0 + q));
+    for (int q = 0; q < 8; ++q) r[q] = fmix32(key ^ static_cast<uint32_t>(byte0 - sr_base + q));
     lo = e2m1_sr_x8(s, r);
     hi = e2m1_sr_x8(s + 8, r + 4);
   } else {
@@ -133,7 +133,7 @@ __device__ __forceinline__ void load_row(const RowScaledArgs &p, uint32_t row, B
 // One row: amax (or the given one), then encode and store.
 template <int DT, bool SR, bool COMPUTE>
 __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row, const Block<DT> (&reg)[kRegBlocks],
-                                            uint32_t *lds_w, uint32_t key) {
+                                            uint32_t *lds_w, uint32_t key, uint64_t sr_base) {
   const int tid = threadIdx.x;
   const uint32_t nblk = p.cols >> 4;
   const uint64_t row_off = static_cast<uint64_t>(row) * p.cols;
@@ -164,7 +164,7 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
 #pragma unroll
   for (int k = 0; k < kRegBlocks; ++k) {
     const uint32_t blk = tid + kThreads * k;
-    encode_block<DT, SR>(reg[k], bm[k], blk < nblk, blk, row, p, S, key);
+    encode_block<DT, SR>(reg[k], bm[k], blk < nblk, blk, row, p, S, key, sr_base);
   }
   for (uint32_t base = kThreads * kRegBlocks; base < nblk; base += kThreads) {  // uniform loop
     const uint32_t blk = base + tid;
@@ -173,7 +173,7 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
       cur = load_block<DT, false>(p.x, row_off + 16ull * blk);
     else
       zero_block<DT>(cur);
-    encode_block<DT, SR>(cur, block_max_bits<DT>(cur), blk < nblk, blk, row, p, S, key);
+    encode_block<DT, SR>(cur, block_max_bits<DT>(cur), blk < nblk, blk, row, p, S, key, sr_base);
   }
 }
 
@@ -188,7 +188,23 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled(RowScaledArgs p) {
   const uint32_t key = SR ? sr_key(p.sr_seed, 0) : 0u;
   Block<DT> a[kRegBlocks];
   load_row<DT>(p, blockIdx.x, a);
-  process_row<DT, SR, COMPUTE>(p, blockIdx.x, a, lds_w, key);
+  process_row<DT, SR, COMPUTE>(p, blockIdx.x, a, lds_w, key, 0);
+}
+
+// Grouped form (row slices, each a row-scaled tensor of its own): the same
+// rows, with the stochastic-rounding byte indices counted from the start of
+// the row's group (t.unit_start holds the groups' first rows). Only
+// stochastic rounding needs it; nearest even runs the plain kernel.
+template <int DT, bool COMPUTE>
+__global__ __launch_bounds__(kThreads) void k_rowscaled_grouped(RowScaledArgs p, GroupTable t) {
+  __shared__ uint32_t lds_w[kWaves];
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+  const uint32_t key = sr_key(p.sr_seed, 0);
+  const uint32_t g = group_of(t, blockIdx.x);
+  Block<DT> a[kRegBlocks];
+  load_row<DT>(p, blockIdx.x, a);
+  process_row<DT, true, COMPUTE>(p, blockIdx.x, a, lds_w, key,
+                                 static_cast<uint64_t>(t.unit_start[g]) * (p.cols >> 1));
 }
 
 template <int DT, bool SR, bool COMPUTE>
@@ -208,6 +224,28 @@ hipError_t launch_dt(const RowScaledArgs &a, bool sr, bool compute, hipStream_t 
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   return dtype == kBF16 ? launch_dt<kBF16>(a, sr, compute_amax, s) : launch_dt<kFP32>(a, sr, compute_amax, s);
+}
+
+hipError_t launch_rowscaled_grouped(const RowScaledArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
+                                    bool sr, bool compute_amax, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  if (!sr) return launch_rowscaled(a, dtype, false, compute_amax, s);  // grouping changes nothing then
+  GroupTable t{};
+  t.ngroups = ngroups;
+  for (uint32_t g = 0; g <= ngroups; ++g) t.unit_start[g] = t.row_start[g] = row_start[g];
+  const dim3 grid(a.rows), block(kThreads);
+  if (dtype == kBF16) {
+    if (compute_amax)
+      hipLaunchKernelGGL((k_rowscaled_grouped<kBF16, true>), grid, block, 0, s, a, t);
+    else
+      hipLaunchKernelGGL((k_rowscaled_grouped<kBF16, false>), grid, block, 0, s, a, t);
+  } else {
+    if (compute_amax)
+      hipLaunchKernelGGL((k_rowscaled_grouped<kFP32, true>), grid, block, 0, s, a, t);
+    else
+      hipLaunchKernelGGL((k_rowscaled_grouped<kFP32, false>), grid, block, 0, s, a, t);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

@@ -232,7 +232,13 @@ def test_grouped_rejections():
     assert call([16, -16, 16]) == nv.NVFP4_ERR_SHAPE
     assert call([16, 8, 16]) == nv.NVFP4_ERR_SHAPE              # column-wise output needs multiples of 16
     assert call([128, 64, 128], cols=128, cfg=nv.make_config(swizzled=True)) == nv.NVFP4_ERR_SHAPE
-    assert call([16, 16, 16], cfg=nv.make_config(row_scaled=True), col=None) == nv.NVFP4_ERR_UNSUPPORTED
+    # row-scaled groups: row-wise only, 1x16, compact, no RHT (valid row-scaled calls are not made here)
+    assert call([16, 16, 16], cfg=nv.make_config(row_scaled=True)) == nv.NVFP4_ERR_UNSUPPORTED
+    assert call([128, 0, 128], cols=128, cfg=nv.make_config(row_scaled=True, swizzled=True), col=None) == \
+        nv.NVFP4_ERR_UNSUPPORTED
+    assert call([16, 16, 16], cfg=nv.make_config(row_scaled=True, block_2d=True), col=None) == \
+        nv.NVFP4_ERR_UNSUPPORTED
+    assert call([16, 16, 16], cfg=nv.make_config(row_scaled=True, rht=True), col=None) == nv.NVFP4_ERR_UNSUPPORTED
     assert call([16, 16, 16], cfg=nv.make_config(rht=True, block_2d=True)) == nv.NVFP4_ERR_UNSUPPORTED
     assert call([16, 16, 16], cols=40) == nv.NVFP4_ERR_SHAPE
 

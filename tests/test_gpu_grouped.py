@@ -233,3 +233,40 @@ def test_grouped_noop_with_workspace_writes_nothing():
     torch.cuda.synchronize()
     for b, t in zip(before, (row.data, row.scales, row.amax, col.data, col.scales, col.amax)):
         assert np.array_equal(b, host(t))
+
+
+@pytest.mark.parametrize("stochastic", [False, True], ids=["rne", "sr"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_grouped_rowscaled(dtype, stochastic):
+    # row-scaled groups: one amax per row, SR byte indices counted per group
+    x = W.c4(rows=200, cols=400, seed=67) if dtype == "bf16" else W.gaussian_fp32(200, 400, 67, 3.0)
+    groups = [37, 0, 100, 1, 62]  # any row counts for row-wise output
+    kw = dict(row_scaled=True, stochastic=stochastic, sr_seed=12)
+    row, col = nv.quantize_grouped(to_device(x), groups, columnwise=False, cfg=nv.make_config(**kw))
+    torch.cuda.synchronize()
+    assert col is None and row.amax.numel() == 200
+    ref = O.quantize_grouped(x, groups, **kw)
+    assert np.array_equal(host(row.data), ref["row_data"])
+    assert np.array_equal(host(row.scales), ref["row_scales"])
+    assert np.array_equal(host(row.amax), ref["amax_row"])
+
+
+def test_grouped_rowscaled_given_amax_and_noop():
+    x = W.c4(rows=96, cols=128, seed=68)
+    xd = to_device(x)
+    groups = [32, 64]
+    row, _ = nv.quantize_grouped(xd, groups, columnwise=False, cfg=nv.make_config(row_scaled=True))
+    torch.cuda.synchronize()
+    before = [host(t).copy() for t in (row.data, row.scales, row.amax)]
+    noop = torch.ones(1, dtype=torch.float32, device=DEV)
+    nv.nvfp4_quantize_grouped(xd * 4, groups, row, None, nv.make_config(row_scaled=True, noop=noop))
+    torch.cuda.synchronize()
+    for b, t in zip(before, (row.data, row.scales, row.amax)):
+        assert np.array_equal(b, host(t))
+    # given per-row amaxes (twice the true ones), stochastic rounding
+    row.amax.copy_(torch.from_numpy(before[2] * 2))
+    nv.nvfp4_quantize_grouped(xd, groups, row, None, nv.make_config(row_scaled=True, compute_amax=False,
+                                                                    stochastic=True, sr_seed=3))
+    torch.cuda.synchronize()
+    ref = O.quantize_grouped(x, groups, row_scaled=True, amax_row=before[2] * 2, stochastic=True, sr_seed=3)
+    assert np.array_equal(host(row.data), ref["row_data"]) and np.array_equal(host(row.scales), ref["row_scales"])
