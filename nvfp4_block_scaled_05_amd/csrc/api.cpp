@@ -50,7 +50,8 @@ nvfp4_status_t hip_status(hipError_t e, const char *what) {
   return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// a * b >= limit for non-negative a, b, without overflow (limit <= 2^63).
+// For non-negative a, b: a * b >= limit, or either is 2^32 or more (no size
+// argument of the kernels may reach 2^32); computed without overflow.
 bool product_at_least(int64_t a, int64_t b, uint64_t limit) {
   if (a == 0 || b == 0) return false;
   if (a >= (int64_t{1} << 32) || b >= (int64_t{1} << 32)) return true;
