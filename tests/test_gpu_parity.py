@@ -526,3 +526,20 @@ def test_cast_events_bracket_the_cast_kernel(mode):
         assert np.array_equal(a, b)
     ms = ev[0].elapsed_time(ev[1])
     assert 0.0 < ms < 100.0
+
+
+@pytest.mark.parametrize("stochastic", [False, True])
+def test_rowscaled_zero_guard_rows(stochastic):
+    # per-row zero guard ("Implement row-scaled NVFP4 fprop recipe",
+    # changed-files table: the reference quantizer guards a zero amax): rows
+    # of zeros (amax 0, S = 1), a row of denormals (2688 / amax overflows and
+    # is clamped), huge rows and ordinary rows side by side
+    x = W.gaussian_fp32(12, 256, 77, 2.0)
+    x[1] = 0.0
+    x[4] = -0.0
+    x[5] = (W.gaussian_fp32(1, 256, 78)[0] * np.float32(1e-41)).astype(np.float32)
+    x[7] = (W.gaussian_fp32(1, 256, 79)[0] * np.float32(3e37)).astype(np.float32)
+    x[9, :] = 0.0
+    x[9, 100] = np.float32(1.5e-45)  # a single smallest denormal
+    check(x, columnwise=False, row_scaled=True, stochastic=stochastic, sr_seed=13,
+          what=f"rowscaled zero guard sr={stochastic}")
