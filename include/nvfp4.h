@@ -12,8 +12,8 @@
  *   "Write both NVFP4 amax buffers" (PR #3750): one reduction fills both
  *     amax buffers after a zeroing pass clears both (Description, Changes);
  *   "Fuse NVFP4 scale swizzling on SM120 and SM121" (PR #3749): scales are
- *     written directly in the GEMM-swizzled layout when rows and columns
- *     are multiples of 128 (Description, Changes);
+ *     written directly in the GEMM-swizzled layout when both dimensions
+ *     are 128-aligned (Description, Changes);
  *   "Implement row-scaled NVFP4 fprop recipe" (PR #2931): one amax per row,
  *     row-wise output only, compact scales (Description, Changes, summary).
  *

@@ -4,7 +4,7 @@
 // table in the kernel arguments).
 //
 // "Write both NVFP4 amax buffers" (Description, Changes): the zeroing kernel
-// clears both buffers and every block applies its atomic max to both, so no
+// clears both buffers and each block's atomic max goes into both, so no
 // copy and no second read are needed. Max is exact and order-free; on
 // non-negative binary32 values an unsigned integer max of the bit patterns
 // is the float max, so each workgroup ends with one global_atomic_umax per

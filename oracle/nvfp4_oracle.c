@@ -503,7 +503,7 @@ int oracle_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int bl
 /* ------------------------------------------------------------------ */
 /* GEMM-swizzled scale layout.                                         */
 /* [P2] Description/Changes: scales may be written directly in the      */
-/* cuBLAS GEMM layout when rows and columns are multiples of 128; four  */
+/* cuBLAS GEMM layout when both dimensions are 128-aligned; four       */
 /* aligned scales of one row then form one 32-bit word. Reading: the    */
 /* cuBLAS block-scaling layout of 128-row x 4-scale tiles, 512 bytes    */
 /* each, tiles in row-major order over the scale matrix, and inside a   */
@@ -523,7 +523,7 @@ int oracle_swizzle_scales(const uint8_t *compact, int64_t rows, int64_t scale_co
   return 0;
 }
 
-/* [P2] Description: shapes with partial scale tiles keep compact scales
+/* [P2] Description: shapes whose scales do not fill whole tiles stay compact
  * from the quantize call, and a separate pass after it produces the GEMM
  * layout. Reading: that pass pads the scale matrix with zeros to whole
  * 128 x 4 tiles, [ceil(rows/128)*128][ceil(scale_cols/4)*4], and lays the

@@ -1,10 +1,11 @@
-"""GPU: the dual-amax test the "Write both NVFP4 amax buffers" page describes
-(Changes, test list): one output reused across inputs whose maximum
-decreases, reaches zero and rises again (8, 2, 0.5, 0, 32), checking the
-amax buffers against the input maximum after every call, for row-only,
-column-only and two-direction outputs, 1D and 2D blocks, BF16 and FP32
-input, aligned and tail shapes; here also with and without a workspace, and
-every output byte against the oracle."""
+"""GPU: the dual-amax check that the "Write both NVFP4 amax buffers" page
+lists among its tests (Changes). A single set of output buffers is used for
+a sequence of inputs with maxima 8, 2, 0.5, 0 and 32 (falling, then zero,
+then up again); after each call every requested amax buffer must hold the
+input's maximum. The cases span the three output choices (rows, columns,
+both), both block shapes, both input types and a 128-aligned and a ragged
+shape; here also with and without a workspace, with every output byte
+compared with the oracle."""
 
 from __future__ import annotations
 

@@ -2,8 +2,8 @@
 
 - Against the oracle's zero-padded layout on shapes with partial tiles.
 - The pages' production-shape check: for the 128-aligned shapes of their
-  swizzle-fusion benchmark, 1D, 2D and RHT quantization with and without
-  stochastic rounding, the scales that nvfp4_quantize writes directly in the
+  swizzle-fusion benchmark, for every quantizer (1x16, 16x16, RHT) and both
+  rounding modes, the scales that nvfp4_quantize writes directly in the
   GEMM layout equal the compact scales of the same call put through the
   separate pass, and the FP4 data and both amaxes are the same
   ("Fuse NVFP4 scale swizzling ...", validation footnote: 10 shapes x 6

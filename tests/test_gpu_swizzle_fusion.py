@@ -1,11 +1,11 @@
-"""GPU: the swizzle-fusion test the "Fuse NVFP4 scale swizzling on SM120 and
-SM121" page describes (Changes, tests): for 1D / 2D / RHT quantizers x
-row / column / both outputs x nearest-even / stochastic rounding x E4M3 /
-UE5M3 scales x BF16 / FP32 input, the call with GEMM-swizzled scales gives
-the same FP4 bytes and amaxes as the compact call, and its scales are an
-independent permutation (the oracle's reshape of the tile layout) of the
-compact ones. The compact call itself is checked against the oracle in the
-option-matrix tests."""
+"""GPU: the swizzle-fusion check that the "Fuse NVFP4 scale swizzling on
+SM120 and SM121" page lists among its tests (Changes). Over every
+combination of quantizer (1x16, 16x16, RHT), requested outputs, rounding
+mode, block-scale format and input type, a call that writes GEMM-swizzled
+scales must produce the FP4 bytes and amaxes of the compact call, and its
+scale bytes must be the compact ones moved by an independent statement of
+the tile permutation (the oracle's reshape). The compact call itself is
+checked against the oracle in the option-matrix tests."""
 
 from __future__ import annotations
 
