@@ -2,22 +2,31 @@
 
 One step = one nvfp4_quantize call on the 8192x5120 BF16 workload with
 16x16 blocks, row-wise and column-wise output, GEMM-swizzled E4M3 scales,
-round to nearest even and a per-tensor amax computed inside the call (amax
-pass storing per-workgroup maxima in a workspace, then the fused
-cast-transpose, which finishes the reduction and writes both amax buffers;
-two launches). Inputs are resident
-in HBM before timing starts; four input/output sets rotate so that no step
-finds its input in the 256 MB Infinity Cache from an earlier step.
+round to nearest even and a per-tensor amax computed inside the call, with
+the library choosing the amax path (NVFP4_AMAX_PATH_AUTO). At this shape
+that is the single-pass form: one launch in which every workgroup holds five
+128x128 tiles in registers across a grid-wide handoff of the amax, so the
+input is read once. Inputs are resident in HBM before timing starts; four
+input/output sets rotate so that no step finds its input in the 256 MB
+Infinity Cache from an earlier step.
 
-value = algorithmic bytes of one call (two reads of the input, both FP4
-outputs, both scale arrays, the amax pair) / seconds per call, in GB/s.
+value = B_alg / seconds per call, in GB/s, with B_alg the method's
+algorithmic bytes of one call: two reads of the input (the amax reduction
+and the cast), both FP4 outputs, both scale arrays, the amax pair
+(214,958,088 B). The config also gives B_min / t, with B_min = one read of
+the input plus the outputs (131,072,008 B), the bytes any implementation
+must move, and the time of the two-pass form (amax pass + cast kernel) on
+the same buffers.
 
-The roofline entry covers the dominant kernel (the fused cast-transpose):
-its algorithmic bytes (one read of the input, both outputs and scales, the
-two amax words) over its average duration, against the 8 TB/s HBM peak.
-The duration comes from timing-only HIP events that the library records on
-the call's stream right before and after the cast launch (cast_events in
-the config), in a second pass of the same calls after the timed region.
+The roofline entry covers the dominant kernel, the one kernel of the
+single-pass call (or the cast kernel of the two-pass form, if that ran):
+algorithmic bytes per launch over its average duration, against the 8 TB/s
+HBM peak; frac_min_bytes puts B_min over the same duration. The duration
+comes from timing-only HIP events that the library records on the call's
+stream right before and after that launch (cast_events in the config), in a
+second pass of the same calls after the timed region. traffic is the HBM
+bytes per launch from the FETCH_SIZE / WRITE_SIZE counters, scaled by a
+plain copy's (profiles/), or null when the kernel's code changed since.
 
 cpu_baseline times the CPU oracle (single thread) on the same workload.
 """
@@ -39,10 +48,14 @@ INPUT_BYTES = 2 * N                      # BF16
 FP4_BYTES = N // 2                        # per orientation
 SCALE_BYTES = N // 16                     # per orientation
 AMAX_BYTES = 4
-# whole call: input read twice (amax pass + cast), both outputs, both scales, two amaxes
+# whole call, the method's bytes: input read twice (amax reduction + cast),
+# both outputs, both scales, two amaxes
 B_ALG_CALL = 2 * INPUT_BYTES + 2 * FP4_BYTES + 2 * SCALE_BYTES + 2 * AMAX_BYTES
-# cast kernel alone: one input read, both outputs and scales, the two amax words
-B_ALG_CAST = INPUT_BYTES + 2 * FP4_BYTES + 2 * SCALE_BYTES + 2 * AMAX_BYTES
+# one input read, both outputs and scales, the two amax words: the least any
+# call moves, and the algorithmic bytes of the two-pass form's cast kernel
+B_MIN = INPUT_BYTES + 2 * FP4_BYTES + 2 * SCALE_BYTES + 2 * AMAX_BYTES
+B_ALG_CAST = B_MIN
+EPOCH_WORD = 8256  # workspace word that advances once per single-pass call
 HBM_PEAK_GBS = 8000.0
 METRIC = "NVFP4 quantize HBM GB/s and % of peak, 8192x5120 BF16, row+col output"
 WORKLOAD = "8192x5120 BF16 N(0,1) x per-column 10^(-3+5u) (seed 1); 16x16 blocks; row+col FP4; " \
@@ -128,6 +141,11 @@ def summarize_trace(db_path, workload="c2"):
             spans.append(b[2] - a[1])
         else:
             evented.append(b[2] - b[1])
+    resident = [e - s for k, s, e in rows if k.startswith("k_cast_rt_resident")]
+    if resident and workload == "c2":
+        med = st.median(resident)
+        print(f"\nsingle-pass calls (one kernel each): {len(resident)}, average {st.mean(resident):.0f} ns, "
+              f"median {med:.0f} ns -> {B_ALG_CALL / med:.1f} GB/s on B_alg, {B_MIN / med:.1f} GB/s on B_min")
     for name, v in (("k_cast in calls without timing events", plain), ("k_cast in calls with timing events", evented)):
         if v:
             print(f"\n{name}: {len(v)} launches, average {st.mean(v):.0f} ns, median {st.median(v):.0f} ns")
@@ -176,9 +194,9 @@ def record_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db):
     write_factor = INPUT_BYTES / cw
     f = _median_counter(fetch_db, "k_cast", "FETCH_SIZE") * 1024.0 * fetch_factor
     w = _median_counter(write_db, "k_cast", "WRITE_SIZE") * 1024.0 * write_factor
-    out = {"kernel": "k_cast_rt<bf16,16x16,rne>", "workload": "8192x5120 bf16 2d swizzled",
+    out = {"kernel": "k_cast_rt_resident<bf16,16x16,rne,5 tiles>", "workload": "8192x5120 bf16 2d swizzled",
            "fetch_bytes": round(f), "write_bytes": round(w), "bytes_per_launch": round(f + w),
-           "algorithmic_bytes_per_launch": B_ALG_CAST, "fetch_factor": round(fetch_factor, 5),
+           "algorithmic_bytes_per_launch": B_ALG_CALL, "min_bytes_per_launch": B_MIN, "fetch_factor": round(fetch_factor, 5),
            "write_factor": round(write_factor, 5), "source_sha256": cast_source_hash()}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
@@ -495,6 +513,8 @@ def main():
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel-only", action="store_true",
+                   help="only the timed calls of the default path, nothing else (for counter runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of the input size (80 MiB read + 80 MiB write), "
                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -549,31 +569,38 @@ def main():
     cfg = nv.make_config(block_2d=True, swizzled=True, workspace=workspace)
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        x, row, col = sets[i % N_SETS]
-        nv.nvfp4_quantize(x, row, col, cfg, stream)
+    def timed_calls(c, steps, warmup):
+        for i in range(warmup):
+            x, row, col = sets[i % N_SETS]
+            nv.nvfp4_quantize(x, row, col, c, stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            x, row, col = sets[i % N_SETS]
+            nv.nvfp4_quantize(x, row, col, c, stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    epoch0 = int(workspace[EPOCH_WORD * 4:EPOCH_WORD * 4 + 4].view(torch.int32).item())
+    ms_per_step = timed_calls(cfg, args.steps, args.warmup)
+    single = int(workspace[EPOCH_WORD * 4:EPOCH_WORD * 4 + 4].view(torch.int32).item()) != epoch0
+    if args.kernel_only:
+        return
+    two_pass_ms = timed_calls(nv.make_config(block_2d=True, swizzled=True, workspace=workspace,
+                                             amax_path=nv.NVFP4_AMAX_PATH_TWO_PASS), args.steps, args.warmup)
 
     # Dominant kernel: the same calls again, with the library recording a
-    # pair of HIP events on the call's stream around the cast kernel's launch
-    # (nvfp4_config_t.cast_events), so the cast is timed inside whole calls.
+    # pair of HIP events on the call's stream around the launch of the
+    # single-pass kernel (or of the cast kernel of the two-pass form),
+    # nvfp4_config_t.cast_events, so the kernel is timed inside whole calls.
     # The events are timing-only (hipEventDisableSystemFence): without the
-    # system-scope cache writeback of an ordinary event, the marker between
-    # the two kernels costs little.
+    # system-scope cache writeback of an ordinary event, a marker costs little.
     cast_ms = time_cast_in_calls(nv, torch, cfg, sets, stream, args.steps)
-    achieved = B_ALG_CAST / (cast_ms * 1e-3) / 1e9
+    kernel_bytes = B_ALG_CALL if single else B_ALG_CAST
+    achieved = kernel_bytes / (cast_ms * 1e-3) / 1e9
 
     value = B_ALG_CALL / (ms_per_step * 1e-3) / 1e9
+    value_min = B_MIN / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -589,12 +616,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "rows": ROWS, "cols": COLS, "input_dtype": "bf16",
                    "block": "16x16", "scales": "e4m3 gemm-swizzled", "rounding": "rne",
+                   "amax_path": "single pass (one launch)" if single else "two pass (amax pass + cast)",
                    "bytes_per_call": B_ALG_CALL, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "buffer_sets_rotated": N_SETS},
-        "roofline": {"bound": "hbm", "kernel": "k_cast_rt<bf16,16x16,rne> (fused cast-transpose)",
+                   "bytes_per_call_min": B_MIN, "GBps_min_bytes": round(value_min, 2),
+                   "pct_of_hbm_peak_min_bytes": round(100 * value_min / HBM_PEAK_GBS, 2),
+                   "two_pass_ms_per_call": round(two_pass_ms, 6), "buffer_sets_rotated": N_SETS},
+        "roofline": {"bound": "hbm",
+                     "kernel": ("k_cast_rt_resident<bf16,16x16,rne,5 tiles> (single-pass quantize)" if single
+                                else "k_cast_rt<bf16,16x16,rne> (fused cast-transpose)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": B_ALG_CAST, "avg_launch_ms": round(cast_ms, 6)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "frac_min_bytes": round(B_MIN / (cast_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(), "bytes_per_launch": kernel_bytes,
+                     "avg_launch_ms": round(cast_ms, 6)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x_host)

@@ -74,6 +74,20 @@ typedef enum {
                            saturating. The global scale numerator becomes 6 * 61440. */
 } nvfp4_scale_fmt_t;
 
+typedef enum {
+  /* the single-pass form where it fits and measured faster (16x16 blocks;
+   * 1x16 blocks up to 2 x 128 x 128 elements per CU), else the two-pass
+   * form */
+  NVFP4_AMAX_PATH_AUTO = 0,
+  /* always the amax pass and the cast kernel (two launches) */
+  NVFP4_AMAX_PATH_TWO_PASS = 1,
+  /* the single-pass form whenever every 128x128 tile fits in the registers
+   * of the workgroups that can be resident at once (BF16: up to 5 tiles per
+   * workgroup, 4 with 16x16 blocks and stochastic rounding; FP32: one; at
+   * most 4 workgroups per CU), else the two-pass form */
+  NVFP4_AMAX_PATH_SINGLE_PASS = 2
+} nvfp4_amax_path_t;
+
 /* One orientation of an NVFP4 tensor. For the row-wise orientation of an
  * R x C input, n = R and k = C; for the column-wise one, n = C and k = R
  * (row j of the column-wise tensor is column j of the input).
@@ -139,12 +153,22 @@ typedef struct {
   const float *noop;
   /* nvfp4_quantize with compute_amax == 1 and a per-tensor amax only (not
    * row_scaled): NULL, or device memory of at least NVFP4_WORKSPACE_BYTES
-   * bytes, 16-byte aligned, owned by the caller. With a workspace the amax
-   * pass stores one maximum per workgroup there and the cast kernel
-   * finishes the reduction and writes the amax buffers, so the call needs
-   * neither the zeroing pass nor atomics (two launches instead of three).
-   * With NULL the amax buffers are zeroed and reduced with atomics. The
-   * contents on entry do not matter and are unspecified on return; calls
+   * bytes, 16-byte aligned, owned by the caller, zero-filled before its
+   * first use. With a workspace the call takes one of two forms:
+   *   single pass (one launch; not with the RHT; see amax_path): each
+   *     workgroup loads its tiles into registers, publishes its maximum in
+   *     the workspace, waits (bounded) until every workgroup has published,
+   *     and encodes from registers, so the input is read once;
+   *   two pass: the amax pass stores one maximum per workgroup there and
+   *     the cast kernel finishes the reduction and writes the amax buffers
+   *     (two launches, no zeroing pass, no atomics).
+   * With NULL the amax buffers are zeroed and reduced with atomics (three
+   * launches). The first 16 KiB of the workspace are scratch (contents on
+   * entry do not matter). The rest holds the single-pass handoff: one
+   * tagged slot per workgroup, an epoch and exit counters, which every call
+   * leaves ready for the next; it must be zero on first use and must not be
+   * written by anything else (a workspace that breaks this still gives
+   * correct results, but each call then falls back to slow reads). Calls
    * that share a workspace must not run concurrently (queue them on one
    * stream). Ignored by the other calls and paths. */
   void *workspace;
@@ -154,10 +178,14 @@ typedef struct {
    * the kernel can be timed inside a whole call. Not recorded when the call
    * is rejected or the input is empty. */
   void *const *cast_events;
+  /* nvfp4_amax_path_t; nvfp4_quantize with a workspace, compute_amax == 1,
+   * a per-tensor amax and no RHT (ignored otherwise). Every path gives the
+   * same bytes. */
+  uint32_t amax_path;
 } nvfp4_config_t;
 
 /* Bytes of the optional quantize workspace (nvfp4_config_t.workspace). */
-#define NVFP4_WORKSPACE_BYTES 16384u
+#define NVFP4_WORKSPACE_BYTES 36864u
 
 /* NVFP4_WORKSPACE_BYTES, for bindings that cannot read the macro. */
 uint64_t nvfp4_workspace_bytes(void);
@@ -293,6 +321,16 @@ nvfp4_status_t nvfp4_debug_rht_colwise(const void *x, nvfp4_dtype_t dtype, int64
  */
 nvfp4_status_t nvfp4_debug_e2m1_pack(const float *v, const uint32_t *r, uint8_t *out, int64_t n, uint32_t flags,
                                      void *stream);
+
+/*
+ * Test hook: the bound, in ticks of the GPU's 100 MHz real-time counter, on
+ * how long a workgroup of the single-pass quantize waits for the others to
+ * publish their maxima before it takes the maximum of the whole input
+ * itself (same result, more reads). 0 restores the default (2,000,000
+ * ticks, 20 ms); 1 makes nearly every wait run out, so that tests can check
+ * that path. Process-wide; takes effect for launches queued afterwards.
+ */
+nvfp4_status_t nvfp4_debug_set_wait_ticks(uint32_t ticks);
 
 #ifdef __cplusplus
 }

@@ -41,6 +41,10 @@ NVFP4_SCALES_GEMM_SWIZZLED = 1
 NVFP4_SCALE_E4M3 = 0
 NVFP4_SCALE_UE5M3 = 1
 
+NVFP4_AMAX_PATH_AUTO = 0
+NVFP4_AMAX_PATH_TWO_PASS = 1
+NVFP4_AMAX_PATH_SINGLE_PASS = 2
+
 NVFP4_DEBUG_SR = 1
 NVFP4_DEBUG_PAIRWISE = 2
 
@@ -48,7 +52,7 @@ NVFP4_MAX_GROUPS = 256
 
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
             "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes", "nvfp4_quantize_grouped",
-            "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack")
+            "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack", "nvfp4_debug_set_wait_ticks")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -70,6 +74,7 @@ class nvfp4_config_t(ctypes.Structure):
         ("noop", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("cast_events", ctypes.c_void_p),
+        ("amax_path", ctypes.c_uint32),
     ]
 
 
@@ -123,6 +128,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_debug_rht_colwise.argtypes = [P, I, I64, I64, U32, P, P]
     lib.nvfp4_debug_e2m1_pack.restype = I
     lib.nvfp4_debug_e2m1_pack.argtypes = [P, P, P, I64, U32, P]
+    lib.nvfp4_debug_set_wait_ticks.restype = I
+    lib.nvfp4_debug_set_wait_ticks.argtypes = [U32]
     _lib = lib
     return lib
 
@@ -176,7 +183,7 @@ def _need_orientation(o, n: int, k: int, amax_len: int, what: str) -> None:
 def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, stochastic=False, sr_seed=0,
                 row_scaled=False, rht=False, rht_sign_mask=0, compute_amax=True,
                 noop: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                rht_bf16=False) -> nvfp4_config_t:
+                rht_bf16=False, amax_path=0) -> nvfp4_config_t:
     """The config struct. It holds references to the noop and workspace
     tensors (a copy made with from_buffer_copy does not: keep them alive
     while such a copy is used)."""
@@ -190,6 +197,7 @@ def make_config(*, block_2d=False, swizzled=False, scale_fmt=NVFP4_SCALE_E4M3, s
                          int(rht_sign_mask) & 0xFFFFFFFF, int(rht_bf16), int(compute_amax),
                          None if noop is None else noop.data_ptr(),
                          None if workspace is None else workspace.data_ptr())
+    cfg.amax_path = int(amax_path)
     cfg._tensors = (noop, workspace)
     return cfg
 
@@ -331,29 +339,55 @@ def empty_orientation(n: int, k: int, device, amax_len: int = 1) -> Orientation:
 
 
 def empty_workspace(device) -> torch.Tensor:
-    """An (uninitialized) quantize workspace; torch's allocator aligns it to 512 bytes."""
-    return torch.empty((nvfp4_workspace_bytes(),), dtype=torch.uint8, device=device)
+    """A zero-filled quantize workspace, as its first use needs (torch's
+    allocator aligns it to 512 bytes). Reuse it for later calls on one stream:
+    the library keeps its arrival counters valid from call to call."""
+    return torch.zeros((nvfp4_workspace_bytes(),), dtype=torch.uint8, device=device)
+
+
+_workspaces = {}
+
+
+def stream_workspace(device, stream=None) -> torch.Tensor:
+    """The workspace that quantize() uses for calls on (device, stream): made
+    once, zero-filled, then reused, so that a call costs no extra launch.
+    Calls on one stream run in order, so they never share it concurrently."""
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    if stream is None:
+        handle = torch.cuda.current_stream(dev).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        handle = stream.cuda_stream
+    else:
+        handle = int(stream)
+    key = (dev.index, handle)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = empty_workspace(dev)
+        _workspaces[key] = ws
+    return ws
+
+
+def nvfp4_debug_set_wait_ticks(ticks: int) -> None:
+    _check(load().nvfp4_debug_set_wait_ticks(int(ticks) & 0xFFFFFFFF))
 
 
 def quantize(x: torch.Tensor, *, rowwise=True, columnwise=True, cfg: Optional[nvfp4_config_t] = None,
              stream=None, use_workspace: bool = True):
     """Allocate outputs for x [R][C] and run nvfp4_quantize. Returns (row, col).
 
-    With use_workspace (and no workspace in cfg) a workspace is allocated for
-    the call, so a computed per-tensor amax takes two launches instead of
-    three; torch's stream-ordered allocator keeps it valid until the call's
-    work is done."""
+    With use_workspace (and no workspace in cfg) the stream's cached
+    workspace is passed, so a computed per-tensor amax takes one launch
+    (single pass) or two instead of three."""
     rows, cols = _shape2d(x)
     cfg = cfg if cfg is not None else make_config()
     row = empty_orientation(rows, cols, x.device, rows if cfg.row_scaled else 1) if rowwise else None
     col = empty_orientation(cols, rows, x.device) if columnwise else None
     ws = None
     if use_workspace and not cfg.workspace and cfg.compute_amax and not cfg.row_scaled:
-        ws = empty_workspace(x.device)
+        ws = stream_workspace(x.device, stream)
         cfg = nvfp4_config_t.from_buffer_copy(cfg)
         cfg.workspace = ws.data_ptr()
-        if stream is not None:  # keep the block from being reused before the call's stream is done
-            ws.record_stream(stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream)))
     nvfp4_quantize(x, row, col, cfg, stream)
-    del ws
     return row, col

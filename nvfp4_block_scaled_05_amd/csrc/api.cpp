@@ -87,6 +87,12 @@ nvfp4_status_t check_out(const nvfp4_out_t *o, const char *name, bool empty) {
 extern "C" const char *nvfp4_last_error(void) { return g_last_error.c_str(); }
 
 extern "C" uint64_t nvfp4_workspace_bytes(void) { return NVFP4_WORKSPACE_BYTES; }
+static_assert(NVFP4_WORKSPACE_BYTES == nvfp4::kWorkspaceWords * 4, "workspace layout and ABI size agree");
+
+extern "C" nvfp4_status_t nvfp4_debug_set_wait_ticks(uint32_t ticks) {
+  nvfp4::set_resident_wait_ticks(ticks);
+  return NVFP4_OK;
+}
 
 extern "C" uint64_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t scale_cols) {
   if (rows <= 0 || scale_cols <= 0 || rows >= (int64_t{1} << 32) || scale_cols >= (int64_t{1} << 32)) return 0;
@@ -167,6 +173,8 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   const bool swz = cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED;
   if (cfg.workspace != nullptr && !aligned(cfg.workspace, 16))
     return fail(NVFP4_ERR_ALIGN, "the workspace is not 16-byte aligned");
+  if (cfg.amax_path > NVFP4_AMAX_PATH_SINGLE_PASS)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown amax path %u", cfg.amax_path);
   if (cfg.row_scaled) {
     if (col) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 is row-wise only");
     if (cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 uses 1x16 blocks");
@@ -206,7 +214,13 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   // pass, which is all it needs.
   uint32_t *partials = nullptr;
   uint32_t npartials = 0;
-  if (cfg.compute_amax) {
+  // single pass: one launch that reads the input once (K tiles per workgroup)
+  const int resident_k = cfg.compute_amax && cfg.workspace != nullptr && !cfg.rht &&
+                                 cfg.amax_path != NVFP4_AMAX_PATH_TWO_PASS
+                             ? nvfp4::resident_plan(dtype, cfg.block_2d != 0, sr, R, C,
+                                                    cfg.amax_path == NVFP4_AMAX_PATH_AUTO)
+                             : 0;
+  if (cfg.compute_amax && resident_k == 0) {
     float *a = ra ? ra : ca;
     float *b = (ca == a) ? nullptr : ca;
     if (cfg.workspace != nullptr && rows * cols > 0) {
@@ -240,6 +254,13 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
                     rht_word(cfg), cfg.noop, partials, npartials};
   a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
+  if (resident_k > 0) {
+    if ((st = record(0)) != NVFP4_OK) return st;
+    st = hip_status(nvfp4::launch_cast_resident(a, static_cast<uint32_t *>(cfg.workspace), dtype,
+                                                cfg.block_2d != 0, sr, resident_k, s),
+                    "single-pass quantize launch");
+    return st != NVFP4_OK ? st : record(1);
+  }
   if ((st = record(0)) != NVFP4_OK) return st;
   st = hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
   return st != NVFP4_OK ? st : record(1);

@@ -24,6 +24,9 @@
 // stores (non-temporal, except the register-tile kernel's column-wise data
 // and compact scales, which merge in L2). Grouped forms of both run the
 // same tile code on the tiles of several row slices, one tensor per slice.
+#include <algorithm>
+#include <atomic>
+
 #include "codec.h"
 #include "launch.h"
 
@@ -75,7 +78,7 @@ __device__ __forceinline__ void workgroup_max(uint32_t (&m)[N], uint32_t *lds) {
 #pragma unroll
     for (int i = 0; i < N; ++i) lds[i * kWaves + (threadIdx.x >> 6)] = m[i];
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     m[i] = lds[i * kWaves];
@@ -239,41 +242,29 @@ __device__ __forceinline__ uint32_t piece_max(const uint32_t (&w)[RT<DT>::kWords
   return m;
 }
 
-template <int DT, bool B2D, bool SR>
-__device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
-  constexpr int W = RT<DT>::kWords;
-  __shared__ float lds_mult[2][256];                   // multiplier per scale code (row, col)
+// LDS of one register tile's encode.
+struct RtLds {
+  float mult[2][256];        // multiplier per scale code (row, col)
   // scale codes of the tile, row-wise [tile row][16-col block] and column-wise
   // [tile col][16-row block]; compact: line * 8 + block; swizzled: the two
   // 512-byte GEMM tiles that the 128 x 8 codes form, in memory order
-  __shared__ __align__(4) uint8_t lds_rs[kRT * 8];
-  __shared__ __align__(4) uint8_t lds_cs[kRT * 8];
-  __shared__ uint32_t lds_cw[16][kRT + 1];             // column-wise data words [row group][tile col]
-  __shared__ uint32_t lds_red[kWaves];
+  uint8_t rs[kRT * 8];
+  uint8_t cs[kRT * 8];
+  uint32_t cw[16][kRT + 1];  // column-wise data words [row group][tile col]
+  uint32_t red[kWaves];
+};
 
-  if (p.noop != nullptr && *p.noop == 1.0f) return;
-
-  const int tid = threadIdx.x;
-  const int ucol = tid & 15;
-  const int rg = tid >> 4;
-  const uint32_t r0 = ty * kRT;
-  const uint32_t c0 = tx * kRT;
-  const uint32_t col = c0 + 8 * ucol;
-  const uint32_t rbase = r0 + 8 * rg;
-  const bool col_ok = col < p.cols;
-  const bool do_row = p.row_data != nullptr;
-  const bool do_col = p.col_data != nullptr;
-
-  u32x4 part[kPartialVecs];
-  if (p.partials != nullptr) load_partials(p.partials, p.npartials, tid, part);
-
-  // Every thread issues all its loads without a branch, so that the wait for
-  // the workspace loads above does not have to wait for these too. In an
-  // edge tile, pieces outside the input load from a clamped address and are
-  // zeroed afterwards.
-  const bool interior = r0 + kRT <= p.rows && c0 + kRT <= p.cols;  // uniform
-  const uint32_t lcol = col_ok ? col : 0u;
-  uint32_t w[8][W];
+// Loads of the thread's 8 x 8 sub-tile of tile (r0, c0), issued without a
+// branch: in an edge tile, pieces outside the input load from a clamped
+// address (a value of the input, so the tile's maximum is unchanged) and are
+// zeroed by rt_clear_outside before the block maxima are taken.
+template <int DT>
+__device__ __forceinline__ void rt_load(const CastArgs &p, uint32_t r0, uint32_t c0,
+                                        uint32_t (&w)[8][RT<DT>::kWords]) {
+  constexpr int W = RT<DT>::kWords;
+  const uint32_t col = c0 + 8 * (threadIdx.x & 15);
+  const uint32_t rbase = r0 + 8 * (threadIdx.x >> 4);
+  const uint32_t lcol = col < p.cols ? col : 0u;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const uint32_t r = min(rbase + k, p.rows - 1);
@@ -288,22 +279,74 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
       w[k][4 * q + 3] = t.w;
     }
   }
+}
+
+// A mask rather than a branch: a per-lane branch around array stores makes
+// the compiler copy the whole register array through the branch.
+template <int DT>
+__device__ __forceinline__ void rt_clear_outside(const CastArgs &p, uint32_t r0, uint32_t c0,
+                                                 uint32_t (&w)[8][RT<DT>::kWords]) {
+  const uint32_t col = c0 + 8 * (threadIdx.x & 15);
+  const uint32_t rbase = r0 + 8 * (threadIdx.x >> 4);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t keep = 0u - static_cast<uint32_t>(col < p.cols && rbase + k < p.rows);
+#pragma unroll
+    for (int q = 0; q < RT<DT>::kWords; ++q) w[k][q] &= keep;
+  }
+}
+
+template <int DT, bool B2D, bool SR>
+__device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32_t ty,
+                                          uint32_t (&w)[8][RT<DT>::kWords], float S_row, float S_col, bool ue,
+                                          RtLds &sh);
+
+template <int DT, bool B2D, bool SR>
+__device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
+  constexpr int W = RT<DT>::kWords;
+  __shared__ RtLds sh;
+
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+
+  const int tid = threadIdx.x;
+  const uint32_t r0 = ty * kRT;
+  const uint32_t c0 = tx * kRT;
+
+  u32x4 part[kPartialVecs];
+  if (p.partials != nullptr) load_partials(p.partials, p.npartials, tid, part);
+
+  // Every thread issues all its loads without a branch, so that the wait for
+  // the workspace loads above does not have to wait for these too.
+  uint32_t w[8][W];
+  rt_load<DT>(p, r0, c0, w);
 
   float amax_row, amax_col;
-  amax_pair<false>(p, part, part, lds_red, (tx | ty) == 0, amax_row, amax_col);
+  amax_pair<false>(p, part, part, sh.red, (tx | ty) == 0, amax_row, amax_col);
   const bool ue = p.ue5m3 != 0;
-  const float S_row = do_row ? global_encode_scale(amax_row, ue) : 1.0f;
-  const float S_col = do_col ? global_encode_scale(amax_col, ue) : 1.0f;
-  fill_multipliers(lds_mult, tid, S_row, S_col, ue);
-  if (!interior) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (!(col_ok && rbase + k < p.rows)) {
-#pragma unroll
-        for (int q = 0; q < W; ++q) w[k][q] = 0;
-      }
-    }
-  }
+  const float S_row = p.row_data != nullptr ? global_encode_scale(amax_row, ue) : 1.0f;
+  const float S_col = p.col_data != nullptr ? global_encode_scale(amax_col, ue) : 1.0f;
+  fill_multipliers(sh.mult, tid, S_row, S_col, ue);
+  rt_clear_outside<DT>(p, r0, c0, w);
+  rt_encode<DT, B2D, SR>(p, tx, ty, w, S_row, S_col, ue, sh);
+}
+
+// Block scales, codes and stores of one tile whose values are in w (zero
+// outside the input) and whose multipliers are in sh.mult; sh.mult is read
+// only after the barrier below, so the caller may fill it right before.
+template <int DT, bool B2D, bool SR>
+__device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32_t ty,
+                                          uint32_t (&w)[8][RT<DT>::kWords], float S_row, float S_col, bool ue,
+                                          RtLds &sh) {
+  const int tid = threadIdx.x;
+  const int ucol = tid & 15;
+  const int rg = tid >> 4;
+  const uint32_t r0 = ty * kRT;
+  const uint32_t c0 = tx * kRT;
+  const uint32_t col = c0 + 8 * ucol;
+  const uint32_t rbase = r0 + 8 * rg;
+  const bool col_ok = col < p.cols;
+  const bool do_row = p.row_data != nullptr;
+  const bool do_col = p.col_data != nullptr;
 
   // ---- block scale codes ----
   uint32_t rcode[8], ccode[8];
@@ -380,19 +423,19 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
   };
   if (do_row && (ucol & 1) == 0) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) lds_rs[code_slot(8 * rg + k, ucol >> 1)] = static_cast<uint8_t>(rcode[k]);
+    for (int k = 0; k < 8; ++k) sh.rs[code_slot(8 * rg + k, ucol >> 1)] = static_cast<uint8_t>(rcode[k]);
   }
   if (do_col && (rg & 1) == 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) lds_cs[code_slot(8 * ucol + c, rg >> 1)] = static_cast<uint8_t>(ccode[c]);
+    for (int c = 0; c < 8; ++c) sh.cs[code_slot(8 * ucol + c, rg >> 1)] = static_cast<uint8_t>(ccode[c]);
   }
-  __syncthreads();
+  lds_barrier();
 
   float re[8], ce[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    re[k] = do_row ? lds_mult[0][rcode[k]] : 0.0f;
-    ce[k] = do_col ? lds_mult[1][ccode[k]] : 0.0f;
+    re[k] = do_row ? sh.mult[0][rcode[k]] : 0.0f;
+    ce[k] = do_col ? sh.mult[1][ccode[k]] : 0.0f;
   }
 
   // ---- encode: row pairs (2i, 2i+1) ----
@@ -458,11 +501,11 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
   }
   if (do_col) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) lds_cw[rg][8 * ucol + c] = colw[c];
+    for (int c = 0; c < 8; ++c) sh.cw[rg][8 * ucol + c] = colw[c];
   }
 
   if (do_col) {
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int e = tid + kThreads * it;
@@ -475,9 +518,9 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
         // tiles share 128-byte lines, which the caches can merge
         if (rr + 32 <= p.rows)
           *reinterpret_cast<u32x4 *>(dst) =
-              u32x4{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc], lds_cw[4 * h + 2][lc], lds_cw[4 * h + 3][lc]};
+              u32x4{sh.cw[4 * h][lc], sh.cw[4 * h + 1][lc], sh.cw[4 * h + 2][lc], sh.cw[4 * h + 3][lc]};
         else
-          *reinterpret_cast<u32x2 *>(dst) = u32x2{lds_cw[4 * h][lc], lds_cw[4 * h + 1][lc]};
+          *reinterpret_cast<u32x2 *>(dst) = u32x2{sh.cw[4 * h][lc], sh.cw[4 * h + 1][lc]};
       }
     }
   }
@@ -486,10 +529,10 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
     // the tile's codes are two whole GEMM tiles, 1 KiB contiguous per orientation
     // (swizzled shapes are multiples of 128, so every tile is complete)
     if (do_row)
-      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(lds_rs)[tid],
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(sh.rs)[tid],
                                   reinterpret_cast<uint32_t *>(p.row_scales + swizzled_scale_offset(r0, c0 >> 4, p.cols >> 4)) + tid);
     if (do_col)
-      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(lds_cs)[tid],
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t *>(sh.cs)[tid],
                                   reinterpret_cast<uint32_t *>(p.col_scales + swizzled_scale_offset(c0, r0 >> 4, p.rows >> 4)) + tid);
     return;
   }
@@ -501,7 +544,7 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
     const uint32_t scale_cols = p.cols >> 4;
     if (row < p.rows && sc < scale_cols)
       store_scale_group(p.row_scales, row, sc, scale_cols, false,
-                        reinterpret_cast<const uint32_t *>(lds_rs)[tid]);
+                        reinterpret_cast<const uint32_t *>(sh.rs)[tid]);
   }
   if (do_col) {
     const uint32_t j = c0 + t_line;
@@ -509,7 +552,7 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
     const uint32_t scale_cols = p.rows >> 4;
     if (j < p.cols && sc < scale_cols)
       store_scale_group(p.col_scales, j, sc, scale_cols, false,
-                        reinterpret_cast<const uint32_t *>(lds_cs)[tid]);
+                        reinterpret_cast<const uint32_t *>(sh.cs)[tid]);
   }
 }
 
@@ -805,6 +848,220 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   cast_rht_tile<DT, SR>(p, tx, ty);
 }
 
+// ---------------------------------------------------------------------------
+// Single-pass register-tile cast (per-tensor amax, no RHT).
+//
+// Every block scale depends on the amax of the whole input, so the
+// two-launch form reads the input twice: in the amax pass and in the cast.
+// Here each workgroup first loads its K tiles into registers (tiles
+// L = blockIdx.x + k * gridDim.x, k < K, in the launch order of k_cast_rt),
+// publishes the maximum of its tiles, waits until every workgroup of the
+// grid has published, and encodes its tiles from registers: the input is
+// read once. The host sizes the grid so that all of it can be resident at
+// once (at most the occupancy limit times the CU count). The waits are
+// bounded all the same: a workgroup that has waited wait_ticks ticks of the
+// 100 MHz real-time counter takes the maximum of the whole input itself, so
+// the kernel ends however the hardware schedules its workgroups, with the
+// same result.
+//
+// Handoff (workspace words in launch.h), with relaxed agent-scope atomic
+// loads and stores only: ordered read-modify-write atomics and fences at
+// agent scope write back or invalidate a whole L2 each, and with hundreds of
+// workgroups they cost tens of microseconds. Workgroup i stores
+// (e + 1) << 32 | max to its slot, e being the epoch read at the start.
+// The first workgroup of each group of kSlotGroup waits (one 64-lane load
+// per poll) until its members' slots carry the tag, then stores the group's
+// maximum, tagged, to the group slot; every workgroup waits for all group
+// slots (at most 32, one load per poll) and reduces them. No value of an
+// earlier call can pass for this call's: the epoch advances once per call,
+// when the last workgroup exits (exit counters at the end of the kernel, off
+// the critical path), so every workgroup of a call reads the same epoch,
+// even one that starts after others stopped waiting.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kDefaultWaitTicks = 2000000;  // 20 ms
+
+__device__ __forceinline__ uint32_t group_members(uint32_t G, uint32_t x) {
+  return (G - x + kBarGroups - 1) / kBarGroups;
+}
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent64(const uint32_t *p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent64(uint32_t *p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// max |x| bit pattern over the whole input, by one workgroup (the fallback
+// after a bounded wait ran out)
+template <int DT>
+__device__ uint32_t input_max(const CastArgs &p) {
+  const u32x4 *x = static_cast<const u32x4 *>(p.x);
+  const uint64_t nvec = static_cast<uint64_t>(p.rows) * p.cols * RT<DT>::kElem / 16;
+  uint32_t m = 0;
+  for (uint64_t i = threadIdx.x; i < nvec; i += kThreads) {
+    const u32x4 v = x[i];
+    if (DT == kBF16) {
+      ushort2_t h = {0, 0};
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.x & 0x7FFF7FFFu));
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.y & 0x7FFF7FFFu));
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.z & 0x7FFF7FFFu));
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.w & 0x7FFF7FFFu));
+      m = max(m, static_cast<uint32_t>(max(h.x, h.y)) << 16);
+    } else {
+      m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+  }
+  return m;
+}
+
+// Wave 0's part of the handoff: publish m, wait for the grid. Returns, in
+// lane 0, whether the wait succeeded and the grid's maximum. e, xb, xbt:
+// the epoch and the exit bases read at the start (lane 0).
+__device__ __forceinline__ bool handoff(uint32_t *ws, uint32_t m, uint32_t wait_ticks, uint32_t e, bool ok,
+                                        uint32_t &amax) {
+  const uint32_t G = gridDim.x, wg = blockIdx.x, lane = threadIdx.x;
+  const uint64_t tag = static_cast<uint64_t>(e + 1) << 32;
+  if (lane == 0) st_agent64(ws + kSlotWord + 2 * wg, tag | m);
+  const uint64_t t0 = wall_clock64();
+  if (ok && wg % kSlotGroup == 0) {  // the group's first workgroup
+    const uint32_t i = wg + lane;
+    uint64_t v;
+    for (;;) {
+      v = i < G ? ld_agent64(ws + kSlotWord + 2 * i) : tag;
+      if (__all((v >> 32) == (tag >> 32))) break;
+      if (wall_clock64() - t0 > wait_ticks) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const uint32_t gm = wave_max(static_cast<uint32_t>(v));
+    if (ok && lane == 0) st_agent64(ws + kGroupSlotWord + 2 * (wg / kSlotGroup), tag | gm);
+  }
+  const uint32_t ngroups = (G + kSlotGroup - 1) / kSlotGroup;
+  uint64_t v = 0;
+  while (ok) {
+    v = lane < ngroups ? ld_agent64(ws + kGroupSlotWord + 2 * lane) : tag;
+    if (__all((v >> 32) == (tag >> 32))) break;
+    if (wall_clock64() - t0 > wait_ticks) ok = false;
+    else __builtin_amdgcn_s_sleep(2);
+  }
+  amax = wave_max(static_cast<uint32_t>(v));
+  return ok;
+}
+
+template <int DT, bool B2D, bool SR, int K>
+__global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, uint32_t *ws, uint32_t wait_ticks) {
+  constexpr int W = RT<DT>::kWords;
+  __shared__ RtLds sh;
+  __shared__ uint32_t lds_ok, lds_amax;
+  __shared__ uint32_t lds_start[3];  // epoch, exit base of the group, exit base over the groups
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+
+  const int tid = threadIdx.x;
+  const uint32_t G = gridDim.x, wg = blockIdx.x;
+  const uint32_t tx_n = (p.cols + kRT - 1) / kRT, ty_n = (p.rows + kRT - 1) / kRT;
+  const uint32_t T = tx_n * ty_n;
+  const uint32_t xg = wg % kBarGroups;
+  const uint32_t nxg = min(G, kBarGroups);
+
+  // this call's epoch and exit bases, read before anything is published; a
+  // counter that is not in a state some call left means a workspace that
+  // was not zero-filled: then only the fallback is trusted
+  uint32_t e = 0;
+  bool sane = true;
+  if (tid == 0) {
+    e = ld_agent(ws + kEpochWord);
+    const uint32_t xb = ld_agent(ws + kExitBaseWord + xg * kBarLine);
+    const uint32_t xbt = ld_agent(ws + kExitTopBaseWord);
+    sane = ld_agent(ws + kExitWord + xg * kBarLine) - xb < group_members(G, xg) &&
+           ld_agent(ws + kExitTopWord) - xbt < nxg;
+    lds_start[0] = e;
+    lds_start[1] = xb;
+    lds_start[2] = xbt;
+  }
+
+  // ---- load every tile, maximum over them ----
+  uint32_t w[K][8][W];
+  uint32_t tile_x[K], tile_y[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    tile_x[k] = tile_y[k] = 0;
+    const uint32_t L = wg + k * G;
+    if (L < T) {
+      tile_xy(p, tile_index(p, L, T), tx_n, ty_n, tile_x[k], tile_y[k]);
+      rt_load<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
+    }
+  }
+  uint32_t m[1] = {0};
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (wg + k * G < T) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m[0] = max(m[0], piece_max<DT>(w[k][r]));
+    }
+  }
+  workgroup_max(m, sh.red);
+
+  // ---- publish, then wait for the whole grid (bounded) ----
+  if (tid < 64) {
+    uint32_t amax = 0;
+    const bool ok = handoff(ws, m[0], wait_ticks, __builtin_amdgcn_readfirstlane(e),
+                            __builtin_amdgcn_readfirstlane(sane ? 1u : 0u) != 0, amax);
+    if (tid == 0) {
+      lds_ok = ok ? 1u : 0u;
+      lds_amax = amax;
+    }
+  }
+  lds_barrier();
+
+  uint32_t a[1] = {lds_amax};
+  if (lds_ok == 0) {  // uniform
+    a[0] = input_max<DT>(p);
+    workgroup_max(a, sh.red);
+  }
+  const float amax = __uint_as_float(a[0]);
+  if (wg == 0 && tid == 0) {
+    if (p.row_amax) *p.row_amax = amax;
+    if (p.col_amax) *p.col_amax = amax;
+  }
+
+  // ---- encode from registers ----
+  const bool ue = p.ue5m3 != 0;
+  const float S_row = p.row_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
+  const float S_col = p.col_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
+  fill_multipliers(sh.mult, tid, S_row, S_col, ue);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (wg + k * G < T) {
+      if (k > 0) lds_barrier();  // the previous tile's LDS reads are done
+      rt_clear_outside<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
+      rt_encode<DT, B2D, SR>(p, tile_x[k], tile_y[k], w[k], S_row, S_col, ue, sh);
+    }
+  }
+
+  // ---- exit: the last workgroup of the grid advances the epoch ----
+  if (tid == 0) {
+    const uint32_t e = lds_start[0], xb = lds_start[1], xbt = lds_start[2];
+    const uint32_t old = __hip_atomic_fetch_add(ws + kExitWord + xg * kBarLine, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old - xb == group_members(G, xg) - 1) {
+      st_agent(ws + kExitBaseWord + xg * kBarLine, old + 1);
+      const uint32_t top = __hip_atomic_fetch_add(ws + kExitTopWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top - xbt == nxg - 1) {
+        st_agent(ws + kExitTopBaseWord, top + 1);
+        st_agent(ws + kEpochWord, e + 1);
+      }
+    }
+  }
+}
+
 // The arguments of group g's own tensor: its rows of the input, its blocks
 // of the concatenated outputs, its amax slots.
 template <int DT>
@@ -923,5 +1180,163 @@ hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bo
   if (a.rows == 0 || a.cols == 0) return hipSuccess;
   return dtype == kBF16 ? launch_dt<kBF16>(a, block_2d, rht, sr, s) : launch_dt<kFP32>(a, block_2d, rht, sr, s);
 }
+
+// ---- single-pass cast: plan and launch ----
+namespace {
+
+// Most tiles per workgroup: 32 VGPRs each (BF16); one more spills
+// registers (16x16 blocks with stochastic rounding: at 5). FP32 tiles take
+// 64 VGPRs: two per workgroup leave room for only two workgroups per CU,
+// which holds no more tiles than one per workgroup at four per CU.
+constexpr int kMaxKBf16 = 5;
+constexpr int kMaxKFp32 = 1;
+template <int DT, bool B2D, bool SR>
+constexpr int max_k() {
+  return DT == kFP32 ? kMaxKFp32 : (B2D && SR ? 4 : kMaxKBf16);
+}
+constexpr int kMaxDevices = 64;
+std::atomic<uint32_t> g_wait_ticks{0};
+
+template <int DT, bool B2D, bool SR, int K>
+const void *resident_kernel() {
+  return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, K>);
+}
+
+template <int DT, bool B2D, bool SR>
+const void *resident_kernel_k(int K) {
+  constexpr int kmax = max_k<DT, B2D, SR>();
+  if (K == 1) return resident_kernel<DT, B2D, SR, 1>();
+  if constexpr (kmax >= 4) {
+    if (K == 2) return resident_kernel<DT, B2D, SR, 2>();
+    switch (K) {
+      case 3: return resident_kernel<DT, B2D, SR, 3>();
+      case 4: return resident_kernel<DT, B2D, SR, 4>();
+    }
+  }
+  if constexpr (kmax >= 5) {
+    if (K == 5) return resident_kernel<DT, B2D, SR, 5>();
+  }
+  return nullptr;
+}
+
+const void *resident_kernel_for(int dtype, bool b2d, bool sr, int K) {
+  if (dtype == kBF16) {
+    if (b2d) return sr ? resident_kernel_k<kBF16, true, true>(K) : resident_kernel_k<kBF16, true, false>(K);
+    return sr ? resident_kernel_k<kBF16, false, true>(K) : resident_kernel_k<kBF16, false, false>(K);
+  }
+  if (b2d) return sr ? resident_kernel_k<kFP32, true, true>(K) : resident_kernel_k<kFP32, true, false>(K);
+  return sr ? resident_kernel_k<kFP32, false, true>(K) : resident_kernel_k<kFP32, false, false>(K);
+}
+
+// Workgroups of one kernel that may run at once: the occupancy limit per CU,
+// but at most kMaxResidentPerCu, times the CU count; cached per device, 0
+// when the runtime cannot tell. Grids at the full occupancy limit (6
+// workgroups per CU for the 1x16 kernel with one tile) were measured not to
+// be resident all at once, so that the waits ran out; grids of 2 to 4 per CU
+// were.
+constexpr int kMaxResidentPerCu = 4;
+
+uint32_t resident_capacity(int dtype, bool b2d, bool sr, int K) {
+  static std::atomic<int32_t> cache[kMaxDevices][2][2][2][kMaxKBf16 + 1];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::atomic<int32_t> &slot = cache[dev][dtype][b2d][sr][K];
+  int32_t v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    const void *f = resident_kernel_for(dtype, b2d, sr, K);
+    if (f == nullptr || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      per_cu = cus = 0;
+    v = per_cu > 0 && cus > 0 ? std::min(per_cu, kMaxResidentPerCu) * cus : -1;
+    slot.store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? static_cast<uint32_t>(v) : 0u;
+}
+
+// CU count of the current device (0 when the runtime cannot tell)
+uint32_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus > 0 ? static_cast<uint32_t>(cus) : 0u;
+}
+
+uint32_t resident_grid(uint32_t tiles, int K) {
+  const uint32_t g = (tiles + K - 1) / K;
+  return (g + kBarGroups - 1) / kBarGroups * kBarGroups;
+}
+
+template <int DT, bool B2D, bool SR>
+hipError_t launch_resident_k(const CastArgs &a, uint32_t *ws, uint32_t G, int K, uint32_t ticks, hipStream_t s) {
+  const dim3 grid(G), block(kThreads);
+  switch (K) {
+    case 1: hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 1>), grid, block, 0, s, a, ws, ticks); break;
+    default: {
+      constexpr int kmax = max_k<DT, B2D, SR>();
+      if constexpr (kmax >= 4) {
+        if (K == 2) {
+          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 2>), grid, block, 0, s, a, ws, ticks);
+          break;
+        }
+        if (K == 3) {
+          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 3>), grid, block, 0, s, a, ws, ticks);
+          break;
+        }
+        if (K == 4) {
+          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 4>), grid, block, 0, s, a, ws, ticks);
+          break;
+        }
+      }
+      if constexpr (kmax >= 5) {
+        if (K == 5) {
+          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 5>), grid, block, 0, s, a, ws, ticks);
+          break;
+        }
+      }
+      return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster) {
+  if (rows == 0 || cols == 0) return 0;
+  const uint32_t tiles = ((rows + kRT - 1) / kRT) * ((cols + kRT - 1) / kRT);
+  // 1x16 blocks encode several times more block scales than 16x16 blocks;
+  // with the tiles held in registers only two workgroups per CU run that
+  // work, and beyond two tiles per CU the two-launch form measured faster
+  // (8192x5120: 40.4 vs 44.4 us; 2048x2048: 14.2 vs 12.4 us)
+  if (when_faster && !block_2d && tiles > 2 * device_cus()) return 0;
+  const int kmax = dtype == kBF16 ? kMaxKBf16 : kMaxKFp32;
+  for (int K = 1; K <= kmax; ++K) {
+    const uint32_t G = resident_grid(tiles, K);
+    if (G <= kMaxPartials && G <= resident_capacity(dtype, block_2d, sr, K)) return K;
+  }
+  return 0;
+}
+
+hipError_t launch_cast_resident(const CastArgs &a, uint32_t *ws, int dtype, bool block_2d, bool sr, int K,
+                                hipStream_t s) {
+  const uint32_t tiles = ((a.rows + kRT - 1) / kRT) * ((a.cols + kRT - 1) / kRT);
+  const uint32_t G = resident_grid(tiles, K);
+  const uint32_t t = g_wait_ticks.load(std::memory_order_relaxed);
+  const uint32_t ticks = t != 0 ? t : kDefaultWaitTicks;
+  if (dtype == kBF16) {
+    if (block_2d) return sr ? launch_resident_k<kBF16, true, true>(a, ws, G, K, ticks, s)
+                            : launch_resident_k<kBF16, true, false>(a, ws, G, K, ticks, s);
+    return sr ? launch_resident_k<kBF16, false, true>(a, ws, G, K, ticks, s)
+              : launch_resident_k<kBF16, false, false>(a, ws, G, K, ticks, s);
+  }
+  if (block_2d) return sr ? launch_resident_k<kFP32, true, true>(a, ws, G, K, ticks, s)
+                          : launch_resident_k<kFP32, true, false>(a, ws, G, K, ticks, s);
+  return sr ? launch_resident_k<kFP32, false, true>(a, ws, G, K, ticks, s)
+            : launch_resident_k<kFP32, false, false>(a, ws, G, K, ticks, s);
+}
+
+void set_resident_wait_ticks(uint32_t ticks) { g_wait_ticks.store(ticks, std::memory_order_relaxed); }
 
 }  // namespace nvfp4

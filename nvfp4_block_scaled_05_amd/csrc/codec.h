@@ -302,6 +302,16 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t x, int s) {
 // Maximum over the wave, uniform: DPP steps leave each row of 16 lanes with
 // its maximum (quad xor 1, quad xor 2, half-row mirror, row mirror), then the
 // four rows are read out as scalars.
+// Workgroup barrier that orders LDS accesses only. __syncthreads() is also a
+// workgroup-scope fence on global memory, which makes every wave wait until
+// all of its global stores have completed: a barrier that follows output
+// stores would then stall for their whole round trip to memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   v = max(v, dpp_mov<kQuadXor1>(v));
   v = max(v, dpp_mov<kQuadXor2>(v));

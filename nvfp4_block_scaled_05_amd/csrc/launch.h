@@ -21,7 +21,34 @@ constexpr uint32_t kMaxPartials = 2048;
 // RHT kernels to round the transformed values to BF16.
 constexpr uint32_t kRhtBf16 = 1u << 16;
 constexpr uint32_t kPartialsGrain = 4;
-static_assert(2 * kMaxPartials * 4 == 16384, "workspace size is part of the ABI");
+
+// Grid-wide handoff of the single-pass cast, in the workspace after the two
+// partials arrays (word offsets):
+//   kSlotWord       one 64-bit slot per workgroup (at most kMaxPartials):
+//                   tag << 32 | the workgroup's maximum;
+//   kGroupSlotWord  one 64-bit slot per group of kSlotGroup workgroups, with
+//                   the group's maximum, written by its first workgroup;
+//   kEpochWord      the epoch e: a call tags its slots e + 1;
+//   kExitWord, kExitBaseWord, kExitTopWord, kExitTopBaseWord
+//                   exit counters (per group of workgroups blockIdx.x mod
+//                   kBarGroups, then over the groups) and their values when
+//                   the call began; the last workgroup to exit advances the
+//                   epoch. Each counter sits in a 128-byte line of its own.
+// All of it must be zero before a workspace is first used; every call
+// leaves the counters equal to their bases, ready for the next call.
+constexpr uint32_t kBarGroups = 8;
+constexpr uint32_t kBarLine = 32;  // words per line
+constexpr uint32_t kSlotGroup = 64;
+constexpr uint32_t kSlotWord = 2 * kMaxPartials;
+constexpr uint32_t kGroupSlotWord = kSlotWord + 2 * kMaxPartials;
+constexpr uint32_t kEpochWord = kGroupSlotWord + 2 * (kMaxPartials / kSlotGroup);
+constexpr uint32_t kExitWord = kEpochWord + kBarLine;
+constexpr uint32_t kExitBaseWord = kExitWord + kBarGroups * kBarLine;
+constexpr uint32_t kExitTopWord = kExitBaseWord + kBarGroups * kBarLine;
+constexpr uint32_t kExitTopBaseWord = kExitTopWord + kBarLine;
+constexpr uint32_t kWorkspaceWords = 9216;
+static_assert(kExitTopBaseWord + kBarLine <= kWorkspaceWords, "handoff words fit the workspace");
+static_assert(kWorkspaceWords * 4 == 36864, "workspace size is part of the ABI");
 
 // Arguments of the fused cast(-transpose) kernels. A direction whose data
 // pointer is NULL is not written.
@@ -66,6 +93,20 @@ hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t col
                            float *row_amax, float *col_amax, uint32_t *partials, uint32_t *npartials,
                            const float *noop, hipStream_t s);
 hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
+// Single-pass quantize with a per-tensor amax: one launch that loads every
+// tile into registers, reduces the amax through the workspace's barrier words
+// and encodes from registers. resident_plan gives the tiles per workgroup, K,
+// or 0 when the tiles of this shape do not fit in the registers of the
+// workgroups that can be resident at once, or (when_faster) where the
+// two-launch form measured faster (the caller then takes the amax pass and
+// launch_cast); launch_cast_resident launches with that K.
+int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster);
+hipError_t launch_cast_resident(const CastArgs &a, uint32_t *workspace, int dtype, bool block_2d, bool sr, int K,
+                                hipStream_t s);
+// Bound on the handoff wait, in ticks of the 100 MHz real-time counter; after
+// it a workgroup computes the amax from the whole input itself. 0 restores
+// the default.
+void set_resident_wait_ticks(uint32_t ticks);
 
 // Grouped forms. row_start: host array of ngroups + 1 prefix sums of the
 // groups' row counts (validated by the caller). `a` describes the whole

@@ -24,8 +24,8 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 def run_quantize(x: np.ndarray, *, rowwise=True, columnwise=True, use_workspace=True, **cfg_kw):
     """Quantize on the GPU; returns a dict shaped like oracle.quantize()'s.
-    use_workspace: reduce a computed amax through a workspace (two launches)
-    rather than the zeroing pass and atomics (three)."""
+    use_workspace: reduce a computed amax through a workspace (one launch or
+    two, by amax_path) rather than the zeroing pass and atomics (three)."""
     xd = to_device(x)
     cfg = nv.make_config(**cfg_kw)
     row, col = nv.quantize(xd, rowwise=rowwise, columnwise=columnwise, cfg=cfg, use_workspace=use_workspace)

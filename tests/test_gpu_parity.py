@@ -37,9 +37,10 @@ def assert_matches(got, ref, *, swizzled=False, what=""):
 
 
 def check(x, *, rowwise=True, columnwise=True, swizzled=False, block_2d=False, stochastic=False, sr_seed=0,
-          row_scaled=False, use_workspace=True, what=""):
+          row_scaled=False, use_workspace=True, amax_path=0, what=""):
     got = run_quantize(x, rowwise=rowwise, columnwise=columnwise, swizzled=swizzled, block_2d=block_2d,
-                       stochastic=stochastic, sr_seed=sr_seed, row_scaled=row_scaled, use_workspace=use_workspace)
+                       stochastic=stochastic, sr_seed=sr_seed, row_scaled=row_scaled, use_workspace=use_workspace,
+                       amax_path=amax_path)
     ref = O.quantize(x, rowwise=rowwise, columnwise=columnwise, block_2d=block_2d, stochastic=stochastic,
                      sr_seed=sr_seed, row_scaled=row_scaled)
     assert_matches(got, ref, swizzled=swizzled, what=what)
@@ -394,7 +395,7 @@ def test_deterministic_across_runs():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("case", ["1d", "2d_swizzled", "fp32_ragged", "row_only", "col_only", "sr"])
-@pytest.mark.parametrize("use_workspace", [True, False])
+@pytest.mark.parametrize("use_workspace", [True, False, "two_pass", "single_pass"])
 def test_amax_reduction_paths(case, use_workspace):
     if case == "1d":
         x, kw = W.c1(), {}
@@ -408,6 +409,9 @@ def test_amax_reduction_paths(case, use_workspace):
         x, kw = W.randn_bf16(96, 272, 93), dict(rowwise=False)
     else:
         x, kw = W.randn_bf16(256, 512, 94), dict(stochastic=True, sr_seed=11)
+    if use_workspace in ("two_pass", "single_pass"):
+        path = nv.NVFP4_AMAX_PATH_TWO_PASS if use_workspace == "two_pass" else nv.NVFP4_AMAX_PATH_SINGLE_PASS
+        use_workspace, kw = True, dict(kw, amax_path=path)
     check(x, use_workspace=use_workspace, what=f"{case} workspace={use_workspace}", **kw)
 
 
@@ -463,7 +467,11 @@ def test_workspace_when_workgroups_loop(case):
     assert with_ws[2][0] == 1000.0
 
 
-@pytest.mark.parametrize("mode", ["2d_swizzled", "1d_sr", "rht", "rowscaled", "2d_swizzled_ws", "rht_ws"])
+SCRATCH_BYTES = 16384  # the workspace's partials arrays; the arrival counters follow
+
+
+@pytest.mark.parametrize("mode", ["2d_swizzled", "1d_sr", "rht", "rowscaled", "2d_swizzled_ws", "rht_ws",
+                                  "2d_swizzled_ws_two_pass", "1d_ws_single_pass"])
 def test_graph_capture_replays_match_eager(mode):
     # The calls queue kernels only (no memset, no allocation, no sync), so a
     # captured graph must reproduce the eager result on every replay, with
@@ -476,7 +484,10 @@ def test_graph_capture_replays_match_eager(mode):
            "rht": nv.make_config(rht=True, rht_sign_mask=0x9A5C),
            "rowscaled": nv.make_config(row_scaled=True),
            "2d_swizzled_ws": nv.make_config(block_2d=True, swizzled=True, workspace=ws),
-           "rht_ws": nv.make_config(rht=True, rht_sign_mask=0x9A5C, workspace=ws)}[mode]
+           "rht_ws": nv.make_config(rht=True, rht_sign_mask=0x9A5C, workspace=ws),
+           "2d_swizzled_ws_two_pass": nv.make_config(block_2d=True, swizzled=True, workspace=ws,
+                                                     amax_path=nv.NVFP4_AMAX_PATH_TWO_PASS),
+           "1d_ws_single_pass": nv.make_config(workspace=ws, amax_path=nv.NVFP4_AMAX_PATH_SINGLE_PASS)}[mode]
     rs = mode == "rowscaled"
     row = nv.empty_orientation(256, 384, DEV, 256 if rs else 1)
     col = None if rs else nv.empty_orientation(384, 256, DEV)
@@ -491,7 +502,7 @@ def test_graph_capture_replays_match_eager(mode):
         nv.nvfp4_quantize(xd, row, col, cfg, s)
     torch.cuda.synchronize()
     for rep in range(3):
-        for t in outs + [ws]:
+        for t in outs + [ws[:SCRATCH_BYTES]]:  # the workspace's scratch part, not its arrival counters
             t.view(torch.uint8).fill_(0x33 + rep)  # eager work between replays
         torch.cuda.synchronize()
         g.replay()

@@ -1,0 +1,184 @@
+"""Single-pass quantize: one launch in which every workgroup holds its tiles
+in registers across a grid-wide handoff of the per-tensor amax through the
+workspace. Checked bit for bit against the oracle and against the two-pass
+form (amax pass + cast), on shapes that give 1 to 5 tiles per workgroup,
+ragged edges, every output choice, one workspace reused across grid sizes,
+the bounded wait forced to run out (each workgroup then reads the whole
+input for the amax), and noop.
+
+The workspace's exit counters and their bases (words 8288 + 32 x and
+8544 + 32 x, x = 0..7; 8800 and 8832 over the groups) must be equal after
+every call, and the epoch (word 8256) must have advanced by one per
+single-pass call: that is what lets the next call start without a reset."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_05_amd as nv
+import oracle as O
+import workloads as W
+from gpu_helpers import DEV, host, to_device
+
+pytestmark = pytest.mark.gpu
+
+SINGLE, TWO = nv.NVFP4_AMAX_PATH_SINGLE_PASS, nv.NVFP4_AMAX_PATH_TWO_PASS
+
+EPOCH, EXIT, EXIT_BASE, EXIT_TOP, EXIT_TOP_BASE, LINE = 8256, 8288, 8544, 8800, 8832, 32
+
+
+def handoff_words(ws):
+    """(epoch, exit counters consistent with their bases)"""
+    w = host(ws).view(np.uint32)
+    ok = (np.array_equal(w[EXIT:EXIT + 8 * LINE:LINE], w[EXIT_BASE:EXIT_BASE + 8 * LINE:LINE])
+          and w[EXIT_TOP] == w[EXIT_TOP_BASE])
+    return int(w[EPOCH]), bool(ok)
+
+
+def run(xd, cfg, rowwise=True, columnwise=True):
+    rows, cols = xd.shape
+    row = nv.empty_orientation(rows, cols, DEV) if rowwise else None
+    col = nv.empty_orientation(cols, rows, DEV) if columnwise else None
+    nv.nvfp4_quantize(xd, row, col, cfg)
+    torch.cuda.synchronize()
+    out = {}
+    for side, o in (("row", row), ("col", col)):
+        if o is not None:
+            out[f"{side}_data"] = host(o.data)
+            out[f"{side}_scales"] = host(o.scales)
+            out[f"amax_{side}"] = host(o.amax)
+    return out
+
+
+def assert_oracle(got, x, *, swizzled=False, what="", **kw):
+    ref = O.quantize(x, **kw)
+    for side in ("row", "col"):
+        if f"{side}_data" not in got:
+            continue
+        assert np.array_equal(got[f"{side}_data"].ravel(), ref[f"{side}_data"].ravel()), f"{what} {side} data"
+        rs = O.swizzle_scales(ref[f"{side}_scales"]) if swizzled else ref[f"{side}_scales"].ravel()
+        assert np.array_equal(got[f"{side}_scales"].ravel(), rs), f"{what} {side} scales"
+        assert np.array_equal(got[f"amax_{side}"], ref[f"amax_{side}"]), f"{what} {side} amax"
+
+
+def assert_same(a, b, what=""):
+    assert a.keys() == b.keys()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), f"{what} {k}"
+
+
+# (name, rows, cols, dtype, options): tile counts 64 .. 2560, so that the
+# library picks 1, 2, 4 and 5 tiles per workgroup (BF16) and 1 (FP32);
+# 16x16 blocks with stochastic rounding stop at 4
+CASES = [
+    ("c1_1d", 1024, 1024, "bf16", dict()),
+    ("ragged_1d_fp32", 1040, 1008, "fp32", dict()),
+    ("2d_6144x4096", 6144, 4096, "bf16", dict(block_2d=True)),
+    ("ragged_1d_6000x4000", 6000, 4000, "bf16", dict()),
+    ("1d_sr_7168x4608", 7168, 4608, "bf16", dict(stochastic=True, sr_seed=21)),
+    ("c2_2d_swizzled", 8192, 5120, "bf16", dict(block_2d=True, swizzled=True)),
+    ("1d_ue5m3_8192x5120", 8192, 5120, "bf16", dict(scale_fmt=nv.NVFP4_SCALE_UE5M3)),
+    ("2d_sr_7168x4608", 7168, 4608, "bf16", dict(block_2d=True, stochastic=True, sr_seed=5)),
+    ("fp32_1d_3072x3072", 3072, 3072, "fp32", dict()),
+    ("fp32_2d_swizzled_2048x4096", 2048, 4096, "fp32", dict(block_2d=True, swizzled=True)),
+]
+
+
+def _input(name, rows, cols, dtype, seed):
+    if name.startswith("c2"):
+        return W.c2(rows=rows, cols=cols, seed=1)
+    if dtype == "fp32":
+        return W.gaussian_fp32(rows, cols, seed, scale=3.0)
+    return W.randn_bf16(rows, cols, seed)
+
+
+def _oracle_kw(opts):
+    kw = {k: v for k, v in opts.items() if k in ("block_2d", "stochastic", "sr_seed")}
+    if opts.get("scale_fmt") == nv.NVFP4_SCALE_UE5M3:
+        kw["scale_fmt"] = O.SCALE_UE5M3
+    return kw
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_single_pass_matches_oracle_and_two_pass(case):
+    name, rows, cols, dtype, opts = case
+    print(f"single pass {name} {rows}x{cols} {dtype} {opts}", flush=True)
+    x = _input(name, rows, cols, dtype, 300 + rows % 97)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    one = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))
+    assert handoff_words(ws) == (1, True), "the single-pass kernel did not run, or left its counters"
+    two = run(xd, nv.make_config(workspace=ws, amax_path=TWO, **opts))
+    assert handoff_words(ws) == (1, True), "the two-pass form touched the handoff words"
+    assert_same(one, two, name)
+    assert_oracle(one, x, swizzled=opts.get("swizzled", False), what=name, **_oracle_kw(opts))
+
+
+@pytest.mark.parametrize("rowwise,columnwise", [(True, False), (False, True)])
+def test_single_pass_one_orientation(rowwise, columnwise):
+    x = W.randn_bf16(7168, 4608, 41)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    got = run(xd, nv.make_config(workspace=ws, block_2d=True, amax_path=SINGLE), rowwise, columnwise)
+    assert_oracle(got, x, what="one orientation", rowwise=rowwise, columnwise=columnwise, block_2d=True)
+    assert handoff_words(ws)[1]
+
+
+def test_workspace_reused_across_grid_sizes():
+    # one workspace through calls whose grids differ (1 .. 5 tiles per
+    # workgroup, 8 .. 512 workgroups), a smaller amax after a larger one,
+    # and a two-pass call in between
+    ws = nv.empty_workspace(DEV)
+    seq = [(8192, 5120, 1.0, {}), (128, 256, 1.0, {}), (7168, 4608, 0.01, dict(block_2d=True)),
+           (1024, 1024, 1e3, dict(amax_path=TWO)), (256, 384, 2.0, dict(swizzled=False)),
+           (8192, 5120, 1e-3, dict(block_2d=True, swizzled=True))]
+    for i, (rows, cols, scale, opts) in enumerate(seq):
+        x = W.randn_bf16(rows, cols, 500 + i)
+        xd = to_device(x) * scale
+        xs = host(xd.view(torch.int16)).view(np.uint16)
+        got = run(xd, nv.make_config(workspace=ws, **dict(dict(amax_path=SINGLE), **opts)))
+        assert_oracle(got, xs, swizzled=opts.get("swizzled", False), what=f"call {i}",
+                      block_2d=opts.get("block_2d", False))
+        assert handoff_words(ws) == (i + (0 if i < 3 else -1) + 1, True), f"call {i}"
+
+
+@pytest.mark.parametrize("rows,cols,opts", [(512, 768, dict(block_2d=True)), (7168, 4608, {})])
+def test_wait_that_runs_out_gives_the_same_bytes(rows, cols, opts):
+    # a wait bound of one tick: nearly every workgroup stops waiting and
+    # reads the whole input for the amax itself
+    x = W.randn_bf16(rows, cols, 61)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    normal = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))
+    nv.nvfp4_debug_set_wait_ticks(1)
+    try:
+        forced = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))
+    finally:
+        nv.nvfp4_debug_set_wait_ticks(0)
+    assert_same(normal, forced, "forced fallback")
+    assert handoff_words(ws) == (2, True)
+    after = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))  # the counters are ready for the next call
+    assert_same(normal, after, "after the fallback")
+    assert_oracle(normal, x, what="fallback shape", **opts)
+
+
+def test_noop_writes_nothing_and_leaves_the_counters():
+    x = W.randn_bf16(1024, 2048, 71)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    run(xd, nv.make_config(workspace=ws, amax_path=SINGLE))
+    words = host(ws).copy()
+    noop = torch.ones(1, dtype=torch.float32, device=DEV)
+    row = nv.empty_orientation(1024, 2048, DEV)
+    col = nv.empty_orientation(2048, 1024, DEV)
+    for o in (row, col):
+        for t in (o.data, o.scales, o.amax):
+            t.view(torch.uint8).fill_(0x5A)
+    nv.nvfp4_quantize(xd, row, col, nv.make_config(workspace=ws, noop=noop, amax_path=SINGLE))
+    torch.cuda.synchronize()
+    for o in (row, col):
+        for t in (o.data, o.scales, o.amax):
+            assert bool((t.view(torch.uint8) == 0x5A).all())
+    assert np.array_equal(host(ws)[16384:], words[16384:])
