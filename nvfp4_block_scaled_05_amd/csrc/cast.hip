@@ -191,7 +191,7 @@ __device__ __forceinline__ uint32_t pick(bool lo, uint32_t a, uint32_t b) {
 }
 
 __device__ __forceinline__ uint32_t block_code(uint32_t m_bits, float S, bool ue5m3) {
-  const float q = __uint_as_float(m_bits) / 6.0f;
+  const float q = div6(__uint_as_float(m_bits));
   return scale_encode(q * S, ue5m3);
 }
 
@@ -296,10 +296,21 @@ __device__ __forceinline__ void rt_clear_outside(const CastArgs &p, uint32_t r0,
   }
 }
 
-template <int DT, bool B2D, bool SR>
+template <int DT, bool B2D, bool SR, bool PRE = false>
 __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32_t ty,
                                           uint32_t (&w)[8][RT<DT>::kWords], float S_row, float S_col, bool ue,
-                                          RtLds &sh);
+                                          RtLds &sh, uint32_t m2d = 0);
+
+// The 16x16 block maximum (bit pattern) of the thread's sub-tile, taken over
+// the four lanes that share the block.
+template <int DT>
+__device__ __forceinline__ uint32_t block2d_max(const uint32_t (&w)[8][RT<DT>::kWords]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = max(m, piece_max<DT>(w[k]));
+  m = max(m, dpp_mov<kQuadXor1>(m));
+  return max(m, swz_xor16(m));
+}
 
 template <int DT, bool B2D, bool SR>
 __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
@@ -326,17 +337,18 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
   const float S_row = p.row_data != nullptr ? global_encode_scale(amax_row, ue) : 1.0f;
   const float S_col = p.col_data != nullptr ? global_encode_scale(amax_col, ue) : 1.0f;
   fill_multipliers(sh.mult, tid, S_row, S_col, ue);
-  rt_clear_outside<DT>(p, r0, c0, w);
   rt_encode<DT, B2D, SR>(p, tx, ty, w, S_row, S_col, ue, sh);
 }
 
 // Block scales, codes and stores of one tile whose values are in w (zero
 // outside the input) and whose multipliers are in sh.mult; sh.mult is read
 // only after the barrier below, so the caller may fill it right before.
-template <int DT, bool B2D, bool SR>
+// PRE: the caller has cleared w outside the input and, with 16x16 blocks,
+// passes the block maximum in m2d.
+template <int DT, bool B2D, bool SR, bool PRE>
 __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32_t ty,
                                           uint32_t (&w)[8][RT<DT>::kWords], float S_row, float S_col, bool ue,
-                                          RtLds &sh) {
+                                          RtLds &sh, uint32_t m2d) {
   const int tid = threadIdx.x;
   const int ucol = tid & 15;
   const int rg = tid >> 4;
@@ -348,16 +360,18 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
   const bool do_row = p.row_data != nullptr;
   const bool do_col = p.col_data != nullptr;
 
+  if (!PRE) rt_clear_outside<DT>(p, r0, c0, w);
+  // 16x16 blocks with equal row and column global scales share their codes
+  // and every product (a uniform branch: the scales come from the same two
+  // amax words in every lane)
+  const bool share = B2D && do_row && do_col && __builtin_amdgcn_readfirstlane(S_row == S_col);
+
   // ---- block scale codes ----
   uint32_t rcode[8], ccode[8];
   if (B2D) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) m = max(m, piece_max<DT>(w[k]));
-    m = max(m, dpp_mov<kQuadXor1>(m));
-    m = max(m, swz_xor16(m));
+    const uint32_t m = PRE ? m2d : block2d_max<DT>(w);
     const uint32_t cr = block_code(m, S_row, ue);
-    const uint32_t cc = block_code(m, S_col, ue);
+    const uint32_t cc = share ? cr : block_code(m, S_col, ue);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       rcode[k] = cr;
@@ -443,9 +457,6 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
   const uint32_t kcol = SR ? sr_key(p.sr_seed, 1) : 0u;
   const uint32_t half_cols = p.cols >> 1;
   const uint32_t half_rows = p.rows >> 1;
-  // 16x16 blocks with equal row and column global scales share every product
-  // (a uniform branch: the scales come from the same two amax words in every lane)
-  const bool share = B2D && do_row && do_col && __builtin_amdgcn_readfirstlane(S_row == S_col);
   uint32_t colw[8];  // byte i is written in row pair i; every byte is written
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -999,12 +1010,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
       rt_load<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
     }
   }
+  // while the loads are in flight the VALU is idle: clear the pieces
+  // outside the input and take the 16x16 block maxima here rather than in
+  // the encode
   uint32_t m[1] = {0};
+  uint32_t m2d[B2D ? K : 1];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     if (wg + k * G < T) {
+      rt_clear_outside<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
+      if (B2D) {
+        m2d[k] = block2d_max<DT>(w[k]);
+        m[0] = max(m[0], m2d[k]);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) m[0] = max(m[0], piece_max<DT>(w[k][r]));
+        for (int r = 0; r < 8; ++r) m[0] = max(m[0], piece_max<DT>(w[k][r]));
+      }
+    } else if (B2D) {
+      m2d[k] = 0;
     }
   }
   workgroup_max(m, sh.red);
@@ -1041,8 +1064,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   for (int k = 0; k < K; ++k) {
     if (wg + k * G < T) {
       if (k > 0) lds_barrier();  // the previous tile's LDS reads are done
-      rt_clear_outside<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
-      rt_encode<DT, B2D, SR>(p, tile_x[k], tile_y[k], w[k], S_row, S_col, ue, sh);
+      rt_encode<DT, B2D, SR, true>(p, tile_x[k], tile_y[k], w[k], S_row, S_col, ue, sh, B2D ? m2d[B2D ? k : 0] : 0u);
     }
   }
 

@@ -97,9 +97,22 @@ struct BlockScale {
   float mult;     // encode multiplier e
 };
 
+// fl(m / 6) for m >= 0 without a division: q0 = fl(m * fl(1/6)), then one
+// Newton correction with the exact residual fma(-q0, 6, m). Compared with
+// the correctly rounded quotient on every non-negative binary32 value, it
+// differs only where the quotient is subnormal (m < 2^-122) and at +inf;
+// those take the division.
+__device__ __forceinline__ float div6(float m) {
+  constexpr float r = 1.0f / 6.0f;
+  const float q0 = m * r;
+  float q = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, m), r, q0);
+  if (!(m >= 0x1p-122f && m <= kFltMax)) q = m / 6.0f;
+  return q;
+}
+
 // sd = fl(fl(m / 6) * S); e = fl(S / value(s)), 0 when s == 0.
 __device__ __forceinline__ BlockScale block_scale(float block_amax, float S, bool ue5m3) {
-  float q = block_amax / 6.0f;
+  float q = div6(block_amax);
   float sd = q * S;
   BlockScale b;
   b.code = scale_encode(sd, ue5m3);
