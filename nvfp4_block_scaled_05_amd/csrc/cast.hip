@@ -446,11 +446,23 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
   lds_barrier();
 
   float re[8], ce[8];
+  if (B2D) {  // one block per thread: one multiplier per orientation
+    const float r = do_row ? sh.mult[0][rcode[0]] : 0.0f;
+    const float c = do_col ? sh.mult[1][ccode[0]] : 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    re[k] = do_row ? sh.mult[0][rcode[k]] : 0.0f;
-    ce[k] = do_col ? sh.mult[1][ccode[k]] : 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      re[k] = r;
+      ce[k] = c;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      re[k] = do_row ? sh.mult[0][rcode[k]] : 0.0f;
+      ce[k] = do_col ? sh.mult[1][ccode[k]] : 0.0f;
+    }
   }
+  // interior tiles (uniform) store without per-lane bounds checks
+  const bool interior = r0 + kRT <= p.rows && c0 + kRT <= p.cols;
 
   // ---- encode: row pairs (2i, 2i+1) ----
   const uint32_t krow = SR ? sr_key(p.sr_seed, 0) : 0u;
@@ -477,10 +489,14 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
       const uint32_t byte0 = row * half_cols + (col >> 1);
       const uint32_t word0 = encode8_scaled<SR>(s0, krow, byte0);
       const uint32_t word1 = encode8_scaled<SR>(s1, krow, byte0 + half_cols);
-      if (col_ok && row < p.rows)
-        __builtin_nontemporal_store(word0, reinterpret_cast<uint32_t *>(p.row_data + byte0));
-      if (col_ok && row + 1 < p.rows)
-        __builtin_nontemporal_store(word1, reinterpret_cast<uint32_t *>(p.row_data + byte0 + half_cols));
+      uint32_t *dst = reinterpret_cast<uint32_t *>(p.row_data + byte0);
+      if (interior) {
+        __builtin_nontemporal_store(word0, dst);
+        __builtin_nontemporal_store(word1, dst + (half_cols >> 2));
+      } else {
+        if (col_ok && row < p.rows) __builtin_nontemporal_store(word0, dst);
+        if (col_ok && row + 1 < p.rows) __builtin_nontemporal_store(word1, dst + (half_cols >> 2));
+      }
     }
     if (do_col) {
       float t0[8], t1[8];
