@@ -998,9 +998,41 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   const uint32_t xg = wg % kBarGroups;
   const uint32_t nxg = min(G, kBarGroups);
 
-  // this call's epoch and exit bases, read before anything is published; a
-  // counter that is not in a state some call left means a workspace that
-  // was not zero-filled: then only the fallback is trusted
+  // ---- load every tile, maximum over them ----
+  // Tile coordinates before any load, so that the loads of successive
+  // tiles are not separated by integer divisions. Swizzled scales keep the
+  // row-major launch order, where slot k + 1 is slot k advanced by G tiles.
+  uint32_t tile_x[K], tile_y[K];
+  if (p.swizzled) {  // uniform
+    const uint32_t dy = G / tx_n, dx = G - dy * tx_n;
+    uint32_t ty = wg / tx_n, tx = wg - ty * tx_n;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      tile_x[k] = tx;
+      tile_y[k] = ty;
+      tx += dx;
+      ty += dy;
+      if (tx >= tx_n) {
+        tx -= tx_n;
+        ++ty;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) tile_xy(p, tile_index(p, min(wg + k * G, T - 1), T), tx_n, ty_n, tile_x[k], tile_y[k]);
+  }
+  uint32_t w[K][8][W];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (wg + k * G < T) rt_load<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
+  }
+  // while the loads are in flight the VALU is idle: clear the pieces
+  // outside the input and take the 16x16 block maxima here rather than in
+  // the encode
+  // this call's epoch and exit bases, read before anything is published
+  // (issued after the tile loads, which need not wait for them); a counter
+  // that is not in a state some call left means a workspace that was not
+  // zero-filled: then only the fallback is trusted
   uint32_t e = 0;
   bool sane = true;
   if (tid == 0) {
@@ -1014,21 +1046,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
     lds_start[2] = xbt;
   }
 
-  // ---- load every tile, maximum over them ----
-  uint32_t w[K][8][W];
-  uint32_t tile_x[K], tile_y[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    tile_x[k] = tile_y[k] = 0;
-    const uint32_t L = wg + k * G;
-    if (L < T) {
-      tile_xy(p, tile_index(p, L, T), tx_n, ty_n, tile_x[k], tile_y[k]);
-      rt_load<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
-    }
-  }
-  // while the loads are in flight the VALU is idle: clear the pieces
-  // outside the input and take the 16x16 block maxima here rather than in
-  // the encode
   uint32_t m[1] = {0};
   uint32_t m2d[B2D ? K : 1];
 #pragma unroll
