@@ -435,14 +435,20 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
   auto code_slot = [swz](int line, int blk) {
     return swz ? ((blk >> 2) << 9) + ((line & 31) << 4) + ((line >> 5) << 2) + (blk & 3) : line * 8 + blk;
   };
-  if (do_row && (ucol & 1) == 0) {
+  // A thread's eight lines are consecutive and stay inside one group of 32,
+  // so their slots are the first one's plus 16 k (swizzled) or 8 k (compact):
+  // constant offsets, in a uniform branch per layout.
+  auto put8 = [swz](uint8_t *dst, int first, const uint32_t (&code)[8]) {
+    if (swz) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) sh.rs[code_slot(8 * rg + k, ucol >> 1)] = static_cast<uint8_t>(rcode[k]);
-  }
-  if (do_col && (rg & 1) == 0) {
+      for (int k = 0; k < 8; ++k) dst[first + 16 * k] = static_cast<uint8_t>(code[k]);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) sh.cs[code_slot(8 * ucol + c, rg >> 1)] = static_cast<uint8_t>(ccode[c]);
-  }
+      for (int k = 0; k < 8; ++k) dst[first + 8 * k] = static_cast<uint8_t>(code[k]);
+    }
+  };
+  if (do_row && (ucol & 1) == 0) put8(sh.rs, code_slot(8 * rg, ucol >> 1), rcode);
+  if (do_col && (rg & 1) == 0) put8(sh.cs, code_slot(8 * ucol, rg >> 1), ccode);
   lds_barrier();
 
   float re[8], ce[8];
@@ -1239,15 +1245,15 @@ hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bo
 // ---- single-pass cast: plan and launch ----
 namespace {
 
-// Most tiles per workgroup: 32 VGPRs each (BF16); one more spills
-// registers (16x16 blocks with stochastic rounding: at 5). FP32 tiles take
-// 64 VGPRs: two per workgroup leave room for only two workgroups per CU,
-// which holds no more tiles than one per workgroup at four per CU.
+// Most tiles per workgroup: 32 VGPRs each (BF16; five take 217-227 VGPRs
+// in all, no spills). FP32 tiles take 64 VGPRs: two per workgroup leave
+// room for only two workgroups per CU, which holds no more tiles than one
+// per workgroup at four per CU.
 constexpr int kMaxKBf16 = 5;
 constexpr int kMaxKFp32 = 1;
 template <int DT, bool B2D, bool SR>
 constexpr int max_k() {
-  return DT == kFP32 ? kMaxKFp32 : (B2D && SR ? 4 : kMaxKBf16);
+  return DT == kFP32 ? kMaxKFp32 : kMaxKBf16;
 }
 constexpr int kMaxDevices = 64;
 std::atomic<uint32_t> g_wait_ticks{0};
@@ -1361,11 +1367,13 @@ hipError_t launch_resident_k(const CastArgs &a, uint32_t *ws, uint32_t G, int K,
 int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster) {
   if (rows == 0 || cols == 0) return 0;
   const uint32_t tiles = ((rows + kRT - 1) / kRT) * ((cols + kRT - 1) / kRT);
-  // 1x16 blocks encode several times more block scales than 16x16 blocks;
-  // with the tiles held in registers only two workgroups per CU run that
-  // work, and beyond two tiles per CU the two-launch form measured faster
-  // (8192x5120: 40.4 vs 44.4 us; 2048x2048: 14.2 vs 12.4 us)
-  if (when_faster && !block_2d && tiles > 2 * device_cus()) return 0;
+  // 1x16 blocks encode several times more block scales than 16x16 blocks,
+  // and stochastic rounding hashes every output byte; with the tiles held in
+  // registers only two workgroups per CU run that work, and beyond two tiles
+  // per CU the two-launch form measured faster (8192x5120 1x16: 40.4 vs
+  // 44.4 us; 16x16 stochastic: 56.8 vs 62.8 us; 2048x2048 1x16: 14.2 vs
+  // 12.4 us the other way)
+  if (when_faster && (!block_2d || sr) && tiles > 2 * device_cus()) return 0;
   const int kmax = dtype == kBF16 ? kMaxKBf16 : kMaxKFp32;
   for (int K = 1; K <= kmax; ++K) {
     const uint32_t G = resident_grid(tiles, K);

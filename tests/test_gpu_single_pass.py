@@ -70,8 +70,7 @@ def assert_same(a, b, what=""):
 
 
 # (name, rows, cols, dtype, options): tile counts 64 .. 2560, so that the
-# library picks 1, 2, 4 and 5 tiles per workgroup (BF16) and 1 (FP32);
-# 16x16 blocks with stochastic rounding stop at 4
+# library picks 1, 2, 4 and 5 tiles per workgroup (BF16) and 1 (FP32)
 CASES = [
     ("c1_1d", 1024, 1024, "bf16", dict()),
     ("ragged_1d_fp32", 1040, 1008, "fp32", dict()),
@@ -81,6 +80,7 @@ CASES = [
     ("c2_2d_swizzled", 8192, 5120, "bf16", dict(block_2d=True, swizzled=True)),
     ("1d_ue5m3_8192x5120", 8192, 5120, "bf16", dict(scale_fmt=nv.NVFP4_SCALE_UE5M3)),
     ("2d_sr_7168x4608", 7168, 4608, "bf16", dict(block_2d=True, stochastic=True, sr_seed=5)),
+    ("2d_sr_swizzled_8192x5120", 8192, 5120, "bf16", dict(block_2d=True, swizzled=True, stochastic=True, sr_seed=9)),
     ("fp32_1d_3072x3072", 3072, 3072, "fp32", dict()),
     ("fp32_2d_swizzled_2048x4096", 2048, 4096, "fp32", dict(block_2d=True, swizzled=True)),
 ]
