@@ -182,3 +182,36 @@ def test_noop_writes_nothing_and_leaves_the_counters():
         for t in (o.data, o.scales, o.amax):
             assert bool((t.view(torch.uint8) == 0x5A).all())
     assert np.array_equal(host(ws)[16384:], words[16384:])
+
+
+def test_graph_replays_of_the_bench_call():
+    # The bench call (8192x5120 BF16, 16x16, swizzled; five tiles per
+    # workgroup) captured in a HIP graph: every replay, with eager writes to
+    # the outputs in between, gives the eager bytes and advances the epoch by
+    # one with the exit counters consistent.
+    x = W.c2(rows=8192, cols=5120, seed=1)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    cfg = nv.make_config(block_2d=True, swizzled=True, workspace=ws, amax_path=SINGLE)
+    row = nv.empty_orientation(8192, 5120, DEV)
+    col = nv.empty_orientation(5120, 8192, DEV)
+    outs = [row.data, row.scales, row.amax, col.data, col.scales, col.amax]
+    nv.nvfp4_quantize(xd, row, col, cfg)
+    torch.cuda.synchronize()
+    eager = [host(t).copy() for t in outs]
+    assert handoff_words(ws) == (1, True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        nv.nvfp4_quantize(xd, row, col, cfg, s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.view(torch.uint8).fill_(0x33 + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for e, t in zip(eager, outs):
+            assert np.array_equal(e, host(t)), rep
+        assert handoff_words(ws) == (2 + rep, True), rep
