@@ -218,7 +218,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   const int resident_k = cfg.compute_amax && cfg.workspace != nullptr && !cfg.rht &&
                                  cfg.amax_path != NVFP4_AMAX_PATH_TWO_PASS
                              ? nvfp4::resident_plan(dtype, cfg.block_2d != 0, sr, R, C,
-                                                    cfg.amax_path == NVFP4_AMAX_PATH_AUTO)
+                                                    cfg.amax_path == NVFP4_AMAX_PATH_AUTO, s)
                              : 0;
   if (cfg.compute_amax && resident_k == 0) {
     float *a = ra ? ra : ca;

@@ -1297,10 +1297,20 @@ const void *resident_kernel_for(int dtype, bool b2d, bool sr, int K) {
 // were.
 constexpr int kMaxResidentPerCu = 4;
 
-uint32_t resident_capacity(int dtype, bool b2d, bool sr, int K) {
+// The device the stream's work runs on (the current device for the null
+// stream), or -1.
+int stream_device(hipStream_t s) {
+  hipDevice_t dev = -1;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess) return -1;
+  return dev >= 0 && dev < kMaxDevices ? static_cast<int>(dev) : -1;
+}
+
+// The occupancy limit comes from the runtime for the current device; the
+// library's devices are assumed to be of one kind (they are on an MI355X
+// node), and the CU count is the stream's device's own.
+uint32_t resident_capacity(int dev, int dtype, bool b2d, bool sr, int K) {
   static std::atomic<int32_t> cache[kMaxDevices][2][2][2][kMaxKBf16 + 1];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return 0;
   std::atomic<int32_t> &slot = cache[dev][dtype][b2d][sr][K];
   int32_t v = slot.load(std::memory_order_relaxed);
   if (v == 0) {
@@ -1315,12 +1325,10 @@ uint32_t resident_capacity(int dtype, bool b2d, bool sr, int K) {
   return v > 0 ? static_cast<uint32_t>(v) : 0u;
 }
 
-// CU count of the current device (0 when the runtime cannot tell)
-uint32_t device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
+// CU count of a device (0 when the runtime cannot tell)
+uint32_t device_cus(int dev) {
+  int cus = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return cus > 0 ? static_cast<uint32_t>(cus) : 0u;
 }
 
@@ -1364,8 +1372,11 @@ hipError_t launch_resident_k(const CastArgs &a, uint32_t *ws, uint32_t G, int K,
 
 }  // namespace
 
-int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster) {
+int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster,
+                  hipStream_t stream) {
   if (rows == 0 || cols == 0) return 0;
+  const int dev = stream_device(stream);
+  if (dev < 0) return 0;
   const uint32_t tiles = ((rows + kRT - 1) / kRT) * ((cols + kRT - 1) / kRT);
   // 1x16 blocks encode several times more block scales than 16x16 blocks,
   // and stochastic rounding hashes every output byte; with the tiles held in
@@ -1373,11 +1384,11 @@ int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t col
   // per CU the two-launch form measured faster (8192x5120 1x16: 40.4 vs
   // 44.4 us; 16x16 stochastic: 56.8 vs 62.8 us; 2048x2048 1x16: 14.2 vs
   // 12.4 us the other way)
-  if (when_faster && (!block_2d || sr) && tiles > 2 * device_cus()) return 0;
+  if (when_faster && (!block_2d || sr) && tiles > 2 * device_cus(dev)) return 0;
   const int kmax = dtype == kBF16 ? kMaxKBf16 : kMaxKFp32;
   for (int K = 1; K <= kmax; ++K) {
     const uint32_t G = resident_grid(tiles, K);
-    if (G <= kMaxPartials && G <= resident_capacity(dtype, block_2d, sr, K)) return K;
+    if (G <= kMaxPartials && G <= resident_capacity(dev, dtype, block_2d, sr, K)) return K;
   }
   return 0;
 }

@@ -100,7 +100,8 @@ hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bo
 // workgroups that can be resident at once, or (when_faster) where the
 // two-launch form measured faster (the caller then takes the amax pass and
 // launch_cast); launch_cast_resident launches with that K.
-int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster);
+int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster,
+                  hipStream_t stream);
 hipError_t launch_cast_resident(const CastArgs &a, uint32_t *workspace, int dtype, bool block_2d, bool sr, int K,
                                 hipStream_t s);
 // Bound on the handoff wait, in ticks of the 100 MHz real-time counter; after
