@@ -30,21 +30,16 @@ __device__ __forceinline__ float global_encode_scale(float amax, bool ue5m3) {
 }
 
 // E4M3 (bias 7, max 448) of a non-negative value, nearest even, saturating.
+// Branch-free: at and above 2^-6 the code is the binary32 pattern rounded
+// to 3 mantissa bits (ties to even, by an integer add of 0x7FFFF plus the
+// kept low bit; a carry bumps the exponent) and rebiased from 127 to 7;
+// below 2^-6 it is the nearest-even multiple of 2^-9 (8 is the smallest
+// normal, code 0x08); codes past 0x7E (448), +inf included, saturate.
 __device__ __forceinline__ uint32_t e4m3_encode(float sd) {
-  if (!(sd < 448.0f)) return 0x7Eu;  // 448 and above (incl. +inf) saturate
-  if (sd < 0.015625f) {
-    // subnormal range, quantum 2^-9: the code is the nearest-even integer
-    // multiple of 2^-9 (a result of 8 is the smallest normal, code 0x08).
-    return static_cast<uint32_t>(__builtin_rintf(sd * 512.0f));
-  }
-  uint32_t u = __float_as_uint(sd);
-  uint32_t exp8 = (u >> 23) - 127u + 7u;  // 1..15
-  uint32_t man = u & 0x7FFFFFu;
-  uint32_t keep = man >> 20;               // top 3 mantissa bits
-  uint32_t rest = man & 0xFFFFFu;
-  uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & keep);
-  uint32_t code = (exp8 << 3) + keep + up;  // a mantissa carry bumps the exponent
-  return code > 0x7Eu ? 0x7Eu : code;
+  const uint32_t u = __float_as_uint(sd);
+  const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(sd * 512.0f));
+  return min(sd < 0.015625f ? sub : normal, 0x7Eu);
 }
 
 __device__ __forceinline__ float e4m3_decode(uint32_t code) {
