@@ -55,20 +55,12 @@ __device__ __forceinline__ float e4m3_decode(uint32_t code) {
 // defined in "Fuse NVFP4 scale swizzling on SM120 and SM121" (Changes); this
 // is the reading the library takes.
 __device__ __forceinline__ uint32_t ue5m3_encode(float sd) {
-  if (!(sd < 61440.0f)) return 0xF7u;  // 61440 and above (incl. +inf) saturate
-  if (sd < 6.103515625e-05f) {
-    // subnormal range (below 2^-14), quantum 2^-17: the nearest-even
-    // integer multiple (a result of 8 is the smallest normal, code 0x08)
-    return static_cast<uint32_t>(__builtin_rintf(sd * 131072.0f));
-  }
-  uint32_t u = __float_as_uint(sd);
-  uint32_t exp5 = (u >> 23) - 127u + 15u;  // 1..30
-  uint32_t man = u & 0x7FFFFFu;
-  uint32_t keep = man >> 20;
-  uint32_t rest = man & 0xFFFFFu;
-  uint32_t up = (rest > 0x80000u) | ((rest == 0x80000u) & keep);
-  uint32_t code = (exp5 << 3) + keep + up;  // a mantissa carry bumps the exponent
-  return code > 0xF7u ? 0xF7u : code;
+  // as e4m3_encode: rounded binary32 pattern rebiased from 127 to 15 at and
+  // above 2^-14, nearest-even multiples of 2^-17 below, saturation at 0xF7
+  const uint32_t u = __float_as_uint(sd);
+  const uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (112u << 3);
+  const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(sd * 131072.0f));
+  return min(sd < 6.103515625e-05f ? sub : normal, 0xF7u);
 }
 
 __device__ __forceinline__ float ue5m3_decode(uint32_t code) {
