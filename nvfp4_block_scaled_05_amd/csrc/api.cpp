@@ -215,12 +215,13 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   uint32_t *partials = nullptr;
   uint32_t npartials = 0;
   // single pass: one launch that reads the input once (K tiles per workgroup)
-  const int resident_k = cfg.compute_amax && cfg.workspace != nullptr && !cfg.rht &&
-                                 cfg.amax_path != NVFP4_AMAX_PATH_TWO_PASS
-                             ? nvfp4::resident_plan(dtype, cfg.block_2d != 0, sr, R, C,
-                                                    cfg.amax_path == NVFP4_AMAX_PATH_AUTO, s)
-                             : 0;
-  if (cfg.compute_amax && resident_k == 0) {
+  const nvfp4::ResidentPlan plan = cfg.compute_amax && cfg.workspace != nullptr && !cfg.rht &&
+                                           cfg.amax_path != NVFP4_AMAX_PATH_TWO_PASS
+                                       ? nvfp4::resident_plan(dtype, cfg.block_2d != 0, sr, R, C,
+                                                              cfg.amax_path == NVFP4_AMAX_PATH_AUTO, s)
+                                       : nvfp4::ResidentPlan{0, 0};
+  const bool resident = plan.variant > 0;
+  if (cfg.compute_amax && !resident) {
     float *a = ra ? ra : ca;
     float *b = (ca == a) ? nullptr : ca;
     if (cfg.workspace != nullptr && rows * cols > 0) {
@@ -254,10 +255,10 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
                     col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
                     rht_word(cfg), cfg.noop, partials, npartials};
   a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
-  if (resident_k > 0) {
+  if (resident) {
     if ((st = record(0)) != NVFP4_OK) return st;
     st = hip_status(nvfp4::launch_cast_resident(a, static_cast<uint32_t *>(cfg.workspace), dtype,
-                                                cfg.block_2d != 0, sr, resident_k, s),
+                                                cfg.block_2d != 0, sr, plan, s),
                     "single-pass quantize launch");
     return st != NVFP4_OK ? st : record(1);
   }

@@ -989,10 +989,33 @@ __device__ __forceinline__ bool handoff(uint32_t *ws, uint32_t m, uint32_t wait_
   return ok;
 }
 
-template <int DT, bool B2D, bool SR, int K>
+// The thread's 8 row pieces of BF16 tile (r0, c0) loaded straight into LDS
+// (no registers): piece k of thread t lands at tl[k][t], since one load of a
+// wave writes its 64 lanes' 16 bytes in lane order from a wave-uniform base.
+// The addresses are rt_load's, clamped in edge tiles.
+__device__ __forceinline__ void rt_load_lds(const CastArgs &p, uint32_t r0, uint32_t c0, u32x4 (*tl)[kThreads]) {
+  const uint32_t col = c0 + 8 * (threadIdx.x & 15);
+  const uint32_t rbase = r0 + 8 * (threadIdx.x >> 4);
+  const uint32_t lcol = col < p.cols ? col : 0u;
+  const uint32_t wave0 = threadIdx.x & ~63u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t r = min(rbase + k, p.rows - 1);
+    const void *src = static_cast<const uint8_t *>(p.x) + (static_cast<uint64_t>(r) * p.cols + lcol) * 2;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(&tl[k][wave0]), 16, 0, 0);
+  }
+}
+
+// K slots per workgroup; with KL = 1 the last one is held in LDS (32 KiB,
+// BF16 only) and the others in registers, so that three workgroups fit on a
+// CU where K register tiles would allow two.
+template <int DT, bool B2D, bool SR, int K, int KL = 0>
 __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, uint32_t *ws, uint32_t wait_ticks) {
   constexpr int W = RT<DT>::kWords;
+  constexpr int KR = K - KL;  // register tiles
+  static_assert(KL == 0 || DT == kBF16, "the LDS tile holds BF16 pieces");
   __shared__ RtLds sh;
+  __shared__ u32x4 tl[KL ? 8 : 1][KL ? kThreads : 1];  // the LDS tile
   __shared__ uint32_t lds_ok, lds_amax;
   __shared__ uint32_t lds_start[3];  // epoch, exit base of the group, exit base over the groups
   if (p.noop != nullptr && *p.noop == 1.0f) return;
@@ -1027,10 +1050,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
 #pragma unroll
     for (int k = 0; k < K; ++k) tile_xy(p, tile_index(p, min(wg + k * G, T - 1), T), tx_n, ty_n, tile_x[k], tile_y[k]);
   }
-  uint32_t w[K][8][W];
+  uint32_t w[KR][8][W];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
+  for (int k = 0; k < KR; ++k) {
     if (wg + k * G < T) rt_load<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
+  }
+  const bool lds_tile = KL && wg + (K - 1) * G < T;  // uniform
+  if constexpr (KL != 0) {
+    if (lds_tile) rt_load_lds(p, tile_y[K - 1] * kRT, tile_x[K - 1] * kRT, tl);
   }
   // while the loads are in flight the VALU is idle: clear the pieces
   // outside the input and take the 16x16 block maxima here rather than in
@@ -1055,7 +1082,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   uint32_t m[1] = {0};
   uint32_t m2d[B2D ? K : 1];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
+  for (int k = 0; k < KR; ++k) {
     if (wg + k * G < T) {
       rt_clear_outside<DT>(p, tile_y[k] * kRT, tile_x[k] * kRT, w[k]);
       if (B2D) {
@@ -1067,6 +1094,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
       }
     } else if (B2D) {
       m2d[k] = 0;
+    }
+  }
+  if (KL) {
+    // the LDS tile's maximum, one piece at a time (its pieces outside the
+    // input are clamped copies of input values: they leave the maximum, and
+    // with 16-row / 16-column blocks every block outside the input, alone)
+    if (B2D) m2d[K - 1] = 0;
+    if (lds_tile) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
+      uint32_t ml = 0;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const u32x4 v = tl[r][tid];
+        const uint32_t piece[W] = {v.x, v.y, v.z, v.w};
+        ml = max(ml, piece_max<DT>(piece));
+      }
+      if (B2D) {
+        ml = max(ml, dpp_mov<kQuadXor1>(ml));
+        ml = max(ml, swz_xor16(ml));
+        m2d[K - 1] = ml;
+      }
+      m[0] = max(m[0], ml);
     }
   }
   workgroup_max(m, sh.red);
@@ -1100,11 +1149,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   const float S_col = p.col_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
   fill_multipliers(sh.mult, tid, S_row, S_col, ue);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
+  for (int k = 0; k < KR; ++k) {
     if (wg + k * G < T) {
       if (k > 0) lds_barrier();  // the previous tile's LDS reads are done
       rt_encode<DT, B2D, SR, true>(p, tile_x[k], tile_y[k], w[k], S_row, S_col, ue, sh, B2D ? m2d[B2D ? k : 0] : 0u);
     }
+  }
+  if (lds_tile) {  // into the registers of the tiles just encoded
+    lds_barrier();
+    uint32_t wl[8][W];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const u32x4 v = tl[r][tid];
+      wl[r][0] = v.x;
+      wl[r][1] = v.y;
+      wl[r][2] = v.z;
+      wl[r][3] = v.w;
+    }
+    const uint32_t ty = tile_y[K - 1], tx = tile_x[K - 1];
+    rt_clear_outside<DT>(p, ty * kRT, tx * kRT, wl);
+    rt_encode<DT, B2D, SR, true>(p, tx, ty, wl, S_row, S_col, ue, sh, B2D ? m2d[B2D ? K - 1 : 0] : 0u);
   }
 
   // ---- exit: the last workgroup of the grid advances the epoch ----
@@ -1251,42 +1315,37 @@ namespace {
 // per workgroup at four per CU.
 constexpr int kMaxKBf16 = 5;
 constexpr int kMaxKFp32 = 1;
-template <int DT, bool B2D, bool SR>
-constexpr int max_k() {
-  return DT == kFP32 ? kMaxKFp32 : kMaxKBf16;
-}
+// Kernel variants: v = 1 .. 5 is K = v register tiles; kLdsVariant is four
+// slots, three in registers and one in LDS (BF16).
+constexpr int kLdsVariant = 6;
+constexpr int kVariants = 7;
 constexpr int kMaxDevices = 64;
 std::atomic<uint32_t> g_wait_ticks{0};
 
-template <int DT, bool B2D, bool SR, int K>
-const void *resident_kernel() {
-  return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, K>);
-}
-
 template <int DT, bool B2D, bool SR>
-const void *resident_kernel_k(int K) {
-  constexpr int kmax = max_k<DT, B2D, SR>();
-  if (K == 1) return resident_kernel<DT, B2D, SR, 1>();
-  if constexpr (kmax >= 4) {
-    if (K == 2) return resident_kernel<DT, B2D, SR, 2>();
-    switch (K) {
-      case 3: return resident_kernel<DT, B2D, SR, 3>();
-      case 4: return resident_kernel<DT, B2D, SR, 4>();
-    }
+const void *resident_kernel_v(int v) {
+  switch (v) {
+    case 1: return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, 1>);
   }
-  if constexpr (kmax >= 5) {
-    if (K == 5) return resident_kernel<DT, B2D, SR, 5>();
+  if constexpr (DT == kBF16) {
+    switch (v) {
+      case 2: return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, 2>);
+      case 3: return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, 3>);
+      case 4: return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, 4>);
+      case 5: return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, 5>);
+      case kLdsVariant: return reinterpret_cast<const void *>(&k_cast_rt_resident<DT, B2D, SR, 4, 1>);
+    }
   }
   return nullptr;
 }
 
-const void *resident_kernel_for(int dtype, bool b2d, bool sr, int K) {
+const void *resident_kernel_for(int dtype, bool b2d, bool sr, int v) {
   if (dtype == kBF16) {
-    if (b2d) return sr ? resident_kernel_k<kBF16, true, true>(K) : resident_kernel_k<kBF16, true, false>(K);
-    return sr ? resident_kernel_k<kBF16, false, true>(K) : resident_kernel_k<kBF16, false, false>(K);
+    if (b2d) return sr ? resident_kernel_v<kBF16, true, true>(v) : resident_kernel_v<kBF16, true, false>(v);
+    return sr ? resident_kernel_v<kBF16, false, true>(v) : resident_kernel_v<kBF16, false, false>(v);
   }
-  if (b2d) return sr ? resident_kernel_k<kFP32, true, true>(K) : resident_kernel_k<kFP32, true, false>(K);
-  return sr ? resident_kernel_k<kFP32, false, true>(K) : resident_kernel_k<kFP32, false, false>(K);
+  if (b2d) return sr ? resident_kernel_v<kFP32, true, true>(v) : resident_kernel_v<kFP32, true, false>(v);
+  return sr ? resident_kernel_v<kFP32, false, true>(v) : resident_kernel_v<kFP32, false, false>(v);
 }
 
 // Workgroups of one kernel that may run at once: the occupancy limit per CU,
@@ -1308,21 +1367,21 @@ int stream_device(hipStream_t s) {
 // The occupancy limit comes from the runtime for the current device; the
 // library's devices are assumed to be of one kind (they are on an MI355X
 // node), and the CU count is the stream's device's own.
-uint32_t resident_capacity(int dev, int dtype, bool b2d, bool sr, int K) {
-  static std::atomic<int32_t> cache[kMaxDevices][2][2][2][kMaxKBf16 + 1];
+uint32_t resident_capacity(int dev, int dtype, bool b2d, bool sr, int v) {
+  static std::atomic<int32_t> cache[kMaxDevices][2][2][2][kVariants];
   if (dev < 0 || dev >= kMaxDevices) return 0;
-  std::atomic<int32_t> &slot = cache[dev][dtype][b2d][sr][K];
-  int32_t v = slot.load(std::memory_order_relaxed);
-  if (v == 0) {
+  std::atomic<int32_t> &slot = cache[dev][dtype][b2d][sr][v];
+  int32_t c = slot.load(std::memory_order_relaxed);
+  if (c == 0) {
     int per_cu = 0, cus = 0;
-    const void *f = resident_kernel_for(dtype, b2d, sr, K);
+    const void *f = resident_kernel_for(dtype, b2d, sr, v);
     if (f == nullptr || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kThreads, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       per_cu = cus = 0;
-    v = per_cu > 0 && cus > 0 ? std::min(per_cu, kMaxResidentPerCu) * cus : -1;
-    slot.store(v, std::memory_order_relaxed);
+    c = per_cu > 0 && cus > 0 ? std::min(per_cu, kMaxResidentPerCu) * cus : -1;
+    slot.store(c, std::memory_order_relaxed);
   }
-  return v > 0 ? static_cast<uint32_t>(v) : 0u;
+  return c > 0 ? static_cast<uint32_t>(c) : 0u;
 }
 
 // CU count of a device (0 when the runtime cannot tell)
@@ -1332,51 +1391,39 @@ uint32_t device_cus(int dev) {
   return cus > 0 ? static_cast<uint32_t>(cus) : 0u;
 }
 
-uint32_t resident_grid(uint32_t tiles, int K) {
-  const uint32_t g = (tiles + K - 1) / K;
-  return (g + kBarGroups - 1) / kBarGroups * kBarGroups;
-}
+uint32_t round8(uint32_t g) { return (g + kBarGroups - 1) / kBarGroups * kBarGroups; }
 
 template <int DT, bool B2D, bool SR>
-hipError_t launch_resident_k(const CastArgs &a, uint32_t *ws, uint32_t G, int K, uint32_t ticks, hipStream_t s) {
+hipError_t launch_resident_v(const CastArgs &a, uint32_t *ws, uint32_t G, int v, uint32_t ticks, hipStream_t s) {
   const dim3 grid(G), block(kThreads);
-  switch (K) {
-    case 1: hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 1>), grid, block, 0, s, a, ws, ticks); break;
-    default: {
-      constexpr int kmax = max_k<DT, B2D, SR>();
-      if constexpr (kmax >= 4) {
-        if (K == 2) {
-          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 2>), grid, block, 0, s, a, ws, ticks);
-          break;
-        }
-        if (K == 3) {
-          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 3>), grid, block, 0, s, a, ws, ticks);
-          break;
-        }
-        if (K == 4) {
-          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 4>), grid, block, 0, s, a, ws, ticks);
-          break;
-        }
-      }
-      if constexpr (kmax >= 5) {
-        if (K == 5) {
-          hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 5>), grid, block, 0, s, a, ws, ticks);
-          break;
-        }
-      }
-      return hipErrorInvalidValue;
-    }
+  if (v == 1) {
+    hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 1>), grid, block, 0, s, a, ws, ticks);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  if constexpr (DT == kBF16) {
+    switch (v) {
+      case 2: hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 2>), grid, block, 0, s, a, ws, ticks); break;
+      case 3: hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 3>), grid, block, 0, s, a, ws, ticks); break;
+      case 4: hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 4>), grid, block, 0, s, a, ws, ticks); break;
+      case 5: hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 5>), grid, block, 0, s, a, ws, ticks); break;
+      case kLdsVariant:
+        hipLaunchKernelGGL((k_cast_rt_resident<DT, B2D, SR, 4, 1>), grid, block, 0, s, a, ws, ticks);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster,
-                  hipStream_t stream) {
-  if (rows == 0 || cols == 0) return 0;
+ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster,
+                           hipStream_t stream) {
+  ResidentPlan none{0, 0};
+  if (rows == 0 || cols == 0) return none;
   const int dev = stream_device(stream);
-  if (dev < 0) return 0;
+  if (dev < 0) return none;
   const uint32_t tiles = ((rows + kRT - 1) / kRT) * ((cols + kRT - 1) / kRT);
   // 1x16 blocks encode several times more block scales than 16x16 blocks,
   // and stochastic rounding hashes every output byte; with the tiles held in
@@ -1384,31 +1431,40 @@ int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t col
   // per CU the two-launch form measured faster (8192x5120 1x16: 40.4 vs
   // 44.4 us; 16x16 stochastic: 56.8 vs 62.8 us; 2048x2048 1x16: 14.2 vs
   // 12.4 us the other way)
-  if (when_faster && (!block_2d || sr) && tiles > 2 * device_cus(dev)) return 0;
+  if (when_faster && (!block_2d || sr) && tiles > 2 * device_cus(dev)) return none;
+  auto fits = [&](int v, uint32_t G) { return G <= kMaxPartials && G <= resident_capacity(dev, dtype, block_2d, sr, v); };
   const int kmax = dtype == kBF16 ? kMaxKBf16 : kMaxKFp32;
   for (int K = 1; K <= kmax; ++K) {
-    const uint32_t G = resident_grid(tiles, K);
-    if (G <= kMaxPartials && G <= resident_capacity(dev, dtype, block_2d, sr, K)) return K;
+    if (K == 4 && dtype == kBF16) {
+      // before four register tiles (two workgroups per CU): three register
+      // tiles and one LDS tile, with a grid of up to three workgroups per CU
+      // (slots past the last tile stay empty)
+      const uint32_t cap = resident_capacity(dev, dtype, block_2d, sr, kLdsVariant);
+      const uint32_t G = std::min(cap / kBarGroups * kBarGroups, round8((tiles + 2) / 3));
+      if (G > 0 && G * 4 >= tiles && fits(kLdsVariant, G)) return ResidentPlan{kLdsVariant, G};
+    }
+    const uint32_t G = round8((tiles + K - 1) / K);
+    if (fits(K, G)) return ResidentPlan{K, G};
   }
-  return 0;
+  return none;
 }
 
-hipError_t launch_cast_resident(const CastArgs &a, uint32_t *ws, int dtype, bool block_2d, bool sr, int K,
-                                hipStream_t s) {
-  const uint32_t tiles = ((a.rows + kRT - 1) / kRT) * ((a.cols + kRT - 1) / kRT);
-  const uint32_t G = resident_grid(tiles, K);
+hipError_t launch_cast_resident(const CastArgs &a, uint32_t *ws, int dtype, bool block_2d, bool sr,
+                                const ResidentPlan &plan, hipStream_t s) {
   const uint32_t t = g_wait_ticks.load(std::memory_order_relaxed);
   const uint32_t ticks = t != 0 ? t : kDefaultWaitTicks;
+  const uint32_t G = plan.grid;
+  const int v = plan.variant;
   if (dtype == kBF16) {
-    if (block_2d) return sr ? launch_resident_k<kBF16, true, true>(a, ws, G, K, ticks, s)
-                            : launch_resident_k<kBF16, true, false>(a, ws, G, K, ticks, s);
-    return sr ? launch_resident_k<kBF16, false, true>(a, ws, G, K, ticks, s)
-              : launch_resident_k<kBF16, false, false>(a, ws, G, K, ticks, s);
+    if (block_2d) return sr ? launch_resident_v<kBF16, true, true>(a, ws, G, v, ticks, s)
+                            : launch_resident_v<kBF16, true, false>(a, ws, G, v, ticks, s);
+    return sr ? launch_resident_v<kBF16, false, true>(a, ws, G, v, ticks, s)
+              : launch_resident_v<kBF16, false, false>(a, ws, G, v, ticks, s);
   }
-  if (block_2d) return sr ? launch_resident_k<kFP32, true, true>(a, ws, G, K, ticks, s)
-                          : launch_resident_k<kFP32, true, false>(a, ws, G, K, ticks, s);
-  return sr ? launch_resident_k<kFP32, false, true>(a, ws, G, K, ticks, s)
-            : launch_resident_k<kFP32, false, false>(a, ws, G, K, ticks, s);
+  if (block_2d) return sr ? launch_resident_v<kFP32, true, true>(a, ws, G, v, ticks, s)
+                          : launch_resident_v<kFP32, true, false>(a, ws, G, v, ticks, s);
+  return sr ? launch_resident_v<kFP32, false, true>(a, ws, G, v, ticks, s)
+            : launch_resident_v<kFP32, false, false>(a, ws, G, v, ticks, s);
 }
 
 void set_resident_wait_ticks(uint32_t ticks) { g_wait_ticks.store(ticks, std::memory_order_relaxed); }

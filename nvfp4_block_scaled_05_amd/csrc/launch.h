@@ -95,15 +95,20 @@ hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t col
 hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
 // Single-pass quantize with a per-tensor amax: one launch that loads every
 // tile into registers, reduces the amax through the workspace's barrier words
-// and encodes from registers. resident_plan gives the tiles per workgroup, K,
-// or 0 when the tiles of this shape do not fit in the registers of the
-// workgroups that can be resident at once, or (when_faster) where the
-// two-launch form measured faster (the caller then takes the amax pass and
-// launch_cast); launch_cast_resident launches with that K.
-int resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster,
-                  hipStream_t stream);
-hipError_t launch_cast_resident(const CastArgs &a, uint32_t *workspace, int dtype, bool block_2d, bool sr, int K,
-                                hipStream_t s);
+// and encodes from registers (one tile per workgroup may be held in LDS).
+// resident_plan gives the kernel variant and grid, or variant 0 when the
+// tiles of this shape do not fit in the workgroups that can be resident at
+// once, or (when_faster) where the two-launch form measured faster (the
+// caller then takes the amax pass and launch_cast); launch_cast_resident
+// launches that plan.
+struct ResidentPlan {
+  int variant;    // 0: the two-pass form; else the kernel variant
+  uint32_t grid;  // workgroups
+};
+ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uint32_t cols, bool when_faster,
+                           hipStream_t stream);
+hipError_t launch_cast_resident(const CastArgs &a, uint32_t *workspace, int dtype, bool block_2d, bool sr,
+                                const ResidentPlan &plan, hipStream_t s);
 // Bound on the handoff wait, in ticks of the 100 MHz real-time counter; after
 // it a workgroup computes the amax from the whole input itself. 0 restores
 // the default.

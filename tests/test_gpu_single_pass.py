@@ -1,7 +1,8 @@
 """Single-pass quantize: one launch in which every workgroup holds its tiles
 in registers across a grid-wide handoff of the per-tensor amax through the
 workspace. Checked bit for bit against the oracle and against the two-pass
-form (amax pass + cast), on shapes that give 1 to 5 tiles per workgroup,
+form (amax pass + cast), on shapes that give 1 to 4 tiles per workgroup
+(the fourth held in LDS),
 ragged edges, every output choice, one workspace reused across grid sizes,
 the bounded wait forced to run out (each workgroup then reads the whole
 input for the amax), and noop.
@@ -70,7 +71,8 @@ def assert_same(a, b, what=""):
 
 
 # (name, rows, cols, dtype, options): tile counts 64 .. 2560, so that the
-# library picks 1, 2, 4 and 5 tiles per workgroup (BF16) and 1 (FP32)
+# library picks 1 to 3 register tiles per workgroup, or 3 register tiles
+# and one LDS tile (BF16), and 1 (FP32)
 CASES = [
     ("c1_1d", 1024, 1024, "bf16", dict()),
     ("ragged_1d_fp32", 1040, 1008, "fp32", dict()),
@@ -81,6 +83,9 @@ CASES = [
     ("1d_ue5m3_8192x5120", 8192, 5120, "bf16", dict(scale_fmt=nv.NVFP4_SCALE_UE5M3)),
     ("2d_sr_7168x4608", 7168, 4608, "bf16", dict(block_2d=True, stochastic=True, sr_seed=5)),
     ("2d_sr_swizzled_8192x5120", 8192, 5120, "bf16", dict(block_2d=True, swizzled=True, stochastic=True, sr_seed=9)),
+    # 2401 tiles: three register tiles and one LDS tile per workgroup, ragged edges
+    ("lds_tile_ragged_1d_6256x6256", 6256, 6256, "bf16", dict()),
+    ("lds_tile_ragged_2d_sr_6256x6256", 6256, 6256, "bf16", dict(block_2d=True, stochastic=True, sr_seed=3)),
     ("fp32_1d_3072x3072", 3072, 3072, "fp32", dict()),
     ("fp32_2d_swizzled_2048x4096", 2048, 4096, "fp32", dict(block_2d=True, swizzled=True)),
 ]
@@ -144,7 +149,8 @@ def test_workspace_reused_across_grid_sizes():
         assert handoff_words(ws) == (i + (0 if i < 3 else -1) + 1, True), f"call {i}"
 
 
-@pytest.mark.parametrize("rows,cols,opts", [(512, 768, dict(block_2d=True)), (7168, 4608, {})])
+@pytest.mark.parametrize("rows,cols,opts", [(512, 768, dict(block_2d=True)), (7168, 4608, {}),
+                                            (6256, 6256, dict(block_2d=True))])
 def test_wait_that_runs_out_gives_the_same_bytes(rows, cols, opts):
     # a wait bound of one tick: nearly every workgroup stops waiting and
     # reads the whole input for the amax itself
