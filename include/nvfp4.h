@@ -75,16 +75,16 @@ typedef enum {
 } nvfp4_scale_fmt_t;
 
 typedef enum {
-  /* the single-pass form where it fits and measured faster (16x16 blocks
-   * with nearest even; 1x16 blocks or stochastic rounding up to
-   * 2 x 128 x 128 elements per CU), else the two-pass form */
+  /* the single-pass form where it fits and measured faster (nearest even;
+   * stochastic rounding up to 2 x 128 x 128 elements per CU), else the
+   * two-pass form */
   NVFP4_AMAX_PATH_AUTO = 0,
   /* always the amax pass and the cast kernel (two launches) */
   NVFP4_AMAX_PATH_TWO_PASS = 1,
-  /* the single-pass form whenever every 128x128 tile fits in the registers
-   * of the workgroups that can be resident at once (BF16: up to 5 tiles per
-   * workgroup; FP32: one; at most 4 workgroups per CU), else the two-pass
-   * form */
+  /* the single-pass form whenever every 128x128 tile fits in the
+   * workgroups that can be resident at once (BF16: up to 3 tiles in
+   * registers and one in LDS per workgroup, or 5 in registers; FP32: one;
+   * at most 4 workgroups per CU), else the two-pass form */
   NVFP4_AMAX_PATH_SINGLE_PASS = 2
 } nvfp4_amax_path_t;
 

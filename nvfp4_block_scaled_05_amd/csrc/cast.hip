@@ -1309,14 +1309,12 @@ hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bo
 // ---- single-pass cast: plan and launch ----
 namespace {
 
-// Most tiles per workgroup: 32 VGPRs each (BF16; five take 217-227 VGPRs
-// in all, no spills). FP32 tiles take 64 VGPRs: two per workgroup leave
+// Kernel variants: v = 1 .. 5 is K = v register tiles (32 VGPRs each for
+// BF16; five take 217-227 VGPRs in all, no spills); kLdsVariant is four
+// slots, three in registers (156-166 VGPRs) and one in LDS. BF16 only
+// beyond one tile: an FP32 tile takes 64 VGPRs, and two per workgroup leave
 // room for only two workgroups per CU, which holds no more tiles than one
 // per workgroup at four per CU.
-constexpr int kMaxKBf16 = 5;
-constexpr int kMaxKFp32 = 1;
-// Kernel variants: v = 1 .. 5 is K = v register tiles; kLdsVariant is four
-// slots, three in registers and one in LDS (BF16).
 constexpr int kLdsVariant = 6;
 constexpr int kVariants = 7;
 constexpr int kMaxDevices = 64;
@@ -1425,26 +1423,24 @@ ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uin
   const int dev = stream_device(stream);
   if (dev < 0) return none;
   const uint32_t tiles = ((rows + kRT - 1) / kRT) * ((cols + kRT - 1) / kRT);
-  // 1x16 blocks encode several times more block scales than 16x16 blocks,
-  // and stochastic rounding hashes every output byte; with the tiles held in
-  // registers only two workgroups per CU run that work, and beyond two tiles
-  // per CU the two-launch form measured faster (8192x5120 1x16: 40.4 vs
-  // 44.4 us; 16x16 stochastic: 56.8 vs 62.8 us; 2048x2048 1x16: 14.2 vs
-  // 12.4 us the other way)
-  if (when_faster && (!block_2d || sr) && tiles > 2 * device_cus(dev)) return none;
-  auto fits = [&](int v, uint32_t G) { return G <= kMaxPartials && G <= resident_capacity(dev, dtype, block_2d, sr, v); };
-  const int kmax = dtype == kBF16 ? kMaxKBf16 : kMaxKFp32;
-  for (int K = 1; K <= kmax; ++K) {
-    if (K == 4 && dtype == kBF16) {
-      // before four register tiles (two workgroups per CU): three register
-      // tiles and one LDS tile, with a grid of up to three workgroups per CU
-      // (slots past the last tile stay empty)
-      const uint32_t cap = resident_capacity(dev, dtype, block_2d, sr, kLdsVariant);
-      const uint32_t G = std::min(cap / kBarGroups * kBarGroups, round8((tiles + 2) / 3));
-      if (G > 0 && G * 4 >= tiles && fits(kLdsVariant, G)) return ResidentPlan{kLdsVariant, G};
-    }
-    const uint32_t G = round8((tiles + K - 1) / K);
-    if (fits(K, G)) return ResidentPlan{K, G};
+  // Stochastic rounding hashes every output byte; beyond two tiles per CU
+  // the two-launch form measured faster with it (8192x5120 16x16: 56.4 vs
+  // 58.3 us; 1x16: 61.7 vs 64.9 us), below it slower (2048x4096 16x16: 19.6
+  // vs 17.6 us).
+  if (when_faster && sr && tiles > 2 * device_cus(dev)) return none;
+  // Variants in order of tiles per workgroup: one to three register tiles,
+  // three plus one LDS tile (three workgroups per CU), four or five register
+  // tiles (two per CU). Each takes as many workgroups as can be resident,
+  // up to one per tile: with fewer, some CUs hold more tiles than others
+  // (8192x4096 1x16 with 688 workgroups of three slots: 35.5 us; 768: the
+  // CUs even).
+  static constexpr int kOrder[] = {1, 2, 3, kLdsVariant, 4, 5};
+  for (int v : kOrder) {
+    const int slots = v == kLdsVariant ? 4 : v;
+    if (v > 1 && dtype != kBF16) break;
+    const uint32_t cap = resident_capacity(dev, dtype, block_2d, sr, v) / kBarGroups * kBarGroups;
+    const uint32_t G = std::min(cap, round8(tiles));
+    if (G > 0 && G <= kMaxPartials && static_cast<uint64_t>(G) * slots >= tiles) return ResidentPlan{v, G};
   }
   return none;
 }
