@@ -886,12 +886,13 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
 //
 // Every block scale depends on the amax of the whole input, so the
 // two-launch form reads the input twice: in the amax pass and in the cast.
-// Here each workgroup first loads its K tiles into registers (tiles
-// L = blockIdx.x + k * gridDim.x, k < K, in the launch order of k_cast_rt),
-// publishes the maximum of its tiles, waits until every workgroup of the
-// grid has published, and encodes its tiles from registers: the input is
-// read once. The host sizes the grid so that all of it can be resident at
-// once (at most the occupancy limit times the CU count). The waits are
+// Here each workgroup first loads its K tiles (tiles L = blockIdx.x +
+// k * gridDim.x, k < K, in the launch order of k_cast_rt) into registers,
+// the last one into LDS in one variant, publishes the maximum of its tiles,
+// waits until every workgroup of the grid has published, and encodes its
+// tiles from registers: the input is read once. The host sizes the grid so
+// that all of it can be resident at once (at most the occupancy limit, and
+// at most four workgroups, per CU times the CU count). The waits are
 // bounded all the same: a workgroup that has waited wait_ticks ticks of the
 // 100 MHz real-time counter takes the maximum of the whole input itself, so
 // the kernel ends however the hardware schedules its workgroups, with the
@@ -1059,9 +1060,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   if constexpr (KL != 0) {
     if (lds_tile) rt_load_lds(p, tile_y[K - 1] * kRT, tile_x[K - 1] * kRT, tl);
   }
-  // while the loads are in flight the VALU is idle: clear the pieces
-  // outside the input and take the 16x16 block maxima here rather than in
-  // the encode
   // this call's epoch and exit bases, read before anything is published
   // (issued after the tile loads, which need not wait for them); a counter
   // that is not in a state some call left means a workspace that was not
@@ -1079,6 +1077,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
     lds_start[2] = xbt;
   }
 
+  // while the loads are in flight the VALU is idle: clear the pieces
+  // outside the input and take the 16x16 block maxima here rather than in
+  // the encode
   uint32_t m[1] = {0};
   uint32_t m2d[B2D ? K : 1];
 #pragma unroll
@@ -1096,7 +1097,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
       m2d[k] = 0;
     }
   }
-  if (KL) {
+  if constexpr (KL != 0) {
     // the LDS tile's maximum, one piece at a time (its pieces outside the
     // input are clamped copies of input values: they leave the maximum, and
     // with 16-row / 16-column blocks every block outside the input, alone)
@@ -1155,20 +1156,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
       rt_encode<DT, B2D, SR, true>(p, tile_x[k], tile_y[k], w[k], S_row, S_col, ue, sh, B2D ? m2d[B2D ? k : 0] : 0u);
     }
   }
-  if (lds_tile) {  // into the registers of the tiles just encoded
-    lds_barrier();
-    uint32_t wl[8][W];
+  if constexpr (KL != 0) {
+    if (lds_tile) {  // into the registers of the tiles just encoded
+      lds_barrier();
+      uint32_t wl[8][W];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const u32x4 v = tl[r][tid];
-      wl[r][0] = v.x;
-      wl[r][1] = v.y;
-      wl[r][2] = v.z;
-      wl[r][3] = v.w;
+      for (int r = 0; r < 8; ++r) {
+        const u32x4 v = tl[r][tid];
+        wl[r][0] = v.x;
+        wl[r][1] = v.y;
+        wl[r][2] = v.z;
+        wl[r][3] = v.w;
+      }
+      const uint32_t ty = tile_y[K - 1], tx = tile_x[K - 1];
+      rt_clear_outside<DT>(p, ty * kRT, tx * kRT, wl);
+      rt_encode<DT, B2D, SR, true>(p, tx, ty, wl, S_row, S_col, ue, sh, B2D ? m2d[B2D ? K - 1 : 0] : 0u);
     }
-    const uint32_t ty = tile_y[K - 1], tx = tile_x[K - 1];
-    rt_clear_outside<DT>(p, ty * kRT, tx * kRT, wl);
-    rt_encode<DT, B2D, SR, true>(p, tx, ty, wl, S_row, S_col, ue, sh, B2D ? m2d[B2D ? K - 1 : 0] : 0u);
   }
 
   // ---- exit: the last workgroup of the grid advances the epoch ----
