@@ -913,6 +913,8 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
 // even one that starts after others stopped waiting.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kDefaultWaitTicks = 2000000;  // 20 ms
+// A call tags its slots epoch + 1, so tags run 1 .. 2^32 - 1 and never 0.
+constexpr uint32_t kLastEpoch = 0xFFFFFFFFu;
 
 __device__ __forceinline__ uint32_t group_members(uint32_t G, uint32_t x) {
   return (G - x + kBarGroups - 1) / kBarGroups;
@@ -1184,7 +1186,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
       const uint32_t top = __hip_atomic_fetch_add(ws + kExitTopWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (top - xbt == nxg - 1) {
         st_agent(ws + kExitTopBaseWord, top + 1);
-        st_agent(ws + kEpochWord, e + 1);
+        if (e + 1 != kLastEpoch) {
+          st_agent(ws + kEpochWord, e + 1);
+        } else {
+          // the next tag would be 0 and tags would start to repeat: clear
+          // every slot (no call tags with 0) and start again at epoch 0, so
+          // that a slot left by a call 2^32 calls ago cannot pass for the
+          // next call's (about 4000 stores, once per 2^32 calls)
+          for (uint32_t i = kSlotWord; i < kEpochWord; ++i) st_agent(ws + i, 0u);
+          st_agent(ws + kEpochWord, 0u);
+        }
       }
     }
   }

@@ -221,3 +221,30 @@ def test_graph_replays_of_the_bench_call():
         for e, t in zip(eager, outs):
             assert np.array_equal(e, host(t)), rep
         assert handoff_words(ws) == (2 + rep, True), rep
+
+
+def test_epoch_wrap_clears_the_slots():
+    # Drive the epoch through the point where 32-bit tags would repeat, with
+    # a slot left as a call 2^32 calls earlier would have left it: tag 1 and
+    # a huge maximum, in a slot that the small calls do not write. The call
+    # that reaches the last epoch clears every slot, so the large call after
+    # it (tag 1 again) cannot take the stale slot for its own.
+    ws = nv.empty_workspace(DEV)
+    words = ws.view(torch.int32)
+    small = W.randn_bf16(2048, 2048, 81)   # 256 tiles: 256 workgroups
+    big = W.c2(rows=8192, cols=5120, seed=1)  # 768 workgroups
+    stale = (1 << 32) | 0x7F000000  # tag 1, max 2^127
+    slot = 4096 + 2 * 600
+    words[EPOCH] = -3  # 0xFFFFFFFD
+    words[slot] = stale & 0xFFFFFFFF
+    words[slot + 1] = stale >> 32
+    torch.cuda.synchronize()
+    for i in range(2):
+        got = run(to_device(small), nv.make_config(workspace=ws, amax_path=SINGLE))
+        assert_oracle(got, small, what=f"small call {i}")
+    epoch, ok = handoff_words(ws)
+    assert ok and epoch == 0
+    assert int(words[slot + 1]) == 0, "the stale slot was not cleared at the wrap"
+    got = run(to_device(big), nv.make_config(workspace=ws, amax_path=SINGLE, block_2d=True, swizzled=True))
+    assert_oracle(got, big, swizzled=True, what="after the wrap", block_2d=True)
+    assert handoff_words(ws) == (1, True)
