@@ -156,9 +156,10 @@ typedef struct {
    * bytes, 16-byte aligned, owned by the caller, zero-filled before its
    * first use. With a workspace the call takes one of two forms:
    *   single pass (one launch; not with the RHT; see amax_path): each
-   *     workgroup loads its tiles into registers, publishes its maximum in
-   *     the workspace, waits (bounded) until every workgroup has published,
-   *     and encodes from registers, so the input is read once;
+   *     workgroup loads its tiles into registers (one of them into LDS in
+   *     one variant), publishes its maximum in the workspace, waits
+   *     (bounded) until every workgroup has published, and encodes from
+   *     registers, so the input is read once;
    *   two pass: the amax pass stores one maximum per workgroup there and
    *     the cast kernel finishes the reduction and writes the amax buffers
    *     (two launches, no zeroing pass, no atomics).
@@ -167,10 +168,11 @@ typedef struct {
    * entry do not matter). The rest holds the single-pass handoff: one
    * tagged slot per workgroup, an epoch and exit counters, which every call
    * leaves ready for the next; it must be zero on first use and must not be
-   * written by anything else (a workspace that breaks this still gives
-   * correct results, but each call then falls back to slow reads). Calls
-   * that share a workspace must not run concurrently (queue them on one
-   * stream). Ignored by the other calls and paths. */
+   * written by anything else. A workspace that breaks this is detected
+   * (barring a chance of about one in 2^32) and every call on it then takes
+   * a slow fallback that still gives the same bytes. Calls that share a
+   * workspace must not run concurrently (queue them on one stream). Ignored
+   * by the other calls and paths. */
   void *workspace;
   /* nvfp4_quantize only: NULL, or the address of two hipEvent_t handles
    * that the call records on its stream just before and just after the
