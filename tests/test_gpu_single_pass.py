@@ -248,3 +248,22 @@ def test_epoch_wrap_clears_the_slots():
     got = run(to_device(big), nv.make_config(workspace=ws, amax_path=SINGLE, block_2d=True, swizzled=True))
     assert_oracle(got, big, swizzled=True, what="after the wrap", block_2d=True)
     assert handoff_words(ws) == (1, True)
+
+
+@pytest.mark.parametrize("fill", ["uniform", "random"])
+def test_workspace_not_zero_filled_still_gives_the_oracle_bytes(fill):
+    # A workspace that was not zero-filled: uniform bytes leave the counters
+    # equal to their bases and no slot with the next tag, so the handoff runs
+    # as usual; random words fail the counters' check and every workgroup
+    # takes the maximum of the whole input itself. Either way the bytes are
+    # the oracle's.
+    x = W.randn_bf16(512, 768, 91)
+    ws = nv.empty_workspace(DEV)
+    if fill == "uniform":
+        ws.fill_(0xA5)
+    else:
+        g = torch.Generator(device=DEV).manual_seed(92)
+        ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8))
+    for i in range(2):
+        got = run(to_device(x), nv.make_config(workspace=ws, amax_path=SINGLE, block_2d=True))
+        assert_oracle(got, x, what=f"{fill} call {i}", block_2d=True)
