@@ -87,6 +87,12 @@ typedef enum {
    * at most 4 workgroups per CU), else the two-pass form */
   NVFP4_AMAX_PATH_SINGLE_PASS = 2
 } nvfp4_amax_path_t;
+/* The single-pass form needs its whole grid on the GPU at once. While
+ * kernels of other streams hold CUs, part of the grid may have to wait for
+ * them; the workgroups already running wait too, for at most 20 ms, and then
+ * read the whole input for the amax themselves: the bytes are the same, the
+ * call much slower. Callers that overlap the quantize with long-running
+ * kernels on other streams should choose NVFP4_AMAX_PATH_TWO_PASS. */
 
 /* One orientation of an NVFP4 tensor. For the row-wise orientation of an
  * R x C input, n = R and k = C; for the column-wise one, n = C and k = R
