@@ -221,13 +221,16 @@ AMAX_RHT_BF16 = 3
 
 
 def compute_amax(x, mode: int = AMAX_PER_TENSOR, sign_mask: int = 0):
-    """Returns (amax_row, amax_col): [1] and [1], or [rows] and None per row."""
+    """Returns (amax_row, amax_col): [1] and [1], or, per row, [rows] and
+    [cols] (the column-wise tensor of a row-scaled quantize is scaled along
+    its own rows, which are the input's columns)."""
     x, dt = _input(x)
     rows, cols = x.shape
     if mode == AMAX_PER_ROW:
         a = np.empty(rows, np.float32)
-        _load().oracle_compute_amax(_ptr(x), dt, rows, cols, mode, sign_mask, _ptr(a), None)
-        return a, None
+        b = np.empty(cols, np.float32)
+        _load().oracle_compute_amax(_ptr(x), dt, rows, cols, mode, sign_mask, _ptr(a), _ptr(b))
+        return a, b
     a = np.empty(1, np.float32)
     b = np.empty(1, np.float32)
     _load().oracle_compute_amax(_ptr(x), dt, rows, cols, mode, sign_mask, _ptr(a), _ptr(b))

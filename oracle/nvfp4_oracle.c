@@ -332,8 +332,9 @@ void oracle_rht_colwise(const void *x, int dtype, int64_t rows, int64_t cols, ui
 /* recipe keeps one amax per row. [P1] GPU-work table / review table:   */
 /* the RHT path reduces max|x| for the row-wise side and max|RHT(x)|    */
 /* for the column-wise side in one op.                                 */
-/* mode 0: per tensor, mode 1: per row, mode 2: RHT pair, mode 3: RHT  */
-/* pair with BF16 transformed values.                                  */
+/* mode 0: per tensor, mode 1: per row (and per column for the         */
+/* column-wise side), mode 2: RHT pair, mode 3: RHT pair with BF16     */
+/* transformed values.                                                 */
 /* amax_row / amax_col may be NULL (that buffer is not requested).     */
 /* ------------------------------------------------------------------ */
 void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, int mode,
@@ -343,6 +344,14 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
       float a = 0.0f;
       for (int64_t j = 0; j < cols; ++j) a = fmaxf(a, fabsf(oracle_load(x, dtype, i * cols + j)));
       if (amax_row) amax_row[i] = a;
+    }
+    /* the column-wise tensor's rows are the input's columns */
+    if (amax_col) {
+      for (int64_t j = 0; j < cols; ++j) {
+        float a = 0.0f;
+        for (int64_t i = 0; i < rows; ++i) a = fmaxf(a, fabsf(oracle_load(x, dtype, i * cols + j)));
+        amax_col[j] = a;
+      }
     }
     return;
   }
@@ -398,7 +407,9 @@ static void encode_row(const float *vals, const float *e_per_block, int64_t n, i
 /* The column-wise tensor is the transpose: its row j holds column j of */
 /* x ([P1] Changes: one call writes both orientations).                */
 /* Amax inputs: amax_row[0] (or amax_row[i] when row_scaled), and       */
-/* amax_col[0]; each direction's global scale comes from its own amax. */
+/* amax_col[0] (or amax_col[j], one per input column, when row_scaled: */
+/* the column-wise tensor is row-scaled along its own rows); each       */
+/* direction's global scale comes from its own amax.                   */
 /* block_2d: one scale per 16x16 block shared by both directions        */
 /* ([P2] Changes: the 2D path); otherwise 1x16 blocks along each        */
 /* direction's rows. rht: column-wise values are the RHT image (rht == */
@@ -413,7 +424,7 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
   int want_col = col_data != NULL;
   if (cols % 16 != 0) return -1;
   if ((want_col || block_2d) && rows % 16 != 0) return -1;
-  if (row_scaled && (want_col || block_2d || rht)) return -1;
+  if (row_scaled && (block_2d || rht)) return -1;
   if (rht && block_2d) return -1;
 
   float *xv = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
@@ -464,10 +475,10 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
       t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
       oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, rht == 2, t);
     }
-    float S = oracle_global_encode_scale_fmt(amax_col[0], scale_fmt);
     float *v = (float *)malloc(sizeof(float) * (size_t)rows);
     float *e = (float *)malloc(sizeof(float) * (size_t)(rows / 16));
     for (int64_t j = 0; j < cols; ++j) {
+      float S = oracle_global_encode_scale_fmt(row_scaled ? amax_col[j] : amax_col[0], scale_fmt);
       for (int64_t i = 0; i < rows; ++i) v[i] = rht ? t[j * rows + i] : xv[i * cols + j];
       for (int64_t b = 0; b < rows / 16; ++b) {
         float m = 0.0f;

@@ -273,9 +273,9 @@ def test_amax_per_tensor_and_per_row_match_numpy():
     xf = W.bf16_to_float(x)
     a, b = O.compute_amax(x)
     assert a[0] == np.abs(xf).max() and b[0] == a[0]
-    r, none = O.compute_amax(x, O.AMAX_PER_ROW)
-    assert none is None
+    r, c = O.compute_amax(x, O.AMAX_PER_ROW)
     np.testing.assert_array_equal(r, np.abs(xf).max(axis=1))
+    np.testing.assert_array_equal(c, np.abs(xf).max(axis=0))
 
 
 def test_amax_sequence_exact_maxima():
@@ -378,6 +378,57 @@ def test_row_scaled_row_equals_per_tensor_single_row():
         assert np.array_equal(q["row_data"][r], qr["row_data"][0])
         assert np.array_equal(q["row_scales"][r], qr["row_scales"][0])
         assert q["amax_row"][r] == qr["amax_row"][0]
+
+
+# Row-scaled column-wise side (reading: the column-wise tensor, whose rows
+# are the input's columns, is row-scaled along its own rows, so its amax
+# buffer has one float per input column, as the row-scaled page's review
+# thread sizes it).
+
+def test_row_scaled_columnwise_column_equals_per_tensor_single_row():
+    x = W.c4(rows=64, cols=48, seed=5)
+    q = O.quantize(x, rowwise=False, row_scaled=True)
+    assert q["amax_col"].shape == (48,)
+    for j in range(48):
+        qj = O.quantize(np.ascontiguousarray(x[:, j:j + 1].T), columnwise=False)
+        assert np.array_equal(q["col_data"][j], qj["row_data"][0]), j
+        assert np.array_equal(q["col_scales"][j], qj["row_scales"][0]), j
+        assert q["amax_col"][j] == qj["amax_row"][0], j
+
+
+def test_row_scaled_columnwise_is_row_scaled_rowwise_of_transpose():
+    x = W.gaussian_fp32(32, 80, 12)
+    x *= (2.0 ** np.linspace(-6, 6, 80)).astype(np.float32)[None, :]
+    q = O.quantize(x, row_scaled=True)
+    qt = O.quantize(np.ascontiguousarray(x.T), columnwise=False, row_scaled=True)
+    assert np.array_equal(q["col_data"], qt["row_data"])
+    assert np.array_equal(q["col_scales"], qt["row_scales"])
+    np.testing.assert_array_equal(q["amax_col"], qt["amax_row"])
+    # and the row-wise side is unchanged by asking for both
+    qr = O.quantize(x, columnwise=False, row_scaled=True)
+    assert np.array_equal(q["row_data"], qr["row_data"]) and np.array_equal(q["row_scales"], qr["row_scales"])
+
+
+def test_row_scaled_columnwise_power_of_two_per_column():
+    x = W.gaussian_fp32(32, 16, 13)
+    q0 = O.quantize(x, rowwise=False, row_scaled=True)
+    f = (2.0 ** np.arange(-8, 8)).astype(np.float32)
+    q1 = O.quantize((x * f[None, :]).astype(np.float32), rowwise=False, row_scaled=True)
+    assert np.array_equal(q0["col_data"], q1["col_data"])
+    assert np.array_equal(q0["col_scales"], q1["col_scales"])
+    np.testing.assert_array_equal(q1["amax_col"], q0["amax_col"] * f)
+
+
+def test_row_scaled_columnwise_equal_column_maxima_is_per_tensor_sr():
+    # every column holds the tensor's maximum, so every per-column global
+    # scale is the per-tensor one, stochastic rounding included
+    x = W.gaussian_fp32(48, 32, 14)
+    x[5, :] = 9.5
+    q = O.quantize(x, rowwise=False, row_scaled=True, stochastic=True, sr_seed=21)
+    qt = O.quantize(x, rowwise=False, stochastic=True, sr_seed=21)
+    assert np.all(q["amax_col"] == 9.5)
+    assert np.array_equal(q["col_data"], qt["col_data"])
+    assert np.array_equal(q["col_scales"], qt["col_scales"])
 
 
 def test_columnwise_is_rowwise_of_transpose():
