@@ -216,6 +216,9 @@ OTHER_WORKLOADS = {
                bytes=2 * 4 * 1088 * 1024 + 2 * (1088 * 1024 // 2 + 1088 * 1024 // 16) + 8),
     "c4": dict(desc="4096x8192 BF16 N(0,1) x per-row exp(2n) (seed 3); per-row amax; row-wise only; compact; RNE",
                bytes=2 * 4096 * 8192 + 4096 * 8192 // 2 + 4096 * 8192 // 16 + 4 * 4096),
+    "c4_both": dict(desc="as c4, both orientations: per-row amax for the row-wise side, per-column amax for the "
+                         "column-wise side (three input reads: fused row pass, column amax, column encode)",
+                    bytes=3 * 2 * 4096 * 8192 + 2 * (4096 * 8192 // 2 + 4096 * 8192 // 16) + 4 * (4096 + 8192)),
     "c5": dict(desc="8192x8192 BF16 N(0,1) + 0.1% at +-200 (seed 4); 1x16; row plain + col 16-point RHT; "
                     "stochastic rounding (seed 5); compact",
                bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),
@@ -256,8 +259,8 @@ def run_other(name, steps, warmup):
         x, cfg, rowwise, columnwise = workloads.c1(), nv.make_config(), True, True
     elif name == "c3":
         x, cfg, rowwise, columnwise = workloads.c3()[0], nv.make_config(), True, True
-    elif name == "c4":
-        x, cfg, rowwise, columnwise = workloads.c4(), nv.make_config(row_scaled=True), True, False
+    elif name in ("c4", "c4_both"):
+        x, cfg, rowwise, columnwise = workloads.c4(), nv.make_config(row_scaled=True), True, name == "c4_both"
     elif name == "c2_ue5m3":
         x = workloads.c2()
         cfg, rowwise, columnwise = nv.make_config(block_2d=True, swizzled=True, scale_fmt=nv.NVFP4_SCALE_UE5M3), True, True
@@ -275,7 +278,7 @@ def run_other(name, steps, warmup):
     for _ in range(n_sets):
         rows, cols = x.shape
         row = nv.empty_orientation(rows, cols, dev, rows if cfg.row_scaled else 1) if rowwise else None
-        col = nv.empty_orientation(cols, rows, dev) if columnwise else None
+        col = nv.empty_orientation(cols, rows, dev, cols if cfg.row_scaled else 1) if columnwise else None
         sets.append((xd.clone() if n_sets > 1 else xd, row, col))
     stream = torch.cuda.current_stream()
     for i in range(warmup):

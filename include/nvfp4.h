@@ -130,8 +130,13 @@ typedef struct {
   uint32_t stochastic;
   uint32_t sr_seed;
   /* 1: one amax per row of the input ("Implement row-scaled NVFP4 fprop
-   * recipe", Changes): row-wise orientation only, 1x16 blocks, compact
-   * scales, no RHT; row->amax holds R floats. */
+   * recipe", Changes): 1x16 blocks, compact scales, no RHT; row->amax
+   * holds R floats. The column-wise orientation, whose rows are the input's
+   * columns, is scaled along its own rows the same way: col->amax holds C
+   * floats, col->amax[j] = max_i |x[i][j]| (the same page's review thread
+   * sizes that buffer by the input's last dimension; how the column-wise
+   * side uses it is not on the page, so this reading is the plainest one),
+   * and row->amax and col->amax must be distinct buffers. */
   uint32_t row_scaled;
   /* 1: the column-wise orientation encodes the 16-point random Hadamard
    * transform of each group of 16 consecutive rows of a column: with
@@ -182,7 +187,8 @@ typedef struct {
   void *workspace;
   /* nvfp4_quantize only: NULL, or the address of two hipEvent_t handles
    * that the call records on its stream just before and just after the
-   * launch of its cast kernel (the row-scaled kernel on that path), so that
+   * launch of its cast kernel (on the row-scaled path: before its first
+   * and after its last kernel, per-column amax pass included), so that
    * the kernel can be timed inside a whole call. Not recorded when the call
    * is rejected or the input is empty. */
   void *const *cast_events;
@@ -205,8 +211,9 @@ uint64_t nvfp4_workspace_bytes(void);
  *   default:   both buffers are set to +0 and then to max|x| by one
  *              reduction; either pointer may be NULL; equal pointers are
  *              written once.
- *   row_scaled: row_amax[i] = max_j |x[i][j]| for each of R rows;
- *              col_amax must be NULL.
+ *   row_scaled: row_amax[i] = max_j |x[i][j]| for each of R rows and
+ *              col_amax[j] = max_i |x[i][j]| for each of C columns; either
+ *              pointer may be NULL; equal pointers are rejected.
  *   rht:       row_amax = max|x|, col_amax = max|t| over the column-wise
  *              RHT image (needs R % 16 == 0), both from one read of x.
  * An empty input (R == 0 or C == 0) writes +0.
@@ -228,7 +235,8 @@ nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t ro
  *
  * With compute_amax == 1 this queues the zeroing pass, the amax reduction
  * and the cast, or with a workspace the amax pass and the cast, which
- * finishes the reduction (row-scaled: one fused kernel); with
+ * finishes the reduction (row-scaled: one fused kernel for the row-wise
+ * side; the column-wise side zeroes, reduces and encodes in three); with
  * compute_amax == 0 only the cast, which reads the amax buffers as given.
  * Either way the amax buffers hold the same values afterwards.
  */
@@ -256,7 +264,7 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
  *        block), amax [G].
  * Each group_rows[g] must be a multiple of 16 for column-wise output, 16x16
  * blocks or the RHT, and of 128 for swizzled scales (C too). Row-scaled
- * configs (row-wise only, 1x16, compact, no RHT) run as one fused launch:
+ * configs (row-wise only here, 1x16, compact, no RHT) run as one fused launch:
  * row->amax then holds one entry per row, [R] (the same page's grouped
  * storage sizes it as the sum of the groups' rows), and nearest-even
  * results equal a single nvfp4_quantize over all rows; stochastic rounding
@@ -277,7 +285,9 @@ nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_
  * k % 16 == 0) into y [rows][cols] FP32 (device, 4-byte aligned):
  * y = (value(code) * value(s)) / S, S from q->amax[0], or q->amax[i] for
  * row i when row_scaled ("Implement row-scaled NVFP4 fprop recipe",
- * Changes: the dequantize kernel selects the row's amax). scale_layout and
+ * Changes: the dequantize kernel selects the row's amax; a row-scaled
+ * column-wise tensor passes its per-column amax, which is per row in its
+ * own orientation). scale_layout and
  * scale_fmt (nvfp4_scale_fmt_t) are those the tensor was quantized with.
  */
 nvfp4_status_t nvfp4_dequantize(const nvfp4_out_t *q, int64_t rows, int64_t cols, uint32_t scale_layout,

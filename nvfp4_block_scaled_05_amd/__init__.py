@@ -227,7 +227,7 @@ def nvfp4_compute_amax(x: torch.Tensor, row_amax: Optional[torch.Tensor], col_am
     if row_amax is not None:
         _need(row_amax, rows if (cfg is not None and cfg.row_scaled) else 1, torch.float32, "row_amax")
     if col_amax is not None:
-        _need(col_amax, 1, torch.float32, "col_amax")
+        _need(col_amax, cols if (cfg is not None and cfg.row_scaled) else 1, torch.float32, "col_amax")
     _check(load().nvfp4_compute_amax(_ptr(x), _dtype_code(x), rows, cols, _ptr(row_amax), _ptr(col_amax),
                                      None if cfg is None else ctypes.byref(cfg), _stream(stream)))
 
@@ -236,7 +236,7 @@ def nvfp4_quantize(x: torch.Tensor, row: Optional[Orientation], col: Optional[Or
                    cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
     rows, cols = _shape2d(x)
     _need_orientation(row, rows, cols, rows if (cfg is not None and cfg.row_scaled) else 1, "row-wise")
-    _need_orientation(col, cols, rows, 1, "column-wise")
+    _need_orientation(col, cols, rows, cols if (cfg is not None and cfg.row_scaled) else 1, "column-wise")
     r = row.as_c() if row is not None else None
     c = col.as_c() if col is not None else None
     _check(load().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, None if r is None else ctypes.byref(r),
@@ -383,7 +383,7 @@ def quantize(x: torch.Tensor, *, rowwise=True, columnwise=True, cfg: Optional[nv
     rows, cols = _shape2d(x)
     cfg = cfg if cfg is not None else make_config()
     row = empty_orientation(rows, cols, x.device, rows if cfg.row_scaled else 1) if rowwise else None
-    col = empty_orientation(cols, rows, x.device) if columnwise else None
+    col = empty_orientation(cols, rows, x.device, cols if cfg.row_scaled else 1) if columnwise else None
     ws = None
     if use_workspace and not cfg.workspace and cfg.compute_amax and not cfg.row_scaled:
         ws = stream_workspace(x.device, stream)

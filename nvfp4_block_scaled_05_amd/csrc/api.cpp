@@ -127,12 +127,19 @@ extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype,
   if (cfg.row_scaled && cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled amax cannot be combined with the RHT");
   if (cfg.rht_bf16 && !cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "rht_bf16 needs rht");
   if (cfg.row_scaled) {
-    if (col_amax != nullptr)
-      return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled amax is row-wise only: col_amax must be NULL");
-    if (row_amax == nullptr) return fail(NVFP4_ERR_NULL, "row-scaled amax needs row_amax");
-    nvfp4::RowScaledArgs a{x, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), nullptr, nullptr,
-                           row_amax, 0u, cfg.noop};
-    return hip_status(nvfp4::launch_rowscaled(a, dtype, false, true, s), "row amax launch");
+    if (row_amax != nullptr && row_amax == col_amax)
+      return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled per-row and per-column amaxes need two distinct buffers");
+    const uint32_t R = static_cast<uint32_t>(rows), C = static_cast<uint32_t>(cols);
+    if (row_amax != nullptr) {
+      nvfp4::RowScaledArgs a{x, R, C, nullptr, nullptr, row_amax, 0u, cfg.noop};
+      if ((st = hip_status(nvfp4::launch_rowscaled(a, dtype, false, true, s), "row amax launch")) != NVFP4_OK)
+        return st;
+    }
+    if (col_amax != nullptr) {
+      nvfp4::RowScaledArgs c{x, R, C, nullptr, nullptr, col_amax, 0u, cfg.noop};
+      return hip_status(nvfp4::launch_colscaled(c, dtype, false, true, s), "column amax launch");
+    }
+    return NVFP4_OK;
   }
   if (cfg.rht) {
     if (rows % 16 != 0) return fail(NVFP4_ERR_SHAPE, "the RHT needs rows %% 16 == 0 (rows = %lld)", (long long)rows);
@@ -176,7 +183,8 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   if (cfg.amax_path > NVFP4_AMAX_PATH_SINGLE_PASS)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown amax path %u", cfg.amax_path);
   if (cfg.row_scaled) {
-    if (col) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 is row-wise only");
+    if (row && col && row->amax == col->amax)
+      return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled per-row and per-column amaxes need two distinct buffers");
     if (cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 uses 1x16 blocks");
     if (cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 cannot be combined with the RHT");
     if (swz) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 keeps compact scales");
@@ -201,10 +209,17 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
                  : NVFP4_OK;
   };
   if (cfg.row_scaled) {
-    nvfp4::RowScaledArgs a{x, R, C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop};
-    a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
+    const uint32_t ue = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
     if ((st = record(0)) != NVFP4_OK) return st;
-    st = hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
+    if (row) {
+      nvfp4::RowScaledArgs a{x, R, C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop, ue};
+      st = hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
+    }
+    if (st == NVFP4_OK && col) {
+      nvfp4::RowScaledArgs c{x, R, C, col->data, col->scales, col->amax, cfg.sr_seed, cfg.noop, ue};
+      st = hip_status(nvfp4::launch_colscaled(c, dtype, sr, cfg.compute_amax != 0, s),
+                      "row-scaled column-wise quantize launch");
+    }
     return st != NVFP4_OK ? st : record(1);
   }
   float *ra = row ? row->amax : nullptr;
@@ -290,7 +305,7 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   if (row && (st = check_out(row, "row-wise", empty)) != NVFP4_OK) return st;
   if (col && (st = check_out(col, "column-wise", empty)) != NVFP4_OK) return st;
   if (cfg.row_scaled) {
-    if (col) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 is row-wise only");
+    if (col) return fail(NVFP4_ERR_UNSUPPORTED, "grouped row-scaled NVFP4 is row-wise only");
     if (cfg.block_2d) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 uses 1x16 blocks");
     if (cfg.rht) return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled NVFP4 cannot be combined with the RHT");
     if (cfg.scale_layout == NVFP4_SCALES_GEMM_SWIZZLED)

@@ -72,12 +72,14 @@ struct CastArgs {
   uint32_t ue5m3;  // block scales in UE5M3 rather than E4M3
 };
 
-// Arguments of the row-scaled (per-row amax) kernel: row-wise output only.
+// Arguments of the row-scaled kernels: the row-wise side (one amax per row)
+// or the column-wise side (one amax per input column; data and scales are
+// the transposed [cols][rows / 2] and [cols][rows / 16] arrays).
 struct RowScaledArgs {
   const void *x;
   uint32_t rows, cols;
-  uint8_t *data, *scales;  // NULL data: only compute the per-row amax
-  float *amax;             // [rows]
+  uint8_t *data, *scales;  // NULL data: only compute the amax
+  float *amax;             // [rows] (row-wise side) or [cols] (column-wise side)
   uint32_t sr_seed;
   const float *noop;
   uint32_t ue5m3;  // block scales in UE5M3 rather than E4M3
@@ -134,6 +136,10 @@ hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, con
                                uint32_t ngroups, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
+// Column-wise side: compute_amax zeroes a.amax ([cols]) and reduces each
+// column's amax (two launches), else a.amax is read; then, unless a.data is
+// NULL, the column-wise encode (rows % 16 == 0).
+hipError_t launch_colscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
 // grouped form: row_start[0..ngroups] are the groups' first rows (stochastic
 // rounding counts byte indices per group)
 hipError_t launch_rowscaled_grouped(const RowScaledArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,

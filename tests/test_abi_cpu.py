@@ -80,10 +80,13 @@ def test_swizzled_scales_reject_partial_tiles():
 
 
 def test_row_scaled_gates():
-    # "Implement row-scaled NVFP4 fprop recipe": row-wise only; compact scales;
+    # "Implement row-scaled NVFP4 fprop recipe": compact scales; the per-row
+    # and per-column amaxes are two arrays, so one buffer for both is refused;
     # "Fuse NVFP4 scale swizzling ...": no row-scaled RHT.
     rs = nv.make_config(row_scaled=True)
-    assert _q(128, 128, row=_out(), col=_out(A2), cfg=rs) == nv.NVFP4_ERR_UNSUPPORTED
+    assert _q(128, 128, row=_out(), col=_out(), cfg=rs) == nv.NVFP4_ERR_UNSUPPORTED
+    assert "distinct" in nv.nvfp4_last_error()
+    assert _q(120, 128, col=_out(A2), cfg=rs) == nv.NVFP4_ERR_SHAPE  # column-wise: rows % 16
     assert _q(128, 128, row=_out(), cfg=nv.make_config(row_scaled=True, swizzled=True)) == nv.NVFP4_ERR_UNSUPPORTED
     assert _q(128, 128, row=_out(), cfg=nv.make_config(row_scaled=True, rht=True)) == nv.NVFP4_ERR_UNSUPPORTED
     assert _q(128, 128, row=_out(), cfg=nv.make_config(row_scaled=True, block_2d=True)) == nv.NVFP4_ERR_UNSUPPORTED
@@ -114,7 +117,7 @@ def test_compute_amax_rejections():
     assert lib.nvfp4_compute_amax(X, 0, 64, 64, None, None, None, None) == nv.NVFP4_ERR_NULL
     assert lib.nvfp4_compute_amax(X, 0, 64, 64, A + 2, None, None, None) == nv.NVFP4_ERR_ALIGN
     rs = nv.make_config(row_scaled=True)
-    assert lib.nvfp4_compute_amax(X, 0, 64, 64, A, A2, ctypes.byref(rs), None) == nv.NVFP4_ERR_UNSUPPORTED
+    assert lib.nvfp4_compute_amax(X, 0, 64, 64, A, A, ctypes.byref(rs), None) == nv.NVFP4_ERR_UNSUPPORTED
     rht = nv.make_config(rht=True)
     assert lib.nvfp4_compute_amax(X, 0, 40, 64, A, A2, ctypes.byref(rht), None) == nv.NVFP4_ERR_SHAPE
     assert lib.nvfp4_compute_amax(X, 0, 64, 64, A, A, ctypes.byref(rht), None) == nv.NVFP4_ERR_UNSUPPORTED
