@@ -381,7 +381,9 @@ __device__ __forceinline__ void encode_unit(const RowScaledArgs &p, const Piece8
       lo = e2m1_rne_x8(s);
       hi = e2m1_rne_x8(s + 8);
     }
-    __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(p.data + byte0));
+    // plain stores: a wave writes 64-byte halves of output lines, which the
+    // L2 merges (non-temporal stores of them measured 7% slower)
+    *reinterpret_cast<u32x2 *>(p.data + byte0) = u32x2{lo, hi};
     p.scales[static_cast<uint64_t>(j) * (p.rows >> 4) + (r0 >> 4)] = static_cast<uint8_t>(bs.code);
   }
 }
