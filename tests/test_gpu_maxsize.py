@@ -1,8 +1,9 @@
 """GPU: the largest accepted input (R * C just below 2^32): 65536 x 65520
 BF16, both orientations, 1x16 blocks, checked on sampled blocks across the
 whole tensor (first, middle and last tiles) against the oracle computing
-those blocks one by one with the tensor's amax. Byte offsets and the
-stochastic-rounding byte indices reach 2^31 here."""
+those blocks one by one with the tensor's amax; and the row-scaled
+column-wise side (one amax per input column) on the same samples. Byte
+offsets and the stochastic-rounding byte indices reach 2^31 here."""
 
 from __future__ import annotations
 
@@ -87,3 +88,21 @@ def test_largest_input(big, stochastic):
     torch.cuda.synchronize()
     _check_samples(big, row, col, stochastic)
     del row, col
+
+
+def test_largest_input_row_scaled_columnwise(big):
+    # one amax per input column; sampled columns checked against a plain
+    # torch reduction of that column, sampled blocks against the oracle with
+    # those amaxes
+    _, col = nv.quantize(big, rowwise=False, cfg=nv.make_config(row_scaled=True))
+    torch.cuda.synchronize()
+    amax = host(col.amax)
+    cd, cs = col.data, col.scales.view(C, R // 16)
+    for (i, j) in SAMPLES:
+        ref_amax = big[:, j:j + 128].abs().amax(dim=0).float().cpu().numpy()
+        np.testing.assert_array_equal(amax[j:j + 128], ref_amax, err_msg=f"column amax at {j}")
+        xs = _host_bf16(big[i:i + 16, j:j + 128])
+        ref = O.quantize(xs, rowwise=False, row_scaled=True, amax_col=ref_amax)
+        assert np.array_equal(host(cd[j:j + 128, i // 2:i // 2 + 8]), ref["col_data"]), (i, j)
+        assert np.array_equal(host(cs[j:j + 128, i // 16:i // 16 + 1]), ref["col_scales"]), (i, j)
+    del col
