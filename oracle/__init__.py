@@ -31,15 +31,22 @@ FP32 = 1
 _lib = None
 
 
+def compile_library(src: str, out: str) -> str:
+    """Compile an oracle source into a shared library with gcc: binary32
+    arithmetic, no contraction, no fast-math."""
+    tmp = out + ".tmp"
+    subprocess.check_call([
+        "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-Wextra",
+        "-fPIC", "-shared", src, "-o", tmp, "-lm",
+    ])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc: binary32 arithmetic, no contraction, no fast-math."""
+    """Compile the oracle (see compile_library)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call([
-            "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-Wextra",
-            "-fPIC", "-shared", _SRC, "-o", tmp, "-lm",
-        ])
-        os.replace(tmp, _LIB)
+        compile_library(_SRC, _LIB)
     return _LIB
 
 
@@ -48,7 +55,13 @@ def _load():
     if _lib is not None:
         return _lib
     build(force=False)
-    lib = ctypes.CDLL(_LIB)
+    _lib = bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def bind(lib):
+    """Set the C signatures on a loaded oracle library (this package's, or a
+    test's deliberately altered copy) and return it."""
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     I = ctypes.c_int
@@ -94,7 +107,6 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 
