@@ -19,10 +19,16 @@
  *
  * Conventions for every call:
  *   - Tensors are row-major. Device buffers are owned by the caller; the
- *     library allocates nothing, keeps no state between calls, and never
- *     synchronizes: work is queued on `stream` (a hipStream_t; NULL means
- *     the null stream) and runs asynchronously. Pointers are never stored,
- *     so calls can be captured in a HIP graph.
+ *     library allocates no device memory and never synchronizes: work is
+ *     queued on `stream` (a hipStream_t; NULL means the null stream) and
+ *     runs asynchronously. Pointers are never stored, so calls can be
+ *     captured in a HIP graph.
+ *   - State kept between calls: on the device, only what a caller's
+ *     workspace holds (nvfp4_config_t.workspace). On the host, process-wide
+ *     caches of per-device launch facts (occupancy limits and compute-unit
+ *     counts, read once from the runtime), the wait bound that
+ *     nvfp4_debug_set_wait_ticks sets, and the per-thread text of
+ *     nvfp4_last_error. None of it changes what a call computes.
  *   - Arguments are validated on the host before anything is queued. On a
  *     bad argument the call returns a non-zero status, queues nothing and
  *     writes nothing; nvfp4_last_error() then describes the problem.
@@ -133,10 +139,11 @@ typedef struct {
    * recipe", Changes): 1x16 blocks, compact scales, no RHT; row->amax
    * holds R floats. The column-wise orientation, whose rows are the input's
    * columns, is scaled along its own rows the same way: col->amax holds C
-   * floats, col->amax[j] = max_i |x[i][j]| (the same page's review thread
-   * sizes that buffer by the input's last dimension; how the column-wise
-   * side uses it is not on the page, so this reading is the plainest one),
-   * and row->amax and col->amax must be distinct buffers. */
+   * floats, col->amax[j] = max_i |x[i][j]| (the quantizer prototype in the
+   * review thread of "Write both NVFP4 amax buffers" sizes the column-wise
+   * amax of a row-scaled tensor by the input's last dimension; how the
+   * column-wise side uses it is on no page, so this reading is the plainest
+   * one), and row->amax and col->amax must be distinct buffers. */
   uint32_t row_scaled;
   /* 1: the column-wise orientation encodes the 16-point random Hadamard
    * transform of each group of 16 consecutive rows of a column: with
@@ -226,6 +233,17 @@ nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype, int64_t ro
  * Quantize x (R x C, device, 16-byte aligned, C % 16 == 0, R * C < 2^32)
  * into the requested orientations; row or col may be NULL, not both. The
  * column-wise orientation needs R % 16 == 0.
+ *
+ * Sources: "Write both NVFP4 amax buffers" (Description, Changes: one
+ * quantize call writes the row-wise and the column-wise orientation, 1D and
+ * 2D blocks, each from its own amax buffer filled by one reduction; GPU work
+ * per quantize call: zeroing, amax, cast); "Fuse NVFP4 scale swizzling on
+ * SM120 and SM121" (Description, Changes: E4M3 or UE5M3 block scales,
+ * stochastic rounding, the RHT column-wise side, scales written in the GEMM
+ * layout by the quantize kernel); "Implement row-scaled NVFP4 fprop recipe"
+ * (Changes, Greptile summary: FP8 block scales relative to a per-tensor or
+ * per-row amax, with a zero guard). The formula below is the reading taken
+ * of that two-level scaling; the pages state no operation order.
  *
  * Per orientation: S = 2688 / amax (368640 / amax with UE5M3 scales; 1
  * when amax == 0, at most FLT_MAX); per block of 16 (or 16x16): m = max|v|,

@@ -3,11 +3,13 @@
 // Every argument is checked before anything is queued, so a rejected call
 // writes nothing. The gates follow the pages: swizzled scales need 128x128
 // alignment and partial tiles are rejected ("Fuse NVFP4 scale swizzling on
-// SM120 and SM121", Changes and Validation); row-scaled NVFP4 is row-wise,
+// SM120 and SM121", Changes and Validation); row-scaled NVFP4 is 1x16,
 // compact and not combined with the RHT ("Implement row-scaled NVFP4 fprop
-// recipe", Changes; "Fuse NVFP4 scale swizzling ...", Changes); an RHT
-// quantize cannot share one float between its two amaxes ("Write both NVFP4
-// amax buffers", review thread).
+// recipe", Changes; "Fuse NVFP4 scale swizzling ...", Changes), its
+// column-wise side taking one amax per input column (the quantizer
+// prototype in the review thread of "Write both NVFP4 amax buffers"); an
+// RHT quantize cannot share one float between its two amaxes ("Write both
+// NVFP4 amax buffers", review thread).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>

@@ -213,9 +213,10 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled_grouped(RowScaledArgs p,
 // Column-wise side of a row-scaled quantize. The column-wise tensor's rows
 // are the input's columns, so it is scaled along them: one amax per input
 // column, and each column's 1x16 blocks (16 consecutive rows) take their
-// E4M3 scales relative to that column's global scale (the row-scaled page
-// sizes the column-wise amax buffer of a row-scaled tensor as one float per
-// input column). Two launches: a column reduction (HBM-bound, one read of
+// E4M3 scales relative to that column's global scale (the quantizer
+// prototype in the review thread of "Write both NVFP4 amax buffers" sizes
+// the column-wise amax of a row-scaled tensor as one float per input
+// column). Two launches: a column reduction (HBM-bound, one read of
 // the input) and the encode (one more read, the transpose written out).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kColAmaxCols = 512;  // 64 lanes x 8 columns: one wave reads 1 KiB (BF16) of a row
@@ -458,8 +459,9 @@ hipError_t launch_colscaled(const RowScaledArgs &a, int dtype, bool sr, bool com
   // resident workgroups: compute units x what one holds (the latter depends
   // on the kernel's registers only, so it is taken once per kernel)
   static std::atomic<int> occupancy[2][2];
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipDevice_t dev = 0;
+  int cus = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);  // the device the work runs on
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   int per_cu = occupancy[dtype == kBF16][sr].load(std::memory_order_relaxed);

@@ -1,7 +1,7 @@
 """GPU parity for the column-wise side of a row-scaled quantize: one amax per
 input column, the column-wise tensor (the transpose) scaled along its own
-rows ("Implement row-scaled NVFP4 fprop recipe", review thread: that amax
-buffer holds one float per input column). Bit-exact against the oracle:
+rows (the quantizer prototype in the review thread of "Write both NVFP4
+amax buffers" gives that amax buffer one float per input column). Bit-exact against the oracle:
 per-column amax, scales, FP4 bytes, dequantized values."""
 
 from __future__ import annotations

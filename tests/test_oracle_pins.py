@@ -382,8 +382,8 @@ def test_row_scaled_row_equals_per_tensor_single_row():
 
 # Row-scaled column-wise side (reading: the column-wise tensor, whose rows
 # are the input's columns, is row-scaled along its own rows, so its amax
-# buffer has one float per input column, as the row-scaled page's review
-# thread sizes it).
+# buffer has one float per input column, as the quantizer prototype in the
+# review thread of "Write both NVFP4 amax buffers" sizes it).
 
 def test_row_scaled_columnwise_column_equals_per_tensor_single_row():
     x = W.c4(rows=64, cols=48, seed=5)
