@@ -15,6 +15,7 @@ numpy arrays in the layouts the C functions document:
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -24,6 +25,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same source built with OpenMP: only the CPU-baseline timing uses it
+_LIB_PARALLEL = os.path.join(_HERE, "liboracle_omp.so")
 
 BF16 = 0
 FP32 = 1
@@ -31,23 +34,52 @@ FP32 = 1
 _lib = None
 
 
-def compile_library(src: str, out: str) -> str:
+def compile_library(src: str, out: str, openmp: bool = False) -> str:
     """Compile an oracle source into a shared library with gcc: binary32
-    arithmetic, no contraction, no fast-math."""
+    arithmetic, no contraction, no fast-math; with openmp, its outer loops
+    run on all cores (same per-element arithmetic)."""
     tmp = out + ".tmp"
     subprocess.check_call([
         "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall", "-Wextra",
-        "-fPIC", "-shared", src, "-o", tmp, "-lm",
+        "-fPIC", "-shared", *(["-fopenmp"] if openmp else []), src, "-o", tmp, "-lm",
     ])
     os.replace(tmp, out)
     return out
 
 
+def _stale(lib: str) -> bool:
+    return not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(_SRC)
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle (see compile_library)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile the oracle, single-threaded (the checker) and with OpenMP
+    (the CPU-baseline timing); returns the checker's path."""
+    if force or _stale(_LIB):
         compile_library(_SRC, _LIB)
+    if force or _stale(_LIB_PARALLEL):
+        compile_library(_SRC, _LIB_PARALLEL, openmp=True)
     return _LIB
+
+
+_lib_parallel = None
+
+
+@contextlib.contextmanager
+def all_cores():
+    """Inside the block, the oracle functions run on the OpenMP build (its
+    outer loops over rows, columns and blocks spread over OMP_NUM_THREADS
+    threads, or all cores). Yields the thread count. Only for timing: the
+    results are the single-threaded checker's, bit for bit."""
+    global _lib, _lib_parallel
+    checker = _load()
+    if _lib_parallel is None:
+        build(force=False)
+        _lib_parallel = bind(ctypes.CDLL(_LIB_PARALLEL))
+    _lib = _lib_parallel
+    try:
+        yield int(_lib_parallel.oracle_num_threads())
+    finally:
+        _lib = checker
 
 
 def _load():
@@ -102,6 +134,7 @@ def bind(lib):
         "oracle_e2m1_sr_array": (None, [P, P, I64, P]),
         "oracle_e4m3_array": (None, [P, I64, P]),
         "oracle_fmix32_array": (None, [P, I64, P]),
+        "oracle_num_threads": (I, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -33,6 +33,24 @@
 #define ORACLE_BF16 0
 #define ORACLE_FP32 1
 
+/* The checker is built without OpenMP and runs single-threaded. For the
+ * CPU-baseline timing the same source is also built with -fopenmp: then the
+ * outer loops over rows, columns and blocks run in parallel. Each element's
+ * arithmetic is the same either way; only the max reductions combine
+ * partial maxima, and a maximum does not depend on that order. */
+#ifdef _OPENMP
+#include <omp.h>
+#define ORACLE_PARALLEL_FOR _Pragma("omp parallel for schedule(static)")
+#define ORACLE_PARALLEL_MAX_A _Pragma("omp parallel for schedule(static) reduction(max : a)")
+#define ORACLE_PARALLEL_MAX_B _Pragma("omp parallel for schedule(static) reduction(max : b)")
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+#define ORACLE_PARALLEL_FOR
+#define ORACLE_PARALLEL_MAX_A
+#define ORACLE_PARALLEL_MAX_B
+int oracle_num_threads(void) { return 1; }
+#endif
+
 /* ------------------------------------------------------------------ */
 /* Input decoding.                                                     */
 /* BF16 is the high half of a binary32 word, so widening is exact.     */
@@ -310,8 +328,9 @@ float oracle_round_bf16(float x) {
  * bf16 != 0 rounds every transformed value to BF16. */
 void oracle_rht_colwise_ex(const void *x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask, int bf16,
                            float *t /* [cols][rows] */) {
-  float w[16], out[16];
+  ORACLE_PARALLEL_FOR
   for (int64_t j = 0; j < cols; ++j) {
+    float w[16], out[16];
     for (int64_t g = 0; g < rows / 16; ++g) {
       for (int k = 0; k < 16; ++k) w[k] = oracle_load(x, dtype, (g * 16 + k) * cols + j);
       oracle_rht16(w, sign_mask, out);
@@ -340,6 +359,7 @@ void oracle_rht_colwise(const void *x, int dtype, int64_t rows, int64_t cols, ui
 void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, int mode,
                          uint32_t sign_mask, float *amax_row, float *amax_col) {
   if (mode == 1) {
+    ORACLE_PARALLEL_FOR
     for (int64_t i = 0; i < rows; ++i) {
       float a = 0.0f;
       for (int64_t j = 0; j < cols; ++j) a = fmaxf(a, fabsf(oracle_load(x, dtype, i * cols + j)));
@@ -347,6 +367,7 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
     }
     /* the column-wise tensor's rows are the input's columns */
     if (amax_col) {
+      ORACLE_PARALLEL_FOR
       for (int64_t j = 0; j < cols; ++j) {
         float a = 0.0f;
         for (int64_t i = 0; i < rows; ++i) a = fmaxf(a, fabsf(oracle_load(x, dtype, i * cols + j)));
@@ -356,6 +377,7 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
     return;
   }
   float a = 0.0f;
+  ORACLE_PARALLEL_MAX_A
   for (int64_t n = 0; n < rows * cols; ++n) a = fmaxf(a, fabsf(oracle_load(x, dtype, n)));
   if (mode == 0) {
     if (amax_row) amax_row[0] = a;
@@ -368,6 +390,7 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
     float *t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
     oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, mode == 3, t);
     float b = 0.0f;
+    ORACLE_PARALLEL_MAX_B
     for (int64_t n = 0; n < rows * cols; ++n) b = fmaxf(b, fabsf(t[n]));
     free(t);
     amax_col[0] = b;
@@ -428,6 +451,7 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
   if (rht && block_2d) return -1;
 
   float *xv = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
+  ORACLE_PARALLEL_FOR
   for (int64_t n = 0; n < rows * cols; ++n) xv[n] = oracle_load(x, dtype, n);
 
   /* 2D: the amax of every 16x16 block; each direction turns it into a
@@ -437,6 +461,7 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
   if (block_2d) {
     int64_t br = rows / 16, bc = cols / 16;
     m2d = (float *)malloc(sizeof(float) * (size_t)(br * bc));
+    ORACLE_PARALLEL_FOR
     for (int64_t bi = 0; bi < br; ++bi)
       for (int64_t bj = 0; bj < bc; ++bj) {
         float m = 0.0f;
@@ -448,8 +473,9 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
 
   /* Row-wise direction: output row i is x[i][:]. */
   if (want_row) {
-    float *e = (float *)malloc(sizeof(float) * (size_t)(cols / 16));
+    ORACLE_PARALLEL_FOR
     for (int64_t i = 0; i < rows; ++i) {
+      float *e = (float *)malloc(sizeof(float) * (size_t)(cols / 16));
       const float *v = xv + i * cols;
       float S = oracle_global_encode_scale_fmt(row_scaled ? amax_row[i] : amax_row[0], scale_fmt);
       for (int64_t b = 0; b < cols / 16; ++b) {
@@ -464,8 +490,8 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
         row_scales[i * (cols / 16) + b] = s;
       }
       encode_row(v, e, cols, stochastic, sr_seed, 0, i * (cols / 2), row_data + i * (cols / 2));
+      free(e);
     }
-    free(e);
   }
 
   /* Column-wise direction: output row j is column j of x, or its RHT image. */
@@ -475,9 +501,10 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
       t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
       oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, rht == 2, t);
     }
-    float *v = (float *)malloc(sizeof(float) * (size_t)rows);
-    float *e = (float *)malloc(sizeof(float) * (size_t)(rows / 16));
+    ORACLE_PARALLEL_FOR
     for (int64_t j = 0; j < cols; ++j) {
+      float *v = (float *)malloc(sizeof(float) * (size_t)rows);
+      float *e = (float *)malloc(sizeof(float) * (size_t)(rows / 16));
       float S = oracle_global_encode_scale_fmt(row_scaled ? amax_col[j] : amax_col[0], scale_fmt);
       for (int64_t i = 0; i < rows; ++i) v[i] = rht ? t[j * rows + i] : xv[i * cols + j];
       for (int64_t b = 0; b < rows / 16; ++b) {
@@ -492,9 +519,9 @@ int oracle_quantize_fmt(const void *x, int dtype, int64_t rows, int64_t cols, in
         col_scales[j * (rows / 16) + b] = s;
       }
       encode_row(v, e, rows, stochastic, sr_seed, 1, j * (rows / 2), col_data + j * (rows / 2));
+      free(v);
+      free(e);
     }
-    free(v);
-    free(e);
     free(t);
   }
 
