@@ -262,6 +262,30 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
                               const nvfp4_out_t *row, const nvfp4_out_t *col,
                               const nvfp4_config_t *cfg, void *stream);
 
+/*
+ * Allocation-free nvfp4_quantize, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, validation, results and errors as
+ * nvfp4_quantize, except that config.workspace must be NULL
+ * (NVFP4_ERR_UNSUPPORTED otherwise): the call uses a workspace of the
+ * library's own instead, a static device array of NVFP4_WORKSPACE_BYTES
+ * (36 KiB) that each GPU holds from its first such call until the process
+ * ends. That size serves every input nvfp4_quantize accepts, so no input is
+ * rejected for its size beyond nvfp4_quantize's own limits.
+ *   - No device memory is allocated or freed, by the library or by any
+ *     library it calls.
+ *   - The first call on a device also queues, on `stream`, one small kernel
+ *     that zero-fills that device's array (the workspace's first-use rule);
+ *     later calls find it as the previous call left it.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     on one GPU (different streams, or different host threads without
+ *     ordering) race on it and can produce wrong results. Queue them on one
+ *     stream.
+ */
+nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                      const nvfp4_out_t *row, const nvfp4_out_t *col,
+                                      const nvfp4_config_t *cfg, void *stream);
+
 /* Most groups of one nvfp4_quantize_grouped call. */
 #define NVFP4_MAX_GROUPS 256
 

@@ -52,7 +52,8 @@ NVFP4_MAX_GROUPS = 256
 
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
             "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes", "nvfp4_quantize_grouped",
-            "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack", "nvfp4_debug_set_wait_ticks")
+            "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack", "nvfp4_debug_set_wait_ticks",
+            "nvfp4_quantize_noalloc")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -110,6 +111,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_quantize.restype = I
     lib.nvfp4_quantize.argtypes = [P, I, I64, I64, ctypes.POINTER(nvfp4_out_t), ctypes.POINTER(nvfp4_out_t),
                                    ctypes.POINTER(nvfp4_config_t), P]
+    lib.nvfp4_quantize_noalloc.restype = I
+    lib.nvfp4_quantize_noalloc.argtypes = lib.nvfp4_quantize.argtypes
     lib.nvfp4_dequantize.restype = I
     lib.nvfp4_dequantize.argtypes = [ctypes.POINTER(nvfp4_out_t), I64, I64, U32, U32, U32, P, P]
     lib.nvfp4_last_error.restype = ctypes.c_char_p
@@ -242,6 +245,20 @@ def nvfp4_quantize(x: torch.Tensor, row: Optional[Orientation], col: Optional[Or
     _check(load().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, cols, None if r is None else ctypes.byref(r),
                                  None if c is None else ctypes.byref(c), None if cfg is None else ctypes.byref(cfg),
                                  _stream(stream)))
+
+
+def nvfp4_quantize_noalloc(x: torch.Tensor, row: Optional[Orientation], col: Optional[Orientation],
+                           cfg: Optional[nvfp4_config_t] = None, stream=None) -> None:
+    """nvfp4_quantize with the library's own per-device scratch in place of a
+    workspace (cfg.workspace must be unset); allocates nothing."""
+    rows, cols = _shape2d(x)
+    _need_orientation(row, rows, cols, rows if (cfg is not None and cfg.row_scaled) else 1, "row-wise")
+    _need_orientation(col, cols, rows, cols if (cfg is not None and cfg.row_scaled) else 1, "column-wise")
+    r = row.as_c() if row is not None else None
+    c = col.as_c() if col is not None else None
+    _check(load().nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x), rows, cols, None if r is None else ctypes.byref(r),
+                                         None if c is None else ctypes.byref(c),
+                                         None if cfg is None else ctypes.byref(cfg), _stream(stream)))
 
 
 def nvfp4_dequantize(q: Orientation, rows: int, cols: int, scale_layout: int, row_scaled: bool, y: torch.Tensor,

@@ -14,6 +14,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -162,13 +163,13 @@ extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype,
       "amax launch");
 }
 
-extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
-                                         const nvfp4_out_t *row, const nvfp4_out_t *col,
-                                         const nvfp4_config_t *cfg_in, void *stream) {
+namespace {
+
+// nvfp4_quantize's validation and, unless check_only, its launches.
+nvfp4_status_t quantize_impl(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols, const nvfp4_out_t *row,
+                             const nvfp4_out_t *col, const nvfp4_config_t &cfg, hipStream_t s, bool check_only) {
   nvfp4_status_t st = check_input(x, dtype, rows, cols);
   if (st != NVFP4_OK) return st;
-  const nvfp4_config_t cfg = config_or_default(cfg_in);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (row == nullptr && col == nullptr) return fail(NVFP4_ERR_NULL, "neither a row-wise nor a column-wise output");
   if (cfg.cast_events != nullptr && (cfg.cast_events[0] == nullptr || cfg.cast_events[1] == nullptr))
     return fail(NVFP4_ERR_NULL, "cast_events holds a NULL event");
@@ -201,6 +202,7 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   if (swz && (rows % 128 != 0 || cols % 128 != 0))
     return fail(NVFP4_ERR_SHAPE, "GEMM-swizzled scales need rows and cols that are multiples of 128 (got %lld x %lld)",
                 (long long)rows, (long long)cols);
+  if (check_only) return NVFP4_OK;
 
   const uint32_t R = static_cast<uint32_t>(rows), C = static_cast<uint32_t>(cols);
   const bool sr = cfg.stochastic != 0;
@@ -282,6 +284,95 @@ extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int
   if ((st = record(0)) != NVFP4_OK) return st;
   st = hip_status(nvfp4::launch_cast(a, dtype, cfg.block_2d != 0, cfg.rht != 0, sr, s), "quantize launch");
   return st != NVFP4_OK ? st : record(1);
+}
+
+}  // namespace
+
+extern "C" nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                         const nvfp4_out_t *row, const nvfp4_out_t *col,
+                                         const nvfp4_config_t *cfg_in, void *stream) {
+  return quantize_impl(x, dtype, rows, cols, row, col, config_or_default(cfg_in), static_cast<hipStream_t>(stream),
+                       false);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free quantize: nvfp4_quantize with the library's own copy of
+// the workspace, a file-scope device array that each GPU holds until the
+// process ends. Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is passed to kernels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr uint32_t kScratchWords = nvfp4::kWorkspaceWords;  // NVFP4_WORKSPACE_BYTES / 4
+static_assert(kScratchWords * 4 == NVFP4_WORKSPACE_BYTES, "scratch holds one quantize workspace");
+__device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch_ptr[kMaxScratchDevices];   // device address of each GPU's copy
+bool g_scratch_cleared[kMaxScratchDevices];    // its clearing kernel has been queued
+
+// Zero-fills n words (a kernel rather than hipMemsetAsync: calls may be
+// captured in a HIP graph).
+__global__ void k_clear_scratch(uint32_t *p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The scratch address on the device that `s` runs on; on the first call for
+// that device it also queues, on `s`, the clearing kernel that the
+// workspace's first use needs.
+nvfp4_status_t device_scratch(hipStream_t s, uint32_t **out) {
+  hipDevice_t dev = -1;
+  nvfp4_status_t st = hip_status(hipStreamGetDevice(s, &dev), "hipStreamGetDevice");
+  if (st != NVFP4_OK) return st;
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(NVFP4_ERR_UNSUPPORTED, "device %d: the allocation-free quantize supports devices 0..%d",
+                static_cast<int>(dev), kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if ((st = hip_status(hipGetDevice(&cur), "hipGetDevice")) != NVFP4_OK) return st;
+    if (cur != dev && (st = hip_status(hipSetDevice(dev), "hipSetDevice")) != NVFP4_OK) return st;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if ((st = hip_status(e, "hipGetSymbolAddress(scratch)")) != NVFP4_OK) return st;
+    if (p == nullptr) return fail(NVFP4_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = static_cast<uint32_t *>(p);
+  }
+  if (!g_scratch_cleared[dev]) {
+    hipLaunchKernelGGL(k_clear_scratch, dim3(kScratchWords / 256), dim3(256), 0, s, g_scratch_ptr[dev], kScratchWords);
+    if ((st = hip_status(hipGetLastError(), "scratch clearing launch")) != NVFP4_OK) return st;
+    g_scratch_cleared[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t dtype, int64_t rows, int64_t cols,
+                                                 const nvfp4_out_t *row, const nvfp4_out_t *col,
+                                                 const nvfp4_config_t *cfg_in, void *stream) {
+  nvfp4_config_t cfg = config_or_default(cfg_in);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg.workspace != nullptr)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_quantize_noalloc uses its own scratch: config.workspace must be NULL");
+  // The workspace the call needs is NVFP4_WORKSPACE_BYTES whatever the
+  // input's size (the amax pass grid-strides beyond its largest grid), so
+  // the scratch covers every input nvfp4_quantize accepts; the check keeps
+  // that promise explicit.
+  if (nvfp4_workspace_bytes() > uint64_t{kScratchWords} * 4)
+    return fail(NVFP4_ERR_UNSUPPORTED, "the call needs %llu bytes of scratch, more than the %llu held",
+                (unsigned long long)nvfp4_workspace_bytes(), (unsigned long long)kScratchWords * 4);
+  nvfp4_status_t st = quantize_impl(x, dtype, rows, cols, row, col, cfg, s, true);  // validation only
+  if (st != NVFP4_OK) return st;
+  uint32_t *ws = nullptr;
+  if ((st = device_scratch(s, &ws)) != NVFP4_OK) return st;
+  cfg.workspace = ws;
+  return quantize_impl(x, dtype, rows, cols, row, col, cfg, s, false);
 }
 
 extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_t num_groups,

@@ -70,6 +70,32 @@ def test_quantize_rejects_bad_arguments(case, expected):
     assert nv.nvfp4_last_error() != ""
 
 
+def _q_noalloc(rows, cols, row=None, col=None, cfg=None, x=X):
+    lib = nv.load()
+    return lib.nvfp4_quantize_noalloc(x, nv.NVFP4_IN_BF16, rows, cols, None if row is None else ctypes.byref(row),
+                                      None if col is None else ctypes.byref(col),
+                                      None if cfg is None else ctypes.byref(cfg), None)
+
+
+@pytest.mark.parametrize("case,expected", [
+    (dict(rows=64, cols=40, row=_out()), nv.NVFP4_ERR_SHAPE),
+    (dict(rows=40, cols=64, col=_out()), nv.NVFP4_ERR_SHAPE),
+    (dict(rows=64, cols=64), nv.NVFP4_ERR_NULL),
+    (dict(rows=64, cols=64, row=_out(), x=X + 2), nv.NVFP4_ERR_ALIGN),
+])
+def test_noalloc_quantize_rejects_bad_arguments(case, expected):
+    # validation comes before the device is touched (no HIP call here)
+    assert _q_noalloc(**case) == expected
+    assert nv.nvfp4_last_error() != ""
+
+
+def test_noalloc_quantize_refuses_a_workspace():
+    cfg = nv.make_config()
+    cfg.workspace = 0x600000
+    assert _q_noalloc(64, 64, row=_out(), cfg=cfg) == nv.NVFP4_ERR_UNSUPPORTED
+    assert "workspace" in nv.nvfp4_last_error()
+
+
 def test_swizzled_scales_reject_partial_tiles():
     # "Fuse NVFP4 scale swizzling on SM120 and SM121": partial 128x128 scale
     # tiles are rejected for swizzled output (e.g. the 1088x1024 tail shape).
