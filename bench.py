@@ -239,13 +239,16 @@ OTHER_WORKLOADS = {
     "grouped": dict(desc="grouped quantize, MoE-like: 64 groups of 0..512 rows (multiples of 128, seed 6; 16768 rows) "
                          "x 4096 BF16 N(0,1) (seed 7); 1x16; row+col; compact; RNE; per-group amax",
                     bytes=2 * 2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64),
+    "swizzle_shapes": dict(desc="separate swizzle pass vs in-kernel swizzled scales at the pages' ten 128-aligned "
+                                "production shapes (BF16 torch.randn, 1x16, row+col, RNE, one input reused)",
+                           bytes=None),
     "swizzle": dict(desc="separate compact -> GEMM-swizzled scale pass, both orientations of 1088x1024 "
                          "(partial tiles: 1088x64 -> 1152x64 and 1024x68 -> 1024x68 padded to 72)",
                     bytes=1088 * 64 + 1152 * 64 + 1024 * 68 + 1024 * 72),
 }
 
 
-def run_other(name, steps, warmup):
+def run_other(name, steps, warmup, rht_unit=0):
     import numpy as np
     import torch
 
@@ -257,6 +260,8 @@ def run_other(name, steps, warmup):
     w = OTHER_WORKLOADS[name]
     if name == "swizzle":
         return run_swizzle(nv, torch, dev, w, steps, warmup)
+    if name == "swizzle_shapes":
+        return run_swizzle_shapes(nv, torch, dev, w, steps, warmup)
     if name == "pages":
         return run_pages(nv, torch, dev, w, steps, warmup)
     if name == "grouped":
@@ -298,6 +303,8 @@ def run_other(name, steps, warmup):
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) * 1e6 / steps
     line = {"workload": name, "config": w["desc"], "us_per_call": round(us, 3),
+            **({"rht_transform": ("cast: matrix cores, amax pass: vector ALU", "vector ALU", "matrix cores")[rht_unit]}
+               if name.startswith("c5") else {}),
             "bytes_per_call": w["bytes"], "GBps": round(w["bytes"] / us / 1e3, 1),
             "pct_of_hbm_peak": round(100 * w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
             "buffer_sets_rotated": n_sets}
@@ -456,6 +463,52 @@ def run_swizzle(nv, torch, dev, w, steps, warmup):
                       "launches_per_call": 2}), flush=True)
 
 
+# The 128-aligned shapes of the pages' fused-swizzle validation ("Fuse NVFP4
+# scale swizzling on SM120 and SM121", Validation, footnote 5).
+PRODUCTION_SHAPES = ((8192, 2560), (8192, 3584), (8192, 5120), (8192, 10240), (2560, 8192), (3584, 8192),
+                     (5120, 8192), (10240, 8192), (4096, 16384), (14336, 16384))
+
+
+def run_swizzle_shapes(nv, torch, dev, w, steps, warmup):
+    """Per production shape (BF16, 1x16 blocks, both orientations, RNE, one
+    reused input as in the pages' loop): the quantize with compact scales,
+    the separate swizzle pass over both orientations' compact scales (two
+    launches), and the quantize that writes swizzled scales itself."""
+    stream = torch.cuda.current_stream()
+    ws = nv.empty_workspace(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps
+
+    for R, C in PRODUCTION_SHAPES:
+        g = torch.Generator(device=dev).manual_seed(0)
+        x = torch.randn((R, C), generator=g, device=dev).to(torch.bfloat16)
+        row, col = nv.empty_orientation(R, C, dev), nv.empty_orientation(C, R, dev)
+        compact = nv.make_config(workspace=ws)
+        fused = nv.make_config(swizzled=True, workspace=ws)
+        jobs = [(row.scales, R, C // 16, torch.empty((nv.nvfp4_swizzled_scales_bytes(R, C // 16),), dtype=torch.uint8,
+                                                       device=dev)),
+                (col.scales, C, R // 16, torch.empty((nv.nvfp4_swizzled_scales_bytes(C, R // 16),), dtype=torch.uint8,
+                                                       device=dev))]
+        us_compact = timed(lambda: nv.nvfp4_quantize(x, row, col, compact, stream))
+        us_pass = timed(lambda: [nv.nvfp4_swizzle_scales(*j, stream) for j in jobs])
+        us_fused = timed(lambda: nv.nvfp4_quantize(x, row, col, fused, stream))
+        pass_bytes = 2 * (R * C // 16) * 2  # read and write every scale byte of both orientations
+        print(json.dumps({"workload": "swizzle_shapes", "shape": f"{R}x{C}", "quantize_compact_us": round(us_compact, 3),
+                          "swizzle_pass_us": round(us_pass, 3), "swizzle_pass_GBps": round(pass_bytes / us_pass / 1e3, 1),
+                          "compact_plus_pass_us": round(us_compact + us_pass, 3),
+                          "quantize_swizzled_in_kernel_us": round(us_fused, 3),
+                          "in_kernel_saves_pct": round(100 * (1 - us_fused / (us_compact + us_pass)), 1)}), flush=True)
+        del x, row, col, jobs
+
+
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
@@ -558,6 +611,9 @@ def main():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of the input size (80 MiB read + 80 MiB write), "
                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--rht-unit", type=int, choices=[0, 1, 2], default=0,
+                   help="unit of the RHT transform for BF16 input: 0 default (cast on the matrix cores, amax pass "
+                        "on the vector ALU), 1 vector ALU in both, 2 matrix cores in both")
     p.add_argument("--workload", default="c2", choices=["c2"] + sorted(OTHER_WORKLOADS),
                    help="c2 (default) is the benchmark line; the others print their own timing line")
     p.add_argument("--summarize-trace", metavar="DB", help="print kernel stats of a rocprofv3 kernel trace")
@@ -574,7 +630,11 @@ def main():
     if args.workload != "c2":
         if args.gpus != 1:
             sys.exit(2)
-        return run_other(args.workload, args.steps, args.warmup)
+        if args.rht_unit:
+            import nvfp4_block_scaled_05_amd as nv
+
+            nv.nvfp4_debug_set_rht_unit(args.rht_unit)
+        return run_other(args.workload, args.steps, args.warmup, args.rht_unit)
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py measures one GPU: --gpus must be 1"}))
         sys.exit(2)

@@ -392,6 +392,20 @@ nvfp4_status_t nvfp4_debug_e2m1_pack(const float *v, const uint32_t *r, uint8_t 
  */
 nvfp4_status_t nvfp4_debug_set_wait_ticks(uint32_t ticks);
 
+/*
+ * Test hook: which unit runs the 16-point transform of BF16 input in the RHT
+ * amax pass and cast (nvfp4_quantize, nvfp4_quantize_grouped,
+ * nvfp4_compute_amax): on the matrix cores, two stages of 4x4 MFMAs per
+ * column; on the vector ALU, butterflies. 0 (the default): the matrix cores
+ * in the cast and the vector ALU in the amax pass, each the faster there on
+ * MI355X; 1: the vector ALU in both; 2: the matrix cores in both. Every form
+ * sums in binary32 and stays within the RHT tolerances of the oracle; they
+ * may differ from each other in the last bits. FP32 input always takes the
+ * vector ALU. Process-wide; takes effect for launches queued afterwards.
+ * Other values: NVFP4_ERR_UNSUPPORTED.
+ */
+nvfp4_status_t nvfp4_debug_set_rht_unit(uint32_t unit);
+
 #ifdef __cplusplus
 }
 #endif

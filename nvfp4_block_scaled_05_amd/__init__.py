@@ -53,7 +53,7 @@ NVFP4_MAX_GROUPS = 256
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
             "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes", "nvfp4_quantize_grouped",
             "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack", "nvfp4_debug_set_wait_ticks",
-            "nvfp4_quantize_noalloc")
+            "nvfp4_quantize_noalloc", "nvfp4_debug_set_rht_unit")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -133,6 +133,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_debug_e2m1_pack.argtypes = [P, P, P, I64, U32, P]
     lib.nvfp4_debug_set_wait_ticks.restype = I
     lib.nvfp4_debug_set_wait_ticks.argtypes = [U32]
+    lib.nvfp4_debug_set_rht_unit.restype = I
+    lib.nvfp4_debug_set_rht_unit.argtypes = [U32]
     _lib = lib
     return lib
 
@@ -388,6 +390,15 @@ def stream_workspace(device, stream=None) -> torch.Tensor:
 
 def nvfp4_debug_set_wait_ticks(ticks: int) -> None:
     _check(load().nvfp4_debug_set_wait_ticks(int(ticks) & 0xFFFFFFFF))
+
+
+RHT_UNIT_DEFAULT = 0
+RHT_UNIT_VALU = 1
+RHT_UNIT_MATRIX = 2
+
+
+def nvfp4_debug_set_rht_unit(unit: int) -> None:
+    _check(load().nvfp4_debug_set_rht_unit(int(unit) & 0xFFFFFFFF))
 
 
 def quantize(x: torch.Tensor, *, rowwise=True, columnwise=True, cfg: Optional[nvfp4_config_t] = None,

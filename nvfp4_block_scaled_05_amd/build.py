@@ -6,6 +6,10 @@ Flags that matter for the numerics:
   (default)           correctly rounded FP32 division, IEEE denormals;
   -Xclang -target-feature -Xclang -packed-fp32-ops
                       no packed FP32 instructions are generated.
+
+For the matrix-core RHT transform, -mllvm -amdgpu-mfma-vgpr-form keeps MFMA
+results in ordinary VGPRs (otherwise they land in accumulation registers
+and every value costs a copy before the vector ALU can use it).
 """
 
 from __future__ import annotations
@@ -27,7 +31,7 @@ ARCH = "gfx950"
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC, "-Wall",
 ]
 

@@ -12,10 +12,21 @@
 // the workgroups store their maxima there instead and the cast kernel
 // reduces them, which needs neither the zeroing pass nor atomics.
 
+#include <atomic>
+
 #include "codec.h"
 #include "launch.h"
 
 namespace nvfp4 {
+
+namespace {
+std::atomic<uint32_t> g_rht_unit{0};
+}  // namespace
+
+void set_rht_unit(uint32_t unit) { g_rht_unit.store(unit, std::memory_order_relaxed); }
+bool rht_cast_on_matrix_cores() { return g_rht_unit.load(std::memory_order_relaxed) != 1; }
+bool rht_amax_on_matrix_cores() { return g_rht_unit.load(std::memory_order_relaxed) == 2; }
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -153,9 +164,13 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
 // One RHT amax unit: this thread's 4 columns c .. c+3 of rows 16 by .. +15.
 // Accumulates max|x| (mx16 / mx32 by input type) and max|unnormalized
 // transform| (ms).
-template <int DT>
+// MFMA (BF16 only): the transform on the matrix cores (fwht16_mfma, with the
+// lane's operands a1 / a2 for the mask), else butterflies on the vector ALU.
+template <int DT, bool MFMA>
 __device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32_t cols, uint32_t by, uint32_t c,
-                                              uint32_t mask, ushort2_t &mx16, uint32_t &mx32, float &ms) {
+                                              uint32_t mask, const uint32_t (&a1)[4][2], const float (&a2)[4],
+                                              ushort2_t &mx16, uint32_t &mx32, float &ms) {
+  static_assert(!MFMA || DT == kBF16, "the matrix-core transform takes BF16 input");
   constexpr int VEC = 4;
   constexpr int W = DT == kBF16 ? 2 : 4;  // 32-bit words per 4-column row piece
   constexpr uint32_t kAbs = DT == kBF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
@@ -185,22 +200,54 @@ __device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32
         mx16 = __builtin_elementwise_max(mx16, __builtin_bit_cast(ushort2_t, w[r][q] & kAbs));
       else
         mx32 = max(mx32, w[r][q] & kAbs);
-      w[r][q] ^= ((mask >> r) & 1u) ? kSign : 0u;  // uniform select
+      if constexpr (!MFMA) w[r][q] ^= ((mask >> r) & 1u) ? kSign : 0u;  // uniform select
     }
   }
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
     float v[16];
+    if constexpr (MFMA) {
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // column j's halves, rows paired
+      uint32_t x2[4][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if constexpr (DT == kBF16)
-        v[r] = (j & 1) ? bf16_hi(w[r][j >> 1]) : bf16_lo(w[r][j >> 1]);
-      else
-        v[r] = __uint_as_float(w[r][j]);
+      for (int g = 0; g < 4; ++g) {
+        x2[g][0] = __builtin_amdgcn_perm(w[4 * g + 1][j >> 1], w[4 * g][j >> 1], sel);
+        x2[g][1] = __builtin_amdgcn_perm(w[4 * g + 3][j >> 1], w[4 * g + 2][j >> 1], sel);
+      }
+      fwht16_mfma(x2, a1, a2, v);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (DT == kBF16)
+          v[r] = (j & 1) ? bf16_hi(w[r][j >> 1]) : bf16_lo(w[r][j >> 1]);
+        else
+          v[r] = __uint_as_float(w[r][j]);
+      }
+      fwht16(v);
     }
-    fwht16(v);
 #pragma unroll
     for (int r = 0; r < 16; ++r) ms = fmaxf(ms, fabsf(v[r]));
+  }
+}
+
+// One unit at column c of every lane of the wave (c >= cols: nothing). With
+// the matrix cores every lane takes part in the transform (a lane that sat
+// out would leave its block of four lanes without its operands), so a lane
+// past the end transforms a clamped column and keeps its maxima.
+template <int DT, bool MFMA>
+__device__ __forceinline__ void rht_amax_step(const void *__restrict__ x, uint32_t cols, uint32_t by, uint32_t c,
+                                              uint32_t mask, const uint32_t (&a1)[4][2], const float (&a2)[4],
+                                              ushort2_t &mx16, uint32_t &mx32, float &ms) {
+  if constexpr (MFMA) {
+    ushort2_t mx16_u = mx16;
+    float ms_u = ms;
+    rht_amax_unit<DT, MFMA>(x, cols, by, c < cols ? c : 0u, mask, a1, a2, mx16_u, mx32, ms_u);
+    if (c < cols) {
+      mx16 = mx16_u;
+      ms = ms_u;
+    }
+  } else {
+    if (c < cols) rht_amax_unit<DT, MFMA>(x, cols, by, c, mask, a1, a2, mx16, mx32, ms);
   }
 }
 
@@ -233,7 +280,7 @@ __device__ __forceinline__ void rht_amax_finish(ushort2_t mx16, uint32_t mx32, f
 // partials[blockIdx.x] and partials[kMaxPartials + blockIdx.x], or with
 // partials == NULL (one unit per workgroup) into row_amax and col_amax by
 // atomic max.
-template <int DT>
+template <int DT, bool MFMA>
 __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restrict__ x, uint32_t rows, uint32_t cols,
                                                        uint32_t gx, uint32_t units, uint32_t mask, float *row_amax,
                                                        float *col_amax, uint32_t *partials, const float *noop) {
@@ -242,10 +289,13 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restric
   ushort2_t mx16 = {0, 0};  // BF16 max|x|, two lanes
   uint32_t mx32 = 0;        // FP32 max|x| bits
   float ms = 0.0f;          // max |unnormalized transform|
+  uint32_t a1[4][2] = {};
+  float a2[4] = {};
+  if constexpr (MFMA) fwht16_mfma_operands(mask, a1, a2);
   for (uint32_t u = blockIdx.x; u < units; u += gridDim.x) {
     const uint32_t by = u / gx;
     const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * 4;
-    if (c < cols) rht_amax_unit<DT>(x, cols, by, c, mask, mx16, mx32, ms);
+    rht_amax_step<DT, MFMA>(x, cols, by, c, mask, a1, a2, mx16, mx32, ms);
   }
   uint32_t mx, mt;
   rht_amax_finish<DT>(mx16, mx32, ms, mask, lds, mx, mt);
@@ -275,7 +325,7 @@ __device__ __forceinline__ void zero_empty_groups(const GroupTable &t, float *a,
 // (gx across, m_g / 16 down; units past the group's end are empty). Results
 // go to partials[b] and partials[kMaxPartials + b], or with partials == NULL
 // into the group's slots by atomic max.
-template <int DT>
+template <int DT, bool MFMA>
 __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *__restrict__ x, uint32_t cols,
                                                                uint32_t gx, GroupTable t, uint32_t per_wg,
                                                                uint32_t mask, float *row_amax, float *col_amax,
@@ -289,11 +339,14 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *_
   ushort2_t mx16 = {0, 0};
   uint32_t mx32 = 0;
   float ms = 0.0f;
+  uint32_t a1[4][2] = {};
+  float a2[4] = {};
+  if constexpr (MFMA) fwht16_mfma_operands(mask, a1, a2);
   const uint32_t u0 = (blockIdx.x - t.unit_start[g]) * per_wg;
   for (uint32_t u = u0; u < u0 + per_wg && u < units; ++u) {
     const uint32_t by = u / gx;
     const uint32_t c = ((u - by * gx) * kAmaxThreads + threadIdx.x) * 4;
-    if (c < cols) rht_amax_unit<DT>(xg, cols, by, c, mask, mx16, mx32, ms);
+    rht_amax_step<DT, MFMA>(xg, cols, by, c, mask, a1, a2, mx16, mx32, ms);
   }
   uint32_t mx, mt;
   rht_amax_finish<DT>(mx16, mx32, ms, mask, lds, mx, mt);
@@ -433,12 +486,15 @@ hipError_t launch_rht_amax(const void *x, int dtype, uint32_t rows, uint32_t col
   const uint32_t units = gx * (rows / 16);  // < 2^32: rows * cols < 2^32
   const uint32_t grid = reduction_grid(units, partials != nullptr);
   if (npartials) *npartials = grid;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_rht_amax<kBF16>, dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units, mask,
-                       row_amax, col_amax, partials, noop);
+  if (dtype == kBF16 && rht_amax_on_matrix_cores())
+    hipLaunchKernelGGL((k_rht_amax<kBF16, true>), dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units,
+                       mask, row_amax, col_amax, partials, noop);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL((k_rht_amax<kBF16, false>), dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units,
+                       mask, row_amax, col_amax, partials, noop);
   else
-    hipLaunchKernelGGL(k_rht_amax<kFP32>, dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units, mask,
-                       row_amax, col_amax, partials, noop);
+    hipLaunchKernelGGL((k_rht_amax<kFP32, false>), dim3(grid), dim3(kAmaxThreads), 0, s, x, rows, cols, gx, units,
+                       mask, row_amax, col_amax, partials, noop);
   return hipGetLastError();
 }
 
@@ -533,12 +589,15 @@ hipError_t launch_rht_amax_grouped(const void *x, int dtype, uint32_t cols, cons
     for (uint32_t g = 0; g <= ngroups; ++g) part_start[g] = t.unit_start[g];
   const uint32_t grid = t.unit_start[ngroups] > 0 ? t.unit_start[ngroups] : (partials ? 1u : 0u);
   if (grid == 0) return hipSuccess;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_rht_amax_grouped<kBF16>, dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t, per_wg, mask,
-                       row_amax, col_amax, partials, noop);
+  if (dtype == kBF16 && rht_amax_on_matrix_cores())
+    hipLaunchKernelGGL((k_rht_amax_grouped<kBF16, true>), dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t, per_wg,
+                       mask, row_amax, col_amax, partials, noop);
+  else if (dtype == kBF16)
+    hipLaunchKernelGGL((k_rht_amax_grouped<kBF16, false>), dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t,
+                       per_wg, mask, row_amax, col_amax, partials, noop);
   else
-    hipLaunchKernelGGL(k_rht_amax_grouped<kFP32>, dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t, per_wg, mask,
-                       row_amax, col_amax, partials, noop);
+    hipLaunchKernelGGL((k_rht_amax_grouped<kFP32, false>), dim3(grid), dim3(kAmaxThreads), 0, s, x, cols, gx, t,
+                       per_wg, mask, row_amax, col_amax, partials, noop);
   return hipGetLastError();
 }
 

@@ -97,6 +97,13 @@ extern "C" nvfp4_status_t nvfp4_debug_set_wait_ticks(uint32_t ticks) {
   return NVFP4_OK;
 }
 
+extern "C" nvfp4_status_t nvfp4_debug_set_rht_unit(uint32_t unit) {
+  if (unit > 2)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown RHT unit %u (0: default, 1: vector ALU, 2: matrix cores)", unit);
+  nvfp4::set_rht_unit(unit);
+  return NVFP4_OK;
+}
+
 extern "C" uint64_t nvfp4_swizzled_scales_bytes(int64_t rows, int64_t scale_cols) {
   if (rows <= 0 || scale_cols <= 0 || rows >= (int64_t{1} << 32) || scale_cols >= (int64_t{1} << 32)) return 0;
   return nvfp4::swizzled_scales_bytes(static_cast<uint64_t>(rows), static_cast<uint64_t>(scale_cols));

@@ -26,6 +26,7 @@
 // same tile code on the tiles of several row slices, one tensor per slice.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "codec.h"
 #include "launch.h"
@@ -600,8 +601,9 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
 // quads (DPP). Row-wise and column-wise data bytes are staged in LDS and
 // leave as 16-byte stores (64 contiguous bytes per row / column).
 // ---------------------------------------------------------------------------
-template <int DT, bool SR>
+template <int DT, bool SR, bool MFMA>
 __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, uint32_t ty) {
+  static_assert(!MFMA || DT == kBF16, "the matrix-core transform takes BF16 input");
   constexpr int kElem = DT == kBF16 ? 2 : 4;
   constexpr int W = kElem;  // 32-bit words per 4-column row piece: 2 (BF16) or 4 (FP32)
   __shared__ float lds_mult[2][256];
@@ -686,9 +688,10 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
     for (int j = 0; j < 4; ++j) mine[j] = 0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) m = max(m, __float_as_uint(value(k, c)) & 0x7FFFFFFFu);
+      // float max of magnitudes (abs modifiers, no masking): for finite
+      // inputs the same as the integer max of the |x| bit patterns
+      uint32_t m = __float_as_uint(fmaxf(fmaxf(fabsf(value(k, 0)), fabsf(value(k, 1))),
+                                         fmaxf(fabsf(value(k, 2)), fabsf(value(k, 3)))));
       m = max(m, dpp_mov<kQuadXor1>(m));
       m = max(m, dpp_mov<kQuadXor2>(m));
       // quad lane q turns rows q, q+4, q+8, q+12 into codes
@@ -706,69 +709,133 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
   }
   __syncthreads();  // multipliers ready
 
-  // ---- row-wise encode: 4 codes (2 bytes) per row ----
-  if (do_row) {
-    const uint32_t krow = SR ? sr_key(p.sr_seed, 0) : 0u;
-    const uint32_t half_cols = p.cols >> 1;
+  // ---- encode ----
+  // Stochastic rounding: each row piece (two output bytes) and each column
+  // half (four bytes) is a run of consecutive output bytes (e2m1_sr_run). Where
+  // the global scales allow it (sr_fold_ok, uniform), the 2^23 of the SR
+  // preparation is folded into each block's multiplier.
+  const uint32_t half_cols = p.cols >> 1;
+  const uint32_t half_rows = p.rows >> 1;
+  auto encode_rows = [&](auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const uint32_t kmix = SR ? sr_key_mix(sr_key(p.sr_seed, 0)) : 0u;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const float e = lds_mult[0][rcode[k]];
-      const float s0 = value(k, 0) * e, s1 = value(k, 1) * e, s2 = value(k, 2) * e, s3 = value(k, 3) * e;
       uint32_t h;
-      if (SR) {
-        const uint32_t byte0 = (rbase + k) * half_cols + (col >> 1);
-        h = e2m1_sr_pair_into(__float_as_uint(s0), s0, s1, fmix32(krow ^ byte0), 0);
-        h = e2m1_sr_pair_into(h, s2, s3, fmix32(krow ^ (byte0 + 1)), 1);
+      if constexpr (SR) {
+        float t[4];
+        if constexpr (FAST) {
+          const float ef = e * kSrScale;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) t[c] = sr_prepare_folded(value(k, c), ef);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) t[c] = sr_prepare(value(k, c) * e);
+        }
+        // bytes b0, b0 + 1 of the row, b0 even
+        h = e2m1_sr_run<2, 0>(t, sr_run_mix((rbase + k) * half_cols + (col >> 1)), kmix);
       } else {
+        const float s0 = value(k, 0) * e, s1 = value(k, 1) * e, s2 = value(k, 2) * e, s3 = value(k, 3) * e;
         h = e2m1_rne_pair_into(__float_as_uint(s0), s0, s1, 0);
         h = e2m1_rne_pair_into(h, s2, s3, 1);
       }
       *reinterpret_cast<uint16_t *>(&lds_rd[16 * rq + k][2 * cg]) = static_cast<uint16_t>(h);
     }
-  }
+  };
 
-  // ---- column-wise: RHT of each 16-row column group, then encode ----
-  // The transform's sign flips go on whole input words (one sign per row; the
+  // Column-wise: RHT of each 16-row column group, then encode. The
+  // transform's sign flips go on whole input words (one sign per row; the
   // row-wise side is done with them), and its 1/4 is folded into the block
   // max (exact: rounding is monotonic) and into the multiplier (exact: a
   // power of two), so each column runs the unnormalized transform only.
-  if (do_col) {
-    const uint32_t kcol = SR ? sr_key(p.sr_seed, 1) : 0u;
-    const uint32_t half_rows = p.rows >> 1;
-    constexpr uint32_t kSign = DT == kBF16 ? 0x80008000u : 0x80000000u;
+  float tv[4][16];   // unnormalized transformed values of the thread's 4 columns
+  uint32_t ccode[4];  // their block scale codes
+  auto transform_cols = [&]() {
+    // MFMA: the 4x4 matrix-core form (fwht16_mfma), signs in its operands;
+    // else butterflies on the vector ALU after sign flips on whole words
+    uint32_t a1[4][2];
+    float a2[4];
+    if constexpr (MFMA) {
+      fwht16_mfma_operands(p.sign_mask, a1, a2);
+    } else {
+      constexpr uint32_t kSign = DT == kBF16 ? 0x80008000u : 0x80000000u;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+      for (int k = 0; k < 16; ++k) {
 #pragma unroll
-      for (int q = 0; q < W; ++q) w[k][q] ^= ((p.sign_mask >> k) & 1u) ? kSign : 0u;  // uniform select
+        for (int q = 0; q < W; ++q) w[k][q] ^= ((p.sign_mask >> k) & 1u) ? kSign : 0u;  // uniform select
+      }
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float v[16];
+      if constexpr (MFMA) {
+        // rows (4j, 4j+1) and (4j+2, 4j+3) of column c as BF16 pairs
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t x2[4][2];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = value(k, c);
-      fwht16(v);
+        for (int j = 0; j < 4; ++j) {
+          x2[j][0] = __builtin_amdgcn_perm(w[4 * j + 1][c >> 1], w[4 * j][c >> 1], sel);
+          x2[j][1] = __builtin_amdgcn_perm(w[4 * j + 3][c >> 1], w[4 * j + 2][c >> 1], sel);
+        }
+        fwht16_mfma(x2, a1, a2, tv[c]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) tv[c][k] = value(k, c);
+        fwht16(tv[c]);
+      }
       // BF16 transformed values: bf16(4t) == 4 bf16(t), so the unnormalized
       // values are rounded and the folding of 1/4 below stays as it is
-      if (p.sign_mask & kRhtBf16) bf16_round16(v);
+      if (p.sign_mask & kRhtBf16) bf16_round16(tv[c]);
       float ms = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) ms = fmaxf(ms, fabsf(v[k]));
-      const uint32_t code = block_code(__float_as_uint(ms * 0.25f), S_col, ue);
-      const float e = lds_mult[1][code] * 0.25f;
+      for (int k = 0; k < 16; ++k) ms = fmaxf(ms, fabsf(tv[c][k]));
+      ccode[c] = block_code(__float_as_uint(ms * 0.25f), S_col, ue);
+      lds_cs[code_slot(4 * cg + c, rq)] = static_cast<uint8_t>(ccode[c]);
+    }
+  };
+  auto encode_cols = [&](auto fast_tag) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const uint32_t kmix = SR ? sr_key_mix(sr_key(p.sr_seed, 1)) : 0u;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] *= e;
+    for (int c = 0; c < 4; ++c) {
+      float v[16];
       uint32_t lo, hi;
-      if (SR) {
-        const uint32_t byte0 = (col + c) * half_rows + (rbase >> 1);
-        lo = encode8_scaled<true>(v, kcol, byte0);
-        hi = encode8_scaled<true>(v + 8, kcol, byte0 + 4);
+      if constexpr (SR) {
+        if constexpr (FAST) {
+          const float ef = lds_mult[1][ccode[c]] * (kSrScale * 0.25f);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) v[k] = sr_prepare_folded(tv[c][k], ef);
+        } else {
+          const float e = lds_mult[1][ccode[c]] * 0.25f;
+#pragma unroll
+          for (int k = 0; k < 16; ++k) v[k] = sr_prepare(tv[c][k] * e);
+        }
+        // bytes b0 .. b0 + 7 of column col + c, b0 a multiple of 8
+        const uint32_t run = sr_run_mix((col + c) * half_rows + (rbase >> 1));
+        lo = e2m1_sr_run<4, 0>(v, run, kmix);
+        hi = e2m1_sr_run<4, 4>(v + 8, run, kmix);
       } else {
+        const float e = lds_mult[1][ccode[c]] * 0.25f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = tv[c][k] * e;
         lo = e2m1_rne_x8(v);
         hi = e2m1_rne_x8(v + 8);
       }
       *reinterpret_cast<u32x2 *>(&lds_cd[4 * cg + c][8 * rq]) = u32x2{lo, hi};
-      lds_cs[code_slot(4 * cg + c, rq)] = static_cast<uint8_t>(code);
     }
+  };
+
+  // one uniform choice per tile; only the stochastic encode differs
+  const bool fast = SR && __builtin_amdgcn_readfirstlane((!do_row || sr_fold_ok(S_row, ue, DT == kFP32, 1)) &&
+                                                         (!do_col || sr_fold_ok(S_col, ue, DT == kFP32, 4)));
+  if (do_row) {
+    if (fast) encode_rows(std::integral_constant<bool, SR>{});
+    else encode_rows(std::false_type{});
+  }
+  if (do_col) {
+    transform_cols();
+    if (fast) encode_cols(std::integral_constant<bool, SR>{});
+    else encode_cols(std::false_type{});
   }
   __syncthreads();
 
@@ -873,12 +940,12 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   cast_rt_tile<DT, B2D, SR>(p, tx, ty);
 }
 
-template <int DT, bool SR>
+template <int DT, bool SR, bool MFMA>
 __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
   const uint32_t t = tile_index(p, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   uint32_t tx, ty;
   tile_xy(p, t, gridDim.x, gridDim.y, tx, ty);
-  cast_rht_tile<DT, SR>(p, tx, ty);
+  cast_rht_tile<DT, SR, MFMA>(p, tx, ty);
 }
 
 // ---------------------------------------------------------------------------
@@ -1241,7 +1308,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt_grouped(CastArgs p, GroupT
   cast_rt_tile<DT, B2D, SR>(q, tx, ty);
 }
 
-template <int DT, bool SR>
+template <int DT, bool SR, bool MFMA>
 __global__ __launch_bounds__(kThreads) void k_cast_rht_grouped(CastArgs p, GroupTable t) {
   const uint32_t u = tile_index(p, blockIdx.x, gridDim.x);
   const uint32_t g = group_of(t, u);
@@ -1250,7 +1317,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht_grouped(CastArgs p, Group
   const CastArgs q = group_args<DT>(p, t, g);
   uint32_t tx, ty;
   tile_xy(p, local, tiles_x, (q.rows + kRT - 1) / kRT, tx, ty);
-  cast_rht_tile<DT, SR>(q, tx, ty);
+  cast_rht_tile<DT, SR, MFMA>(q, tx, ty);
 }
 
 template <int DT, bool B2D, bool SR>
@@ -1263,7 +1330,10 @@ hipError_t launch_rt(const CastArgs &a, hipStream_t s) {
 template <int DT, bool SR>
 hipError_t launch_rht(const CastArgs &a, hipStream_t s) {
   dim3 grid((a.cols + kRT - 1) / kRT, (a.rows + kRT - 1) / kRT);
-  hipLaunchKernelGGL((k_cast_rht<DT, SR>), grid, dim3(kThreads), 0, s, a);
+  if (DT == kBF16 && rht_cast_on_matrix_cores())
+    hipLaunchKernelGGL((k_cast_rht<DT, SR, DT == kBF16>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_cast_rht<DT, SR, false>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1278,10 +1348,15 @@ template <int DT>
 hipError_t launch_grouped_dt(const CastArgs &a, const GroupTable &t, bool block_2d, bool rht, bool sr, hipStream_t s) {
   const dim3 grid(t.unit_start[t.ngroups]), block(kThreads);
   if (rht) {
-    if (sr)
-      hipLaunchKernelGGL((k_cast_rht_grouped<DT, true>), grid, block, 0, s, a, t);
+    const bool mfma = DT == kBF16 && rht_cast_on_matrix_cores();
+    if (sr && mfma)
+      hipLaunchKernelGGL((k_cast_rht_grouped<DT, true, DT == kBF16>), grid, block, 0, s, a, t);
+    else if (sr)
+      hipLaunchKernelGGL((k_cast_rht_grouped<DT, true, false>), grid, block, 0, s, a, t);
+    else if (mfma)
+      hipLaunchKernelGGL((k_cast_rht_grouped<DT, false, DT == kBF16>), grid, block, 0, s, a, t);
     else
-      hipLaunchKernelGGL((k_cast_rht_grouped<DT, false>), grid, block, 0, s, a, t);
+      hipLaunchKernelGGL((k_cast_rht_grouped<DT, false, false>), grid, block, 0, s, a, t);
   } else if (block_2d) {
     if (sr)
       hipLaunchKernelGGL((k_cast_rt_grouped<DT, true, true>), grid, block, 0, s, a, t);

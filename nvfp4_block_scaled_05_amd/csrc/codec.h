@@ -228,6 +228,127 @@ __device__ __forceinline__ uint32_t sr_key(uint32_t seed, uint32_t orientation) 
 }
 
 // ---------------------------------------------------------------------------
+// Stochastic rounding of runs of consecutive output bytes, the same rule as
+// e2m1_sr_byte with fewer instructions per byte.
+//
+// Random words. For a byte b = b0 + i of a run whose first index b0 is a
+// multiple of a power of two above i (so b = b0 ^ i and b >> 16 == b0 >> 16),
+// fmix32's first step x ^ (x >> 16) of x = K ^ b splits into
+//   (K ^ (K >> 16)) ^ (b0 ^ (b0 >> 16)) ^ i:
+// a per-orientation part (sr_key_mix, uniform), a per-run part (sr_run_mix)
+// and the constant i, one xor per byte.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t sr_key_mix(uint32_t key) { return key ^ (key >> 16); }
+__device__ __forceinline__ uint32_t sr_run_mix(uint32_t b0) { return b0 ^ (b0 >> 16); }
+
+// fmix32 after its first step (x already x ^ (x >> 16)), without the final
+// xor-shift: fmix32 = h ^ (h >> 16) for the h returned.
+__device__ __forceinline__ uint32_t fmix32_after_first(uint32_t x) {
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  return x * 0xC2B2AE35u;
+}
+
+// Both SR conversions of one pair (a, b), the even one into byte SEL of
+// `even` and the odd one into byte SEL of `odd`, each keeping its other three
+// bytes (checked on gfx950 with an in-bounds probe). The builtin does not tie
+// its destination to the value it preserves, so the instructions are written
+// out here, and with them the wait states the compiler would otherwise add:
+// it never lets a VALU write a register that a byte-selecting conversion
+// reads next, nor a VALU read a conversion's result right after it, so one
+// s_nop stands on each side. Both outputs are early-clobber: the first
+// conversion writes `even` while the second still reads the pair, so neither
+// may share a register with an input (`even` starts as a copy of a[0]'s bits,
+// which the allocator would otherwise merge with the pair).
+#define NVFP4_CVT_SR_PAIR(OPSEL)                                                                   \
+  asm("s_nop 0\n\t"                                                                               \
+      "v_cvt_scalef32_sr_pk_fp4_f32 %0, %2, %3, %5" OPSEL "\n\t"                                  \
+      "v_cvt_scalef32_sr_pk_fp4_f32 %1, %2, %4, %5" OPSEL "\n\t"                                  \
+      "s_nop 0"                                                                                    \
+      : "+&v"(even), "+&v"(odd)                                                                    \
+      : "v"(pair), "v"(re), "v"(ro), "s"(scale))
+
+template <int SEL>
+__device__ __forceinline__ void cvt_sr_pair_into(uint32_t &even, uint32_t &odd, float a, float b, uint32_t re,
+                                                 uint32_t ro) {
+  const sr_float2 pair{a, b};
+  const float scale = kSrScale;
+  if constexpr (SEL == 0)
+    NVFP4_CVT_SR_PAIR("");
+  else if constexpr (SEL == 1)
+    NVFP4_CVT_SR_PAIR(" op_sel:[0,0,1,0]");
+  else if constexpr (SEL == 2)
+    NVFP4_CVT_SR_PAIR(" op_sel:[0,0,0,1]");
+  else
+    NVFP4_CVT_SR_PAIR(" op_sel:[0,0,1,1]");
+}
+#undef NVFP4_CVT_SR_PAIR
+
+// Stochastic codes of the N pairs (t[2i], t[2i+1]) of prepared values (as
+// sr_prepare gives them), pair i into byte i of the result (N <= 4; higher
+// bytes are undefined). Pair i is output byte b0 + I0 + i of its orientation;
+// run_mix = sr_run_mix(b0), key_mix = sr_key_mix(K), and b0 must be a
+// multiple of a power of two above I0 + N - 1. The even conversions of all
+// pairs go into one word and the odd ones into another, each conversion
+// filling one byte, and one bit-field merge takes the low nibbles from the
+// first and the high nibbles from the second (see e2m1_sr_byte for the two
+// random operands).
+template <int N, int I0>
+__device__ __forceinline__ uint32_t e2m1_sr_run(const float *t, uint32_t run_mix, uint32_t key_mix) {
+  static_assert(N >= 1 && N <= 4, "a run fills at most one word");
+  uint32_t even = 0, odd = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t h = fmix32_after_first(run_mix ^ key_mix ^ static_cast<uint32_t>(I0 + i));
+    const uint32_t nr = ~(h ^ (h >> 16));  // 65535 - r16 in each half
+    const uint32_t re = (nr << 16) | 0xFFFFu, ro = (nr >> 1) | 0x7FFFu;
+    if (i == 0) {
+      // the words start as values that die here (any start will do: every
+      // used byte is written), which saves copying into them
+      even = h;
+      odd = nr;
+    }
+    if (i == 0)
+      cvt_sr_pair_into<0>(even, odd, t[0], t[1], re, ro);
+    else if (i == 1)
+      cvt_sr_pair_into<1>(even, odd, t[2], t[3], re, ro);
+    else if (i == 2)
+      cvt_sr_pair_into<2>(even, odd, t[4], t[5], re, ro);
+    else
+      cvt_sr_pair_into<3>(even, odd, t[6], t[7], re, ro);
+  }
+  return odd ^ ((odd ^ even) & 0x0F0F0F0Fu);  // one v_bfi: even's low nibbles, odd's high ones
+}
+
+// sr_prepare(v * e) with one multiply fewer: ceil(|v| * e_fold) with v's sign,
+// where e_fold = e * 2^23 (exact). Equal to sr_prepare(fl(v * e)) wherever
+// neither product under- or overflows, which sr_fold_ok guarantees for every
+// block of a tensor from its global encode scale S alone (pinned on the CPU
+// by tests/test_sr_fold_cpu.py). The sign of fl(v * e) is v's (e >= 0).
+__device__ __forceinline__ float sr_prepare_folded(float v, float e_fold) {
+  return __builtin_copysignf(__builtin_ceilf(fabsf(v) * e_fold), v);
+}
+
+// Where the fold above is exact: log2 bounds lo <= log2(S) <= hi by scale
+// format, input type and the factor c folded into the multiplier (4 on the
+// RHT column side, 1 elsewhere). lo keeps every non-zero |v| * e above
+// 2^-149 for the smallest non-zero input of the type (2^-133 BF16, 2^-149
+// FP32; the RHT sums are multiples of it) and the largest scale; hi keeps
+// e * 2^23 / c at most 2^126 for the smallest non-zero scale.
+struct FoldRange {
+  int ue5m3, fp32, c, lo, hi;
+};
+constexpr FoldRange kFoldRanges[] = {
+    {0, 0, 1, -7, 94}, {0, 0, 4, -5, 94}, {0, 1, 1, 9, 94},  {0, 1, 4, 11, 94},
+    {1, 0, 1, 0, 86},  {1, 0, 4, 2, 86},  {1, 1, 1, 16, 86}, {1, 1, 4, 18, 86},
+};
+
+__device__ __forceinline__ bool sr_fold_ok(float S, bool ue5m3, bool fp32, int c) {
+  const FoldRange &r = kFoldRanges[(ue5m3 ? 4 : 0) + (fp32 ? 2 : 0) + (c == 4 ? 1 : 0)];
+  return S >= __builtin_ldexpf(1.0f, r.lo) && S <= __builtin_ldexpf(1.0f, r.hi);
+}
+
+// ---------------------------------------------------------------------------
 // 16-point random Hadamard transform in registers: sign flips from the mask,
 // an in-place fast Walsh-Hadamard transform (natural = Sylvester order), and
 // the orthonormal factor 1/4 (exact).
@@ -244,6 +365,60 @@ __device__ __forceinline__ void fwht16(float (&v)[16]) {
         v[i + h] = a - b;
       }
     }
+  }
+}
+
+// The same unnormalized transform of one column of 16 BF16 values with the
+// sign flips, on the matrix cores. H16 = H4 (x) H4 in Sylvester order:
+// t[4r + m] = sum_j H4[r][j] * y_j[m], y_j[m] = sum_k H4[m][k] * s_{4j+k} x_{4j+k}.
+// The 4x4 MFMAs work on 16 blocks of four lanes: lane (b, n) gives column n
+// of B and gets column n of D, lane (b, m) gives row m of A (checked with an
+// in-bounds probe). So with every lane giving its own column as B, each lane
+// transforms its own vector:
+//   stage 1, bf16 4x4x4: A = H4 diag(s_{4j..4j+3}) (exact in BF16), B = the
+//     lane's rows 4j..4j+3 -> y_j (products exact, summed in FP32);
+//   stage 2, f32 4x4x1, four accumulating steps j: A = column j of H4,
+//     B = y_j[m] -> t[4r + m] in register r.
+// Operands: x2[j] holds rows (4j, 4j+1) and (4j+2, 4j+3) of the column as
+// BF16 pairs; a1[j] is the lane's row (lane % 4) of H4 diag(s) for group j as
+// BF16 pairs, a2[j] = H4[lane % 4][j]. Both units keep denormals (probed).
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void fwht16_mfma(const uint32_t (&x2)[4][2], const uint32_t (&a1)[4][2],
+                                            const float (&a2)[4], float (&t)[16]) {
+  f32x4_t y[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x4_t a = __builtin_bit_cast(bf16x4_t, u32x2_t{a1[j][0], a1[j][1]});
+    const bf16x4_t b = __builtin_bit_cast(bf16x4_t, u32x2_t{x2[j][0], x2[j][1]});
+    y[j] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_4x4x1f32(a2[j], y[j][m], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[4 * r + m] = acc[r];
+  }
+}
+
+// The lane's A operands of fwht16_mfma for a 16-bit sign mask.
+__device__ __forceinline__ void fwht16_mfma_operands(uint32_t sign_mask, uint32_t (&a1)[4][2], float (&a2)[4]) {
+  const uint32_t m = threadIdx.x & 3u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t neg = (__builtin_popcount(m & static_cast<uint32_t>(k)) & 1u) ^ ((sign_mask >> (4 * j + k)) & 1u);
+      h[k] = neg ? 0xBF80u : 0x3F80u;  // BF16 -1 / +1
+    }
+    a1[j][0] = h[0] | (h[1] << 16);
+    a1[j][1] = h[2] | (h[3] << 16);
+    a2[j] = (__builtin_popcount(m & static_cast<uint32_t>(j)) & 1u) ? -1.0f : 1.0f;
   }
 }
 
@@ -280,9 +455,12 @@ __device__ __forceinline__ uint64_t swizzled_scale_offset(uint64_t r, uint64_t c
 // ---------------------------------------------------------------------------
 // Cross-lane helpers (wave64).
 // ---------------------------------------------------------------------------
+// Every pattern used here (quad permutations, row mirrors) reads a valid lane
+// for every lane, so bound_ctrl changes nothing; set, it lets the compiler
+// fold the move into the instruction that consumes it.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), CTRL, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, true));
 }
 
 // quad_perm controls: lane ^ 1 and lane ^ 2 within each group of four

@@ -111,6 +111,13 @@ ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uin
                            hipStream_t stream);
 hipError_t launch_cast_resident(const CastArgs &a, uint32_t *workspace, int dtype, bool block_2d, bool sr,
                                 const ResidentPlan &plan, hipStream_t s);
+// Which unit runs the 16-point transform of BF16 input in the RHT kernels,
+// process-wide: 0 (default) the matrix cores in the cast and the vector ALU
+// in the amax pass (each measured faster there), 1 the vector ALU in both,
+// 2 the matrix cores in both.
+void set_rht_unit(uint32_t unit);
+bool rht_cast_on_matrix_cores();
+bool rht_amax_on_matrix_cores();
 // Bound on the handoff wait, in ticks of the 100 MHz real-time counter; after
 // it a workgroup computes the amax from the whole input itself. 0 restores
 // the default.
