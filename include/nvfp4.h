@@ -33,7 +33,14 @@
  *     bad argument the call returns a non-zero status, queues nothing and
  *     writes nothing; nvfp4_last_error() then describes the problem.
  *   - A failure reported by the HIP runtime at launch returns NVFP4_ERR_HIP.
- *     Errors inside kernels are not detected (inputs are assumed finite).
+ *     Errors inside kernels are not detected.
+ *   - Non-finite inputs (the method assumes finite data): every amax the
+ *     library computes (per tensor, per row, per column, either of the RHT
+ *     pair) is NaN when the values it covers include a NaN, and +inf when
+ *     they include an infinity and no NaN (on the RHT column side, an
+ *     infinity that meets another one of the opposite sign in a 16-point
+ *     group gives NaN). FP4 data and scales derived from non-finite values
+ *     are unspecified; every access stays inside the caller's buffers.
  *   - No call throws across the ABI.
  */
 #ifndef NVFP4_H

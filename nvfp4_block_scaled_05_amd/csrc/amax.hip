@@ -169,7 +169,7 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
 template <int DT, bool MFMA>
 __device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32_t cols, uint32_t by, uint32_t c,
                                               uint32_t mask, const uint32_t (&a1)[4][2], const float (&a2)[4],
-                                              ushort2_t &mx16, uint32_t &mx32, float &ms) {
+                                              ushort2_t &mx16, uint32_t &mx32, uint32_t &ms) {
   static_assert(!MFMA || DT == kBF16, "the matrix-core transform takes BF16 input");
   constexpr int VEC = 4;
   constexpr int W = DT == kBF16 ? 2 : 4;  // 32-bit words per 4-column row piece
@@ -226,7 +226,7 @@ __device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32
       fwht16(v);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ms = fmaxf(ms, fabsf(v[r]));
+    for (int r = 0; r < 16; ++r) ms = max(ms, __float_as_uint(v[r]) & 0x7FFFFFFFu);  // NaN stays NaN
   }
 }
 
@@ -237,10 +237,10 @@ __device__ __forceinline__ void rht_amax_unit(const void *__restrict__ x, uint32
 template <int DT, bool MFMA>
 __device__ __forceinline__ void rht_amax_step(const void *__restrict__ x, uint32_t cols, uint32_t by, uint32_t c,
                                               uint32_t mask, const uint32_t (&a1)[4][2], const float (&a2)[4],
-                                              ushort2_t &mx16, uint32_t &mx32, float &ms) {
+                                              ushort2_t &mx16, uint32_t &mx32, uint32_t &ms) {
   if constexpr (MFMA) {
     ushort2_t mx16_u = mx16;
-    float ms_u = ms;
+    uint32_t ms_u = ms;
     rht_amax_unit<DT, MFMA>(x, cols, by, c < cols ? c : 0u, mask, a1, a2, mx16_u, mx32, ms_u);
     if (c < cols) {
       mx16 = mx16_u;
@@ -254,10 +254,10 @@ __device__ __forceinline__ void rht_amax_step(const void *__restrict__ x, uint32
 // Workgroup maxima of an RHT amax pass: (max|x|, max|t|) as float bits, in
 // every thread.
 template <int DT>
-__device__ __forceinline__ void rht_amax_finish(ushort2_t mx16, uint32_t mx32, float ms, uint32_t mask, uint32_t *lds,
+__device__ __forceinline__ void rht_amax_finish(ushort2_t mx16, uint32_t mx32, uint32_t ms, uint32_t mask, uint32_t *lds,
                                                 uint32_t &mx, uint32_t &mt) {
   mx = DT == kBF16 ? (static_cast<uint32_t>(max(mx16.x, mx16.y)) << 16) : mx32;
-  float t = ms * 0.25f;
+  float t = __uint_as_float(ms) * 0.25f;
   if (mask & kRhtBf16) {  // rounding is monotonic: max|bf16(t)| == bf16(max|t|)
     float unused = 0.0f;
     bf16_round_pair(t, unused);
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax(const void *__restric
   if (noop_set(noop)) return;
   ushort2_t mx16 = {0, 0};  // BF16 max|x|, two lanes
   uint32_t mx32 = 0;        // FP32 max|x| bits
-  float ms = 0.0f;          // max |unnormalized transform|
+  uint32_t ms = 0;          // max |unnormalized transform| (bit pattern)
   uint32_t a1[4][2] = {};
   float a2[4] = {};
   if constexpr (MFMA) fwht16_mfma_operands(mask, a1, a2);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *_
   const void *xg = static_cast<const uint8_t *>(x) + static_cast<uint64_t>(t.row_start[g]) * cols * (DT == kBF16 ? 2 : 4);
   ushort2_t mx16 = {0, 0};
   uint32_t mx32 = 0;
-  float ms = 0.0f;
+  uint32_t ms = 0;
   uint32_t a1[4][2] = {};
   float a2[4] = {};
   if constexpr (MFMA) fwht16_mfma_operands(mask, a1, a2);

@@ -43,11 +43,15 @@
 #define ORACLE_PARALLEL_FOR _Pragma("omp parallel for schedule(static)")
 #define ORACLE_PARALLEL_MAX_A _Pragma("omp parallel for schedule(static) reduction(max : a)")
 #define ORACLE_PARALLEL_MAX_B _Pragma("omp parallel for schedule(static) reduction(max : b)")
+#define ORACLE_PARALLEL_FOR_OR_NAN _Pragma("omp parallel for schedule(static) reduction(| : any_nan)")
+#define ORACLE_PARALLEL_FOR_OR_TNAN _Pragma("omp parallel for schedule(static) reduction(| : t_nan)")
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 #else
 #define ORACLE_PARALLEL_FOR
 #define ORACLE_PARALLEL_MAX_A
 #define ORACLE_PARALLEL_MAX_B
+#define ORACLE_PARALLEL_FOR_OR_NAN
+#define ORACLE_PARALLEL_FOR_OR_TNAN
 int oracle_num_threads(void) { return 1; }
 #endif
 
@@ -356,13 +360,23 @@ void oracle_rht_colwise(const void *x, int dtype, int64_t rows, int64_t cols, ui
 /* transformed values.                                                 */
 /* amax_row / amax_col may be NULL (that buffer is not requested).     */
 /* ------------------------------------------------------------------ */
+/* Non-finite inputs (the pages assume finite data; this is the library's
+ * stated policy): an amax over values that include a NaN is NaN, and one
+ * over values that include an infinity but no NaN is +inf. Written out here
+ * rather than left to fmaxf, which would drop a NaN. */
+static float amax_step(float a, float v) {
+  const float m = fabsf(v);
+  if (isnan(a) || isnan(m)) return NAN;
+  return m > a ? m : a;
+}
+
 void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, int mode,
                          uint32_t sign_mask, float *amax_row, float *amax_col) {
   if (mode == 1) {
     ORACLE_PARALLEL_FOR
     for (int64_t i = 0; i < rows; ++i) {
       float a = 0.0f;
-      for (int64_t j = 0; j < cols; ++j) a = fmaxf(a, fabsf(oracle_load(x, dtype, i * cols + j)));
+      for (int64_t j = 0; j < cols; ++j) a = amax_step(a, oracle_load(x, dtype, i * cols + j));
       if (amax_row) amax_row[i] = a;
     }
     /* the column-wise tensor's rows are the input's columns */
@@ -370,15 +384,19 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
       ORACLE_PARALLEL_FOR
       for (int64_t j = 0; j < cols; ++j) {
         float a = 0.0f;
-        for (int64_t i = 0; i < rows; ++i) a = fmaxf(a, fabsf(oracle_load(x, dtype, i * cols + j)));
+        for (int64_t i = 0; i < rows; ++i) a = amax_step(a, oracle_load(x, dtype, i * cols + j));
         amax_col[j] = a;
       }
     }
     return;
   }
   float a = 0.0f;
+  int any_nan = 0;
   ORACLE_PARALLEL_MAX_A
   for (int64_t n = 0; n < rows * cols; ++n) a = fmaxf(a, fabsf(oracle_load(x, dtype, n)));
+  ORACLE_PARALLEL_FOR_OR_NAN
+  for (int64_t n = 0; n < rows * cols; ++n) any_nan |= isnan(oracle_load(x, dtype, n)) ? 1 : 0;
+  if (any_nan) a = NAN;
   if (mode == 0) {
     if (amax_row) amax_row[0] = a;
     if (amax_col) amax_col[0] = a;
@@ -390,10 +408,13 @@ void oracle_compute_amax(const void *x, int dtype, int64_t rows, int64_t cols, i
     float *t = (float *)malloc(sizeof(float) * (size_t)(rows * cols));
     oracle_rht_colwise_ex(x, dtype, rows, cols, sign_mask, mode == 3, t);
     float b = 0.0f;
+    int t_nan = 0;
     ORACLE_PARALLEL_MAX_B
     for (int64_t n = 0; n < rows * cols; ++n) b = fmaxf(b, fabsf(t[n]));
+    ORACLE_PARALLEL_FOR_OR_TNAN
+    for (int64_t n = 0; n < rows * cols; ++n) t_nan |= isnan(t[n]) ? 1 : 0;
     free(t);
-    amax_col[0] = b;
+    amax_col[0] = t_nan ? NAN : b;
   }
 }
 

@@ -800,3 +800,33 @@ def test_grouped_rowscaled_with_nearest_even_is_one_rowscaled_call():
     last = O.quantize(x[64:], columnwise=False, row_scaled=True, stochastic=True, sr_seed=6)
     assert np.array_equal(gs["row_data"][64 * 48:], last["row_data"].reshape(-1))
     assert np.array_equal(gs["row_scales"], q["row_scales"].reshape(-1))  # scales are always nearest even
+
+
+# ----------------------------------------------------------------------------
+# Non-finite inputs: the stated amax policy (NaN wins, else +inf), written out
+# in the oracle rather than left to fmaxf (which drops a NaN).
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["tensor", "row", "rht"])
+def test_amax_propagates_nan_and_inf(mode):
+    for bad, want in ((np.nan, "nan"), (np.inf, "inf"), (-np.inf, "inf")):
+        x = np.full((32, 48), 0.5, np.float32)
+        x[17, 9] = bad
+        x[3, 40] = -7.0  # a finite maximum elsewhere must not hide the NaN or inf
+        if mode == "tensor":
+            a, b = O.compute_amax(x)
+            vals = [a[0], b[0]]
+        elif mode == "row":
+            a, b = O.compute_amax(x, O.AMAX_PER_ROW)
+            vals = [a[17], b[9]]
+            assert a[3] == 7.0 and b[40] == 7.0 and a[0] == 0.5 and b[0] == 0.5
+        else:
+            a, b = O.compute_amax(x, O.AMAX_RHT, 0x9C3A)
+            vals = [a[0], b[0]]
+        for v in vals:
+            assert (np.isnan(v) if want == "nan" else v == np.inf), (mode, bad, vals)
+    # NaN beats +inf anywhere
+    x = np.zeros((16, 16), np.float32)
+    x[0, 0] = np.inf
+    x[15, 15] = np.nan
+    assert np.isnan(O.compute_amax(x)[0][0])
