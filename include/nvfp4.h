@@ -26,8 +26,8 @@
  *   - State kept between calls: on the device, only what a caller's
  *     workspace holds (nvfp4_config_t.workspace). On the host, process-wide
  *     caches of per-device launch facts (occupancy limits and compute-unit
- *     counts, read once from the runtime), the wait bound that
- *     nvfp4_debug_set_wait_ticks sets, and the per-thread text of
+ *     counts, read once from the runtime), the settings of the nvfp4_debug_set_*
+ *     test hooks, and the per-thread text of
  *     nvfp4_last_error. None of it changes what a call computes.
  *   - Arguments are validated on the host before anything is queued. On a
  *     bad argument the call returns a non-zero status, queues nothing and
@@ -100,12 +100,13 @@ typedef enum {
    * at most 4 workgroups per CU), else the two-pass form */
   NVFP4_AMAX_PATH_SINGLE_PASS = 2
 } nvfp4_amax_path_t;
-/* The single-pass form needs its whole grid on the GPU at once. While
- * kernels of other streams hold CUs, part of the grid may have to wait for
- * them; the workgroups already running wait too, for at most 20 ms, and then
- * read the whole input for the amax themselves: the bytes are the same, the
- * call much slower. Callers that overlap the quantize with long-running
- * kernels on other streams should choose NVFP4_AMAX_PATH_TWO_PASS. */
+/* The single-pass form is fastest with its whole grid on the GPU at once.
+ * While kernels of other streams hold CUs, part of the grid may have to wait
+ * for them; the workgroups already running then wait 50 us, take over the
+ * amax of the tiles of the workgroups that have not started (reading those
+ * tiles twice) and go on: the bytes are the same, the call slower. Callers
+ * that overlap the quantize with long-running kernels on other streams may
+ * prefer NVFP4_AMAX_PATH_TWO_PASS. */
 
 /* One orientation of an NVFP4 tensor. For the row-wise orientation of an
  * R x C input, n = R and k = C; for the column-wise one, n = C and k = R
@@ -392,12 +393,28 @@ nvfp4_status_t nvfp4_debug_e2m1_pack(const float *v, const uint32_t *r, uint8_t 
 /*
  * Test hook: the bound, in ticks of the GPU's 100 MHz real-time counter, on
  * how long a workgroup of the single-pass quantize waits for the others to
- * publish their maxima before it takes the maximum of the whole input
- * itself (same result, more reads). 0 restores the default (2,000,000
- * ticks, 20 ms); 1 makes nearly every wait run out, so that tests can check
- * that path. Process-wide; takes effect for launches queued afterwards.
+ * publish their maxima before it takes the slow path: it claims the tiles of
+ * workgroups that have not started, takes their maxima from memory, and
+ * reduces every workgroup's maximum itself (same result, the claimed tiles
+ * read twice). 0 restores the default (5,000 ticks, 50 us); 1 sends nearly
+ * every workgroup down the slow path, so that tests can check it.
+ * Process-wide; takes effect for launches queued afterwards.
  */
 nvfp4_status_t nvfp4_debug_set_wait_ticks(uint32_t ticks);
+
+/*
+ * Test hook: the tiles of 128 x 128 elements that each workgroup of the
+ * single-pass quantize holds. 0 (the default): the library's choice, which
+ * keeps the whole grid resident. 1 .. 5: that many tiles in registers (BF16
+ * input; FP32 takes 1 only); 6: three in registers and one in LDS (BF16).
+ * A forced choice launches one workgroup per that many tiles, up to 2048
+ * workgroups, even where they cannot all be resident at once (the handoff's
+ * slow path then completes the call), so that tests can check that case;
+ * beyond 2048 workgroups, or for a choice the input type does not have, the
+ * library's choice stands. Process-wide; takes effect for calls made
+ * afterwards. Other values: NVFP4_ERR_UNSUPPORTED.
+ */
+nvfp4_status_t nvfp4_debug_set_resident_variant(uint32_t tiles_per_workgroup);
 
 /*
  * Test hook: which unit runs the 16-point transform of BF16 input in the RHT

@@ -53,7 +53,7 @@ NVFP4_MAX_GROUPS = 256
 EXPORTED = ("nvfp4_compute_amax", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_last_error",
             "nvfp4_workspace_bytes", "nvfp4_swizzle_scales", "nvfp4_swizzled_scales_bytes", "nvfp4_quantize_grouped",
             "nvfp4_debug_rht_colwise", "nvfp4_debug_e2m1_pack", "nvfp4_debug_set_wait_ticks",
-            "nvfp4_quantize_noalloc", "nvfp4_debug_set_rht_unit")
+            "nvfp4_quantize_noalloc", "nvfp4_debug_set_rht_unit", "nvfp4_debug_set_resident_variant")
 
 
 class nvfp4_out_t(ctypes.Structure):
@@ -135,6 +135,8 @@ def load(build_if_missing: bool = True) -> ctypes.CDLL:
     lib.nvfp4_debug_set_wait_ticks.argtypes = [U32]
     lib.nvfp4_debug_set_rht_unit.restype = I
     lib.nvfp4_debug_set_rht_unit.argtypes = [U32]
+    lib.nvfp4_debug_set_resident_variant.restype = I
+    lib.nvfp4_debug_set_resident_variant.argtypes = [U32]
     _lib = lib
     return lib
 
@@ -390,6 +392,10 @@ def stream_workspace(device, stream=None) -> torch.Tensor:
 
 def nvfp4_debug_set_wait_ticks(ticks: int) -> None:
     _check(load().nvfp4_debug_set_wait_ticks(int(ticks) & 0xFFFFFFFF))
+
+
+def nvfp4_debug_set_resident_variant(tiles_per_workgroup: int) -> None:
+    _check(load().nvfp4_debug_set_resident_variant(int(tiles_per_workgroup) & 0xFFFFFFFF))
 
 
 RHT_UNIT_DEFAULT = 0

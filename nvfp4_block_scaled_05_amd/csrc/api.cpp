@@ -97,6 +97,13 @@ extern "C" nvfp4_status_t nvfp4_debug_set_wait_ticks(uint32_t ticks) {
   return NVFP4_OK;
 }
 
+extern "C" nvfp4_status_t nvfp4_debug_set_resident_variant(uint32_t tiles_per_workgroup) {
+  if (!nvfp4::set_resident_variant(tiles_per_workgroup))
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown single-pass variant %u (0: the library's choice, 1 .. 6)",
+                tiles_per_workgroup);
+  return NVFP4_OK;
+}
+
 extern "C" nvfp4_status_t nvfp4_debug_set_rht_unit(uint32_t unit) {
   if (unit > 2)
     return fail(NVFP4_ERR_UNSUPPORTED, "unknown RHT unit %u (0: default, 1: vector ALU, 2: matrix cores)", unit);

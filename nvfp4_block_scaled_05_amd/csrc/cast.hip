@@ -956,32 +956,53 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
 // Here each workgroup first loads its K tiles (tiles L = blockIdx.x +
 // k * gridDim.x, k < K, in the launch order of k_cast_rt) into registers,
 // the last one into LDS in one variant, publishes the maximum of its tiles,
-// waits until every workgroup of the grid has published, and encodes its
-// tiles from registers: the input is read once. The host sizes the grid so
-// that all of it can be resident at once (at most the occupancy limit, and
-// at most four workgroups, per CU times the CU count). The waits are
-// bounded all the same: a workgroup that has waited wait_ticks ticks of the
-// 100 MHz real-time counter takes the maximum of the whole input itself, so
-// the kernel ends however the hardware schedules its workgroups, with the
-// same result.
+// waits until the grid's maximum is known, and encodes its tiles from
+// registers: the input is read once. The host sizes the grid so that all of
+// it can be resident at once (at most the occupancy limit, and at most four
+// workgroups, per CU times the CU count), but the kernel does not rely on
+// it: while other streams' kernels hold CUs, part of the grid may start
+// only after the rest has finished.
 //
-// Handoff (workspace words in launch.h), with relaxed agent-scope atomic
-// loads and stores only: ordered read-modify-write atomics and fences at
-// agent scope write back or invalidate a whole L2 each, and with hundreds of
-// workgroups they cost tens of microseconds. Workgroup i stores
-// (e + 1) << 32 | max to its slot, e being the epoch read at the start.
-// The first workgroup of each group of kSlotGroup waits (one 64-lane load
-// per poll) until its members' slots carry the tag, then stores the group's
-// maximum, tagged, to the group slot; every workgroup waits for all group
-// slots (at most 32, one load per poll) and reduces them. No value of an
-// earlier call can pass for this call's: the epoch advances once per call,
-// when the last workgroup exits (exit counters at the end of the kernel, off
-// the critical path), so every workgroup of a call reads the same epoch,
-// even one that starts after others stopped waiting.
+// Handoff (workspace words in launch.h), with relaxed agent-scope atomics
+// only: ordered read-modify-write atomics and fences at agent scope write
+// back or invalidate a whole L2 each, and with hundreds of workgroups they
+// cost tens of microseconds. A call tags its words with t = e + 1, e being
+// the epoch read at the start. Workgroup i marks its slot started
+// (t << 32 | kSlotStarted) as it starts, and stores t << 32 | max once it
+// has the maximum of its tiles.
+//   Fast path: the first workgroup of each group of kSlotGroup waits (one
+//   64-lane load per poll) until its members' slots carry maxima tagged t,
+//   and stores the group's maximum, tagged, to the group slot; every
+//   workgroup waits for all group slots (at most 32, one load per poll), or
+//   for the done word, and reduces them.
+//   Slow path, after fast_ticks of waiting, or as soon as the wait shows
+//   workgroups that have not started (handoff_fast): the workgroup claims,
+//   by compare-and-swap, the slots among kClaimSpan slots from a spread
+//   start that no workgroup of this call has touched yet (their owners have
+//   not started), takes the maximum of each such workgroup's tiles from
+//   memory and stores it, tagged, to the slot. Then the first workgroup to
+//   tag the reducer word claims what is left over every slot, waits until
+//   every slot carries a maximum tagged t, reduces them and stores the
+//   result to the done word; the others wait for the done word. Every slot
+//   the reducer waits for belongs to a workgroup that is running, its owner
+//   or its claimer, so the wait ends however many workgroups the hardware
+//   runs at once; an owner that starts later stores the same maximum over
+//   its claimer's and takes the done word. Only the chunks of workgroups
+//   that had not started are read twice. The slow path is bounded all the
+//   same (kLastResortTicks): past it, and in a workspace whose exit
+//   counters are not in a state that a call left, a workgroup takes the
+//   maximum of the whole input itself.
+// No value of an earlier call can pass for this call's: the epoch advances
+// once per call, when the last workgroup exits (exit counters at the end of
+// the kernel, off the critical path), so every workgroup of a call reads the
+// same epoch, even one that starts after others stopped waiting.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kDefaultWaitTicks = 2000000;  // 20 ms
+constexpr uint32_t kDefaultFastTicks = 5000;   // 50 us of the 100 MHz counter
+constexpr uint32_t kClaimSpan = 512;           // slots each workgroup of the slow path scans for claims
+constexpr uint32_t kLastResortTicks = 2000000;  // 20 ms
 // A call tags its slots epoch + 1, so tags run 1 .. 2^32 - 1 and never 0.
 constexpr uint32_t kLastEpoch = 0xFFFFFFFFu;
+static_assert(kMaxPartials / kSlotGroup < 63, "lane 63 of the group-slot poll reads the done word");
 
 __device__ __forceinline__ uint32_t group_members(uint32_t G, uint32_t x) {
   return (G - x + kBarGroups - 1) / kBarGroups;
@@ -1000,8 +1021,13 @@ __device__ __forceinline__ void st_agent64(uint32_t *p, uint64_t v) {
   __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// max |x| bit pattern over the whole input, by one workgroup (the fallback
-// after a bounded wait ran out)
+// a slot value that carries a maximum of the call tagged t
+__device__ __forceinline__ bool holds_max(uint64_t v, uint32_t t) {
+  return static_cast<uint32_t>(v >> 32) == t && static_cast<uint32_t>(v) < 0x80000000u;
+}
+
+// max |x| bit pattern over the whole input, by one workgroup (the last
+// resort after the slow wait ran out)
 template <int DT>
 __device__ uint32_t input_max(const CastArgs &p) {
   const u32x4 *x = static_cast<const u32x4 *>(p.x);
@@ -1023,40 +1049,248 @@ __device__ uint32_t input_max(const CastArgs &p) {
   return m;
 }
 
-// Wave 0's part of the handoff: publish m, wait for the grid. Returns, in
-// lane 0, whether the wait succeeded and the grid's maximum. e, xb, xbt:
-// the epoch and the exit bases read at the start (lane 0).
-__device__ __forceinline__ bool handoff(uint32_t *ws, uint32_t m, uint32_t wait_ticks, uint32_t e, bool ok,
-                                        uint32_t &amax) {
+// max |x| bit pattern of the thread's pieces of tile (r0, c0) that lie in
+// the input, read from memory (a claimed workgroup's tile), from clamped
+// addresses as in rt_load: all eight pieces' loads in flight at once for
+// BF16, four at a time for FP32 (registers: the slow path runs with the
+// workgroup's own tiles held)
+template <int DT>
+__device__ uint32_t tile_part_max(const CastArgs &p, uint32_t r0, uint32_t c0) {
+  constexpr int W = RT<DT>::kWords;
+  constexpr int B = DT == kBF16 ? 8 : 4;
+  const uint32_t col = c0 + 8 * (threadIdx.x & 15);
+  const uint32_t rbase = r0 + 8 * (threadIdx.x >> 4);
+  const uint32_t lcol = col < p.cols ? col : 0u;
+  uint32_t m = 0;
+#pragma unroll
+  for (int h = 0; h < 8; h += B) {
+    uint32_t w[B][W];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const uint32_t r = min(rbase + h + k, p.rows - 1);
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(p.x) +
+                                                         (static_cast<uint64_t>(r) * p.cols + lcol) * RT<DT>::kElem);
+#pragma unroll
+      for (int q = 0; q < W / 4; ++q) {
+        const u32x4 t = src[q];
+        w[k][4 * q] = t.x;
+        w[k][4 * q + 1] = t.y;
+        w[k][4 * q + 2] = t.z;
+        w[k][4 * q + 3] = t.w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const uint32_t pm = piece_max<DT>(w[k]);
+      m = max(m, col < p.cols && rbase + h + k < p.rows ? pm : 0u);
+    }
+  }
+  return m;
+}
+
+// the thread's part of the maximum over the K tiles of workgroup c
+template <int DT, int K>
+__device__ uint32_t chunk_part_max(const CastArgs &p, uint32_t c, uint32_t G, uint32_t T, uint32_t tx_n,
+                                   uint32_t ty_n) {
+  uint32_t m = 0;
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    const uint32_t L = c + k * G;
+    if (L >= T) break;
+    uint32_t tx, ty;
+    tile_xy(p, tile_index(p, L, T), tx_n, ty_n, tx, ty);
+    m = max(m, tile_part_max<DT>(p, ty * kRT, tx * kRT));
+  }
+  return m;
+}
+
+// Wave 0's fast path: publish m, then wait at most fast_ticks for the group
+// slots or the done word. Returns (in every lane) whether the grid's
+// maximum, amax, was found. Every workgroup of the grid that is running
+// marked its slot started within a few microseconds of its start, long
+// before this one finished its loads; so once kGraceTicks have passed, a
+// member slot without this call's tag, or a missing group slot whose
+// first workgroup's slot has no tag, means workgroups that have not
+// started because the grid is not all resident: then the wait stops at
+// once, for the slow path.
+constexpr uint32_t kGraceTicks = 1000;  // 10 us
+__device__ __forceinline__ bool handoff_fast(uint32_t *ws, uint32_t m, uint32_t fast_ticks, uint32_t t, bool ok,
+                                             uint32_t &amax) {
   const uint32_t G = gridDim.x, wg = blockIdx.x, lane = threadIdx.x;
-  const uint64_t tag = static_cast<uint64_t>(e + 1) << 32;
-  if (lane == 0) st_agent64(ws + kSlotWord + 2 * wg, tag | m);
+  const uint64_t tagged = static_cast<uint64_t>(t) << 32;
+  if (lane == 0) st_agent64(ws + kSlotWord + 2 * wg, tagged | m);
   const uint64_t t0 = wall_clock64();
   if (ok && wg % kSlotGroup == 0) {  // the group's first workgroup
     const uint32_t i = wg + lane;
     uint64_t v;
     for (;;) {
-      v = i < G ? ld_agent64(ws + kSlotWord + 2 * i) : tag;
-      if (__all((v >> 32) == (tag >> 32))) break;
-      if (wall_clock64() - t0 > wait_ticks) {
+      v = i < G ? ld_agent64(ws + kSlotWord + 2 * i) : tagged;
+      const uint64_t d = lane == 0 ? ld_agent64(ws + kDoneWord) : 0;
+      if (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(d >> 32)) == t) {  // the slow path's reducer is done
+        amax = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(d));
+        return true;
+      }
+      if (__all(holds_max(v, t))) break;
+      const uint64_t dt = wall_clock64() - t0;
+      if (dt > fast_ticks || (dt > kGraceTicks && __any(static_cast<uint32_t>(v >> 32) != t))) {
         ok = false;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
     const uint32_t gm = wave_max(static_cast<uint32_t>(v));
-    if (ok && lane == 0) st_agent64(ws + kGroupSlotWord + 2 * (wg / kSlotGroup), tag | gm);
+    if (ok && lane == 0) st_agent64(ws + kGroupSlotWord + 2 * (wg / kSlotGroup), tagged | gm);
   }
   const uint32_t ngroups = (G + kSlotGroup - 1) / kSlotGroup;
-  uint64_t v = 0;
   while (ok) {
-    v = lane < ngroups ? ld_agent64(ws + kGroupSlotWord + 2 * lane) : tag;
-    if (__all((v >> 32) == (tag >> 32))) break;
-    if (wall_clock64() - t0 > wait_ticks) ok = false;
-    else __builtin_amdgcn_s_sleep(2);
+    const uint64_t v = lane < ngroups ? ld_agent64(ws + kGroupSlotWord + 2 * lane)
+                       : lane == 63   ? ld_agent64(ws + kDoneWord)
+                                      : tagged;
+    const bool mine = static_cast<uint32_t>(v >> 32) == t;
+    const uint64_t b = __ballot(mine);
+    if (b >> 63) {  // a workgroup of the slow path reduced every slot
+      amax = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63));
+      return true;
+    }
+    if ((b | (1ull << 63)) == ~0ull) {
+      amax = wave_max(lane < ngroups ? static_cast<uint32_t>(v) : 0u);
+      return true;
+    }
+    const uint64_t dt = wall_clock64() - t0;
+    if (dt > fast_ticks) {
+      ok = false;
+    } else if (dt > kGraceTicks) {
+      const bool missing = lane < ngroups && !mine;
+      const uint64_t lv = missing ? ld_agent64(ws + kSlotWord + 2 * kSlotGroup * lane) : tagged;
+      if (__any(static_cast<uint32_t>(lv >> 32) != t)) ok = false;
+      else __builtin_amdgcn_s_sleep(2);
+    } else {
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
-  amax = wave_max(static_cast<uint32_t>(v));
-  return ok;
+  return false;
+}
+
+// Wave 0: claim the next slot, from position `base` (below `limit`) of the
+// scan order (start, start + 1, ... mod G), that no workgroup of this call
+// has touched. Returns its workgroup, or G when none is left below limit or
+// the reducer has already stored the done word. Four windows of 64 slots
+// per step, their loads in flight together; base advances past the steps
+// found without such a slot. Workgroups that scan the same windows would
+// all try the same slot first: each tries the first candidate at or after
+// its own lane `pick` of the first window at or after its own window
+// pick >> 6 that has one. A compare-and-swap lost to another workgroup
+// leaves the slot tagged t, so every step either claims a slot, removes a
+// candidate or advances, and the scan ends.
+__device__ uint32_t claim_next(uint32_t *ws, uint32_t t, uint32_t G, uint32_t limit, uint32_t start, uint32_t pick,
+                               uint32_t &base) {
+  const uint32_t lane = threadIdx.x;
+  const uint64_t tagged = static_cast<uint64_t>(t) << 32;
+  const uint32_t r = pick & 63;
+  while (base < limit) {
+    uint64_t v[4];
+    uint32_t idx[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t pos = base + 64 * q + lane;
+      idx[q] = start + pos >= G ? start + pos - G : start + pos;  // start < G and pos < G where loaded
+      v[q] = pos < limit ? ld_agent64(ws + kSlotWord + 2 * idx[q]) : tagged;
+    }
+    const uint64_t done = lane == 0 ? ld_agent64(ws + kDoneWord) : 0;
+    if (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(done >> 32)) == t) return G;
+    uint64_t cand[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cand[q] = __ballot(static_cast<uint32_t>(v[q] >> 32) != t);
+    int q = -1;
+#pragma unroll
+    for (int k = 3; k >= 0; --k) {  // the first window with a candidate, from window (pick >> 6) & 3 on
+      const int w = (k + (pick >> 6)) & 3;
+      if (cand[w] != 0) q = w;
+    }
+    if (q < 0) {
+      base += 256;
+      continue;
+    }
+    uint64_t c = 0;
+    uint32_t i = 0, vlo = 0, vhi = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // keep the arrays in registers: no dynamic index
+      if (w == q) {
+        c = cand[w];
+        i = idx[w];
+        vlo = static_cast<uint32_t>(v[w]);
+        vhi = static_cast<uint32_t>(v[w] >> 32);
+      }
+    }
+    const uint64_t rot = r ? (c >> r) | (c << (64 - r)) : c;
+    const uint32_t j = (static_cast<uint32_t>(__builtin_ctzll(rot)) + r) & 63;
+    bool won = false;
+    if (lane == j) {
+      uint64_t expect = static_cast<uint64_t>(vhi) << 32 | vlo;
+      won = __hip_atomic_compare_exchange_strong(reinterpret_cast<uint64_t *>(ws + kSlotWord + 2 * i), &expect,
+                                                 tagged | kSlotClaimed, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (__ballot(won) != 0) return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(i), j));
+  }
+  return G;
+}
+
+// Polls back off, up to about 2 us apart: hundreds of workgroups may poll
+// one line at once.
+__device__ __forceinline__ void poll_backoff(uint32_t &backoff) {
+  for (uint32_t k = 0; k < backoff; ++k) __builtin_amdgcn_s_sleep(8);
+  backoff = min(2 * backoff, 8u);
+}
+
+// Wave 0 of the reducer: wait at most `ticks` until every slot carries a
+// maximum tagged t, and reduce them. Four windows of 64 slots per step,
+// their loads in flight together; windows found complete are not read
+// again.
+__device__ bool wait_all_slots(const uint32_t *ws, uint32_t t, uint32_t G, uint32_t ticks, uint32_t &amax) {
+  const uint32_t lane = threadIdx.x;
+  const uint64_t tagged = static_cast<uint64_t>(t) << 32;
+  const uint64_t t0 = wall_clock64();
+  uint32_t from = 0, m = 0, backoff = 1;
+  for (;;) {
+    for (; from < G; from += 256) {
+      uint64_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t i = from + 64 * q + lane;
+        v[q] = i < G ? ld_agent64(ws + kSlotWord + 2 * i) : tagged;
+      }
+      bool all = true;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool h = holds_max(v[q], t);
+        all = all && h;
+        if (h) m = max(m, static_cast<uint32_t>(v[q]));  // max is idempotent: re-reads are harmless
+      }
+      if (!__all(all)) break;
+    }
+    if (from >= G) break;
+    if (wall_clock64() - t0 > ticks) return false;
+    poll_backoff(backoff);
+  }
+  amax = wave_max(m);
+  return true;
+}
+
+// Wave 0 of every other workgroup of the slow path: wait at most `ticks`
+// for the done word.
+__device__ bool wait_done(const uint32_t *ws, uint32_t t, uint32_t ticks, uint32_t &amax) {
+  const uint64_t t0 = wall_clock64();
+  uint32_t backoff = 1;
+  for (;;) {
+    const uint64_t d = threadIdx.x == 0 ? ld_agent64(ws + kDoneWord) : 0;
+    if (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(d >> 32)) == t) {
+      amax = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(d));
+      return true;
+    }
+    if (wall_clock64() - t0 > ticks) return false;
+    poll_backoff(backoff);
+  }
 }
 
 // The thread's 8 row pieces of BF16 tile (r0, c0) loaded straight into LDS
@@ -1080,14 +1314,14 @@ __device__ __forceinline__ void rt_load_lds(const CastArgs &p, uint32_t r0, uint
 // BF16 only) and the others in registers, so that three workgroups fit on a
 // CU where K register tiles would allow two.
 template <int DT, bool B2D, bool SR, int K, int KL = 0>
-__global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, uint32_t *ws, uint32_t wait_ticks) {
+__global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, uint32_t *ws, uint32_t fast_ticks) {
   constexpr int W = RT<DT>::kWords;
   constexpr int KR = K - KL;  // register tiles
   static_assert(KL == 0 || DT == kBF16, "the LDS tile holds BF16 pieces");
   __shared__ RtLds sh;
   __shared__ u32x4 tl[KL ? 8 : 1][KL ? kThreads : 1];  // the LDS tile
-  __shared__ uint32_t lds_ok, lds_amax;
-  __shared__ uint32_t lds_start[3];  // epoch, exit base of the group, exit base over the groups
+  __shared__ uint32_t lds_ok, lds_amax, lds_step, lds_claim;
+  __shared__ uint32_t lds_start[4];  // epoch, exit base of the group, exit base over the groups, sane
   if (p.noop != nullptr && *p.noop == 1.0f) return;
 
   const int tid = threadIdx.x;
@@ -1096,6 +1330,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   const uint32_t T = tx_n * ty_n;
   const uint32_t xg = wg % kBarGroups;
   const uint32_t nxg = min(G, kBarGroups);
+
+  // this call's epoch, and the started mark: by the second wave, before
+  // its tile loads, so that the grid's running workgroups are marked
+  // within microseconds of their start (the other waves' loads go first)
+  if (tid == 64) {
+    const uint32_t e = ld_agent(ws + kEpochWord);
+    st_agent64(ws + kSlotWord + 2 * wg, static_cast<uint64_t>(e + 1) << 32 | kSlotStarted);
+    lds_start[0] = e;
+  }
 
   // ---- load every tile, maximum over them ----
   // Tile coordinates before any load, so that the loads of successive
@@ -1129,21 +1372,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   if constexpr (KL != 0) {
     if (lds_tile) rt_load_lds(p, tile_y[K - 1] * kRT, tile_x[K - 1] * kRT, tl);
   }
-  // this call's epoch and exit bases, read before anything is published
-  // (issued after the tile loads, which need not wait for them); a counter
-  // that is not in a state some call left means a workspace that was not
-  // zero-filled: then only the fallback is trusted
-  uint32_t e = 0;
-  bool sane = true;
+  // the exit bases (issued after the tile loads, which need not wait for
+  // them); a counter that is not in a state some call left means a
+  // workspace that was not zero-filled: then only the whole-input maximum
+  // is trusted
   if (tid == 0) {
-    e = ld_agent(ws + kEpochWord);
     const uint32_t xb = ld_agent(ws + kExitBaseWord + xg * kBarLine);
     const uint32_t xbt = ld_agent(ws + kExitTopBaseWord);
-    sane = ld_agent(ws + kExitWord + xg * kBarLine) - xb < group_members(G, xg) &&
-           ld_agent(ws + kExitTopWord) - xbt < nxg;
-    lds_start[0] = e;
+    const bool sane = ld_agent(ws + kExitWord + xg * kBarLine) - xb < group_members(G, xg) &&
+                      ld_agent(ws + kExitTopWord) - xbt < nxg;
     lds_start[1] = xb;
     lds_start[2] = xbt;
+    lds_start[3] = sane ? 1u : 0u;
   }
 
   // while the loads are in flight the VALU is idle: clear the pieces
@@ -1188,13 +1428,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
       m[0] = max(m[0], ml);
     }
   }
-  workgroup_max(m, sh.red);
+  workgroup_max(m, sh.red);  // its barrier also publishes lds_start
 
-  // ---- publish, then wait for the whole grid (bounded) ----
+  // ---- publish, then wait for the grid ----
+  const uint32_t t = lds_start[0] + 1;
+  const bool ws_sane = lds_start[3] != 0;  // uniform
   if (tid < 64) {
     uint32_t amax = 0;
-    const bool ok = handoff(ws, m[0], wait_ticks, __builtin_amdgcn_readfirstlane(e),
-                            __builtin_amdgcn_readfirstlane(sane ? 1u : 0u) != 0, amax);
+    const bool ok = handoff_fast(ws, m[0], fast_ticks, t, ws_sane, amax);
     if (tid == 0) {
       lds_ok = ok ? 1u : 0u;
       lds_amax = amax;
@@ -1203,9 +1444,63 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   lds_barrier();
 
   uint32_t a[1] = {lds_amax};
-  if (lds_ok == 0) {  // uniform
-    a[0] = input_max<DT>(p);
-    workgroup_max(a, sh.red);
+  if (lds_ok == 0) {  // uniform: the slow path
+    if (ws_sane) {
+      const uint64_t tagged = static_cast<uint64_t>(t) << 32;
+      const uint64_t t0 = wall_clock64();
+      // claims: within kClaimSpan slots of a spread start; the reducer then
+      // scans every slot for what is left
+      const uint32_t h = wg * 0x9E3779B9u;
+      const uint32_t start = static_cast<uint32_t>((static_cast<uint64_t>(h) * G) >> 32);
+      const uint32_t pick = (h >> 8) & 255;
+      bool reducer = false;  // uniform
+      for (int pass = 0; pass < 2; ++pass) {
+        uint32_t base = 0;  // wave 0's scan position
+        const uint32_t limit = pass == 0 ? min(G, kClaimSpan) : G;
+        for (;;) {
+          if (tid < 64) {
+            const uint32_t c = claim_next(ws, t, G, limit, start, pick, base);
+            if (tid == 0) lds_claim = c;
+          }
+          lds_barrier();
+          const uint32_t c = lds_claim;  // uniform
+          if (c >= G) break;
+          uint32_t cm[1] = {chunk_part_max<DT, K>(p, c, G, T, tx_n, ty_n)};
+          workgroup_max(cm, sh.red);
+          if (tid == 0) st_agent64(ws + kSlotWord + 2 * c, tagged | cm[0]);
+        }
+        if (pass == 1) break;
+        // elect the reducer: the first workgroup to tag the reducer word
+        if (tid == 0) {
+          uint64_t r = ld_agent64(ws + kReducerWord);
+          bool won = false;
+          if (static_cast<uint32_t>(r >> 32) != t)
+            won = __hip_atomic_compare_exchange_strong(reinterpret_cast<uint64_t *>(ws + kReducerWord), &r,
+                                                       tagged | wg, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+          lds_step = won ? 1u : 0u;
+        }
+        lds_barrier();
+        reducer = lds_step != 0;
+        if (!reducer) break;
+      }
+      if (tid < 64) {
+        const uint64_t spent = wall_clock64() - t0;
+        const uint32_t left = spent < kLastResortTicks ? kLastResortTicks - static_cast<uint32_t>(spent) : 0u;
+        uint32_t am = 0;
+        const bool ok = reducer ? wait_all_slots(ws, t, G, left, am) : wait_done(ws, t, left, am);
+        if (tid == 0) {
+          if (ok && reducer) st_agent64(ws + kDoneWord, tagged | am);
+          lds_amax = ok ? am : 0xFFFFFFFFu;  // no maximum: the last resort below
+        }
+      }
+      lds_barrier();
+      a[0] = lds_amax;
+    }
+    if (!ws_sane || a[0] == 0xFFFFFFFFu) {  // uniform: the last resort
+      a[0] = input_max<DT>(p);
+      workgroup_max(a, sh.red);
+    }
   }
   const float amax = __uint_as_float(a[0]);
   if (wg == 0 && tid == 0) {
@@ -1257,10 +1552,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
           st_agent(ws + kEpochWord, e + 1);
         } else {
           // the next tag would be 0 and tags would start to repeat: clear
-          // every slot (no call tags with 0) and start again at epoch 0, so
-          // that a slot left by a call 2^32 calls ago cannot pass for the
-          // next call's (about 4000 stores, once per 2^32 calls)
+          // every slot, the done and reducer words (no call tags with 0) and start
+          // again at epoch 0, so that a word left by a call 2^32 calls ago
+          // cannot pass for the next call's (about 4000 stores, once per
+          // 2^32 calls)
           for (uint32_t i = kSlotWord; i < kEpochWord; ++i) st_agent(ws + i, 0u);
+          st_agent64(ws + kDoneWord, 0u);
+          st_agent64(ws + kReducerWord, 0u);
           st_agent(ws + kEpochWord, 0u);
         }
       }
@@ -1408,6 +1706,7 @@ constexpr int kLdsVariant = 6;
 constexpr int kVariants = 7;
 constexpr int kMaxDevices = 64;
 std::atomic<uint32_t> g_wait_ticks{0};
+std::atomic<uint32_t> g_forced_variant{0};
 
 template <int DT, bool B2D, bool SR>
 const void *resident_kernel_v(int v) {
@@ -1524,6 +1823,14 @@ ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uin
   // (8192x4096 1x16 with 688 workgroups of three slots: 35.5 us; 768: the
   // CUs even).
   static constexpr int kOrder[] = {1, 2, 3, kLdsVariant, 4, 5};
+  // A forced variant takes one workgroup per `slots` tiles, however many
+  // that is (it may be more than can be resident at once).
+  const int forced = static_cast<int>(g_forced_variant.load(std::memory_order_relaxed));
+  if (forced != 0 && (dtype == kBF16 || forced == 1)) {
+    const uint64_t slots = forced == kLdsVariant ? 4 : forced;
+    const uint64_t G = round8(static_cast<uint32_t>((tiles + slots - 1) / slots));
+    if (G <= kMaxPartials) return ResidentPlan{forced, static_cast<uint32_t>(G)};
+  }
   for (int v : kOrder) {
     const int slots = v == kLdsVariant ? 4 : v;
     if (v > 1 && dtype != kBF16) break;
@@ -1537,7 +1844,7 @@ ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uin
 hipError_t launch_cast_resident(const CastArgs &a, uint32_t *ws, int dtype, bool block_2d, bool sr,
                                 const ResidentPlan &plan, hipStream_t s) {
   const uint32_t t = g_wait_ticks.load(std::memory_order_relaxed);
-  const uint32_t ticks = t != 0 ? t : kDefaultWaitTicks;
+  const uint32_t ticks = t != 0 ? t : kDefaultFastTicks;
   const uint32_t G = plan.grid;
   const int v = plan.variant;
   if (dtype == kBF16) {
@@ -1553,5 +1860,11 @@ hipError_t launch_cast_resident(const CastArgs &a, uint32_t *ws, int dtype, bool
 }
 
 void set_resident_wait_ticks(uint32_t ticks) { g_wait_ticks.store(ticks, std::memory_order_relaxed); }
+
+bool set_resident_variant(uint32_t v) {
+  if (v >= static_cast<uint32_t>(kVariants)) return false;
+  g_forced_variant.store(v, std::memory_order_relaxed);
+  return true;
+}
 
 }  // namespace nvfp4

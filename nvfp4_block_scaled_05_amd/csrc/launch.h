@@ -25,7 +25,10 @@ constexpr uint32_t kPartialsGrain = 4;
 // Grid-wide handoff of the single-pass cast, in the workspace after the two
 // partials arrays (word offsets):
 //   kSlotWord       one 64-bit slot per workgroup (at most kMaxPartials):
-//                   tag << 32 | the workgroup's maximum;
+//                   tag << 32 | the maximum of the workgroup's tiles, or
+//                   tag << 32 | kSlotStarted (the workgroup runs and will
+//                   store its maximum) or kSlotClaimed (another workgroup
+//                   took over the maximum of those tiles);
 //   kGroupSlotWord  one 64-bit slot per group of kSlotGroup workgroups, with
 //                   the group's maximum, written by its first workgroup;
 //   kEpochWord      the epoch e: a call tags its slots e + 1;
@@ -33,7 +36,11 @@ constexpr uint32_t kPartialsGrain = 4;
 //                   exit counters (per group of workgroups blockIdx.x mod
 //                   kBarGroups, then over the groups) and their values when
 //                   the call began; the last workgroup to exit advances the
-//                   epoch. Each counter sits in a 128-byte line of its own.
+//                   epoch. Each counter sits in a 128-byte line of its own;
+//   kDoneWord       tag << 32 | the grid's maximum, stored by the reducer
+//                   of the slow path;
+//   kReducerWord    tag << 32 | the workgroup elected to reduce every slot
+//                   in the slow path.
 // All of it must be zero before a workspace is first used; every call
 // leaves the counters equal to their bases, ready for the next call.
 constexpr uint32_t kBarGroups = 8;
@@ -46,8 +53,14 @@ constexpr uint32_t kExitWord = kEpochWord + kBarLine;
 constexpr uint32_t kExitBaseWord = kExitWord + kBarGroups * kBarLine;
 constexpr uint32_t kExitTopWord = kExitBaseWord + kBarGroups * kBarLine;
 constexpr uint32_t kExitTopBaseWord = kExitTopWord + kBarLine;
+constexpr uint32_t kDoneWord = kExitTopBaseWord + kBarLine;
+constexpr uint32_t kReducerWord = kDoneWord + kBarLine;
 constexpr uint32_t kWorkspaceWords = 9216;
-static_assert(kExitTopBaseWord + kBarLine <= kWorkspaceWords, "handoff words fit the workspace");
+static_assert(kReducerWord + 2 <= kWorkspaceWords, "handoff words fit the workspace");
+// Low words of a slot that carry no maximum (a maximum is a non-negative
+// float's bit pattern, below 2^31).
+constexpr uint32_t kSlotStarted = 0xFFFFFFFEu;
+constexpr uint32_t kSlotClaimed = 0xFFFFFFFFu;
 static_assert(kWorkspaceWords * 4 == 36864, "workspace size is part of the ABI");
 
 // Arguments of the fused cast(-transpose) kernels. A direction whose data
@@ -118,10 +131,15 @@ hipError_t launch_cast_resident(const CastArgs &a, uint32_t *workspace, int dtyp
 void set_rht_unit(uint32_t unit);
 bool rht_cast_on_matrix_cores();
 bool rht_amax_on_matrix_cores();
-// Bound on the handoff wait, in ticks of the 100 MHz real-time counter; after
-// it a workgroup computes the amax from the whole input itself. 0 restores
-// the default.
+// Bound on the fast handoff wait, in ticks of the 100 MHz real-time counter;
+// after it a workgroup claims the tiles of workgroups that have not started.
+// 0 restores the default.
 void set_resident_wait_ticks(uint32_t ticks);
+// Test hook: 0 lets resident_plan choose; 1 .. 6 forces that variant (tiles
+// per workgroup; 6: three register tiles and one LDS tile) with one
+// workgroup per that many tiles, even beyond what can be resident at once.
+// Returns false for other values.
+bool set_resident_variant(uint32_t v);
 
 // Grouped forms. row_start: host array of ngroups + 1 prefix sums of the
 // groups' row counts (validated by the caller). `a` describes the whole

@@ -4,13 +4,17 @@ workspace. Checked bit for bit against the oracle and against the two-pass
 form (amax pass + cast), on shapes that give 1 to 4 tiles per workgroup
 (the fourth held in LDS),
 ragged edges, every output choice, one workspace reused across grid sizes,
-the bounded wait forced to run out (each workgroup then reads the whole
-input for the amax), and noop.
+the fast wait forced to run out (nearly every workgroup then takes the slow
+path: it claims the tiles of workgroups that have not started and reduces
+every slot itself), grids forced beyond what can be resident at once (the
+slow path must complete them), and noop.
 
 The workspace's exit counters and their bases (words 8288 + 32 x and
 8544 + 32 x, x = 0..7; 8800 and 8832 over the groups) must be equal after
 every call, and the epoch (word 8256) must have advanced by one per
-single-pass call: that is what lets the next call start without a reset."""
+single-pass call: that is what lets the next call start without a reset.
+The done word (64 bits at word 8864: tag << 32 | amax bits) carries the
+call's tag exactly when a workgroup took the slow path."""
 
 from __future__ import annotations
 
@@ -27,7 +31,7 @@ pytestmark = pytest.mark.gpu
 
 SINGLE, TWO = nv.NVFP4_AMAX_PATH_SINGLE_PASS, nv.NVFP4_AMAX_PATH_TWO_PASS
 
-EPOCH, EXIT, EXIT_BASE, EXIT_TOP, EXIT_TOP_BASE, LINE = 8256, 8288, 8544, 8800, 8832, 32
+EPOCH, EXIT, EXIT_BASE, EXIT_TOP, EXIT_TOP_BASE, LINE, DONE = 8256, 8288, 8544, 8800, 8832, 32, 8864
 
 
 def handoff_words(ws):
@@ -36,6 +40,12 @@ def handoff_words(ws):
     ok = (np.array_equal(w[EXIT:EXIT + 8 * LINE:LINE], w[EXIT_BASE:EXIT_BASE + 8 * LINE:LINE])
           and w[EXIT_TOP] == w[EXIT_TOP_BASE])
     return int(w[EPOCH]), bool(ok)
+
+
+def done_word(ws):
+    """(tag, amax bits) of the done word"""
+    w = host(ws).view(np.uint32)
+    return int(w[DONE + 1]), int(w[DONE])
 
 
 def run(xd, cfg, rowwise=True, columnwise=True):
@@ -152,8 +162,8 @@ def test_workspace_reused_across_grid_sizes():
 @pytest.mark.parametrize("rows,cols,opts", [(512, 768, dict(block_2d=True)), (7168, 4608, {}),
                                             (6256, 6256, dict(block_2d=True))])
 def test_wait_that_runs_out_gives_the_same_bytes(rows, cols, opts):
-    # a wait bound of one tick: nearly every workgroup stops waiting and
-    # reads the whole input for the amax itself
+    # a fast wait bound of one tick: nearly every workgroup takes the slow
+    # path (claims, then reduces every slot itself)
     x = W.randn_bf16(rows, cols, 61)
     xd = to_device(x)
     ws = nv.empty_workspace(DEV)
@@ -163,11 +173,50 @@ def test_wait_that_runs_out_gives_the_same_bytes(rows, cols, opts):
         forced = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))
     finally:
         nv.nvfp4_debug_set_wait_ticks(0)
-    assert_same(normal, forced, "forced fallback")
+    assert_same(normal, forced, "forced slow path")
     assert handoff_words(ws) == (2, True)
+    assert done_word(ws) == (2, int(forced["amax_row"].view(np.uint32)[0])), "the slow path did not run"
     after = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))  # the counters are ready for the next call
-    assert_same(normal, after, "after the fallback")
-    assert_oracle(normal, x, what="fallback shape", **opts)
+    assert_same(normal, after, "after the slow path")
+    assert_oracle(normal, x, what="slow path shape", **opts)
+
+
+# (variant, rows, cols, dtype, options): one workgroup per `variant` tiles
+# gives grids of 1024 to 2048 workgroups, more than the variant's occupancy
+# lets the GPU hold at once (its VGPRs or LDS allow 3 to 5 per CU on 256
+# CUs), so part of the grid starts only after the rest has finished
+OVERSUBSCRIBED = [
+    (1, 8192, 4096, "bf16", dict(block_2d=True)),
+    (1, 4096, 8192, "fp32", dict()),
+    (2, 8192, 8192, "bf16", dict()),
+    (3, 8192, 8192, "bf16", dict(block_2d=True, stochastic=True, sr_seed=13)),
+    (6, 8192, 8192, "bf16", dict(swizzled=True)),
+]
+
+
+@pytest.mark.parametrize("case", OVERSUBSCRIBED, ids=[f"v{c[0]}_{c[1]}x{c[2]}_{c[3]}" for c in OVERSUBSCRIBED])
+def test_grid_beyond_residency_completes_with_the_same_bytes(case):
+    v, rows, cols, dtype, opts = case
+    print(f"oversubscribed variant {v} {rows}x{cols} {dtype} {opts}", flush=True)
+    x = W.gaussian_fp32(rows, cols, 77, scale=2.0) if dtype == "fp32" else W.randn_bf16(rows, cols, 77)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    two = run(xd, nv.make_config(workspace=ws, amax_path=TWO, **opts))
+    nv.nvfp4_debug_set_resident_variant(v)
+    try:
+        for i in range(2):
+            one = run(xd, nv.make_config(workspace=ws, amax_path=SINGLE, **opts))
+            assert_same(one, two, f"call {i}")
+            assert handoff_words(ws) == (i + 1, True), f"call {i}"
+            assert done_word(ws) == (i + 1, int(one["amax_row"].view(np.uint32)[0])), f"call {i}: no slow path"
+    finally:
+        nv.nvfp4_debug_set_resident_variant(0)
+
+
+def test_unknown_variant_is_rejected():
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.nvfp4_debug_set_resident_variant(7)
+    assert e.value.status == nv.NVFP4_ERR_UNSUPPORTED
 
 
 def test_noop_writes_nothing_and_leaves_the_counters():
@@ -236,8 +285,9 @@ def test_epoch_wrap_clears_the_slots():
     stale = (1 << 32) | 0x7F000000  # tag 1, max 2^127
     slot = 4096 + 2 * 600
     words[EPOCH] = -3  # 0xFFFFFFFD
-    words[slot] = stale & 0xFFFFFFFF
-    words[slot + 1] = stale >> 32
+    for w in (slot, DONE):  # a slot and the done word, as such a call left them
+        words[w] = stale & 0xFFFFFFFF
+        words[w + 1] = stale >> 32
     torch.cuda.synchronize()
     for i in range(2):
         got = run(to_device(small), nv.make_config(workspace=ws, amax_path=SINGLE))
@@ -245,6 +295,7 @@ def test_epoch_wrap_clears_the_slots():
     epoch, ok = handoff_words(ws)
     assert ok and epoch == 0
     assert int(words[slot + 1]) == 0, "the stale slot was not cleared at the wrap"
+    assert int(words[DONE + 1]) == 0, "the stale done word was not cleared at the wrap"
     got = run(to_device(big), nv.make_config(workspace=ws, amax_path=SINGLE, block_2d=True, swizzled=True))
     assert_oracle(got, big, swizzled=True, what="after the wrap", block_2d=True)
     assert handoff_words(ws) == (1, True)
