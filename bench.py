@@ -25,10 +25,14 @@ read of the input, both outputs and scale arrays, the amax pair), over its
 average duration, against the 8 TB/s HBM peak: a kernel that reads its input
 once cannot be credited with the method's second read. achieved_alg_bytes
 puts B_alg over the same duration (the method's figure; it can exceed the
-peak for a one-read kernel). The duration comes from timing-only HIP events
-that the library records on the call's stream right before and after that
-launch (cast_events in the config), in a second pass of the same calls
-after the timed region. traffic is the HBM bytes per launch from the
+peak for a one-read kernel). The duration comes from HIP events on the
+call's stream, in a second pass of the same calls after the timed region:
+for the single-pass form, whose call is that one launch, a pair of events
+around all the calls (launches back to back, as in use; per-launch markers
+would keep each launch from overlapping the previous one's end); for the
+two-pass form, timing-only events that the library records right before
+and after each cast launch (cast_events in the config). traffic is the HBM
+bytes per launch from the
 FETCH_SIZE / WRITE_SIZE counters, scaled by a plain copy's (profiles/), or
 null when the kernel's code changed since.
 
@@ -512,6 +516,20 @@ def run_swizzle_shapes(nv, torch, dev, w, steps, warmup):
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
+def time_launches(torch, cfg, sets, stream, steps, nv):
+    """Average time per call in ms from one pair of HIP events recorded on
+    the calls' stream around `steps` calls (each call one launch)."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        x, row, col = sets[i % len(sets)]
+        nv.nvfp4_quantize(x, row, col, cfg, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def time_cast_in_calls(nv, torch, cfg, sets, stream, steps):
     """Average cast-kernel time in ms over `steps` whole calls, from HIP
     events that the library records around the cast launch."""
@@ -689,13 +707,13 @@ def main():
     two_pass_ms = timed_calls(nv.make_config(block_2d=True, swizzled=True, workspace=workspace,
                                              amax_path=nv.NVFP4_AMAX_PATH_TWO_PASS), args.steps, args.warmup)
 
-    # Dominant kernel: the same calls again, with the library recording a
-    # pair of HIP events on the call's stream around the launch of the
-    # single-pass kernel (or of the cast kernel of the two-pass form),
-    # nvfp4_config_t.cast_events, so the kernel is timed inside whole calls.
-    # The events are timing-only (hipEventDisableSystemFence): without the
-    # system-scope cache writeback of an ordinary event, a marker costs little.
-    cast_ms = time_cast_in_calls(nv, torch, cfg, sets, stream, args.steps)
+    # Dominant kernel: the same calls again. A single-pass call is that one
+    # launch: one pair of HIP events on the call's stream around all of them.
+    # In the two-pass form the library records a pair of timing-only events
+    # (hipEventDisableSystemFence) around each cast launch,
+    # nvfp4_config_t.cast_events, so the cast is timed inside whole calls.
+    cast_ms = (time_launches(torch, cfg, sets, stream, args.steps, nv) if single
+               else time_cast_in_calls(nv, torch, cfg, sets, stream, args.steps))
     # bytes the kernel moves: one read of the input plus every output, for
     # the single-pass kernel and for the two-pass form's cast alike
     kernel_bytes = B_MIN
