@@ -227,8 +227,8 @@ OTHER_WORKLOADS = {
     "c4": dict(desc="4096x8192 BF16 N(0,1) x per-row exp(2n) (seed 3); per-row amax; row-wise only; compact; RNE",
                bytes=2 * 4096 * 8192 + 4096 * 8192 // 2 + 4096 * 8192 // 16 + 4 * 4096),
     "c4_both": dict(desc="as c4, both orientations: per-row amax for the row-wise side, per-column amax for the "
-                         "column-wise side (three input reads: fused row pass, column amax, column encode)",
-                    bytes=3 * 2 * 4096 * 8192 + 2 * (4096 * 8192 // 2 + 4096 * 8192 // 16) + 4 * (4096 + 8192)),
+                         "column-wise side (two input reads: both amax arrays, then both orientations)",
+                    bytes=2 * 2 * 4096 * 8192 + 2 * (4096 * 8192 // 2 + 4096 * 8192 // 16) + 4 * (4096 + 8192)),
     "c5": dict(desc="8192x8192 BF16 N(0,1) + 0.1% at +-200 (seed 4); 1x16; row plain + col 16-point RHT; "
                     "stochastic rounding (seed 5); compact",
                bytes=2 * 2 * 8192 * 8192 + 2 * (8192 * 8192 // 2 + 8192 * 8192 // 16) + 8),

@@ -147,16 +147,11 @@ extern "C" nvfp4_status_t nvfp4_compute_amax(const void *x, nvfp4_dtype_t dtype,
     if (row_amax != nullptr && row_amax == col_amax)
       return fail(NVFP4_ERR_UNSUPPORTED, "row-scaled per-row and per-column amaxes need two distinct buffers");
     const uint32_t R = static_cast<uint32_t>(rows), C = static_cast<uint32_t>(cols);
-    if (row_amax != nullptr) {
+    if (col_amax == nullptr) {  // per-row only: one workgroup per row, no atomics
       nvfp4::RowScaledArgs a{x, R, C, nullptr, nullptr, row_amax, 0u, cfg.noop};
-      if ((st = hip_status(nvfp4::launch_rowscaled(a, dtype, false, true, s), "row amax launch")) != NVFP4_OK)
-        return st;
+      return hip_status(nvfp4::launch_rowscaled(a, dtype, false, true, s), "row amax launch");
     }
-    if (col_amax != nullptr) {
-      nvfp4::RowScaledArgs c{x, R, C, nullptr, nullptr, col_amax, 0u, cfg.noop};
-      return hip_status(nvfp4::launch_colscaled(c, dtype, false, true, s), "column amax launch");
-    }
-    return NVFP4_OK;
+    return hip_status(nvfp4::launch_dual_amax(x, dtype, R, C, row_amax, col_amax, cfg.noop, s), "row-scaled amax launch");
   }
   if (cfg.rht) {
     if (rows % 16 != 0) return fail(NVFP4_ERR_SHAPE, "the RHT needs rows %% 16 == 0 (rows = %lld)", (long long)rows);
@@ -229,14 +224,22 @@ nvfp4_status_t quantize_impl(const void *x, nvfp4_dtype_t dtype, int64_t rows, i
   if (cfg.row_scaled) {
     const uint32_t ue = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
     if ((st = record(0)) != NVFP4_OK) return st;
-    if (row) {
+    if (!col) {  // row-wise only: one launch that reduces each row and encodes it from registers
       nvfp4::RowScaledArgs a{x, R, C, row->data, row->scales, row->amax, cfg.sr_seed, cfg.noop, ue};
       st = hip_status(nvfp4::launch_rowscaled(a, dtype, sr, cfg.compute_amax != 0, s), "row-scaled quantize launch");
+      return st != NVFP4_OK ? st : record(1);
     }
-    if (st == NVFP4_OK && col) {
-      nvfp4::RowScaledArgs c{x, R, C, col->data, col->scales, col->amax, cfg.sr_seed, cfg.noop, ue};
-      st = hip_status(nvfp4::launch_colscaled(c, dtype, sr, cfg.compute_amax != 0, s),
-                      "row-scaled column-wise quantize launch");
+    // column-wise output: the per-row and per-column amax in one read, then
+    // both orientations by register tiles in a second read
+    if (cfg.compute_amax)
+      st = hip_status(nvfp4::launch_dual_amax(x, dtype, R, C, row ? row->amax : nullptr, col->amax, cfg.noop, s),
+                      "row-scaled amax launch");
+    if (st == NVFP4_OK) {
+      nvfp4::CastArgs a{x,  R,          C,           row ? row->data : nullptr, row ? row->scales : nullptr,
+                        row ? row->amax : nullptr, col->data, col->scales, col->amax, 0u, cfg.sr_seed,
+                        0u, cfg.noop,  nullptr,    0u};
+      a.ue5m3 = ue;
+      st = hip_status(nvfp4::launch_cast_rowscaled(a, dtype, sr, s), "row-scaled quantize launch");
     }
     return st != NVFP4_OK ? st : record(1);
   }

@@ -298,7 +298,7 @@ __device__ __forceinline__ void rt_clear_outside(const CastArgs &p, uint32_t r0,
   }
 }
 
-template <int DT, bool B2D, bool SR, bool PRE = false>
+template <int DT, bool B2D, bool SR, bool PRE = false, bool RS = false>
 __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32_t ty,
                                           uint32_t (&w)[8][RT<DT>::kWords], float S_row, float S_col, bool ue,
                                           RtLds &sh, uint32_t m2d = 0);
@@ -347,10 +347,16 @@ __device__ __forceinline__ void cast_rt_tile(const CastArgs &p, uint32_t tx, uin
 // only after the barrier below, so the caller may fill it right before.
 // PRE: the caller has cleared w outside the input and, with 16x16 blocks,
 // passes the block maximum in m2d.
-template <int DT, bool B2D, bool SR, bool PRE>
+// RS (row-scaled, 1x16 blocks): every row and every column has a global
+// scale of its own, which the caller has put in sh.mult[0][tile row] and
+// sh.mult[1][tile column] before a barrier; S_row and S_col are unused, and
+// each block's multiplier is divided out from its own scale rather than
+// looked up.
+template <int DT, bool B2D, bool SR, bool PRE, bool RS>
 __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32_t ty,
                                           uint32_t (&w)[8][RT<DT>::kWords], float S_row, float S_col, bool ue,
                                           RtLds &sh, uint32_t m2d) {
+  static_assert(!(RS && B2D), "row-scaled tiles have 1x16 blocks");
   const int tid = threadIdx.x;
   const int ucol = tid & 15;
   const int rg = tid >> 4;
@@ -370,6 +376,7 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
 
   // ---- block scale codes ----
   uint32_t rcode[8], ccode[8];
+  float rmul[RS ? 8 : 1], cmul[RS ? 8 : 1];  // RS: the blocks' multipliers
   if (B2D) {
     const uint32_t m = PRE ? m2d : block2d_max<DT>(w);
     const uint32_t cr = block_code(m, S_row, ue);
@@ -392,10 +399,17 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
       const bool lo = (ucol & 1) == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t mine = block_code(pick(lo, mr[j], mr[j + 4]), S_row, ue);
+        const float S = RS ? sh.mult[0][8 * rg + (lo ? j : j + 4)] : S_row;
+        const uint32_t mine = block_code(pick(lo, mr[j], mr[j + 4]), S, ue);
         const uint32_t other = dpp_mov<kQuadXor1>(mine);
         rcode[j] = pick(lo, mine, other);
         rcode[j + 4] = pick(lo, other, mine);
+        if (RS) {
+          const uint32_t mm = __float_as_uint(code_multiplier(mine, S, ue));
+          const uint32_t om = dpp_mov<kQuadXor1>(mm);
+          rmul[j] = __uint_as_float(pick(lo, mm, om));
+          rmul[j + 4] = __uint_as_float(pick(lo, om, mm));
+        }
       }
     }
     if (do_col) {
@@ -425,10 +439,17 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
       const bool lo = (rg & 1) == 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t mine = block_code(pick(lo, mc[j], mc[j + 4]), S_col, ue);
+        const float S = RS ? sh.mult[1][8 * ucol + (lo ? j : j + 4)] : S_col;
+        const uint32_t mine = block_code(pick(lo, mc[j], mc[j + 4]), S, ue);
         const uint32_t other = swz_xor16(mine);
         ccode[j] = pick(lo, mine, other);
         ccode[j + 4] = pick(lo, other, mine);
+        if (RS) {
+          const uint32_t mm = __float_as_uint(code_multiplier(mine, S, ue));
+          const uint32_t om = swz_xor16(mm);
+          cmul[j] = __uint_as_float(pick(lo, mm, om));
+          cmul[j + 4] = __uint_as_float(pick(lo, om, mm));
+        }
       }
     }
   }
@@ -461,6 +482,12 @@ __device__ __forceinline__ void rt_encode(const CastArgs &p, uint32_t tx, uint32
     for (int k = 0; k < 8; ++k) {
       re[k] = r;
       ce[k] = c;
+    }
+  } else if (RS) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      re[k] = do_row ? rmul[k] : 0.0f;
+      ce[k] = do_col ? cmul[k] : 0.0f;
     }
   } else {
 #pragma unroll
@@ -969,6 +996,37 @@ __global__ __launch_bounds__(kThreads) void k_cast_rt(CastArgs p) {
   uint32_t tx, ty;
   tile_xy(p, t, gridDim.x, gridDim.y, tx, ty);
   cast_rt_tile<DT, B2D, SR>(p, tx, ty);
+}
+
+// Row-scaled quantize of one tile per workgroup: the global scales of the
+// tile's 128 rows and 128 columns from the per-row and per-column amax
+// arrays (p.row_amax, p.col_amax), one division per thread, then the tile
+// encode with each block's multiplier divided out from its own scale
+// ("Implement row-scaled NVFP4 fprop recipe", Greptile summary: block scales
+// relative to a per-row amax; the column-wise side relative to a per-column
+// amax as the review thread of "Write both NVFP4 amax buffers" sizes it).
+template <int DT, bool SR>
+__global__ __launch_bounds__(kThreads) void k_cast_rt_rowscaled(CastArgs p) {
+  constexpr int W = RT<DT>::kWords;
+  __shared__ RtLds sh;
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+  const uint32_t t = tile_index(p, blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  uint32_t tx, ty;
+  tile_xy(p, t, gridDim.x, gridDim.y, tx, ty);
+  const int tid = threadIdx.x;
+  const uint32_t r0 = ty * kRT, c0 = tx * kRT;
+  uint32_t w[8][W];
+  rt_load<DT>(p, r0, c0, w);
+  const bool ue = p.ue5m3 != 0;
+  if (tid < kRT) {
+    const uint32_t r = r0 + tid;
+    sh.mult[0][tid] = p.row_data != nullptr && r < p.rows ? global_encode_scale(p.row_amax[r], ue) : 1.0f;
+  } else {
+    const uint32_t c = c0 + (tid - kRT);
+    sh.mult[1][tid - kRT] = p.col_data != nullptr && c < p.cols ? global_encode_scale(p.col_amax[c], ue) : 1.0f;
+  }
+  lds_barrier();
+  rt_encode<DT, false, SR, false, true>(p, tx, ty, w, 1.0f, 1.0f, ue, sh);
 }
 
 template <int DT, bool SR, bool MFMA>
@@ -1717,6 +1775,19 @@ hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, con
   if (t.unit_start[ngroups] == 0) return hipSuccess;
   return dtype == kBF16 ? launch_grouped_dt<kBF16>(a, t, block_2d, rht, sr, s)
                         : launch_grouped_dt<kFP32>(a, t, block_2d, rht, sr, s);
+}
+
+hipError_t launch_cast_rowscaled(const CastArgs &a, int dtype, bool sr, hipStream_t s) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  const dim3 grid((a.cols + kRT - 1) / kRT, (a.rows + kRT - 1) / kRT), block(kThreads);
+  if (dtype == kBF16) {
+    if (sr) hipLaunchKernelGGL((k_cast_rt_rowscaled<kBF16, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_cast_rt_rowscaled<kBF16, false>), grid, block, 0, s, a);
+  } else {
+    if (sr) hipLaunchKernelGGL((k_cast_rt_rowscaled<kFP32, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_cast_rt_rowscaled<kFP32, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_cast(const CastArgs &a, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s) {

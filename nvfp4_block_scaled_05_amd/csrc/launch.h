@@ -161,10 +161,15 @@ hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, con
                                uint32_t ngroups, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
-// Column-wise side: compute_amax zeroes a.amax ([cols]) and reduces each
-// column's amax (two launches), else a.amax is read; then, unless a.data is
-// NULL, the column-wise encode (rows % 16 == 0).
-hipError_t launch_colscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
+// Per-row ([rows]) and per-column ([cols]) amax of the input, either may be
+// NULL: one zeroing launch and one reduction that reads the input once.
+hipError_t launch_dual_amax(const void *x, int dtype, uint32_t rows, uint32_t cols, float *row_amax, float *col_amax,
+                            const float *noop, hipStream_t s);
+// Row-scaled quantize by 128x128 register tiles: the row-wise side (if
+// a.row_data) with 1x16 blocks scaled by a.row_amax[row], the column-wise side
+// (if a.col_data) with 1x16 blocks down each column scaled by
+// a.col_amax[column]; the amax arrays are read, compact scales only.
+hipError_t launch_cast_rowscaled(const CastArgs &a, int dtype, bool sr, hipStream_t s);
 // grouped form: row_start[0..ngroups] are the groups' first rows (stochastic
 // rounding counts byte indices per group)
 hipError_t launch_rowscaled_grouped(const RowScaledArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,

@@ -12,8 +12,6 @@
 // four scale codes of an aligned group (four consecutive threads) are
 // gathered with DPP, and the row maximum is a DPP wave reduction plus one
 // barrier.
-#include <atomic>
-
 #include "codec.h"
 #include "launch.h"
 
@@ -210,23 +208,18 @@ __global__ __launch_bounds__(kThreads) void k_rowscaled_grouped(RowScaledArgs p,
 }
 
 // ---------------------------------------------------------------------------
-// Column-wise side of a row-scaled quantize. The column-wise tensor's rows
-// are the input's columns, so it is scaled along them: one amax per input
-// column, and each column's 1x16 blocks (16 consecutive rows) take their
-// E4M3 scales relative to that column's global scale (the quantizer
-// prototype in the review thread of "Write both NVFP4 amax buffers" sizes
-// the column-wise amax of a row-scaled tensor as one float per input
-// column). Two launches: a column reduction (HBM-bound, one read of
-// the input) and the encode (one more read, the transpose written out).
+// Per-row and per-column amax of a row-scaled quantize with both
+// orientations. The column-wise tensor's rows are the input's columns, so it
+// is scaled along them: one amax per input column, and each column's 1x16
+// blocks (16 consecutive rows) take their scales relative to that column's
+// global scale (the quantizer prototype in the review thread of "Write both
+// NVFP4 amax buffers" sizes the column-wise amax of a row-scaled tensor as
+// one float per input column). Both orientations then take one read each:
+// this reduction of both amax arrays, and the register-tile encode of both
+// orientations with per-row and per-column global scales (cast.hip).
 // ---------------------------------------------------------------------------
 constexpr uint32_t kColAmaxCols = 512;  // 64 lanes x 8 columns: one wave reads 1 KiB (BF16) of a row
-constexpr uint32_t kColAmaxRows = 128;  // rows per workgroup of the reduction
-constexpr uint32_t kColStrip = 64;      // columns per encode workgroup (8 lanes x 8 columns)
-constexpr uint32_t kColRows = 512;      // rows per encode unit (32 lane groups x 16 rows)
-#ifndef NVFP4_COL_WGS_PER_CU
-#define NVFP4_COL_WGS_PER_CU 2
-#endif
-constexpr int kColWgsPerCu = NVFP4_COL_WGS_PER_CU;  // encode workgroups kept per compute unit
+constexpr uint32_t kColAmaxRows = 64;   // rows per workgroup of the reduction: one batch per wave
 
 template <int DT>
 struct Piece8 {  // 8 consecutive elements of one row
@@ -240,7 +233,7 @@ __device__ __forceinline__ Piece8<DT> load_piece8(const void *x, uint64_t elem_o
   const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(x) + elem_off * (DT == kBF16 ? 2 : 4));
 #pragma unroll
   for (int q = 0; q < Piece8<DT>::kWords / 4; ++q) {
-    const u32x4 t = __builtin_nontemporal_load(src + q);
+    const u32x4 t = src[q];
     b.w[4 * q] = t.x;
     b.w[4 * q + 1] = t.y;
     b.w[4 * q + 2] = t.z;
@@ -275,47 +268,102 @@ struct ColMax<kBF16> {
   }
 };
 
+// max |x| of a piece as the bit pattern of a non-negative float
 template <int DT>
-__device__ __forceinline__ float piece8_value(const Piece8<DT> &b, int c) {
-  if (DT == kBF16) return (c & 1) ? bf16_hi(b.w[c >> 1]) : bf16_lo(b.w[c >> 1]);
-  return __uint_as_float(b.w[c]);
+__device__ __forceinline__ uint32_t piece8_max(const Piece8<DT> &b) {
+  if (DT == kBF16) {
+    ushort2_t h = {0, 0};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, b.w[q] & 0x7FFF7FFFu));
+    return static_cast<uint32_t>(max(h.x, h.y)) << 16;
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < Piece8<DT>::kWords; ++q) m = max(m, b.w[q] & 0x7FFFFFFFu);
+  return m;
 }
 
-__global__ __launch_bounds__(kThreads) void k_colamax_zero(float *amax, uint32_t n, const float *noop) {
+__global__ __launch_bounds__(kThreads) void k_amax_zero2(float *a, uint32_t na, float *b, uint32_t nb,
+                                                       const float *noop) {
   if (noop != nullptr && *noop == 1.0f) return;
   const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) amax[i] = 0.0f;
+  if (a != nullptr && i < na) a[i] = 0.0f;
+  if (b != nullptr && i < nb) b[i] = 0.0f;
 }
 
-// amax[j] = max over rows of |x[i][j]|, after k_colamax_zero: each
+// One batch of the reduction: rows r, r + 4, ..., r + 4 (N - 1) of the
+// lane's 8 columns (KEEP: a lane outside the input reads column 0 and
+// discards it). The column maxima fold into acc; with row_amax, each row's
+// maximum over the wave's 512 columns goes to the row's slot by atomic max:
+// the lanes' row maxima are transposed through LDS (lds_r, the wave's
+// [64][17] words), lane l reduces row l % 16 over lanes 16 (l / 16) ..
+// 16 (l / 16) + 15, two lane exchanges combine the four quarters, and lanes
+// 0 .. N - 1 issue the atomics in one instruction.
+template <int DT, int N, bool KEEP>
+__device__ __forceinline__ void dual_amax_rows(const RowScaledArgs &p, float *row_amax, uint32_t r, uint32_t c0,
+                                               bool lane_ok, ColMax<DT> &acc, uint32_t *lds_r) {
+  Piece8<DT> b[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) b[u] = load_piece8<DT>(p.x, static_cast<uint64_t>(r + kWaves * u) * p.cols + c0);
+  if (KEEP) {
+    const uint32_t keep = lane_ok ? ~0u : 0u;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+#pragma unroll
+      for (int q = 0; q < Piece8<DT>::kWords; ++q) b[u].w[q] &= keep;
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) acc.fold(b[u]);
+  if (row_amax != nullptr) {  // uniform
+    static_assert(N <= 16, "one row per lane of a quarter wave");
+    const uint32_t lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < N; ++u) lds_r[lane * 17 + u] = piece8_max<DT>(b[u]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+    const uint32_t u = lane & 15, q = lane >> 4;
+    uint32_t m = 0;
+    if (u < N) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m = max(m, lds_r[(16 * q + k) * 17 + u]);
+    }
+    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16)));
+    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
+    if (lane < N && m != 0) atomicMax(reinterpret_cast<unsigned int *>(row_amax) + r + kWaves * lane, m);
+    __builtin_amdgcn_wave_barrier();  // the reads above are done before a later batch writes lds_r
+  }
+}
+
+// Per-column maxima (p.amax, when not NULL) and per-row maxima (row_amax,
+// when not NULL) in one read of the input, after k_amax_zero2: each
 // workgroup reduces kColAmaxRows rows of kColAmaxCols columns (wave v takes
 // rows v, v + 4, ...) and folds its maxima in with one atomic max per
-// column (non-negative floats order as their bit patterns).
+// column and per row (non-negative floats order as their bit patterns).
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_colamax(RowScaledArgs p) {
+__global__ __launch_bounds__(kThreads) void k_dual_amax(RowScaledArgs p, float *row_amax) {
   __shared__ uint32_t lds_m[kWaves][kColAmaxCols];
+  __shared__ uint32_t lds_r[kWaves][64 * 17];
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // one-dimensional grid (either extent alone may pass 65535): column strip
   // fastest, so consecutive workgroups read neighbouring parts of a row
   const uint32_t nstrip = (p.cols + kColAmaxCols - 1) / kColAmaxCols;
   const uint32_t chunk = blockIdx.x / nstrip, strip = blockIdx.x - chunk * nstrip;
-  const uint32_t c0 = strip * kColAmaxCols + 8 * lane;
+  const bool full = (strip + 1) * kColAmaxCols <= p.cols;  // uniform
+  // cols % 16 == 0: a lane's 8 columns are all inside or all outside
+  const bool lane_ok = strip * kColAmaxCols + 8 * lane < p.cols;
+  const uint32_t c0 = lane_ok ? strip * kColAmaxCols + 8 * lane : 0u;
   const uint32_t rbeg = chunk * kColAmaxRows;
   const uint32_t rend = min(rbeg + kColAmaxRows, p.rows);
   ColMax<DT> acc;
-  if (c0 < p.cols) {  // cols % 16 == 0: a lane's 8 columns are all inside or all outside
-    constexpr int kUnroll = 16;
-    uint32_t r = rbeg + wave;
-    for (; r + kWaves * (kUnroll - 1) < rend; r += kWaves * kUnroll) {
-      Piece8<DT> b[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) b[u] = load_piece8<DT>(p.x, static_cast<uint64_t>(r + kWaves * u) * p.cols + c0);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) acc.fold(b[u]);
-    }
-    for (; r < rend; r += kWaves) acc.fold(load_piece8<DT>(p.x, static_cast<uint64_t>(r) * p.cols + c0));
+  constexpr int kUnroll = DT == kBF16 ? 16 : 8;  // 256 bytes of loads in flight per lane
+  uint32_t r = rbeg + wave;
+  for (; r + kWaves * (kUnroll - 1) < rend; r += kWaves * kUnroll) {
+    if (full) dual_amax_rows<DT, kUnroll, false>(p, row_amax, r, c0, lane_ok, acc, lds_r[wave]);
+    else dual_amax_rows<DT, kUnroll, true>(p, row_amax, r, c0, lane_ok, acc, lds_r[wave]);
   }
+  for (; r < rend; r += kWaves) dual_amax_rows<DT, 1, true>(p, row_amax, r, c0, lane_ok, acc, lds_r[wave]);
+  if (p.amax == nullptr) return;  // uniform
 #pragma unroll
   for (int c = 0; c < 8; ++c) lds_m[wave][8 * lane + c] = acc.get(c);
   __syncthreads();
@@ -328,92 +376,6 @@ __global__ __launch_bounds__(kThreads) void k_colamax(RowScaledArgs p) {
     for (int w = 1; w < kWaves; ++w) v = max(v, lds_m[w][k]);
     if (j < p.cols && v != 0) atomicMax(reinterpret_cast<unsigned int *>(p.amax) + j, v);
   }
-}
-
-// Column-wise encode with the per-column amax. A unit is 512 rows x 64
-// columns: thread (lane group g = tid / 8, column piece tid % 8) owns 8
-// columns x 16 rows of it, one 1x16 block of each of its 8 columns, and
-// writes each block's 8 data bytes and scale to the transposed arrays
-// ([cols][rows / 2], [cols][rows / 16]). The grid is what stays resident and
-// each workgroup walks units with the next unit's loads issued before the
-// current unit is encoded, so the encode overlaps the reads; a grid of one
-// unit per workgroup would load everything first and encode afterwards.
-template <int DT>
-__device__ __forceinline__ void load_unit(const RowScaledArgs &p, uint32_t unit, uint32_t nstrip, Piece8<DT> (&b)[16],
-                                          uint32_t &c0, uint32_t &r0, bool &ok) {
-  const uint32_t chunk = unit / nstrip, strip = unit - chunk * nstrip;
-  c0 = strip * kColStrip + 8 * (threadIdx.x & 7);
-  r0 = chunk * kColRows + 16 * (threadIdx.x >> 3);
-  ok = c0 < p.cols && r0 < p.rows;  // rows % 16 == 0, cols % 16 == 0: whole blocks
-  // a lane outside the input loads (and later discards) the first 16 rows,
-  // which exist: rows >= 16
-  const uint64_t base = ok ? static_cast<uint64_t>(r0) * p.cols + c0 : 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) b[k] = load_piece8<DT>(p.x, base + static_cast<uint64_t>(k) * p.cols);
-}
-
-template <int DT, bool SR>
-__device__ __forceinline__ void encode_unit(const RowScaledArgs &p, const Piece8<DT> (&b)[16], uint32_t c0,
-                                            uint32_t r0, bool ok) {
-  if (!ok) return;
-  const bool ue = p.ue5m3 != 0;
-  const uint32_t key = SR ? sr_key(p.sr_seed, 1) : 0u;
-  const uint64_t half_rows = p.rows >> 1;
-  ColMax<DT> acc;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) acc.fold(b[k]);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t j = c0 + c;
-    const float S = global_encode_scale(p.amax[j], ue);
-    const BlockScale bs = block_scale(__uint_as_float(acc.get(c)), S, ue);
-    float s[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) s[k] = piece8_value<DT>(b[k], c) * bs.mult;
-    const uint64_t byte0 = j * half_rows + (r0 >> 1);
-    uint32_t lo, hi;
-    if (SR) {
-      uint32_t r[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) r[q] = fmix32(key ^ static_cast<uint32_t>(byte0 + q));
-      lo = e2m1_sr_x8(s, r);
-      hi = e2m1_sr_x8(s + 8, r + 4);
-    } else {
-      lo = e2m1_rne_x8(s);
-      hi = e2m1_rne_x8(s + 8);
-    }
-    // plain stores: a wave writes 64-byte halves of output lines, which the
-    // L2 merges (non-temporal stores of them measured 7% slower)
-    *reinterpret_cast<u32x2 *>(p.data + byte0) = u32x2{lo, hi};
-    p.scales[static_cast<uint64_t>(j) * (p.rows >> 4) + (r0 >> 4)] = static_cast<uint8_t>(bs.code);
-  }
-}
-
-template <int DT, bool SR>
-__global__ __launch_bounds__(kThreads) void k_colscaled(RowScaledArgs p, uint32_t units) {
-  if (p.noop != nullptr && *p.noop == 1.0f) return;
-  const uint32_t nstrip = (p.cols + kColStrip - 1) / kColStrip;  // strip fastest: neighbouring row parts
-  uint32_t u = blockIdx.x;  // < units (the grid is at most one workgroup per unit)
-  Piece8<DT> cur[16];
-  uint32_t c0, r0;
-  bool ok;
-  load_unit<DT>(p, u, nstrip, cur, c0, r0, ok);
-  for (;;) {  // no barrier inside: lanes may leave at different units only through `ok`
-    const uint32_t next = u + gridDim.x;
-    if (next >= units) break;  // uniform
-    Piece8<DT> nxt[16];
-    uint32_t nc0, nr0;
-    bool nok;
-    load_unit<DT>(p, next, nstrip, nxt, nc0, nr0, nok);
-    encode_unit<DT, SR>(p, cur, c0, r0, ok);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) cur[k] = nxt[k];
-    c0 = nc0;
-    r0 = nr0;
-    ok = nok;
-    u = next;
-  }
-  encode_unit<DT, SR>(p, cur, c0, r0, ok);
 }
 
 template <int DT, bool SR, bool COMPUTE>
@@ -435,52 +397,20 @@ hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool com
   return dtype == kBF16 ? launch_dt<kBF16>(a, sr, compute_amax, s) : launch_dt<kFP32>(a, sr, compute_amax, s);
 }
 
-hipError_t launch_colscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s) {
-  if (a.cols == 0) return hipSuccess;
-  if (compute_amax) {
-    hipLaunchKernelGGL(k_colamax_zero, dim3((a.cols + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a.amax, a.cols,
-                       a.noop);
-    if (a.rows > 0) {
-      const dim3 grid(((a.cols + kColAmaxCols - 1) / kColAmaxCols) * ((a.rows + kColAmaxRows - 1) / kColAmaxRows));
-      if (dtype == kBF16)
-        hipLaunchKernelGGL(k_colamax<kBF16>, grid, dim3(kThreads), 0, s, a);
-      else
-        hipLaunchKernelGGL(k_colamax<kFP32>, grid, dim3(kThreads), 0, s, a);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (a.data == nullptr || a.rows == 0) return hipSuccess;
-  const uint32_t units = ((a.cols + kColStrip - 1) / kColStrip) * ((a.rows + kColRows - 1) / kColRows);
-  const void *fn = dtype == kBF16 ? (sr ? reinterpret_cast<const void *>(&k_colscaled<kBF16, true>)
-                                        : reinterpret_cast<const void *>(&k_colscaled<kBF16, false>))
-                                  : (sr ? reinterpret_cast<const void *>(&k_colscaled<kFP32, true>)
-                                        : reinterpret_cast<const void *>(&k_colscaled<kFP32, false>));
-  // resident workgroups: compute units x what one holds (the latter depends
-  // on the kernel's registers only, so it is taken once per kernel)
-  static std::atomic<int> occupancy[2][2];
-  hipDevice_t dev = 0;
-  int cus = 0;
-  hipError_t e = hipStreamGetDevice(s, &dev);  // the device the work runs on
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  int per_cu = occupancy[dtype == kBF16][sr].load(std::memory_order_relaxed);
-  if (per_cu == 0) {
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0)) != hipSuccess) return e;
-    occupancy[dtype == kBF16][sr].store(per_cu, std::memory_order_relaxed);
-  }
-  const uint32_t resident = static_cast<uint32_t>(max(cus, 1)) * static_cast<uint32_t>(min(max(per_cu, 1), kColWgsPerCu));
-  const dim3 grid(min(units, resident));
-  if (dtype == kBF16) {
-    if (sr)
-      hipLaunchKernelGGL((k_colscaled<kBF16, true>), grid, dim3(kThreads), 0, s, a, units);
+hipError_t launch_dual_amax(const void *x, int dtype, uint32_t rows, uint32_t cols, float *row_amax, float *col_amax,
+                            const float *noop, hipStream_t s) {
+  if (row_amax == nullptr && col_amax == nullptr) return hipSuccess;
+  const uint32_t n = max(row_amax ? rows : 0u, col_amax ? cols : 0u);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_amax_zero2, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s, row_amax, rows, col_amax,
+                     cols, noop);
+  if (rows > 0 && cols > 0) {
+    RowScaledArgs a{x, rows, cols, nullptr, nullptr, col_amax, 0u, noop};
+    const dim3 grid(((cols + kColAmaxCols - 1) / kColAmaxCols) * ((rows + kColAmaxRows - 1) / kColAmaxRows));
+    if (dtype == kBF16)
+      hipLaunchKernelGGL(k_dual_amax<kBF16>, grid, dim3(kThreads), 0, s, a, row_amax);
     else
-      hipLaunchKernelGGL((k_colscaled<kBF16, false>), grid, dim3(kThreads), 0, s, a, units);
-  } else {
-    if (sr)
-      hipLaunchKernelGGL((k_colscaled<kFP32, true>), grid, dim3(kThreads), 0, s, a, units);
-    else
-      hipLaunchKernelGGL((k_colscaled<kFP32, false>), grid, dim3(kThreads), 0, s, a, units);
+      hipLaunchKernelGGL(k_dual_amax<kFP32>, grid, dim3(kThreads), 0, s, a, row_amax);
   }
   return hipGetLastError();
 }
