@@ -177,8 +177,9 @@ typedef struct {
   /* Device pointer or NULL. When *noop == 1.0f the call writes nothing, amax
    * buffers included ("Write both NVFP4 amax buffers", Changes). */
   const float *noop;
-  /* nvfp4_quantize with compute_amax == 1 and a per-tensor amax only (not
-   * row_scaled): NULL, or device memory of at least NVFP4_WORKSPACE_BYTES
+  /* nvfp4_quantize (and nvfp4_quantize_grouped) with compute_amax == 1 and
+   * a per-tensor (per-group) amax only (not row_scaled): NULL, or device
+   * memory of at least NVFP4_WORKSPACE_BYTES
    * bytes, 16-byte aligned, owned by the caller, zero-filled before its
    * first use. With a workspace the call takes one of two forms:
    *   single pass (one launch; not with the RHT; see amax_path): each
@@ -192,8 +193,9 @@ typedef struct {
    * With NULL the amax buffers are zeroed and reduced with atomics (three
    * launches). The first 16 KiB of the workspace are scratch (contents on
    * entry do not matter). The rest holds the single-pass handoff: one
-   * tagged slot per workgroup, an epoch and exit counters, which every call
-   * leaves ready for the next; it must be zero on first use and must not be
+   * tagged slot per workgroup, one per group of a grouped call, an epoch
+   * and exit counters, which every call leaves ready for the next; it must
+   * be zero on first use and must not be
    * written by anything else. A workspace that breaks this is detected
    * (barring a chance of about one in 2^32) and every call on it then takes
    * a slow fallback that still gives the same bytes. Calls that share a
@@ -207,14 +209,14 @@ typedef struct {
    * the kernel can be timed inside a whole call. Not recorded when the call
    * is rejected or the input is empty. */
   void *const *cast_events;
-  /* nvfp4_amax_path_t; nvfp4_quantize with a workspace, compute_amax == 1,
-   * a per-tensor amax and no RHT (ignored otherwise). Every path gives the
-   * same bytes. */
+  /* nvfp4_amax_path_t; nvfp4_quantize or nvfp4_quantize_grouped with a
+   * workspace, compute_amax == 1, a per-tensor (per-group) amax and no RHT
+   * (ignored otherwise). Every path gives the same bytes. */
   uint32_t amax_path;
 } nvfp4_config_t;
 
 /* Bytes of the optional quantize workspace (nvfp4_config_t.workspace). */
-#define NVFP4_WORKSPACE_BYTES 36864u
+#define NVFP4_WORKSPACE_BYTES 98304u
 
 /* NVFP4_WORKSPACE_BYTES, for bindings that cannot read the macro. */
 uint64_t nvfp4_workspace_bytes(void);
@@ -319,12 +321,17 @@ nvfp4_status_t nvfp4_quantize_noalloc(const void *x, nvfp4_dtype_t dtype, int64_
  * storage sizes it as the sum of the groups' rows), and nearest-even
  * results equal a single nvfp4_quantize over all rows; stochastic rounding
  * counts its byte indices within each group. Otherwise a computed amax
- * takes two launches (amax pass, cast)
- * with a workspace, each group's workgroup maxima in a range of it that the
- * group's cast tiles reduce (the slots of empty groups are written +0);
- * without one it is zeroed and reduced by atomic max (three launches). The
- * same workspace rule holds as for nvfp4_quantize: one call at a time per
- * workspace, in stream order.
+ * with a workspace takes one launch when no group has more than 512
+ * 128x128 tiles, there is no RHT and amax_path is not
+ * NVFP4_AMAX_PATH_TWO_PASS: each group's tiles load into registers, hand
+ * their maxima to a head workgroup of the group through the workspace and
+ * encode once it has published the group's amax (the input is read once).
+ * Else it takes two launches (amax pass, cast), each group's workgroup
+ * maxima in a range of the workspace that the group's cast tiles reduce
+ * (the slots of empty groups are written +0); without a workspace the amax
+ * is zeroed and reduced by atomic max (three launches). The same workspace
+ * rule holds as for nvfp4_quantize: one call at a time per workspace, in
+ * stream order.
  */
 nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dtype, int64_t num_groups,
                                       const int64_t *group_rows, int64_t cols, const nvfp4_out_t *row,

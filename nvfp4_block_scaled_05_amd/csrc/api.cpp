@@ -453,6 +453,26 @@ extern "C" nvfp4_status_t nvfp4_quantize_grouped(const void *x, nvfp4_dtype_t dt
   }
   float *ra = row ? row->amax : nullptr;
   float *ca = col ? col->amax : nullptr;
+  if (cfg.amax_path > NVFP4_AMAX_PATH_SINGLE_PASS)
+    return fail(NVFP4_ERR_UNSUPPORTED, "unknown amax path %u", cfg.amax_path);
+  // With a workspace (no RHT) and groups of at most kMaxFusedGroupTiles
+  // tiles, one launch: each group's tiles hand their maxima to the group's
+  // head workgroup and encode from registers (the input is read once).
+  uint64_t most_tiles = 0;
+  for (uint32_t g = 0; g < G; ++g) {
+    const uint64_t n = (uint64_t{row_start[g + 1] - row_start[g]} + 127) / 128 * ((uint64_t{C} + 127) / 128);
+    most_tiles = n > most_tiles ? n : most_tiles;
+  }
+  if (cfg.compute_amax && cfg.workspace != nullptr && !cfg.rht && !empty && cfg.amax_path != NVFP4_AMAX_PATH_TWO_PASS &&
+      most_tiles <= nvfp4::kMaxFusedGroupTiles) {
+    nvfp4::CastArgs a{x, static_cast<uint32_t>(rows), C, row ? row->data : nullptr, row ? row->scales : nullptr, ra,
+                      col ? col->data : nullptr, col ? col->scales : nullptr, ca, swz ? 1u : 0u, cfg.sr_seed,
+                      rht_word(cfg), cfg.noop, nullptr, 0};
+    a.ue5m3 = cfg.scale_fmt == NVFP4_SCALE_UE5M3;
+    return hip_status(nvfp4::launch_grouped_fused(a, row_start, G, dtype, cfg.block_2d != 0, sr,
+                                                  static_cast<uint32_t *>(cfg.workspace), s),
+                      "grouped one-launch quantize");
+  }
   // With a workspace each group's amax workgroups leave their maxima in a
   // range of it (part_start) that the group's cast tiles reduce; without
   // one, the slots are zeroed and reduced by atomic max.

@@ -1089,12 +1089,18 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
 constexpr uint32_t kDefaultFastTicks = 5000;   // 50 us of the 100 MHz counter
 constexpr uint32_t kClaimSpan = 512;           // slots each workgroup of the slow path scans for claims
 constexpr uint32_t kLastResortTicks = 2000000;  // 20 ms
-// A call tags its slots epoch + 1, so tags run 1 .. 2^32 - 1 and never 0.
-constexpr uint32_t kLastEpoch = 0xFFFFFFFFu;
+// Tags run 1 .. 2^32 - 1, never 0. A call tags with e + 1 .. e + adv (adv:
+// 1, or the grouped kernel's laps over the slots, at most kMaxLaps) and
+// leaves the epoch at e + adv; once that passes kEpochLimit, every tagged
+// word is cleared and the epoch restarts at 0, so the next call's tags stay
+// below 2^32 and no word left 2^32 calls earlier can pass for its own.
+constexpr uint32_t kMaxLaps = 256;  // above (2^32 / (128 x 128)) / kMaxPartials = 128
+constexpr uint32_t kEpochLimit = 0xFFFFFFFFu - kMaxLaps;
 static_assert(kMaxPartials / kSlotGroup < 63, "lane 63 of the group-slot poll reads the done word");
 
-__device__ __forceinline__ uint32_t group_members(uint32_t G, uint32_t x) {
-  return (G - x + kBarGroups - 1) / kBarGroups;
+// workgroups of a grid of G whose exits count on line x
+__device__ __forceinline__ uint32_t line_members(uint32_t G, uint32_t x) {
+  return (G - x + kExitLines - 1) / kExitLines;
 }
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
@@ -1382,6 +1388,45 @@ __device__ bool wait_done(const uint32_t *ws, uint32_t t, uint32_t ticks, uint32
   }
 }
 
+// The end of a call that follows the workspace's epoch protocol (thread 0
+// of every workgroup): exit counters per line x = blockIdx.x mod kExitLines,
+// then over the lines; the last workgroup of the grid advances the epoch
+// by adv (and only it returns true). e, xb, xbt: the epoch and exit bases
+// read at the start.
+__device__ __forceinline__ bool epoch_exit(uint32_t *ws, uint32_t e, uint32_t adv, uint32_t xb, uint32_t xbt,
+                                           uint32_t G, uint32_t x, uint32_t nx) {
+  uint32_t *line = ws + kExitWord + 2 * kBarLine * x;
+  const uint32_t old = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old - xb != line_members(G, x) - 1) return false;
+  st_agent(line + kBarLine, old + 1);
+  const uint32_t top = __hip_atomic_fetch_add(ws + kExitTopWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (top - xbt != nx - 1) return false;
+  st_agent(ws + kExitTopBaseWord, top + 1);
+  if (e + adv <= kEpochLimit) {
+    st_agent(ws + kEpochWord, e + adv);
+  } else {
+    // about 4600 stores, once per 2^32 calls
+    for (uint32_t i = kSlotWord; i < kEpochWord; ++i) st_agent(ws + i, 0u);
+    st_agent64(ws + kDoneWord, 0u);
+    st_agent64(ws + kReducerWord, 0u);
+    for (uint32_t g = 0; g < kMaxGroups; ++g) st_agent64(ws + kGroupDoneWord + kBarLine * g, 0u);
+    st_agent(ws + kEpochWord, 0u);
+  }
+  return true;
+}
+
+// The start of such a call (thread 0): the exit bases of the workgroup's
+// line and over the lines, and whether the counters are in a state that
+// some call left (else the workspace was not zero-filled, and only maxima
+// computed by the workgroup itself are trusted).
+__device__ __forceinline__ void epoch_bases(const uint32_t *ws, uint32_t G, uint32_t x, uint32_t nx, uint32_t &xb,
+                                            uint32_t &xbt, bool &sane) {
+  const uint32_t *line = ws + kExitWord + 2 * kBarLine * x;
+  xb = ld_agent(line + kBarLine);
+  xbt = ld_agent(ws + kExitTopBaseWord);
+  sane = ld_agent(line) - xb < line_members(G, x) && ld_agent(ws + kExitTopWord) - xbt < nx;
+}
+
 // The thread's 8 row pieces of BF16 tile (r0, c0) loaded straight into LDS
 // (no registers): piece k of thread t lands at tl[k][t], since one load of a
 // wave writes its 64 lanes' 16 bytes in lane order from a wave-uniform base.
@@ -1417,8 +1462,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   const uint32_t G = gridDim.x, wg = blockIdx.x;
   const uint32_t tx_n = (p.cols + kRT - 1) / kRT, ty_n = (p.rows + kRT - 1) / kRT;
   const uint32_t T = tx_n * ty_n;
-  const uint32_t xg = wg % kBarGroups;
-  const uint32_t nxg = min(G, kBarGroups);
+  const uint32_t xg = wg % kExitLines;
+  const uint32_t nxg = min(G, kExitLines);
 
   // this call's epoch, and the started mark: by the second wave, before
   // its tile loads, so that the grid's running workgroups are marked
@@ -1466,10 +1511,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   // workspace that was not zero-filled: then only the whole-input maximum
   // is trusted
   if (tid == 0) {
-    const uint32_t xb = ld_agent(ws + kExitBaseWord + xg * kBarLine);
-    const uint32_t xbt = ld_agent(ws + kExitTopBaseWord);
-    const bool sane = ld_agent(ws + kExitWord + xg * kBarLine) - xb < group_members(G, xg) &&
-                      ld_agent(ws + kExitTopWord) - xbt < nxg;
+    uint32_t xb, xbt;
+    bool sane;
+    epoch_bases(ws, G, xg, nxg, xb, xbt, sane);
     lds_start[1] = xb;
     lds_start[2] = xbt;
     lds_start[3] = sane ? 1u : 0u;
@@ -1628,31 +1672,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
   }
 
   // ---- exit: the last workgroup of the grid advances the epoch ----
-  if (tid == 0) {
-    const uint32_t e = lds_start[0], xb = lds_start[1], xbt = lds_start[2];
-    const uint32_t old = __hip_atomic_fetch_add(ws + kExitWord + xg * kBarLine, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old - xb == group_members(G, xg) - 1) {
-      st_agent(ws + kExitBaseWord + xg * kBarLine, old + 1);
-      const uint32_t top = __hip_atomic_fetch_add(ws + kExitTopWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (top - xbt == nxg - 1) {
-        st_agent(ws + kExitTopBaseWord, top + 1);
-        if (e + 1 != kLastEpoch) {
-          st_agent(ws + kEpochWord, e + 1);
-        } else {
-          // the next tag would be 0 and tags would start to repeat: clear
-          // every slot, the done and reducer words (no call tags with 0) and start
-          // again at epoch 0, so that a word left by a call 2^32 calls ago
-          // cannot pass for the next call's (about 4000 stores, once per
-          // 2^32 calls)
-          for (uint32_t i = kSlotWord; i < kEpochWord; ++i) st_agent(ws + i, 0u);
-          st_agent64(ws + kDoneWord, 0u);
-          st_agent64(ws + kReducerWord, 0u);
-          st_agent(ws + kEpochWord, 0u);
-        }
-      }
-    }
-  }
+  if (tid == 0) epoch_exit(ws, lds_start[0], 1, lds_start[1], lds_start[2], G, xg, nxg);
 }
 
 // The arguments of group g's own tensor: its rows of the input, its blocks
@@ -1705,6 +1725,227 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht_grouped(CastArgs p, Group
   uint32_t tx, ty;
   tile_xy(p, local, tiles_x, (q.rows + kRT - 1) / kRT, tx, ty);
   cast_rht_tile<DT, SR, MFMA>(q, tx, ty);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped quantize with a per-group amax in one launch. A group's cast needs
+// that group's amax only, and a group's work is a run of consecutive
+// workgroups, which start together: first the group's head, then one
+// workgroup per tile. Each tile loads into registers and stores its
+// maximum to its slot (workgroup i: slot i mod kMaxPartials, tagged with the
+// call's first tag + i / kMaxPartials, its lap over the slots). The head
+// gathers the group's slots, stores the group's maximum to the group's done
+// slot and writes the amax; the tiles wait for that slot and encode from
+// registers. The input is read once, and no two workgroups update one word
+// (atomics on one line are serialized) other than the exit counters, which
+// are spread over kExitLines lines. The head holds no tile, so gathering up
+// to kMaxFusedGroupTiles slots at once costs the tiles no registers.
+//
+// Waits. The head started before its group's tiles (workgroups start in
+// index order) and waits for nothing but their slots, at most lead_ticks; a
+// slot still missing then, or overwritten by a workgroup of a later lap, it
+// replaces by reading that tile's maximum from the input. So the head
+// always publishes, and the tiles wait for it at most wait_ticks (then take
+// the group's maximum from the input). With every group at most
+// kMaxFusedGroupTiles tiles, a group fits on the GPU beside the groups
+// before it that are still finishing. The epoch advances only when every
+// workgroup has exited (the single-pass protocol), so no workgroup of a
+// call can take the next call's tags.
+// ---------------------------------------------------------------------------
+
+// no maximum (a maximum is below 2^31)
+constexpr uint32_t kNoMax = 0xFFFFFFFFu;
+
+// max |x| bit pattern of the thread's share of tile (r0, c0), one 16-byte
+// load at a time (few registers: the caller holds its own tile's)
+template <int DT>
+__device__ uint32_t tile_max_lean(const CastArgs &p, uint32_t r0, uint32_t c0) {
+  constexpr uint32_t E = RT<DT>::kElem;
+  const u32x4 *x = static_cast<const u32x4 *>(p.x);
+  const uint32_t vpr = p.cols * E / 16;                       // 16-byte vectors per row
+  const uint32_t v0 = c0 * E / 16, nv = min(kRT * E / 16, vpr - v0);  // the tile's, per row
+  const uint32_t n = min(kRT, p.rows - r0) * nv;
+  uint32_t m = 0;
+#pragma unroll 1
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
+    const uint32_t r = i / nv;
+    const u32x4 v = x[static_cast<uint64_t>(r0 + r) * vpr + v0 + (i - r * nv)];
+    if (DT == kBF16) {
+      ushort2_t h = __builtin_bit_cast(ushort2_t, v.x & 0x7FFF7FFFu);
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.y & 0x7FFF7FFFu));
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.z & 0x7FFF7FFFu));
+      h = __builtin_elementwise_max(h, __builtin_bit_cast(ushort2_t, v.w & 0x7FFF7FFFu));
+      m = max(m, static_cast<uint32_t>(max(h.x, h.y)) << 16);
+    } else {
+      m = max(m, max(max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+  }
+  return m;
+}
+
+// The head of group g: the group's maximum from the slots of its tiles,
+// workgroups first + 1 .. first + ntiles (or, for slots missing after
+// lead_ticks or taken by a later lap, from the tiles themselves).
+template <int DT>
+__device__ uint32_t gather_group(const CastArgs &q, const uint32_t *ws, uint32_t b, uint32_t laps, bool sane,
+                                 uint32_t first, uint32_t ntiles, uint32_t lead_ticks, uint32_t *lds_direct,
+                                 uint32_t &lds_ndirect, uint32_t &lds_m, uint32_t *red) {
+  constexpr uint32_t kPolls = kMaxFusedGroupTiles / 64;  // slots per lane
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    // lane l: the tiles l + 64 k (workgroups first + 1 + l + 64 k)
+    uint32_t pending = 0, direct = 0, m = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPolls; ++k)
+      if (tid + 64 * k < ntiles) (sane ? pending : direct) |= 1u << k;  // no tag can be trusted: read every tile
+    const uint64_t t0 = wall_clock64();
+    while (__any(pending != 0)) {
+      uint64_t v[kPolls];
+#pragma unroll
+      for (uint32_t k = 0; k < kPolls; ++k) {
+        const uint32_t i = first + 1 + tid + 64 * k;
+        v[k] = (pending >> k & 1u) ? ld_agent64(ws + kSlotWord + 2 * (i % kMaxPartials)) : 0;
+      }
+#pragma unroll
+      for (uint32_t k = 0; k < kPolls; ++k) {
+        if (!(pending >> k & 1u)) continue;
+        const uint32_t i = first + 1 + tid + 64 * k;
+        const uint32_t want = b + i / kMaxPartials, tag = static_cast<uint32_t>(v[k] >> 32);
+        if (tag == want && static_cast<uint32_t>(v[k]) < 0x80000000u) {
+          m = max(m, static_cast<uint32_t>(v[k]));
+          pending &= ~(1u << k);
+        } else if (tag > want && tag < b + laps) {  // a later lap's workgroup took the slot
+          pending &= ~(1u << k);
+          direct |= 1u << k;
+        }
+      }
+      if (__any(pending != 0)) {
+        if (wall_clock64() - t0 > lead_ticks) {
+          direct |= pending;
+          pending = 0;
+        } else {
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kPolls; ++k) {
+      if (direct >> k & 1u) lds_direct[atomicAdd(&lds_ndirect, 1u)] = tid + 64 * k;
+    }
+    m = wave_max(m);
+    if (tid == 0) lds_m = m;
+  }
+  lds_barrier();
+  uint32_t a[1] = {lds_m};
+  const uint32_t nd = lds_ndirect;
+  if (nd != 0) {  // uniform: the missing tiles' maxima from the input
+    const uint32_t tiles_x = (q.cols + kRT - 1) / kRT, tiles_y = (q.rows + kRT - 1) / kRT;
+    uint32_t dm = 0;
+    for (uint32_t d = 0; d < nd; ++d) {
+      uint32_t dx, dy;
+      tile_xy(q, tile_index(q, lds_direct[d], ntiles), tiles_x, tiles_y, dx, dy);
+      dm = max(dm, tile_max_lean<DT>(q, dy * kRT, dx * kRT));
+    }
+    uint32_t r[1] = {dm};
+    workgroup_max(r, red);
+    a[0] = max(a[0], r[0]);
+  }
+  return a[0];
+}
+
+template <int DT, bool B2D, bool SR>
+__global__ __launch_bounds__(kThreads) void k_grouped_fused(CastArgs p, GroupTable t, uint32_t *ws,
+                                                            uint32_t lead_ticks, uint32_t wait_ticks) {
+  constexpr int W = RT<DT>::kWords;
+  __shared__ RtLds sh;
+  __shared__ uint32_t lds_start[4];  // epoch, exit base of the line, exit base over the lines, sane
+  __shared__ uint32_t lds_amax, lds_ndirect;
+  __shared__ uint32_t lds_direct[kMaxFusedGroupTiles];  // tiles whose maxima the head reads itself
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+  const int tid = threadIdx.x;
+  const uint32_t G = gridDim.x, wg = blockIdx.x;
+  const uint32_t x = wg % kExitLines, nx = min(G, kExitLines);
+  const uint32_t laps = (G + kMaxPartials - 1) / kMaxPartials;
+  if (tid == 0) {
+    uint32_t xb, xbt;
+    bool sane;
+    lds_start[0] = ld_agent(ws + kEpochWord);
+    epoch_bases(ws, G, x, nx, xb, xbt, sane);
+    lds_start[1] = xb;
+    lds_start[2] = xbt;
+    lds_start[3] = sane ? 1u : 0u;
+    lds_ndirect = 0;
+  }
+  if (wg == 0) {  // empty groups: amax 0 and nothing else
+    for (uint32_t g = tid; g < t.ngroups; g += kThreads) {
+      if (t.row_start[g + 1] == t.row_start[g]) {
+        if (p.row_amax) p.row_amax[g] = 0.0f;
+        if (p.col_amax) p.col_amax[g] = 0.0f;
+      }
+    }
+  }
+  const uint32_t g = group_of(t, wg);
+  const uint32_t first = t.unit_start[g];  // the group's head
+  const uint32_t ntiles = t.unit_start[g + 1] - first - 1;
+  const CastArgs q = group_args<DT>(p, t, g);
+  uint32_t *done = ws + kGroupDoneWord + kBarLine * g;
+
+  if (wg == first) {  // the head (uniform)
+    lds_barrier();    // lds_start
+    const uint32_t m = gather_group<DT>(q, ws, lds_start[0] + 1, laps, lds_start[3] != 0, first, ntiles, lead_ticks,
+                                        lds_direct, lds_ndirect, lds_amax, sh.red);
+    if (tid == 0) {
+      st_agent64(done, static_cast<uint64_t>(lds_start[0] + 1) << 32 | m);
+      if (q.row_amax) *q.row_amax = __uint_as_float(m);
+      if (q.col_amax) *q.col_amax = __uint_as_float(m);
+      epoch_exit(ws, lds_start[0], laps, lds_start[1], lds_start[2], G, x, nx);
+    }
+    return;
+  }
+
+  // a tile: inside a group tile_index gives each XCD a contiguous run of its
+  // tiles (workgroup i runs on XCD i % 8, and local indices keep that map
+  // one to one), so that neighbouring tiles' scale pieces merge in one L2
+  const uint32_t tiles_x = (p.cols + kRT - 1) / kRT, tiles_y = (q.rows + kRT - 1) / kRT;
+  uint32_t tx, ty;
+  tile_xy(p, tile_index(p, wg - first - 1, ntiles), tiles_x, tiles_y, tx, ty);
+  uint32_t w[8][W];
+  rt_load<DT>(q, ty * kRT, tx * kRT, w);
+  uint32_t a[1] = {0};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[0] = max(a[0], piece_max<DT>(w[k]));
+  workgroup_max(a, sh.red);  // its barrier also publishes lds_start
+  const uint32_t b = lds_start[0] + 1;  // the call's first tag
+  if (tid == 0) {
+    st_agent64(ws + kSlotWord + 2 * (wg % kMaxPartials), static_cast<uint64_t>(b + wg / kMaxPartials) << 32 | a[0]);
+    uint32_t am = kNoMax;
+    if (lds_start[3] != 0) {
+      const uint64_t t0 = wall_clock64();
+      for (;;) {
+        const uint64_t v = ld_agent64(done);
+        if (static_cast<uint32_t>(v >> 32) == b && static_cast<uint32_t>(v) < 0x80000000u) {
+          am = static_cast<uint32_t>(v);
+          break;
+        }
+        if (wall_clock64() - t0 > wait_ticks) break;
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    lds_amax = am;
+  }
+  lds_barrier();
+  a[0] = lds_amax;
+  if (a[0] == kNoMax) {  // uniform: the group's maximum from its input
+    a[0] = input_max<DT>(q);
+    workgroup_max(a, sh.red);
+  }
+  const float amax = __uint_as_float(a[0]);
+  const bool ue = q.ue5m3 != 0;
+  const float S_row = q.row_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
+  const float S_col = q.col_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
+  fill_multipliers(sh.mult, tid, S_row, S_col, ue);
+  rt_encode<DT, B2D, SR>(q, tx, ty, w, S_row, S_col, ue, sh);
+  if (tid == 0) epoch_exit(ws, lds_start[0], laps, lds_start[1], lds_start[2], G, x, nx);
 }
 
 template <int DT, bool B2D, bool SR>
@@ -1879,7 +2120,7 @@ uint32_t device_cus(int dev) {
   return cus > 0 ? static_cast<uint32_t>(cus) : 0u;
 }
 
-uint32_t round8(uint32_t g) { return (g + kBarGroups - 1) / kBarGroups * kBarGroups; }
+uint32_t round8(uint32_t g) { return (g + kGridGrain - 1) / kGridGrain * kGridGrain; }
 
 template <int DT, bool B2D, bool SR>
 hipError_t launch_resident_v(const CastArgs &a, uint32_t *ws, uint32_t G, int v, uint32_t ticks, hipStream_t s) {
@@ -1936,7 +2177,7 @@ ResidentPlan resident_plan(int dtype, bool block_2d, bool sr, uint32_t rows, uin
   for (int v : kOrder) {
     const int slots = v == kLdsVariant ? 4 : v;
     if (v > 1 && dtype != kBF16) break;
-    const uint32_t cap = resident_capacity(dev, dtype, block_2d, sr, v) / kBarGroups * kBarGroups;
+    const uint32_t cap = resident_capacity(dev, dtype, block_2d, sr, v) / kGridGrain * kGridGrain;
     const uint32_t G = std::min(cap, round8(tiles));
     if (G > 0 && G <= kMaxPartials && static_cast<uint64_t>(G) * slots >= tiles) return ResidentPlan{v, G};
   }
@@ -1959,6 +2200,36 @@ hipError_t launch_cast_resident(const CastArgs &a, uint32_t *ws, int dtype, bool
                           : launch_resident_v<kFP32, true, false>(a, ws, G, v, ticks, s);
   return sr ? launch_resident_v<kFP32, false, true>(a, ws, G, v, ticks, s)
             : launch_resident_v<kFP32, false, false>(a, ws, G, v, ticks, s);
+}
+
+hipError_t launch_grouped_fused(const CastArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
+                                bool block_2d, bool sr, uint32_t *ws, hipStream_t s) {
+  GroupTable t{};
+  t.ngroups = ngroups;
+  const uint32_t tiles_x = (a.cols + kRT - 1) / kRT;
+  t.unit_start[0] = 0;
+  for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
+  for (uint32_t g = 0; g < ngroups; ++g) {  // a head and the tiles of each non-empty group
+    const uint32_t n = (row_start[g + 1] - row_start[g] + kRT - 1) / kRT * tiles_x;
+    t.unit_start[g + 1] = t.unit_start[g] + (n != 0 ? 1 + n : 0);
+  }
+  if (t.unit_start[ngroups] == 0) return hipSuccess;
+  // The head waits at most the fast bound for its group's slots (then
+  // reads the missing tiles itself); the tiles wait for the head, which
+  // always publishes, at most the last-resort time. The test hook sets both.
+  const uint32_t tw = g_wait_ticks.load(std::memory_order_relaxed);
+  const uint32_t lead = tw != 0 ? tw : kDefaultFastTicks, wait = tw != 0 ? tw : kLastResortTicks;
+  const dim3 grid(t.unit_start[ngroups]), block(kThreads);
+#define NVFP4_FUSED(D, B, R) hipLaunchKernelGGL((k_grouped_fused<D, B, R>), grid, block, 0, s, a, t, ws, lead, wait)
+  if (dtype == kBF16) {
+    if (block_2d) { if (sr) NVFP4_FUSED(kBF16, true, true); else NVFP4_FUSED(kBF16, true, false); }
+    else { if (sr) NVFP4_FUSED(kBF16, false, true); else NVFP4_FUSED(kBF16, false, false); }
+  } else {
+    if (block_2d) { if (sr) NVFP4_FUSED(kFP32, true, true); else NVFP4_FUSED(kFP32, true, false); }
+    else { if (sr) NVFP4_FUSED(kFP32, false, true); else NVFP4_FUSED(kFP32, false, false); }
+  }
+#undef NVFP4_FUSED
+  return hipGetLastError();
 }
 
 void set_resident_wait_ticks(uint32_t ticks) { g_wait_ticks.store(ticks, std::memory_order_relaxed); }

@@ -22,46 +22,56 @@ constexpr uint32_t kMaxPartials = 2048;
 constexpr uint32_t kRhtBf16 = 1u << 16;
 constexpr uint32_t kPartialsGrain = 4;
 
-// Grid-wide handoff of the single-pass cast, in the workspace after the two
-// partials arrays (word offsets):
+// Grid-wide handoff of the single-pass kernels, in the workspace after the
+// two partials arrays (word offsets; a line is 128 bytes):
 //   kSlotWord       one 64-bit slot per workgroup (at most kMaxPartials):
 //                   tag << 32 | the maximum of the workgroup's tiles, or
 //                   tag << 32 | kSlotStarted (the workgroup runs and will
 //                   store its maximum) or kSlotClaimed (another workgroup
-//                   took over the maximum of those tiles);
+//                   took over the maximum of those tiles). The grouped
+//                   kernel's workgroup i uses slot i mod kMaxPartials, tagged
+//                   with the call's first tag + i / kMaxPartials;
 //   kGroupSlotWord  one 64-bit slot per group of kSlotGroup workgroups, with
 //                   the group's maximum, written by its first workgroup;
-//   kEpochWord      the epoch e: a call tags its slots e + 1;
-//   kExitWord, kExitBaseWord, kExitTopWord, kExitTopBaseWord
-//                   exit counters (per group of workgroups blockIdx.x mod
-//                   kBarGroups, then over the groups) and their values when
-//                   the call began; the last workgroup to exit advances the
-//                   epoch. Each counter sits in a 128-byte line of its own;
+//   kEpochWord      the epoch e: a call tags its slots e + 1 (the grouped
+//                   kernel e + 1 .. e + its laps over the slots) and its last
+//                   workgroup to exit advances e past them;
 //   kDoneWord       tag << 32 | the grid's maximum, stored by the reducer
 //                   of the slow path;
 //   kReducerWord    tag << 32 | the workgroup elected to reduce every slot
-//                   in the slow path.
+//                   in the slow path;
+//   kExitTopWord, kExitTopBaseWord
+//                   the exit counter over the kExitLines lines below and its
+//                   value when the call began;
+//   kExitWord       per line x (workgroups blockIdx.x mod kExitLines): the
+//                   exit counter at kExitWord + 2 kBarLine x and its value
+//                   when the call began one line later. Exits spread over
+//                   many lines: atomics on one line are serialized;
+//   kGroupDoneWord  per group g of the grouped kernel, one line each:
+//                   tag << 32 | the group's maximum, stored by its leader.
 // All of it must be zero before a workspace is first used; every call
 // leaves the counters equal to their bases, ready for the next call.
-constexpr uint32_t kBarGroups = 8;
 constexpr uint32_t kBarLine = 32;  // words per line
+constexpr uint32_t kExitLines = 64;
 constexpr uint32_t kSlotGroup = 64;
 constexpr uint32_t kSlotWord = 2 * kMaxPartials;
 constexpr uint32_t kGroupSlotWord = kSlotWord + 2 * kMaxPartials;
 constexpr uint32_t kEpochWord = kGroupSlotWord + 2 * (kMaxPartials / kSlotGroup);
-constexpr uint32_t kExitWord = kEpochWord + kBarLine;
-constexpr uint32_t kExitBaseWord = kExitWord + kBarGroups * kBarLine;
-constexpr uint32_t kExitTopWord = kExitBaseWord + kBarGroups * kBarLine;
-constexpr uint32_t kExitTopBaseWord = kExitTopWord + kBarLine;
-constexpr uint32_t kDoneWord = kExitTopBaseWord + kBarLine;
+constexpr uint32_t kDoneWord = kEpochWord + kBarLine;
 constexpr uint32_t kReducerWord = kDoneWord + kBarLine;
-constexpr uint32_t kWorkspaceWords = 9216;
-static_assert(kReducerWord + 2 <= kWorkspaceWords, "handoff words fit the workspace");
+constexpr uint32_t kExitTopWord = kReducerWord + kBarLine;
+constexpr uint32_t kExitTopBaseWord = kExitTopWord + kBarLine;
+constexpr uint32_t kExitWord = kExitTopBaseWord + kBarLine;
+constexpr uint32_t kGroupDoneWord = kExitWord + 2 * kBarLine * kExitLines;
+constexpr uint32_t kWorkspaceWords = 24576;
+static_assert(kGroupDoneWord + kBarLine * kMaxGroups <= kWorkspaceWords, "handoff words fit the workspace");
 // Low words of a slot that carry no maximum (a maximum is a non-negative
 // float's bit pattern, below 2^31).
 constexpr uint32_t kSlotStarted = 0xFFFFFFFEu;
 constexpr uint32_t kSlotClaimed = 0xFFFFFFFFu;
-static_assert(kWorkspaceWords * 4 == 36864, "workspace size is part of the ABI");
+static_assert(kWorkspaceWords * 4 == 98304, "workspace size is part of the ABI");
+// Grids of the single-pass kernel are a multiple of the 8 XCDs.
+constexpr uint32_t kGridGrain = 8;
 
 // Arguments of the fused cast(-transpose) kernels. A direction whose data
 // pointer is NULL is not written.
@@ -159,6 +169,14 @@ hipError_t launch_rht_amax_grouped(const void *x, int dtype, uint32_t cols, cons
                                    uint32_t *partials, uint32_t *part_start, const float *noop, hipStream_t s);
 hipError_t launch_cast_grouped(const CastArgs &a, const uint32_t *row_start, const uint32_t *part_start,
                                uint32_t ngroups, int dtype, bool block_2d, bool rht, bool sr, hipStream_t s);
+// Grouped quantize with a per-group amax in one launch: each group's tiles
+// hand their maxima over through the workspace (a slot per workgroup, a
+// done slot per group) and encode from registers. Every group has at most
+// kMaxFusedGroupTiles 128x128 tiles; a.partials is unused; the amax buffers
+// are written.
+constexpr uint32_t kMaxFusedGroupTiles = 512;
+hipError_t launch_grouped_fused(const CastArgs &a, const uint32_t *row_start, uint32_t ngroups, int dtype,
+                                bool block_2d, bool sr, uint32_t *ws, hipStream_t s);
 // compute_amax: reduce each row's amax in the kernel (else read a.amax).
 hipError_t launch_rowscaled(const RowScaledArgs &a, int dtype, bool sr, bool compute_amax, hipStream_t s);
 // Per-row ([rows]) and per-column ([cols]) amax of the input, either may be

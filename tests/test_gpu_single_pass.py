@@ -9,11 +9,11 @@ path: it claims the tiles of workgroups that have not started and reduces
 every slot itself), grids forced beyond what can be resident at once (the
 slow path must complete them), and noop.
 
-The workspace's exit counters and their bases (words 8288 + 32 x and
-8544 + 32 x, x = 0..7; 8800 and 8832 over the groups) must be equal after
+The workspace's exit counters and their bases (words 8416 + 64 x and
+8448 + 64 x, x = 0..63; 8352 and 8384 over the lines) must be equal after
 every call, and the epoch (word 8256) must have advanced by one per
 single-pass call: that is what lets the next call start without a reset.
-The done word (64 bits at word 8864: tag << 32 | amax bits) carries the
+The done word (64 bits at word 8288: tag << 32 | amax bits) carries the
 call's tag exactly when a workgroup took the slow path."""
 
 from __future__ import annotations
@@ -31,13 +31,14 @@ pytestmark = pytest.mark.gpu
 
 SINGLE, TWO = nv.NVFP4_AMAX_PATH_SINGLE_PASS, nv.NVFP4_AMAX_PATH_TWO_PASS
 
-EPOCH, EXIT, EXIT_BASE, EXIT_TOP, EXIT_TOP_BASE, LINE, DONE = 8256, 8288, 8544, 8800, 8832, 32, 8864
+EPOCH, DONE, EXIT_TOP, EXIT_TOP_BASE, EXIT, LINES = 8256, 8288, 8352, 8384, 8416, 64
+EPOCH_LIMIT = 0xFFFFFFFF - 256  # past it the last workgroup clears the tagged words and restarts at 0
 
 
 def handoff_words(ws):
     """(epoch, exit counters consistent with their bases)"""
     w = host(ws).view(np.uint32)
-    ok = (np.array_equal(w[EXIT:EXIT + 8 * LINE:LINE], w[EXIT_BASE:EXIT_BASE + 8 * LINE:LINE])
+    ok = (np.array_equal(w[EXIT:EXIT + 64 * LINES:64], w[EXIT + 32:EXIT + 32 + 64 * LINES:64])
           and w[EXIT_TOP] == w[EXIT_TOP_BASE])
     return int(w[EPOCH]), bool(ok)
 
@@ -276,15 +277,16 @@ def test_epoch_wrap_clears_the_slots():
     # Drive the epoch through the point where 32-bit tags would repeat, with
     # a slot left as a call 2^32 calls earlier would have left it: tag 1 and
     # a huge maximum, in a slot that the small calls do not write. The call
-    # that reaches the last epoch clears every slot, so the large call after
-    # it (tag 1 again) cannot take the stale slot for its own.
+    # that takes the epoch past its limit (which keeps the next call's tags
+    # below 2^32) clears every slot, so the large call after it (tag 1
+    # again) cannot take the stale slot for its own.
     ws = nv.empty_workspace(DEV)
     words = ws.view(torch.int32)
     small = W.randn_bf16(2048, 2048, 81)   # 256 tiles: 256 workgroups
     big = W.c2(rows=8192, cols=5120, seed=1)  # 768 workgroups
     stale = (1 << 32) | 0x7F000000  # tag 1, max 2^127
     slot = 4096 + 2 * 600
-    words[EPOCH] = -3  # 0xFFFFFFFD
+    words[EPOCH] = EPOCH_LIMIT - 1 - (1 << 32)  # the second call passes the limit
     for w in (slot, DONE):  # a slot and the done word, as such a call left them
         words[w] = stale & 0xFFFFFFFF
         words[w + 1] = stale >> 32
