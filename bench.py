@@ -158,6 +158,13 @@ def summarize_trace(db_path, workload="c2"):
         med = st.median(resident)
         print(f"\nsingle-pass calls (one kernel each): {len(resident)}, average {st.mean(resident):.0f} ns, "
               f"median {med:.0f} ns -> {B_ALG_CALL / med:.1f} GB/s on B_alg, {B_MIN / med:.1f} GB/s on B_min")
+    fused = [e - s for k, s, e in rows if k.startswith("k_grouped_fused")]
+    if fused and grouped:
+        med = st.median(fused)
+        mb = OTHER_WORKLOADS["grouped"]["min_bytes"]
+        print(f"\none-launch grouped calls (k_grouped_fused, one kernel each): {len(fused)}, average "
+              f"{st.mean(fused):.0f} ns, median {med:.0f} ns -> {call_bytes / med:.1f} GB/s on the algorithmic "
+              f"bytes, {mb / med:.1f} GB/s on the bytes moved")
     for name, v in (("k_cast in calls without timing events", plain), ("k_cast in calls with timing events", evented)):
         if v:
             print(f"\n{name}: {len(v)} launches, average {st.mean(v):.0f} ns, median {st.median(v):.0f} ns")
@@ -242,7 +249,8 @@ OTHER_WORKLOADS = {
                   bytes=None),
     "grouped": dict(desc="grouped quantize, MoE-like: 64 groups of 0..512 rows (multiples of 128, seed 6; 16768 rows) "
                          "x 4096 BF16 N(0,1) (seed 7); 1x16; row+col; compact; RNE; per-group amax",
-                    bytes=2 * 2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64),
+                    bytes=2 * 2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64,
+                    min_bytes=2 * 16768 * 4096 + 2 * (16768 * 4096 // 2 + 16768 * 4096 // 16) + 2 * 4 * 64),
     "swizzle_shapes": dict(desc="separate swizzle pass vs in-kernel swizzled scales at the pages' ten 128-aligned "
                                 "production shapes (BF16 torch.randn, 1x16, row+col, RNE, one input reused)",
                            bytes=None),
@@ -343,10 +351,11 @@ def grouped_rows():
 
 
 def run_grouped(nv, torch, dev, w, steps, warmup):
-    """Grouped quantize of an MoE-like split (one call: amax pass and cast
-    with a workspace), and for comparison the same call without a workspace
-    (zeroing, atomic amax, cast) and the same work as one nvfp4_quantize
-    call per group."""
+    """Grouped quantize of an MoE-like split with a workspace (the
+    library's choice: one launch, each group's tiles handing their maxima to
+    a head workgroup, where every group fits), and for comparison the same
+    call in two launches (amax pass, cast), without a workspace (zeroing,
+    atomic amax, cast) and as one nvfp4_quantize call per group."""
     groups = grouped_rows()
     R, C = sum(groups), 4096
     assert R == 16768, R
@@ -358,6 +367,7 @@ def run_grouped(nv, torch, dev, w, steps, warmup):
     stream = torch.cuda.current_stream()
     ws = nv.empty_workspace(dev)
     cfg_ws = nv.make_config(workspace=ws)
+    cfg_two = nv.make_config(workspace=ws, amax_path=nv.NVFP4_AMAX_PATH_TWO_PASS)
     cfg_atomic = nv.make_config()
 
     def timed(fn):
@@ -388,14 +398,22 @@ def run_grouped(nv, torch, dev, w, steps, warmup):
             nv.nvfp4_quantize(xs, row, col, cfg_ws, stream)
 
     us = timed(grouped_call)
+    us_two = timed(lambda i: grouped_call(i, cfg_two))
     us_atomic = timed(lambda i: grouped_call(i, cfg_atomic))
     us_sep = timed(per_group_calls)
+    # the call's form: one launch advances the workspace's epoch
+    epoch0 = int(ws[EPOCH_WORD * 4:EPOCH_WORD * 4 + 4].view(torch.int32).item())
+    grouped_call(0)
+    one_launch = int(ws[EPOCH_WORD * 4:EPOCH_WORD * 4 + 4].view(torch.int32).item()) != epoch0
     print(json.dumps({"workload": "grouped", "config": w["desc"], "us_per_call": round(us, 3),
+                      "form": "one launch" if one_launch else "two launches",
                       "bytes_per_call": w["bytes"], "GBps": round(w["bytes"] / us / 1e3, 1),
                       "pct_of_hbm_peak": round(100 * w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
+                      "min_bytes_per_call": w["min_bytes"],
+                      "pct_of_hbm_peak_min_bytes": round(100 * w["min_bytes"] / us / 1e3 / HBM_PEAK_GBS, 2),
                       "nonempty_groups": sum(1 for m in groups if m),
-                      "no_workspace_us": round(us_atomic, 3), "one_call_per_group_us": round(us_sep, 3),
-                      "buffer_sets_rotated": N_SETS}), flush=True)
+                      "two_launch_us": round(us_two, 3), "no_workspace_us": round(us_atomic, 3),
+                      "one_call_per_group_us": round(us_sep, 3), "buffer_sets_rotated": N_SETS}), flush=True)
 
 
 # Host wall-clock time per quantize call printed on the pages for an RTX 5050

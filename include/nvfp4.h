@@ -279,7 +279,7 @@ nvfp4_status_t nvfp4_quantize(const void *x, nvfp4_dtype_t dtype, int64_t rows, 
  * nvfp4_quantize, except that config.workspace must be NULL
  * (NVFP4_ERR_UNSUPPORTED otherwise): the call uses a workspace of the
  * library's own instead, a static device array of NVFP4_WORKSPACE_BYTES
- * (36 KiB) that each GPU holds from its first such call until the process
+ * (96 KiB) that each GPU holds from its first such call until the process
  * ends. That size serves every input nvfp4_quantize accepts, so no input is
  * rejected for its size beyond nvfp4_quantize's own limits.
  *   - No device memory is allocated or freed, by the library or by any
