@@ -234,3 +234,49 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for e, t in zip(eager, outs):
             assert np.array_equal(e, host(t)), rep
+
+
+@pytest.mark.parametrize("fill", ["uniform", "random"])
+def test_workspace_not_zero_filled_still_gives_the_oracle_bytes(fill):
+    # Uniform bytes leave the exit counters equal to their bases and no slot
+    # with the next tags, so the handoff runs as usual; random words fail the
+    # counters' check, and then the head reads every tile itself and the
+    # tiles take their group's maximum from the input. Either way the bytes
+    # are the oracle's, on this call and the next.
+    groups = [128, 0, 256, 128, 384]
+    x = W.randn_bf16(sum(groups), 640, 160)
+    xd = to_device(x)
+    ws = nv.empty_workspace(DEV)
+    if fill == "uniform":
+        ws.fill_(0xA5)
+    else:
+        g = torch.Generator(device=DEV).manual_seed(161)
+        ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device=DEV, dtype=torch.int32).to(torch.uint8))
+    kw = dict(stochastic=True, sr_seed=17)
+    for i in range(2):
+        got = run(xd, groups, ws, AUTO, **kw)
+        assert_oracle(got, x, groups, f"{fill} call {i}", **kw)
+
+
+def test_one_and_two_launch_calls_alternate_on_one_workspace():
+    # the two-launch form writes its per-workgroup maxima into the scratch
+    # part of the same workspace; the one-launch form's tags live elsewhere
+    ws = nv.empty_workspace(DEV)
+    groups = moe_groups(20, 170)
+    x = W.randn_bf16(sum(groups), 768, 171)
+    xd = to_device(x)
+    ref = O.quantize_grouped(x, groups)
+    for i, path in enumerate((AUTO, TWO, AUTO, TWO, AUTO)):
+        got = run(xd, groups, ws, path)
+        for k in got:
+            assert np.array_equal(got[k].ravel(), ref[k].ravel()), (i, k)
+
+
+def test_fp32_ue5m3_sr_one_launch():
+    groups = [48, 0, 208, 16, 96]
+    x = W.gaussian_fp32(sum(groups), 336, 180, 2.0)
+    kw = dict(stochastic=True, sr_seed=23)
+    ws = nv.empty_workspace(DEV)
+    got = run(to_device(x), groups, ws, AUTO, scale_fmt=nv.NVFP4_SCALE_UE5M3, **kw)
+    assert int(host(ws).view(np.uint32)[EPOCH]) == 1
+    assert_oracle(got, x, groups, "fp32 ue5m3 sr", scale_fmt=O.SCALE_UE5M3, **kw)
