@@ -65,6 +65,8 @@ CASES = [
     ("bf16_2d_sr_swizzled", moe_groups(16, 4), 2048, "bf16",
      dict(block_2d=True, stochastic=True, sr_seed=12, swizzled=True)),
     ("bf16_ue5m3", moe_groups(16, 5), 1024, "bf16", dict(scale_fmt=nv.NVFP4_SCALE_UE5M3)),
+    ("bf16_1d_swizzled", moe_groups(16, 10), 1536, "bf16", dict(swizzled=True)),
+    ("fp32_1d_sr_swizzled", moe_groups(10, 11), 1024, "fp32", dict(swizzled=True, stochastic=True, sr_seed=14)),
     ("fp32_1d_ragged_cols", moe_groups(12, 6, unit=16, most=24), 1008, "fp32", {}),
     ("fp32_2d_sr", moe_groups(12, 7, unit=16, most=24), 528, "fp32", dict(block_2d=True, stochastic=True, sr_seed=3)),
     ("row_only", moe_groups(24, 8), 1024, "bf16", dict(rowwise_only=True)),
