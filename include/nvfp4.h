@@ -104,9 +104,12 @@ typedef enum {
  * While kernels of other streams hold CUs, part of the grid may have to wait
  * for them; the workgroups already running then wait 50 us, take over the
  * amax of the tiles of the workgroups that have not started (reading those
- * tiles twice) and go on: the bytes are the same, the call slower. Callers
- * that overlap the quantize with long-running kernels on other streams may
- * prefer NVFP4_AMAX_PATH_TWO_PASS. */
+ * tiles twice) and go on: the bytes are the same, the call slower. The
+ * one-launch grouped form waits the same way, per group: after 50 us a
+ * group's head reads the maxima of the group's tiles that have not started
+ * from the input itself. Callers that overlap the quantize with
+ * long-running kernels on other streams may prefer
+ * NVFP4_AMAX_PATH_TWO_PASS. */
 
 /* One orientation of an NVFP4 tensor. For the row-wise orientation of an
  * R x C input, n = R and k = C; for the column-wise one, n = C and k = R
