@@ -82,17 +82,31 @@ constexpr int kAmaxThreads = 256;     // RHT amax pair (512 and 1024 measured sl
 constexpr int kMaxThreads = 256;      // per-tensor amax
 constexpr int kMaxVecPerThread = 8;   // loads in flight per thread and pass
 constexpr uint32_t kMaxGrid = 1280;   // 5 workgroups per CU on 256 CUs
+// The form that publishes by atomics takes workgroups four times as large
+// (the same threads and loads in flight): every workgroup's publish reads
+// the amax word past the caches, and those reads of one word serialize
+// (8192x5120 BF16: 23.5 -> 19.6 us per nvfp4_compute_amax call; half as many
+// of these workgroups, 23.2 us). The form with a workspace stays at 256
+// threads, where it measured faster (the two-pass 8192x5120 16x16 call:
+// 36.4 against 38.1 us).
+constexpr int kMaxThreadsAtomic = 1024;
+constexpr uint32_t kMaxGridAtomic = kMaxGrid * kMaxThreads / kMaxThreadsAtomic;
+// RHT amax pair without a workspace: workgroups loop over 16-row units
+// (8192x5120 BF16 nvfp4_compute_amax: 38.2 us with a workgroup per unit,
+// 35.6 with at most 2048 workgroups, 27.8 with 1024, 20.5-21.3 with 512,
+// 21.4-21.7 with 384, 27.1 with 256)
+constexpr uint32_t kMaxGridRhtAtomic = 512;
 
-template <int DT>
-__global__ __launch_bounds__(kMaxThreads) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a, float *b,
-                                                      uint32_t *partials, const float *noop) {
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a, float *b,
+                                             uint32_t *partials, const float *noop) {
   constexpr int VPT = kMaxVecPerThread;
-  __shared__ uint32_t lds[kMaxThreads / 64];
+  __shared__ uint32_t lds[NT / 64];
   if (noop_set(noop)) return;
   uint32_t m32 = 0;        // FP32: max of |x| bit patterns
   ushort2_t m16 = {0, 0};  // BF16: max of 15-bit magnitudes, two lanes
-  const uint64_t span = static_cast<uint64_t>(gridDim.x) * kMaxThreads;
-  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * kMaxThreads + threadIdx.x; i0 < nvec; i0 += span * VPT) {
+  const uint64_t span = static_cast<uint64_t>(gridDim.x) * NT;
+  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * NT + threadIdx.x; i0 < nvec; i0 += span * VPT) {
     uint4 v[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -112,7 +126,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_amax(const uint4 *__restrict__ 
     }
   }
   uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
-  m = block_umax<kMaxThreads>(m, lds);
+  m = block_umax<NT>(m, lds);
   if (threadIdx.x == 0) {
     if (partials != nullptr) {
       partials[blockIdx.x] = m;
@@ -452,7 +466,10 @@ namespace {
 // atomic form; for the workspace form at most kMaxPartials workgroups, padded
 // to a multiple of kPartialsGrain (the extra workgroups store +0).
 uint32_t reduction_grid(uint64_t work, bool to_partials) {
-  if (!to_partials) return static_cast<uint32_t>(work);
+  // the form without a workspace publishes each workgroup's maximum by a
+  // read of the amax word past the caches, and those reads of one word
+  // serialize: at most kMaxGridRhtAtomic workgroups there
+  if (!to_partials) return static_cast<uint32_t>(work < kMaxGridRhtAtomic ? work : kMaxGridRhtAtomic);
   const uint64_t g = (work + kPartialsGrain - 1) / kPartialsGrain * kPartialsGrain;
   return static_cast<uint32_t>(g < kMaxPartials ? g : kMaxPartials);
 }
@@ -464,17 +481,27 @@ hipError_t launch_amax(const void *x, int dtype, uint64_t n, float *a, float *b,
   const uint64_t nvec = n * (dtype == kBF16 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
   // one pass of kMaxVecPerThread loads per thread covers the input when it
-  // fits; at most kMaxGrid workgroups (both forms: few atomics per buffer)
-  const uint64_t want = (nvec + kMaxThreads * kMaxVecPerThread - 1) / (kMaxThreads * kMaxVecPerThread);
-  uint32_t grid = static_cast<uint32_t>(want < kMaxGrid ? want : kMaxGrid);
+  // fits; at most kMaxGrid (kMaxGridAtomic) workgroups
+  const uint32_t nt = partials != nullptr ? kMaxThreads : kMaxThreadsAtomic;
+  const uint32_t cap = partials != nullptr ? kMaxGrid : kMaxGridAtomic;
+  const uint64_t want = (nvec + uint64_t{nt} * kMaxVecPerThread - 1) / (uint64_t{nt} * kMaxVecPerThread);
+  uint32_t grid = static_cast<uint32_t>(want < cap ? want : cap);
   if (partials != nullptr) grid = reduction_grid(grid, true);
   if (npartials) *npartials = grid;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_amax<kBF16>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x), nvec, a, b,
-                       partials, noop);
-  else
-    hipLaunchKernelGGL(k_amax<kFP32>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x), nvec, a, b,
-                       partials, noop);
+  const uint4 *xv = static_cast<const uint4 *>(x);
+  if (partials != nullptr) {
+    if (dtype == kBF16)
+      hipLaunchKernelGGL((k_amax<kBF16, kMaxThreads>), dim3(grid), dim3(nt), 0, s, xv, nvec, a, b, partials, noop);
+    else
+      hipLaunchKernelGGL((k_amax<kFP32, kMaxThreads>), dim3(grid), dim3(nt), 0, s, xv, nvec, a, b, partials, noop);
+  } else {
+    if (dtype == kBF16)
+      hipLaunchKernelGGL((k_amax<kBF16, kMaxThreadsAtomic>), dim3(grid), dim3(nt), 0, s, xv, nvec, a, b, partials,
+                         noop);
+    else
+      hipLaunchKernelGGL((k_amax<kFP32, kMaxThreadsAtomic>), dim3(grid), dim3(nt), 0, s, xv, nvec, a, b, partials,
+                         noop);
+  }
   return hipGetLastError();
 }
 
