@@ -380,21 +380,20 @@ __global__ __launch_bounds__(kAmaxThreads) void k_rht_amax_grouped(const void *_
 // (here group-wide) contiguous spans, kMaxVecPerThread loads per thread in
 // flight. Result to partials[b], or with partials == NULL into the group's
 // slots by atomic max.
-template <int DT>
-__global__ __launch_bounds__(kMaxThreads) void k_amax_grouped(const uint4 *__restrict__ x, uint32_t vec_per_row,
-                                                              GroupTable t, float *a, float *b, uint32_t *partials,
-                                                              const float *noop) {
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) void k_amax_grouped(const uint4 *__restrict__ x, uint32_t vec_per_row, GroupTable t,
+                                                     float *a, float *b, uint32_t *partials, const float *noop) {
   constexpr int VPT = kMaxVecPerThread;
-  __shared__ uint32_t lds[kMaxThreads / 64];
+  __shared__ uint32_t lds[NT / 64];
   if (noop_set(noop)) return;
   if (partials != nullptr && blockIdx.x == 0) zero_empty_groups(t, a, b);
   const uint32_t g = group_of(t, blockIdx.x);
   const uint64_t first = static_cast<uint64_t>(t.row_start[g]) * vec_per_row;
   const uint64_t nvec = static_cast<uint64_t>(t.row_start[g + 1] - t.row_start[g]) * vec_per_row;
-  const uint64_t span = static_cast<uint64_t>(t.unit_start[g + 1] - t.unit_start[g]) * kMaxThreads;
+  const uint64_t span = static_cast<uint64_t>(t.unit_start[g + 1] - t.unit_start[g]) * NT;
   uint32_t m32 = 0;
   ushort2_t m16 = {0, 0};
-  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * kMaxThreads + threadIdx.x; i0 < nvec;
+  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x - t.unit_start[g]) * NT + threadIdx.x; i0 < nvec;
        i0 += span * VPT) {
     // all loads in flight at once: past the group's end the index is
     // clamped to its last vector, which cannot change a maximum
@@ -414,7 +413,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_amax_grouped(const uint4 *__res
     }
   }
   uint32_t m = DT == kBF16 ? (static_cast<uint32_t>(max(m16.x, m16.y)) << 16) : m32;
-  m = block_umax<kMaxThreads>(m, lds);
+  m = block_umax<NT>(m, lds);
   if (threadIdx.x == 0) {
     if (partials != nullptr) {
       partials[blockIdx.x] = m;
@@ -552,16 +551,17 @@ uint32_t plan_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, G
   }
 }
 
-// Workgroups per group for the per-tensor amax: shares of about kMaxGrid
-// in proportion to each group's chunks (at least one, at most its chunk
-// count), so that the whole pass runs as one k_amax over the tensor would.
+// Workgroups per group for the per-tensor amax: shares of about `target`
+// (the pass's grid cap) in proportion to each group's chunks (at least one,
+// at most its chunk count), so that the whole pass runs as one k_amax over
+// the tensor would.
 // The workspace form pads each share to a multiple of kPartialsGrain and
 // lowers the target so that the sum stays within kMaxPartials:
 // sum <= target + ngroups (rounding up) + 3 ngroups (padding).
-void share_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, GroupTable &t) {
+void share_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, GroupTable &t,
+                  uint64_t target = kMaxGrid) {
   uint64_t total = 0;
   for (uint32_t g = 0; g < ngroups; ++g) total += work[g];
-  uint64_t target = kMaxGrid;
   if (to_partials && target + 4ull * ngroups > kMaxPartials) target = kMaxPartials - 4ull * ngroups;
   t.unit_start[0] = 0;
   for (uint32_t g = 0; g < ngroups; ++g) {
@@ -583,22 +583,36 @@ hipError_t launch_amax_grouped(const void *x, int dtype, uint32_t cols, const ui
   GroupTable t{};
   t.ngroups = ngroups;
   const uint32_t vec_per_row = cols * (dtype == kBF16 ? 2 : 4) / 16;
-  const uint64_t chunk = kMaxThreads * kMaxVecPerThread;
+  // the form without a workspace takes the per-tensor pass's larger
+  // workgroups (fewer publishes: the groups' amax words share a few lines)
+  const bool atomic = partials == nullptr;
+  const uint32_t nt = atomic ? kMaxThreadsAtomic : kMaxThreads;
+  const uint64_t chunk = uint64_t{nt} * kMaxVecPerThread;
   uint64_t work[kMaxGroups];
   for (uint32_t g = 0; g <= ngroups; ++g) t.row_start[g] = row_start[g];
   for (uint32_t g = 0; g < ngroups; ++g)
     work[g] = (static_cast<uint64_t>(row_start[g + 1] - row_start[g]) * vec_per_row + chunk - 1) / chunk;
-  share_groups(work, ngroups, partials != nullptr, t);
+  share_groups(work, ngroups, !atomic, t, atomic ? kMaxGridAtomic : kMaxGrid);
   if (part_start)
     for (uint32_t g = 0; g <= ngroups; ++g) part_start[g] = t.unit_start[g];
   const uint32_t grid = t.unit_start[ngroups] > 0 ? t.unit_start[ngroups] : (partials ? 1u : 0u);
   if (grid == 0) return hipSuccess;
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_amax_grouped<kBF16>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x),
-                       vec_per_row, t, a, b, partials, noop);
-  else
-    hipLaunchKernelGGL(k_amax_grouped<kFP32>, dim3(grid), dim3(kMaxThreads), 0, s, static_cast<const uint4 *>(x),
-                       vec_per_row, t, a, b, partials, noop);
+  const uint4 *xv = static_cast<const uint4 *>(x);
+  if (!atomic) {
+    if (dtype == kBF16)
+      hipLaunchKernelGGL((k_amax_grouped<kBF16, kMaxThreads>), dim3(grid), dim3(nt), 0, s, xv, vec_per_row, t, a, b,
+                         partials, noop);
+    else
+      hipLaunchKernelGGL((k_amax_grouped<kFP32, kMaxThreads>), dim3(grid), dim3(nt), 0, s, xv, vec_per_row, t, a, b,
+                         partials, noop);
+  } else {
+    if (dtype == kBF16)
+      hipLaunchKernelGGL((k_amax_grouped<kBF16, kMaxThreadsAtomic>), dim3(grid), dim3(nt), 0, s, xv, vec_per_row, t, a,
+                         b, partials, noop);
+    else
+      hipLaunchKernelGGL((k_amax_grouped<kFP32, kMaxThreadsAtomic>), dim3(grid), dim3(nt), 0, s, xv, vec_per_row, t, a,
+                         b, partials, noop);
+  }
   return hipGetLastError();
 }
 
