@@ -96,6 +96,7 @@ constexpr uint32_t kMaxGridAtomic = kMaxGrid * kMaxThreads / kMaxThreadsAtomic;
 // 35.6 with at most 2048 workgroups, 27.8 with 1024, 20.5-21.3 with 512,
 // 21.4-21.7 with 384, 27.1 with 256)
 constexpr uint32_t kMaxGridRhtAtomic = 512;
+static_assert(kMaxGroups <= kMaxGridRhtAtomic, "one workgroup per group fits the grouped atomic grid");
 
 template <int DT, int NT>
 __global__ __launch_bounds__(NT) void k_amax(const uint4 *__restrict__ x, uint64_t nvec, float *a, float *b,
@@ -532,9 +533,9 @@ hipError_t launch_zero_amax_n(float *a, float *b, uint32_t n, const float *noop,
 namespace {
 
 // Work units per group for a grouped amax pass: `work[g]` units of group g,
-// `per` of them per workgroup. The atomic form takes per = 1. The workspace
-// form doubles `per` until every group's workgroup count, padded to a
-// multiple of kPartialsGrain, fits kMaxPartials in total.
+// `per` of them per workgroup. `per` doubles until the workgroups fit:
+// kMaxPartials in total for the workspace form (each group's count padded to
+// a multiple of kPartialsGrain), kMaxGridRhtAtomic for the atomic form.
 uint32_t plan_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, GroupTable &t) {
   uint32_t per = 1;
   for (;;) {
@@ -546,7 +547,10 @@ uint32_t plan_groups(const uint64_t *work, uint32_t ngroups, bool to_partials, G
       total += n;
       t.unit_start[g + 1] = static_cast<uint32_t>(total < 0xFFFFFFFFull ? total : 0xFFFFFFFFull);
     }
-    if (!to_partials || total <= kMaxPartials) return per;
+    // the workspace form's workgroups fit its slots; the atomic form's stay
+    // few, since their publishes serialize (ngroups <= kMaxGroups keeps both
+    // reachable with one workgroup per group)
+    if (total <= (to_partials ? kMaxPartials : kMaxGridRhtAtomic)) return per;
     per *= 2;
   }
 }
