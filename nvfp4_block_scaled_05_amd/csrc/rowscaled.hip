@@ -4,14 +4,14 @@
 // row gets its own FP32 amax and the E4M3 block scales are taken relative to
 // it; output is row-wise only with compact scales. There the row amax is a
 // separate kernel run before the quantize kernel. Here the two are one
-// kernel: thread t keeps 1x16 blocks t and t + 256 of a row in registers (up
+// kernel: each thread keeps two whole 1x16 blocks of a row in registers (up
 // to 8192 elements per row) between the reduction and the cast, so the input
 // is read from HBM once; longer rows re-read the part beyond that from cache.
 //
 // With whole blocks per thread, a block's maximum needs no other lane; the
-// four scale codes of an aligned group (four consecutive threads) are
-// gathered with DPP, and the row maximum is a DPP wave reduction plus one
-// barrier.
+// four scale codes of an aligned group are gathered by lane exchanges
+// (DPP or swizzles, see reg_block), and the row maximum is a DPP wave
+// reduction plus one barrier.
 #include "codec.h"
 #include "launch.h"
 
@@ -79,7 +79,25 @@ __device__ __forceinline__ float block_value(const Block<DT> &b, int k) {
 // Encode block `blk` of `row` (16 elements, block max bits m) and store its 8
 // data bytes; lane 0 of each group of four stores the group's 4 scale codes.
 // Executed by all lanes (DPP), stores predicated on `valid`.
-template <int DT, bool SR>
+// The four scale codes of an aligned group of blocks, for the lane that
+// holds its first block. QUAD: the group's blocks are in the lanes of a quad;
+// else in lanes t, t + 2, t + 4, t + 6 (the BF16 register blocks, see
+// reg_block).
+template <bool QUAD>
+__device__ __forceinline__ uint32_t scale_group(uint32_t code) {
+  if (QUAD)
+    return quad_bcast(code, 0) | (quad_bcast(code, 1) << 8) | (quad_bcast(code, 2) << 16) |
+           (quad_bcast(code, 3) << 24);
+  // bit-mask swizzles within 32 lanes: lane (t & 0b11001) | 2i
+  const auto from = [](uint32_t x, auto pattern) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), decltype(pattern)::value));
+  };
+  return from(code, std::integral_constant<int, 0x19>{}) | (from(code, std::integral_constant<int, 0x19 | (2 << 5)>{}) << 8) |
+         (from(code, std::integral_constant<int, 0x19 | (4 << 5)>{}) << 16) |
+         (from(code, std::integral_constant<int, 0x19 | (6 << 5)>{}) << 24);
+}
+
+template <int DT, bool SR, bool QUAD = true>
 __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, bool valid, uint32_t blk, uint32_t row,
                                              const RowScaledArgs &p, float S, uint32_t key, uint64_t sr_base) {
   const BlockScale bs = block_scale(__uint_as_float(m), S, p.ue5m3 != 0);
@@ -99,8 +117,7 @@ __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, boo
     hi = e2m1_rne_x8(s + 8);
   }
   if (valid) __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(p.data + byte0));
-  const uint32_t group = quad_bcast(bs.code, 0) | (quad_bcast(bs.code, 1) << 8) | (quad_bcast(bs.code, 2) << 16) |
-                         (quad_bcast(bs.code, 3) << 24);
+  const uint32_t group = scale_group<QUAD>(bs.code);
   if (valid && (blk & 3u) == 0) {
     const uint32_t scale_cols = p.cols >> 4;
     const uint64_t off = static_cast<uint64_t>(row) * scale_cols + blk;
@@ -114,19 +131,66 @@ __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, boo
   }
 }
 
-// The register part of one row (blocks t, t + kThreads, ...), zero past the
-// row's end.
+// Block index of the thread's register block k. FP32: blocks t, t + 256.
+// BF16: the row is loaded in 16-byte pieces, load j taking piece
+// j * 256 + t, so that each load instruction of a wave reads 1 KiB
+// contiguous (a layout with whole 32-byte blocks per thread measured about
+// 1 us slower per 4096x8192 call in a traffic-only probe); lanes 2m and
+// 2m + 1 then swap halves so that each holds whole blocks: lane 2m the
+// block of pieces 2m, 2m + 1 of loads 0 and 2 (blocks m and 256 + m),
+// lane 2m + 1 that of loads 1 and 3 (blocks 128 + m and 384 + m).
+template <int DT>
+__device__ __forceinline__ uint32_t reg_block(int k) {
+  const uint32_t t = threadIdx.x;
+  if (DT == kBF16) return kThreads * k + ((t & 1) ? kThreads / 2 + (t >> 1) : (t >> 1));
+  return kThreads * k + t;
+}
+
+// The register part of one row (blocks reg_block(k)), zero past the row's
+// end.
 template <int DT>
 __device__ __forceinline__ void load_row(const RowScaledArgs &p, uint32_t row, Block<DT> (&r)[kRegBlocks]) {
   const uint32_t nblk = p.cols >> 4;
   const uint64_t row_off = static_cast<uint64_t>(row) * p.cols;
+  if constexpr (DT == kBF16) {
+    static_assert(kRegBlocks == 2, "two pairs of piece loads");
+    const uint32_t t = threadIdx.x;
+    const uint32_t npieces = p.cols >> 3;  // even: cols % 16 == 0
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(p.x) + row_off * 2);
+    u32x4 v[2 * kRegBlocks];
 #pragma unroll
-  for (int k = 0; k < kRegBlocks; ++k) {
-    const uint32_t blk = threadIdx.x + kThreads * k;
-    if (blk < nblk)
-      r[k] = load_block<DT, true>(p.x, row_off + 16ull * blk);
-    else
-      zero_block<DT>(r[k]);
+    for (int j = 0; j < 2 * kRegBlocks; ++j) {
+      const uint32_t q = kThreads * j + t;
+      v[j] = q < npieces ? __builtin_nontemporal_load(src + q) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // a block's two pieces are valid together (block b: pieces 2b, 2b + 1)
+    const bool odd = (t & 1) != 0;
+#pragma unroll
+    for (int k = 0; k < kRegBlocks; ++k) {
+      const u32x4 a = v[2 * k], b = v[2 * k + 1];
+      // the even lane needs its neighbour's piece of load 2k, the odd lane
+      // its neighbour's piece of load 2k + 1
+      const uint32_t send[4] = {odd ? a.x : b.x, odd ? a.y : b.y, odd ? a.z : b.z, odd ? a.w : b.w};
+      uint32_t got[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) got[c] = dpp_mov<kQuadXor1>(send[c]);
+      const uint32_t own_lo[4] = {a.x, a.y, a.z, a.w};
+      const uint32_t own_hi[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        r[k].w[c] = odd ? got[c] : own_lo[c];
+        r[k].w[4 + c] = odd ? own_hi[c] : got[c];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kRegBlocks; ++k) {
+      const uint32_t blk = reg_block<DT>(k);
+      if (blk < nblk)
+        r[k] = load_block<DT, true>(p.x, row_off + 16ull * blk);
+      else
+        zero_block<DT>(r[k]);
+    }
   }
 }
 
@@ -163,8 +227,8 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
   const float S = global_encode_scale(amax, p.ue5m3 != 0);
 #pragma unroll
   for (int k = 0; k < kRegBlocks; ++k) {
-    const uint32_t blk = tid + kThreads * k;
-    encode_block<DT, SR>(reg[k], bm[k], blk < nblk, blk, row, p, S, key, sr_base);
+    const uint32_t blk = reg_block<DT>(k);
+    encode_block<DT, SR, DT != kBF16>(reg[k], bm[k], blk < nblk, blk, row, p, S, key, sr_base);
   }
   for (uint32_t base = kThreads * kRegBlocks; base < nblk; base += kThreads) {  // uniform loop
     const uint32_t blk = base + tid;
