@@ -130,6 +130,15 @@ def test_rowscaled_row_lengths(shape):
     check(W.c4(rows=shape[0], cols=shape[1], seed=41), columnwise=False, row_scaled=True, what=f"rowscaled {shape}")
 
 
+@pytest.mark.parametrize("shape", [(48, 784), (8, 8240), (16, 4096)])
+def test_rowscaled_bf16_sr(shape):
+    # BF16 rows are loaded in 16-byte pieces and regrouped into whole blocks
+    # between lane pairs: the stochastic-rounding byte index of every block,
+    # a partial last group of scale codes and the part beyond 8192 columns
+    check(W.c4(rows=shape[0], cols=shape[1], seed=43), columnwise=False, row_scaled=True, stochastic=True, sr_seed=21,
+          what=f"rowscaled bf16 sr {shape}")
+
+
 def test_rowscaled_fp32_sr():
     x = W.gaussian_fp32(33, 1024, 42, scale=3.0)
     check(x, columnwise=False, row_scaled=True, stochastic=True, sr_seed=9, what="rowscaled sr")
