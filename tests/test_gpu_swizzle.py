@@ -33,11 +33,31 @@ def swizzle_on_gpu(compact: np.ndarray) -> np.ndarray:
 
 
 @pytest.mark.parametrize("shape", [(1088, 64), (1088, 68), (100, 7), (129, 5), (128, 4), (8192, 320), (5120, 512),
-                                   (1, 1), (300, 33)])
+                                   (1, 1), (300, 33), (300, 200), (1000, 517), (256, 1024), (129, 132)])
 def test_swizzle_pass_matches_oracle(shape):
     rng = np.random.default_rng(shape[0] * 7 + shape[1])
     compact = rng.integers(0, 256, size=shape, dtype=np.uint8)
     assert np.array_equal(swizzle_on_gpu(compact), O.swizzle_scales_padded(compact))
+
+
+@pytest.mark.parametrize("shape", [(300, 200), (256, 1024), (1000, 517)])
+def test_swizzle_pass_with_buffers_only_4_byte_aligned(shape):
+    # both buffers 4 bytes past a 16-byte boundary: the pass may not use its
+    # 16-byte loads or stores there
+    rows, sc = shape
+    rng = np.random.default_rng(rows + 3 * sc)
+    compact = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    n = nv.nvfp4_swizzled_scales_bytes(rows, sc)
+    src_buf = torch.zeros((rows * sc + 16,), dtype=torch.uint8, device=DEV)
+    src = src_buf[4:4 + rows * sc]
+    src.copy_(torch.from_numpy(compact.reshape(-1)).to(DEV))
+    out_buf = torch.full((n + 16,), 0xA5, dtype=torch.uint8, device=DEV)
+    out = out_buf[4:4 + n]
+    assert src.data_ptr() % 16 == 4 and out.data_ptr() % 16 == 4
+    nv.nvfp4_swizzle_scales(src, rows, sc, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), O.swizzle_scales_padded(compact))
+    assert np.all(host(out_buf[:4]) == 0xA5) and np.all(host(out_buf[4 + n:]) == 0xA5)
 
 
 def test_swizzle_pass_of_a_real_quantize_with_partial_tiles():
