@@ -76,9 +76,6 @@ __device__ __forceinline__ float block_value(const Block<DT> &b, int k) {
   return __uint_as_float(b.w[k]);
 }
 
-// Encode block `blk` of `row` (16 elements, block max bits m) and store its 8
-// data bytes; lane 0 of each group of four stores the group's 4 scale codes.
-// Executed by all lanes (DPP), stores predicated on `valid`.
 // The four scale codes of an aligned group of blocks, for the lane that
 // holds its first block. QUAD: the group's blocks are in the lanes of a quad;
 // else in lanes t, t + 2, t + 4, t + 6 (the BF16 register blocks, see
@@ -97,6 +94,10 @@ __device__ __forceinline__ uint32_t scale_group(uint32_t code) {
          (from(code, std::integral_constant<int, 0x19 | (6 << 5)>{}) << 24);
 }
 
+// Encode block `blk` of `row` (16 elements, block max bits m) and store its 8
+// data bytes; the lane holding the first block of an aligned group of four
+// stores the group's 4 scale codes. Executed by all lanes (lane exchanges),
+// stores predicated on `valid`.
 template <int DT, bool SR, bool QUAD = true>
 __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, bool valid, uint32_t blk, uint32_t row,
                                              const RowScaledArgs &p, float S, uint32_t key, uint64_t sr_base) {
