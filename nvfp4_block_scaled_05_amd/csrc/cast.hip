@@ -695,11 +695,14 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
   // are zeroed afterwards.
   const bool interior = r0 + kRT <= p.rows && c0 + kRT <= p.cols;  // uniform
   const uint32_t lcol = col_ok ? col : 0u;
+  // interior tiles: one uniform base per row of the thread's group and one
+  // 32-bit lane offset for all 16 loads (scalar address arithmetic); the
+  // offset stays below 2^32 while 128 rows of the input do
+  const bool lane_offset = interior && p.cols <= (1u << 22);  // uniform
+  const uint8_t *tile_base = static_cast<const uint8_t *>(p.x) + static_cast<uint64_t>(r0) * p.cols * kElem;
+  const uint32_t lane_off = ((rbase - r0) * p.cols + col) * kElem;
   uint32_t w[16][W];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const uint32_t r = min(rbase + k, p.rows - 1);
-    const uint8_t *src = static_cast<const uint8_t *>(p.x) + (static_cast<uint64_t>(r) * p.cols + lcol) * kElem;
+  auto load_piece = [&](int k, const uint8_t *src) {
     if constexpr (DT == kBF16) {
       const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(src));
       w[k][0] = t.x;
@@ -710,6 +713,16 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
       w[k][1] = t.y;
       w[k][2] = t.z;
       w[k][3] = t.w;
+    }
+  };
+  if (lane_offset) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) load_piece(k, tile_base + static_cast<uint64_t>(k) * p.cols * kElem + lane_off);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t r = min(rbase + k, p.rows - 1);
+      load_piece(k, static_cast<const uint8_t *>(p.x) + (static_cast<uint64_t>(r) * p.cols + lcol) * kElem);
     }
   }
   auto value = [&](int k, int c) -> float {
@@ -746,10 +759,18 @@ __device__ __forceinline__ void cast_rht_tile(const CastArgs &p, uint32_t tx, ui
     for (int j = 0; j < 4; ++j) mine[j] = 0;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      // float max of magnitudes (abs modifiers, no masking): for finite
-      // inputs the same as the integer max of the |x| bit patterns
-      uint32_t m = __float_as_uint(fmaxf(fmaxf(fabsf(value(k, 0)), fabsf(value(k, 1))),
-                                         fmaxf(fabsf(value(k, 2)), fabsf(value(k, 3)))));
+      // max |x| of the row piece: BF16 as a packed 16-bit max of the
+      // magnitude bits (no unpacking), FP32 as a float max with abs
+      // modifiers; for finite inputs both are the max of the |x| bit patterns
+      uint32_t m;
+      if constexpr (DT == kBF16) {
+        const ushort2_t h = __builtin_elementwise_max(__builtin_bit_cast(ushort2_t, w[k][0] & 0x7FFF7FFFu),
+                                                      __builtin_bit_cast(ushort2_t, w[k][1] & 0x7FFF7FFFu));
+        m = static_cast<uint32_t>(max(h.x, h.y)) << 16;
+      } else {
+        m = __float_as_uint(fmaxf(fmaxf(fabsf(value(k, 0)), fabsf(value(k, 1))),
+                                  fmaxf(fabsf(value(k, 2)), fabsf(value(k, 3)))));
+      }
       m = max(m, dpp_mov<kQuadXor1>(m));
       m = max(m, dpp_mov<kQuadXor2>(m));
       // quad lane q turns rows q, q+4, q+8, q+12 into codes
