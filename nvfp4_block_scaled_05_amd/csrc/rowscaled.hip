@@ -77,28 +77,32 @@ __device__ __forceinline__ float block_value(const Block<DT> &b, int k) {
 }
 
 // The four scale codes of an aligned group of blocks, for the lane that
-// holds its first block. QUAD: the group's blocks are in the lanes of a quad;
-// else in lanes t, t + 2, t + 4, t + 6 (the BF16 register blocks, see
-// reg_block).
-template <bool QUAD>
+// holds its first block: the group's blocks are in lanes t, t + STRIDE,
+// t + 2 STRIDE, t + 3 STRIDE (1: a lane quad; 2 and 4: the BF16 and FP32
+// register blocks, see reg_block).
+template <int STRIDE>
 __device__ __forceinline__ uint32_t scale_group(uint32_t code) {
-  if (QUAD)
+  static_assert(STRIDE == 1 || STRIDE == 2 || STRIDE == 4, "lane strides of the register layouts");
+  if (STRIDE == 1)
     return quad_bcast(code, 0) | (quad_bcast(code, 1) << 8) | (quad_bcast(code, 2) << 16) |
            (quad_bcast(code, 3) << 24);
-  // bit-mask swizzles within 32 lanes: lane (t & 0b11001) | 2i
+  // bit-mask swizzles within 32 lanes: lane (t with the stride's two bits
+  // cleared) | STRIDE i
+  constexpr int kAnd = STRIDE == 2 ? 0x19 : 0x13;
   const auto from = [](uint32_t x, auto pattern) {
     return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), decltype(pattern)::value));
   };
-  return from(code, std::integral_constant<int, 0x19>{}) | (from(code, std::integral_constant<int, 0x19 | (2 << 5)>{}) << 8) |
-         (from(code, std::integral_constant<int, 0x19 | (4 << 5)>{}) << 16) |
-         (from(code, std::integral_constant<int, 0x19 | (6 << 5)>{}) << 24);
+  return from(code, std::integral_constant<int, kAnd>{}) |
+         (from(code, std::integral_constant<int, kAnd | ((1 * STRIDE) << 5)>{}) << 8) |
+         (from(code, std::integral_constant<int, kAnd | ((2 * STRIDE) << 5)>{}) << 16) |
+         (from(code, std::integral_constant<int, kAnd | ((3 * STRIDE) << 5)>{}) << 24);
 }
 
 // Encode block `blk` of `row` (16 elements, block max bits m) and store its 8
 // data bytes; the lane holding the first block of an aligned group of four
 // stores the group's 4 scale codes. Executed by all lanes (lane exchanges),
 // stores predicated on `valid`.
-template <int DT, bool SR, bool QUAD = true>
+template <int DT, bool SR, int STRIDE = 1>
 __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, bool valid, uint32_t blk, uint32_t row,
                                              const RowScaledArgs &p, float S, uint32_t key, uint64_t sr_base) {
   const BlockScale bs = block_scale(__uint_as_float(m), S, p.ue5m3 != 0);
@@ -118,7 +122,7 @@ __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, boo
     hi = e2m1_rne_x8(s + 8);
   }
   if (valid) __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(p.data + byte0));
-  const uint32_t group = scale_group<QUAD>(bs.code);
+  const uint32_t group = scale_group<STRIDE>(bs.code);
   if (valid && (blk & 3u) == 0) {
     const uint32_t scale_cols = p.cols >> 4;
     const uint64_t off = static_cast<uint64_t>(row) * scale_cols + blk;
@@ -132,20 +136,27 @@ __device__ __forceinline__ void encode_block(const Block<DT> &b, uint32_t m, boo
   }
 }
 
-// Block index of the thread's register block k. FP32: blocks t, t + 256.
-// BF16: the row is loaded in 16-byte pieces, load j taking piece
-// j * 256 + t, so that each load instruction of a wave reads 1 KiB
-// contiguous (a layout with whole 32-byte blocks per thread measured about
-// 1 us slower per 4096x8192 call in a traffic-only probe); lanes 2m and
-// 2m + 1 then swap halves so that each holds whole blocks: lane 2m the
-// block of pieces 2m, 2m + 1 of loads 0 and 2 (blocks m and 256 + m),
-// lane 2m + 1 that of loads 1 and 3 (blocks 128 + m and 384 + m).
+// Block index of the thread's register block k. The row is loaded in
+// 16-byte pieces, load j taking piece j * 256 + t, so that each load
+// instruction of a wave reads 1 KiB contiguous (a layout with whole blocks
+// per thread measured about 1 us slower per 4096x8192 BF16 call in a
+// traffic-only probe); lanes then exchange pieces so that each holds whole
+// blocks. BF16 (2 pieces per block, 4 loads): lanes 2m and 2m + 1 swap
+// halves, lane 2m taking the blocks of loads 0 and 2 (blocks m and
+// 256 + m), lane 2m + 1 those of loads 1 and 3 (128 + m and 384 + m). FP32
+// (4 pieces per block, 8 loads): the lanes 4m + i of a quad transpose each
+// group of four loads, lane 4m + i taking the block of load 4k + i, block
+// (4k + i) * 64 + m.
 template <int DT>
 __device__ __forceinline__ uint32_t reg_block(int k) {
   const uint32_t t = threadIdx.x;
   if (DT == kBF16) return kThreads * k + ((t & 1) ? kThreads / 2 + (t >> 1) : (t >> 1));
-  return kThreads * k + t;
+  return (4 * k + (t & 3)) * (kThreads / 4) + (t >> 2);
 }
+
+// Lane stride between consecutive register blocks (scale_group)
+template <int DT>
+constexpr int kRegStride = DT == kBF16 ? 2 : 4;
 
 // The register part of one row (blocks reg_block(k)), zero past the row's
 // end.
@@ -184,13 +195,38 @@ __device__ __forceinline__ void load_row(const RowScaledArgs &p, uint32_t row, B
       }
     }
   } else {
+    const uint32_t t = threadIdx.x;
+    const uint32_t npieces = p.cols >> 2;  // a multiple of 4: cols % 16 == 0
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(p.x) + row_off * 4);
+    u32x4 v[4 * kRegBlocks];
+#pragma unroll
+    for (int j = 0; j < 4 * kRegBlocks; ++j) {
+      const uint32_t q = kThreads * j + t;
+      v[j] = q < npieces ? __builtin_nontemporal_load(src + q) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // per group of four loads and per dword, a 4x4 transpose over the lane
+    // quad in two exchange stages (lane ^ 1, then lane ^ 2): afterwards lane
+    // i of the quad holds, as its piece j, what lane j loaded in load 4k + i
+    const uint32_t i = t & 3;
 #pragma unroll
     for (int k = 0; k < kRegBlocks; ++k) {
-      const uint32_t blk = reg_block<DT>(k);
-      if (blk < nblk)
-        r[k] = load_block<DT, true>(p.x, row_off + 16ull * blk);
-      else
-        zero_block<DT>(r[k]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = v[4 * k + j][d];
+        uint32_t n[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t other = dpp_mov<kQuadXor1>(m[j ^ 1]);
+          n[j] = ((static_cast<uint32_t>(j) ^ i) & 1u) ? other : m[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t other = dpp_mov<kQuadXor2>(n[j ^ 2]);
+          r[k].w[4 * j + d] = ((static_cast<uint32_t>(j) ^ i) & 2u) ? other : n[j];
+        }
+      }
     }
   }
 }
@@ -229,7 +265,7 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
 #pragma unroll
   for (int k = 0; k < kRegBlocks; ++k) {
     const uint32_t blk = reg_block<DT>(k);
-    encode_block<DT, SR, DT != kBF16>(reg[k], bm[k], blk < nblk, blk, row, p, S, key, sr_base);
+    encode_block<DT, SR, kRegStride<DT>>(reg[k], bm[k], blk < nblk, blk, row, p, S, key, sr_base);
   }
   for (uint32_t base = kThreads * kRegBlocks; base < nblk; base += kThreads) {  // uniform loop
     const uint32_t blk = base + tid;

@@ -130,6 +130,16 @@ def test_rowscaled_row_lengths(shape):
     check(W.c4(rows=shape[0], cols=shape[1], seed=41), columnwise=False, row_scaled=True, what=f"rowscaled {shape}")
 
 
+@pytest.mark.parametrize("stochastic", [False, True], ids=["rne", "sr"])
+@pytest.mark.parametrize("shape", [(5, 16), (7, 784), (3, 10000), (64, 8208), (40, 8192)])
+def test_rowscaled_fp32_row_lengths(shape, stochastic):
+    # FP32 rows load as 16-byte pieces and are regrouped into whole blocks
+    # by a transpose over lane quads: short rows, a partial last group of
+    # scale codes, whole 8192-column rows and rows past the register part
+    x = W.gaussian_fp32(shape[0], shape[1], 44, scale=3.0)
+    check(x, columnwise=False, row_scaled=True, stochastic=stochastic, sr_seed=23, what=f"rowscaled fp32 {shape}")
+
+
 @pytest.mark.parametrize("shape", [(48, 784), (8, 8240), (16, 4096)])
 def test_rowscaled_bf16_sr(shape):
     # BF16 rows are loaded in 16-byte pieces and regrouped into whole blocks
