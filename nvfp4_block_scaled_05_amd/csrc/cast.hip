@@ -171,11 +171,12 @@ __device__ __forceinline__ void store_scale_group(uint8_t *base, uint32_t r, uin
 // workgroup (one correctly rounded division per code) and looked up in LDS.
 // Scale codes and column-wise data words go through LDS so that they leave
 // as 32-bit scale words and 64 contiguous bytes per column. The input is read
-// once and the outputs are not read back, so loads and most stores are
-// non-temporal (streamed past the caches). Column-wise data is the exception:
-// a tile writes half of each 128-byte line it touches, the tile below it the
-// other half, and ordinary stores let the caches merge the two (measured
-// faster than streaming them).
+// once and the outputs are not read back, so loads and data stores are
+// non-temporal (streamed past the caches), the column-wise pieces too,
+// although a tile writes only half of each 128-byte line it touches and the
+// tile below it the other half: cached, the caches merged the halves but the
+// kernels measured slower (the dirty lines were written back at the end).
+// Compact scale pieces are the exception (store_scale_group).
 // ---------------------------------------------------------------------------
 constexpr int kRT = 128;  // register-tile edge
 
