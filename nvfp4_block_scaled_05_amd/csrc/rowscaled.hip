@@ -32,15 +32,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
-// NT: non-temporal (the part of a row that stays in registers is read once);
-// the part beyond that is read twice and goes through the caches.
-template <int DT, bool NT>
+// One block of the part of a row beyond the register part (rows longer than
+// 8192 elements): read twice, for the reduction and for the encode, so
+// through the caches.
+template <int DT>
 __device__ __forceinline__ Block<DT> load_block(const void *x, uint64_t elem_off) {
   Block<DT> b;
   const u32x4 *src = reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(x) + elem_off * (DT == kBF16 ? 2 : 4));
 #pragma unroll
   for (int q = 0; q < Block<DT>::kWords / 4; ++q) {
-    const u32x4 t = NT ? __builtin_nontemporal_load(src + q) : src[q];
+    const u32x4 t = src[q];
     b.w[4 * q] = t.x;
     b.w[4 * q + 1] = t.y;
     b.w[4 * q + 2] = t.z;
@@ -247,7 +248,7 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
 #pragma unroll
     for (int k = 1; k < kRegBlocks; ++k) m = max(m, bm[k]);
     for (uint32_t blk = tid + kThreads * kRegBlocks; blk < nblk; blk += kThreads)
-      m = max(m, block_max_bits<DT>(load_block<DT, false>(p.x, row_off + 16ull * blk)));
+      m = max(m, block_max_bits<DT>(load_block<DT>(p.x, row_off + 16ull * blk)));
     m = wave_max(m);
     if ((tid & 63) == 0) lds_w[tid >> 6] = m;
     __syncthreads();
@@ -271,7 +272,7 @@ __device__ __forceinline__ void process_row(const RowScaledArgs &p, uint32_t row
     const uint32_t blk = base + tid;
     Block<DT> cur;
     if (blk < nblk)
-      cur = load_block<DT, false>(p.x, row_off + 16ull * blk);
+      cur = load_block<DT>(p.x, row_off + 16ull * blk);
     else
       zero_block<DT>(cur);
     encode_block<DT, SR>(cur, block_max_bits<DT>(cur), blk < nblk, blk, row, p, S, key, sr_base);
