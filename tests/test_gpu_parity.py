@@ -130,6 +130,13 @@ def test_rowscaled_row_lengths(shape):
     check(W.c4(rows=shape[0], cols=shape[1], seed=41), columnwise=False, row_scaled=True, what=f"rowscaled {shape}")
 
 
+def test_rowscaled_fp32_full():
+    # c4's shape with FP32 input, every byte against the oracle
+    x = W.gaussian_fp32(4096, 8192, 45, scale=2.0)
+    x *= np.exp(2.0 * W.gaussian_fp32(4096, 1, 46)).astype(np.float32)  # per-row magnitudes, as c4
+    check(x, columnwise=False, row_scaled=True, what="rowscaled fp32 4096x8192")
+
+
 @pytest.mark.parametrize("stochastic", [False, True], ids=["rne", "sr"])
 @pytest.mark.parametrize("shape", [(5, 16), (7, 784), (3, 10000), (64, 8208), (40, 8192)])
 def test_rowscaled_fp32_row_lengths(shape, stochastic):
