@@ -164,18 +164,6 @@ __device__ __forceinline__ void load_strip(const void *x, uint32_t cols, uint32_
   }
 }
 
-// RHT amax pair. The input is cut into units of 16 rows x (kAmaxThreads * 4)
-// columns, gx units across; a workgroup reduces units blockIdx.x,
-// blockIdx.x + gridDim.x, ... Each thread loads 4 adjacent columns of one
-// 16-row group as raw words: max|x| comes from the words themselves, the
-// sign flips of the transform are applied to whole words (one sign per row),
-// and each column's 16 values then go through the unnormalized transform.
-// max|t| = fl(max|sum| / 4): scaling by 1/4 is exact up to rounding in the
-// denormal range, and rounding is monotonic, so this is the maximum of the
-// transformed values t = fl(sum / 4) themselves. Results go to
-// partials[blockIdx.x] and partials[kMaxPartials + blockIdx.x], or with
-// partials == NULL (one unit per workgroup) into row_amax and col_amax by
-// atomic max.
 // One RHT amax unit: this thread's 4 columns c .. c+3 of rows 16 by .. +15.
 // Accumulates max|x| (mx16 / mx32 by input type) and max|unnormalized
 // transform| (ms).
