@@ -1104,9 +1104,10 @@ __global__ __launch_bounds__(kThreads) void k_cast_rht(CastArgs p) {
 //   counters are not in a state that a call left, a workgroup takes the
 //   maximum of the whole input itself.
 // No value of an earlier call can pass for this call's: the epoch advances
-// once per call, when the last workgroup exits (exit counters at the end of
-// the kernel, off the critical path), so every workgroup of a call reads the
-// same epoch, even one that starts after others stopped waiting.
+// once per call, when the last workgroup counts out (exit counters, which
+// a workgroup passes once it holds the call's maximum, before its encode),
+// so every workgroup of a call reads the same epoch, even one that starts
+// after others stopped waiting.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kDefaultFastTicks = 5000;   // 50 us of the 100 MHz counter
 constexpr uint32_t kClaimSpan = 512;           // slots each workgroup of the slow path scans for claims
@@ -1410,8 +1411,9 @@ __device__ bool wait_done(const uint32_t *ws, uint32_t t, uint32_t ticks, uint32
   }
 }
 
-// The end of a call that follows the workspace's epoch protocol (thread 0
-// of every workgroup): exit counters per line x = blockIdx.x mod kExitLines,
+// The count-out of a call that follows the workspace's epoch protocol
+// (thread 0 of every workgroup, once it touches no tagged word any more):
+// exit counters per line x = blockIdx.x mod kExitLines,
 // then over the lines; the last workgroup of the grid advances the epoch
 // by adv (and only it returns true). e, xb, xbt: the epoch and exit bases
 // read at the start.
@@ -1663,6 +1665,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
     if (p.col_amax) *p.col_amax = amax;
   }
 
+  // ---- count out: the last workgroup of the grid advances the epoch ----
+  // The workgroup holds the call's maximum and touches no tagged word from
+  // here on; a workgroup that has not started has not counted, so the epoch
+  // only advances once every workgroup has read it. Counting here rather
+  // than after the encode takes the counters' atomics off the kernel's tail.
+  if (tid == 0) epoch_exit(ws, lds_start[0], 1, lds_start[1], lds_start[2], G, xg, nxg);
+
   // ---- encode from registers ----
   const bool ue = p.ue5m3 != 0;
   const float S_row = p.row_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
@@ -1693,8 +1702,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_cast_rt_resident(CastArgs p, ui
     }
   }
 
-  // ---- exit: the last workgroup of the grid advances the epoch ----
-  if (tid == 0) epoch_exit(ws, lds_start[0], 1, lds_start[1], lds_start[2], G, xg, nxg);
 }
 
 // The arguments of group g's own tensor: its rows of the input, its blocks
@@ -1961,13 +1968,14 @@ __global__ __launch_bounds__(kThreads) void k_grouped_fused(CastArgs p, GroupTab
     a[0] = input_max<DT>(q);
     workgroup_max(a, sh.red);
   }
+  // count out before the encode: no tagged word is touched from here on
+  if (tid == 0) epoch_exit(ws, lds_start[0], laps, lds_start[1], lds_start[2], G, x, nx);
   const float amax = __uint_as_float(a[0]);
   const bool ue = q.ue5m3 != 0;
   const float S_row = q.row_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
   const float S_col = q.col_data != nullptr ? global_encode_scale(amax, ue) : 1.0f;
   fill_multipliers(sh.mult, tid, S_row, S_col, ue);
   rt_encode<DT, B2D, SR>(q, tx, ty, w, S_row, S_col, ue, sh);
-  if (tid == 0) epoch_exit(ws, lds_start[0], laps, lds_start[1], lds_start[2], G, x, nx);
 }
 
 template <int DT, bool B2D, bool SR>

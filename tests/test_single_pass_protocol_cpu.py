@@ -20,7 +20,8 @@ launch.h; all accesses relaxed atomics on 64-bit words tag << 32 | low):
            claims what is left over every slot, waits until every slot
            holds a maximum, reduces them and stores the done word; the
            others wait for the done word
-  exit     exit counter; the last workgroup advances the epoch
+  count    exit counter; the last workgroup advances the epoch
+  encode   from its registers (a few steps); then the workgroup exits
 
 A workgroup runs only while it holds one of R resident places; a place
 frees when a workgroup exits, and the next workgroup in launch order starts.
@@ -147,12 +148,14 @@ def workgroup(ws, wg, G, chunk_max, fast_polls, load_steps, grace):
             while ws.done >> 32 != e + 1:
                 yield
             amax = ws.done & 0xFFFFFFFF
-    # encode (not modelled), then exit
+    # count out, then encode (touches no workspace word), then exit
     ws.exits += 1
     if ws.exits == G:
         ws.epoch = e + 1
         ws.exits = 0
     yield
+    for _ in range(load_steps):
+        yield
     return amax
 
 
