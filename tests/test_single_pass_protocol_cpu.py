@@ -26,8 +26,10 @@ launch.h; all accesses relaxed atomics on 64-bit words tag << 32 | low):
 A workgroup runs only while it holds one of R resident places; a place
 frees when a workgroup exits, and the next workgroup in launch order starts.
 Every run must end (no workgroup waits forever) with every workgroup
-holding the true maximum, the epoch advanced once, and no work duplicated
-beyond the claimed chunks of workgroups that had not started.
+holding the true maximum, the epoch advanced once, no tagged word touched
+after the epoch advanced (the last workgroup to count out may clear them
+all when the epoch wraps), and no work duplicated beyond the claimed chunks
+of workgroups that had not started.
 """
 
 from __future__ import annotations
@@ -42,16 +44,64 @@ GROUP = 64
 SPAN = 40  # slots each workgroup of the slow path scans for claims (the kernel: 512 of up to 2048)
 
 
+class _TaggedWords(list):
+    """Tagged workspace words: every access checks that the call's epoch has
+    not advanced yet."""
+
+    def __init__(self, ws, n):
+        super().__init__([0] * n)
+        self._ws = ws
+
+    def __getitem__(self, i):
+        self._ws.check_live()
+        return super().__getitem__(i)
+
+    def __setitem__(self, i, v):
+        self._ws.check_live()
+        super().__setitem__(i, v)
+
+    def __iter__(self):
+        self._ws.check_live()
+        return super().__iter__()
+
+
 class Workspace:
     def __init__(self, G):
-        self.slot = [0] * G
-        self.group = [0] * ((G + GROUP - 1) // GROUP)
-        self.done = 0
-        self.reducer = 0
+        self.advanced = False  # the current call's epoch has advanced
+        self.slot = _TaggedWords(self, G)
+        self.group = _TaggedWords(self, (G + GROUP - 1) // GROUP)
+        self._done = 0
+        self._reducer = 0
         self.reducers = 0  # workgroups elected to reduce in the current call
         self.epoch = 0
         self.exits = 0
         self.memory_reads = 0  # chunks whose maximum was read from memory by a claimer
+
+    def check_live(self):
+        # once the last workgroup has counted out, the kernel may clear every
+        # tagged word (the epoch's wrap-around): no workgroup of the call may
+        # touch one after that
+        assert not self.advanced, "a tagged word was touched after the epoch advanced"
+
+    @property
+    def done(self):
+        self.check_live()
+        return self._done
+
+    @done.setter
+    def done(self, v):
+        self.check_live()
+        self._done = v
+
+    @property
+    def reducer(self):
+        self.check_live()
+        return self._reducer
+
+    @reducer.setter
+    def reducer(self, v):
+        self.check_live()
+        self._reducer = v
 
     def cas_slot(self, w, expect, new):
         if self.slot[w] == expect:
@@ -153,6 +203,7 @@ def workgroup(ws, wg, G, chunk_max, fast_polls, load_steps, grace):
     if ws.exits == G:
         ws.epoch = e + 1
         ws.exits = 0
+        ws.advanced = True
     yield
     for _ in range(load_steps):
         yield
@@ -166,6 +217,7 @@ def run(G, R, seed, fast_polls, load_steps=3, calls=2, step_limit=2_000_000, gra
     for call in range(calls):
         chunk_max = [rng.randrange(0, 1 << 30) for _ in range(G)]
         epoch0 = ws.epoch
+        ws.advanced = False
         pending = list(range(G))
         running = {}
         results = {}
