@@ -17,12 +17,16 @@ atomics on 64-bit words tag << 32 | low):
            // S < tag < b + laps) is read from memory at once; past the bound
            every slot still missing is read from memory; then store the
            group's maximum tagged b to the group's done slot
-  exit     exit counter; the last workgroup advances the epoch by laps
+  count    (a tile once it holds its group's maximum, a head after its
+           store) exit counter; the last workgroup advances the epoch by laps
+  encode   a tile then encodes from its registers (a few steps) and exits
 
 A workgroup runs only while it holds one of R resident places; a place frees
 when a workgroup exits, and the next workgroup in launch order starts. Every
 run must end (no workgroup waits forever) with every head and tile holding
-its group's true maximum and the epoch advanced by laps, call after call.
+its group's true maximum and the epoch advanced by laps, call after call,
+and no tagged word touched after the epoch advanced (the last workgroup to
+count out may clear them all when the epoch wraps).
 """
 
 from __future__ import annotations
@@ -34,14 +38,45 @@ import pytest
 LOW = 0xFFFFFFFF
 
 
+class _TaggedWords(list):
+    """Tagged workspace words: every access checks that the call's epoch has
+    not advanced yet."""
+
+    def __init__(self, ws, n):
+        super().__init__([0] * n)
+        self._ws = ws
+
+    def __getitem__(self, i):
+        self._ws.check_live()
+        return super().__getitem__(i)
+
+    def __setitem__(self, i, v):
+        self._ws.check_live()
+        super().__setitem__(i, v)
+
+
 class Workspace:
     def __init__(self, S, ngroups):
-        self.slot = [0] * S
-        self.done = [0] * ngroups
+        self.slot = _TaggedWords(self, S)
+        self.done = _TaggedWords(self, ngroups)
         self.epoch = 0
         self.exits = 0
+        self.G = 0          # workgroups of the current call
+        self.laps = 0       # its laps over the slots
+        self.advanced = False  # the current call's epoch has advanced
         self.tile_reads = 0   # tiles whose maximum a head read from memory
         self.group_reads = 0  # groups whose maximum a tile read from memory
+
+    def check_live(self):
+        assert not self.advanced, "a tagged word was touched after the epoch advanced"
+
+    def count_out(self, e):
+        # the last workgroup advances the epoch past the call's tags
+        self.exits += 1
+        if self.exits == self.G:
+            self.epoch = e + self.laps
+            self.exits = 0
+            self.advanced = True
 
 
 def plan(groups):
@@ -74,6 +109,10 @@ def tile_wg(ws, i, g, u, S, tile_max, group_max, load_steps, wait_polls):
             yield
         ws.group_reads += 1
         amax = group_max[g]
+    ws.count_out(e)
+    yield
+    for _ in range(load_steps):  # the encode touches no workspace word
+        yield
     return amax
 
 
@@ -109,6 +148,8 @@ def head_wg(ws, i, g, n, S, laps, tile_max, load_steps, lead_polls):
         m = max(m, tile_max[g][u])
     ws.done[g] = b << 32 | m
     yield
+    ws.count_out(e)
+    yield
     return m
 
 
@@ -120,7 +161,9 @@ def run(groups, S, R, seed, lead_polls=10_000, wait_polls=1_000_000, load_steps=
     laps = -(-G // S)
     ws = Workspace(S, len(groups))
     ws.epoch = epoch0
+    ws.G, ws.laps = G, laps
     for call in range(calls):
+        ws.advanced = False
         tile_max = [[rng.randrange(0, 1 << 30) for _ in range(n)] for n in groups]
         group_max = [max(t) if t else 0 for t in tile_max]
         e0 = ws.epoch
@@ -141,10 +184,6 @@ def run(groups, S, R, seed, lead_polls=10_000, wait_polls=1_000_000, load_steps=
             except StopIteration as stop:
                 results[i] = stop.value
                 del running[i]
-                ws.exits += 1
-                if ws.exits == G:  # the last workgroup advances the epoch past the call's tags
-                    ws.epoch = e0 + laps
-                    ws.exits = 0
             steps += 1
             assert steps < step_limit, f"no progress: groups={groups} S={S} R={R} seed={seed} call={call}"
         for i, (kind, g, u) in enumerate(order):
